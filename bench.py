@@ -1,0 +1,190 @@
+"""Benchmark of the GDN hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+
+A timed step is one chunked varlen prefill of the 4 x 4096-token workload
+(h_k = 16, h_v = 32, d = 128, bf16 q/k/v, fp32 g/beta/state/output, width-4
+conv + SiLU + q/k L2 norm, final recurrent and conv states written), inputs
+resident in HBM.  `value` is prefill tokens/s.  The decode half of the metric
+(256 slots x 32 value heads, d = 128, 512 MiB fp32 state pool updated in
+place, 100 consecutive steps) is timed separately and reported under
+"decode".  One JSON line is printed.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_F16_PEAK_TFLOPS = 2500.0  # dense fp16/bf16 matrix cores
+PREFILL_KERNEL = "prefill_kernel"
+DECODE_KERNEL = "decode_kernel"
+
+
+def prefill_algorithmic(T, N, h_k, h_v, d, in_bytes=2, out_bytes=4, chunk=64):
+    """Bytes: each input read once, outputs and final states written once.
+    Flops per (token, value head): (4/G + 6) * chunk * d + 6 * d^2."""
+    G = h_v // h_k
+    C = 2 * h_k * d + h_v * d
+    per_token = (2 * h_k * d + h_v * d) * in_bytes + 2 * h_v * 4 + h_v * d * out_bytes
+    bytes_ = T * per_token + N * h_v * d * d * 4 + C * 4 * in_bytes + (N + 1) * 4 + N * C * 3 * in_bytes
+    flops = T * h_v * ((4.0 / G + 6.0) * chunk * d + 6.0 * d * d)
+    return bytes_, flops
+
+
+def decode_algorithmic(N, h_k, h_v, d, in_bytes=2, out_bytes=4):
+    """State read + write, q/k/v/g/beta read, o written; ~ (6 d^2 + O(d)) flops per (slot, head)."""
+    state = N * h_v * d * d * 4
+    bytes_ = 2 * state + N * (2 * h_k * d + h_v * d) * in_bytes + N * h_v * 2 * 4 + N * h_v * d * out_bytes
+    flops = N * h_v * 7.0 * d * d
+    return bytes_, flops
+
+
+def cpu_baseline(x, nthreads):
+    """The fp64 oracle on the same seeded inputs (all sequences, all heads), wall clock."""
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import oracle
+    oracle.build(force=False)
+    g = x.geom
+    dims = oracle.Dims(g.h_k, g.h_v, g.d_k, g.d_v, conv_width=4)
+    t0 = time.perf_counter()
+    oracle.prefill(dims, x.cu_seqlens, x.q, x.k, x.v, x.g, x.beta, x.conv_w, nthreads=nthreads)
+    dt = time.perf_counter() - t0
+    return {"value": x.total_tokens / dt, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"whole workload ({x.num_seqs} x {x.total_tokens // x.num_seqs} tokens, all heads), "
+                      f"fp64, one run of {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=100)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the recurrence shards by heads or sequences with no exchange; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gateddeltanet_chunked_delta_amd as gdn
+    from gateddeltanet_chunked_delta_amd.inputs import Geometry, decode_inputs, prefill_inputs, state_pool
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    geom = Geometry(16, 32, 128, 128)
+    B, Tseq = 4, 4096
+    print(f"[bench] generating prefill inputs {B}x{Tseq} h_k=16 h_v=32 d=128 bf16", file=sys.stderr, flush=True)
+    x = prefill_inputs(1, [Tseq] * B, geom, "bf16")
+    bf = torch.bfloat16
+    q = torch.from_numpy(x.q).to(dev, bf)
+    k = torch.from_numpy(x.k).to(dev, bf)
+    v = torch.from_numpy(x.v).to(dev, bf)
+    g = torch.from_numpy(x.g).to(dev)
+    beta = torch.from_numpy(x.beta).to(dev)
+    w = torch.from_numpy(x.conv_w).to(dev, bf)
+    cu = torch.from_numpy(x.cu_seqlens.astype(np.int32)).to(dev)
+    T = x.total_tokens
+    o = torch.empty((T, 32, 128), dtype=torch.float32, device=dev)
+    fs = torch.empty((B, 32, 128, 128), dtype=torch.float32, device=dev)
+    cso = torch.empty((B, geom.channels, 3), dtype=bf, device=dev)
+    ws = torch.empty(4096, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        gdn.gdn_prefill_varlen(q, k, v, g, beta, cu, conv_weight=w, out=o, final_state_out=fs,
+                               conv_state_out=cso, workspace=ws, validate=False)
+
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    call_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+    ms_step = wall * 1e3 / args.steps
+    avg_call_s = float(np.mean(call_ms)) / 1e3
+    pbytes, pflops = prefill_algorithmic(T, B, 16, 32, 128)
+    print(f"[bench] prefill: {ms_step:.3f} ms/step wall, {avg_call_s * 1e3:.3f} ms/call (events)",
+          file=sys.stderr, flush=True)
+
+    result = {
+        "metric": "GDN prefill tokens/s (MFMA util); decode state-update HBM GB/s vs peak",
+        "value": T / (wall / args.steps),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "chunked varlen prefill, 4 sequences x 4096 tokens, h_k=16, h_v=32, "
+                               "d_k=d_v=128, bf16 q/k/v, fp32 g/beta/state/o, conv4+SiLU+L2, chunk 64",
+                   "num_seqs": B, "seq_len": Tseq, "h_k": 16, "h_v": 32, "d": 128},
+        "roofline": {"bound": "hbm", "achieved": pbytes / avg_call_s / 1e9, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": pbytes / avg_call_s / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": PREFILL_KERNEL, "algorithmic_bytes": pbytes, "avg_call_us": avg_call_s * 1e6},
+        "mfma_util": pflops / avg_call_s / (MFMA_F16_PEAK_TFLOPS * 1e12),
+        "algorithmic_tflops": pflops / avg_call_s / 1e12,
+    }
+
+    if not args.no_decode:
+        N = 256
+        print("[bench] decode: 256 slots, 512 MiB pool", file=sys.stderr, flush=True)
+        pool = torch.from_numpy(state_pool(3, N, geom)).to(dev)
+        nsteps = args.decode_steps
+        dins = []
+        for s in range(nsteps):
+            d = decode_inputs(3, s, N, geom, "bf16")
+            dins.append(tuple(torch.from_numpy(a).to(dev, dt) for a, dt in
+                              ((d.q, bf), (d.k, bf), (d.v, bf), (d.g, torch.float32), (d.beta, torch.float32))))
+        od = torch.empty((N, 32, 128), dtype=torch.float32, device=dev)
+        for s in range(min(5, nsteps)):
+            gdn.gdn_decode_step(*dins[s], pool, out=od, validate=False)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for s in range(nsteps):
+            gdn.gdn_decode_step(*dins[s], pool, out=od, validate=False)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / nsteps
+        dbytes, dflops = decode_algorithmic(N, 16, 32, 128)
+        gbs = dbytes / (us * 1e-6) / 1e9
+        result["decode"] = {"workload": "decode step, 256 slots x 32 value heads (16 key heads), d=128, "
+                                        "bf16 q/k/v, fp32 512 MiB state pool in place",
+                            "steps": nsteps, "us_per_step": us, "GB/s": gbs,
+                            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                         "frac": gbs / HBM_PEAK_GBS, "traffic": None, "kernel": DECODE_KERNEL,
+                                         "algorithmic_bytes": dbytes}}
+        print(f"[bench] decode: {us:.1f} us/step, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
+
+    if not args.no_cpu_baseline:
+        n = len(os.sched_getaffinity(0))
+        n = min(n, int(os.environ.get("OMP_NUM_THREADS", n)))
+        print(f"[bench] cpu baseline: fp64 oracle on {n} threads", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(x, n)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

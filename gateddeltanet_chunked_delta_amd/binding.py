@@ -1,0 +1,260 @@
+"""ctypes binding of libgdn.so: argument checks and marshalling only.
+
+Every step of the computation runs in the HIP kernels behind the C ABI
+(include/gdn.h).  PyTorch supplies device memory and the current stream.
+There is no fallback: if libgdn.so is missing or a call fails, this module
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgdn.so")
+
+GDN_F32, GDN_BF16 = 0, 1
+_STATUS = {0: "GDN_OK", -1: "GDN_ERR_NULL", -2: "GDN_ERR_SHAPE", -3: "GDN_ERR_DTYPE",
+           -4: "GDN_ERR_UNSUPPORTED", -5: "GDN_ERR_WORKSPACE", -6: "GDN_ERR_HIP", -7: "GDN_ERR_ALIAS"}
+EXPORTED = ("gdn_prefill_workspace_bytes", "gdn_prefill_varlen", "gdn_decode_step", "gdn_status_string")
+
+
+class GdnProblem(ctypes.Structure):
+    """Mirror of gdn_problem in include/gdn.h."""
+    _fields_ = [("num_seqs", ctypes.c_int32), ("total_tokens", ctypes.c_int64),
+                ("h_k", ctypes.c_int32), ("h_v", ctypes.c_int32),
+                ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("qkv_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("qk_l2norm", ctypes.c_int32),
+                ("l2_eps", ctypes.c_float), ("conv_width", ctypes.c_int32)]
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {_STATUS.get(status, status)} ({status_string(status)})")
+        self.status = status
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Loads libgdn.so (built in-tree by build.py); raises if it is absent."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m gateddeltanet_chunked_delta_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, c64 = ctypes.c_void_p, ctypes.c_size_t
+        lib.gdn_prefill_workspace_bytes.argtypes = [ctypes.POINTER(GdnProblem)]
+        lib.gdn_prefill_workspace_bytes.restype = c64
+        lib.gdn_prefill_varlen.argtypes = [ctypes.POINTER(GdnProblem)] + [vp] * 14 + [c64, vp]
+        lib.gdn_prefill_varlen.restype = ctypes.c_int
+        lib.gdn_decode_step.argtypes = [ctypes.POINTER(GdnProblem)] + [vp] * 11 + [vp]
+        lib.gdn_decode_step.restype = ctypes.c_int
+        lib.gdn_status_string.argtypes = [ctypes.c_int]
+        lib.gdn_status_string.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return load().gdn_status_string(int(status)).decode()
+
+
+def _dtype_code(dt: torch.dtype, what: str) -> int:
+    if dt == torch.bfloat16:
+        return GDN_BF16
+    if dt == torch.float32:
+        return GDN_F32
+    raise ValueError(f"{what}: dtype {dt} not supported (bfloat16 or float32)")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t, name, shape, dtype, device):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)} != expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype} != expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def make_problem(num_seqs, total_tokens, h_k, h_v, d_k, d_v, qkv_dtype, out_dtype, scale=None,
+                 qk_l2norm=True, l2_eps=1e-6, conv_width=4) -> GdnProblem:
+    return GdnProblem(int(num_seqs), int(total_tokens), int(h_k), int(h_v), int(d_k), int(d_v),
+                      int(qkv_dtype), int(out_dtype), float(0.0 if scale is None else scale),
+                      int(bool(qk_l2norm)), float(l2_eps), int(conv_width))
+
+
+def gdn_prefill_workspace_bytes(problem: GdnProblem) -> int:
+    return int(load().gdn_prefill_workspace_bytes(ctypes.byref(problem)))
+
+
+def _validate_cu(cu_host: torch.Tensor, T: int):
+    if cu_host.numel() < 1 or int(cu_host[0]) != 0:
+        raise ValueError("cu_seqlens[0] must be 0")
+    if int(cu_host[-1]) != T:
+        raise ValueError(f"cu_seqlens[-1] = {int(cu_host[-1])} != total tokens {T}")
+    if bool((cu_host[1:] < cu_host[:-1]).any()):
+        raise ValueError("cu_seqlens must be non-decreasing")
+
+
+def gdn_prefill_varlen(q, k, v, g, beta, cu_seqlens=None, *, conv_weight=None, conv_bias=None,
+                       conv_state=None, initial_state=None, output_final_state=True,
+                       output_conv_state=True, use_qk_l2norm=True, scale=None, l2_eps=1e-6,
+                       out_dtype=torch.float32, validate=True, out=None, final_state_out=None,
+                       conv_state_out=None, workspace=None, stream=None):
+    """Chunked varlen prefill (C ABI ``gdn_prefill_varlen``).
+
+    q, k: ``[T, h_k, d_k]`` (or ``[B, T, h_k, d_k]`` with equal lengths and no
+    cu_seqlens); v: ``[T, h_v, d_v]``; g, beta: ``[T, h_v]`` fp32; cu_seqlens:
+    int32 ``[N+1]`` on the device (or a CPU tensor / list, copied).  Returns
+    ``(o, final_state or None, conv_state_out or None)``.
+    """
+    if q.dim() == 4:
+        if cu_seqlens is not None:
+            raise ValueError("with cu_seqlens, q/k/v must be packed [T, H, D] (no batch dimension)")
+        B, Tb = q.shape[0], q.shape[1]
+        q, k, v = q.reshape(B * Tb, *q.shape[2:]), k.reshape(B * Tb, *k.shape[2:]), v.reshape(B * Tb, *v.shape[2:])
+        g, beta = g.reshape(B * Tb, -1), beta.reshape(B * Tb, -1)
+        cu_seqlens = torch.arange(0, (B + 1) * Tb, Tb, dtype=torch.int32)
+    if q.dim() != 3:
+        raise ValueError("q must be [T, h_k, d_k] (time-first, packed)")
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on the GPU")
+    T, h_k, d_k = q.shape
+    if v.dim() != 3 or v.shape[0] != T:
+        raise ValueError("v must be [T, h_v, d_v]")
+    h_v, d_v = v.shape[1], v.shape[2]
+    qdt = q.dtype
+    qcode = _dtype_code(qdt, "q")
+    ocode = _dtype_code(out_dtype, "out_dtype")
+    _check(q, "q", (T, h_k, d_k), qdt, dev)
+    _check(k, "k", (T, h_k, d_k), qdt, dev)
+    _check(v, "v", (T, h_v, d_v), qdt, dev)
+    _check(g, "g", (T, h_v), torch.float32, dev)
+    _check(beta, "beta", (T, h_v), torch.float32, dev)
+    if cu_seqlens is None:
+        cu_seqlens = torch.tensor([0, T], dtype=torch.int32)
+    if not isinstance(cu_seqlens, torch.Tensor):
+        cu_seqlens = torch.tensor(list(cu_seqlens), dtype=torch.int32)
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+        raise ValueError("cu_seqlens must be a 1-D int32 tensor")
+    if validate:
+        _validate_cu(cu_seqlens.cpu(), T)
+    if cu_seqlens.device != dev:
+        cu_seqlens = cu_seqlens.to(dev)
+    cu_seqlens = cu_seqlens.contiguous()
+    N = cu_seqlens.numel() - 1
+    C = 2 * h_k * d_k + h_v * d_v
+    conv_width = 4 if conv_weight is not None else 0
+    if conv_weight is not None:
+        _check(conv_weight, "conv_weight", (C, 4), qdt, dev)
+        _check(conv_bias, "conv_bias", (C,), qdt, dev)
+        _check(conv_state, "conv_state", (N, C, 3), qdt, dev)
+    elif conv_bias is not None or conv_state is not None:
+        raise ValueError("conv_bias/conv_state given without conv_weight")
+    _check(initial_state, "initial_state", (N, h_v, d_k, d_v), torch.float32, dev)
+
+    o = out if out is not None else torch.empty((T, h_v, d_v), dtype=out_dtype, device=dev)
+    _check(o, "out", (T, h_v, d_v), out_dtype, dev)
+    fs = None
+    if output_final_state:
+        fs = final_state_out if final_state_out is not None else torch.empty((N, h_v, d_k, d_v), dtype=torch.float32, device=dev)
+        _check(fs, "final_state_out", (N, h_v, d_k, d_v), torch.float32, dev)
+    cso = None
+    if output_conv_state and conv_width:
+        cso = conv_state_out if conv_state_out is not None else torch.empty((N, C, 3), dtype=qdt, device=dev)
+        _check(cso, "conv_state_out", (N, C, 3), qdt, dev)
+    prob = make_problem(N, T, h_k, h_v, d_k, d_v, qcode, ocode, scale, use_qk_l2norm, l2_eps, conv_width)
+    ws_bytes = gdn_prefill_workspace_bytes(prob)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    elif workspace.numel() < ws_bytes:
+        raise ValueError("workspace too small")
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    st = load().gdn_prefill_varlen(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                   _ptr(cu_seqlens), _ptr(conv_weight), _ptr(conv_bias), _ptr(conv_state),
+                                   _ptr(cso), _ptr(initial_state), _ptr(o), _ptr(fs), _ptr(workspace),
+                                   ctypes.c_size_t(workspace.numel()), ctypes.c_void_p(stream))
+    if st != 0:
+        raise GdnError(st, "gdn_prefill_varlen")
+    return o, fs, cso
+
+
+def gdn_decode_step(q, k, v, g, beta, state_pool, *, state_indices=None, conv_weight=None,
+                    conv_bias=None, conv_state_pool=None, use_qk_l2norm=True, scale=None, l2_eps=1e-6,
+                    out_dtype=torch.float32, validate=True, out=None, stream=None):
+    """One decode step over a state pool, in place (C ABI ``gdn_decode_step``).
+
+    q, k: ``[N, h_k, d_k]``; v: ``[N, h_v, d_v]``; g, beta: ``[N, h_v]`` fp32;
+    state_pool: fp32 ``[P, h_v, d_k, d_v]`` (updated in place); state_indices:
+    int32 ``[N]`` or None (slot n uses entry n); -1 skips a slot.  Returns o.
+    """
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, v must be [N, H, D]")
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on the GPU")
+    N, h_k, d_k = q.shape
+    h_v, d_v = v.shape[1], v.shape[2]
+    qdt = q.dtype
+    qcode = _dtype_code(qdt, "q")
+    ocode = _dtype_code(out_dtype, "out_dtype")
+    _check(q, "q", (N, h_k, d_k), qdt, dev)
+    _check(k, "k", (N, h_k, d_k), qdt, dev)
+    _check(v, "v", (N, h_v, d_v), qdt, dev)
+    _check(g, "g", (N, h_v), torch.float32, dev)
+    _check(beta, "beta", (N, h_v), torch.float32, dev)
+    if state_pool.dim() != 4:
+        raise ValueError("state_pool must be [P, h_v, d_k, d_v]")
+    P = state_pool.shape[0]
+    _check(state_pool, "state_pool", (P, h_v, d_k, d_v), torch.float32, dev)
+    C = 2 * h_k * d_k + h_v * d_v
+    conv_width = 4 if conv_weight is not None else 0
+    if conv_weight is not None:
+        _check(conv_weight, "conv_weight", (C, 4), qdt, dev)
+        _check(conv_bias, "conv_bias", (C,), qdt, dev)
+        if conv_state_pool is None:
+            raise ValueError("conv_weight needs conv_state_pool")
+        if conv_state_pool.dim() != 3:
+            raise ValueError("conv_state_pool must be [P, C, 3]")
+        _check(conv_state_pool, "conv_state_pool", (conv_state_pool.shape[0], C, 3), qdt, dev)
+    if state_indices is not None:
+        _check(state_indices, "state_indices", (N,), torch.int32, dev)
+        if validate and N:
+            idx = state_indices.cpu()
+            used = idx[idx >= 0]
+            if bool((idx < -1).any()) or bool((used >= P).any()):
+                raise ValueError("state_indices out of range")
+            if conv_width and bool((used >= conv_state_pool.shape[0]).any()):
+                raise ValueError("state_indices out of range of conv_state_pool")
+            if used.numel() != torch.unique(used).numel():
+                raise ValueError("state_indices must be distinct")
+    elif validate and (N > P or (conv_width and N > conv_state_pool.shape[0])):
+        raise ValueError("without state_indices the pools need at least N entries")
+    o = out if out is not None else torch.empty((N, h_v, d_v), dtype=out_dtype, device=dev)
+    _check(o, "out", (N, h_v, d_v), out_dtype, dev)
+    prob = make_problem(N, N, h_k, h_v, d_k, d_v, qcode, ocode, scale, use_qk_l2norm, l2_eps, conv_width)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    st = load().gdn_decode_step(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                _ptr(conv_weight), _ptr(conv_bias), _ptr(conv_state_pool), _ptr(state_pool),
+                                _ptr(state_indices), _ptr(o), ctypes.c_void_p(stream))
+    if st != 0:
+        raise GdnError(st, "gdn_decode_step")
+    return o

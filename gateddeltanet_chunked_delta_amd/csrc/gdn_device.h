@@ -1,0 +1,151 @@
+// Device-side helpers for the gfx950 GDN kernels: element conversion,
+// 16-byte vector loads and the 16x16x32 matrix-core step.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+// bf16 is carried as its uint16_t bit pattern.
+typedef uint16_t bf16_t;
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round to nearest even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<bf16_t>(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+    static constexpr int kVec = 4;  // elements per 16-byte load
+    __device__ __forceinline__ static float get(const float* p) { return *p; }
+    __device__ __forceinline__ static void load16(const float* p, float* out) {
+        float4 x = *reinterpret_cast<const float4*>(p);
+        out[0] = x.x; out[1] = x.y; out[2] = x.z; out[3] = x.w;
+    }
+    __device__ __forceinline__ static void put(float* p, float x) { *p = x; }
+};
+template <> struct Elem<bf16_t> {
+    static constexpr int kVec = 8;
+    __device__ __forceinline__ static float get(const bf16_t* p) { return bf16_to_f32(*p); }
+    __device__ __forceinline__ static void load16(const bf16_t* p, float* out) {
+        uint4 x = *reinterpret_cast<const uint4*>(p);
+        uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            out[2 * i] = __uint_as_float(w[i] << 16);
+            out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+    __device__ __forceinline__ static void put(bf16_t* p, float x) { *p = f32_to_bf16(x); }
+};
+
+// Matrix-core lane layout (16x16 output tile, K-step 32): lane l supplies
+// A[l%16][8*(l/16) + e] and B[8*(l/16) + e][l%16], e = 0..7, and owns
+// D[4*(l/16) + i][l%16], i = 0..3.
+
+__device__ __forceinline__ float silu(float y) { return y / (1.0f + expf(-y)); }
+
+// ---- split-fp16 operands: x ~= hi + lo * 2^-11, hi = fp16(x), lo = fp16((x - hi) 2^11) ----
+// Scaling the residual by 2^11 keeps lo out of fp16's subnormal range (whose
+// fixed 2^-24 grid would cap the precision of small operands), so each operand
+// keeps about 22 significant bits for |x| >= 2^-14.  A product takes three
+// fp16 matrix-core steps: hi*hi into one accumulator, lo*hi + hi*lo into a
+// second one that is scaled by 2^-11 when the sum is complete (lo*lo dropped).
+constexpr float kLoScale = 2048.0f;
+constexpr float kLoUnscale = 1.0f / 2048.0f;
+
+struct SFrag {
+    half8_t hi, lo;
+};
+
+// hi is x rounded to fp16's 11 significant bits (ties to even) in integer
+// arithmetic, so it is exactly representable in fp16 and the value stored as
+// hi is the value the residual is taken from, whatever instruction the
+// compiler picks for the conversion (converters that break ties differently
+// would otherwise leave the pair one fp16 ulp off on exact ties).  Values
+// below fp16's normal range (2^-14) go entirely into lo.
+__device__ __forceinline__ void split1(float x, _Float16& hi, _Float16& lo) {
+    const uint32_t u = __float_as_uint(x);
+    float h = __uint_as_float((u + 0x0FFFu + ((u >> 13) & 1u)) & 0xFFFFE000u);
+    if (fabsf(x) < 6.103515625e-05f) h = 0.0f;
+    hi = static_cast<_Float16>(h);
+    lo = static_cast<_Float16>((x - h) * kLoScale);
+}
+
+__device__ __forceinline__ SFrag split8(const float (&x)[8]) {
+    SFrag f;
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+        _Float16 h, l;
+        split1(x[e], h, l);
+        f.hi[e] = h;
+        f.lo[e] = l;
+    }
+    return f;
+}
+
+// Split accumulation: hh += A.hi B.hi, xx += A.lo B.hi + A.hi B.lo.
+__device__ __forceinline__ void mma3(float4_t& hh, float4_t& xx, const SFrag& a, const SFrag& b) {
+    xx = __builtin_amdgcn_mfma_f32_16x16x32_f16(a.lo, b.hi, xx, 0, 0, 0);
+    xx = __builtin_amdgcn_mfma_f32_16x16x32_f16(a.hi, b.lo, xx, 0, 0, 0);
+    hh = __builtin_amdgcn_mfma_f32_16x16x32_f16(a.hi, b.hi, hh, 0, 0, 0);
+}
+
+// The finished product: hh + xx 2^-11.
+__device__ __forceinline__ float4_t combine(const float4_t& hh, const float4_t& xx) {
+    float4_t r;
+#pragma unroll
+    for (int i = 0; i < 4; i++) r[i] = hh[i] + xx[i] * kLoUnscale;
+    return r;
+}
+
+constexpr float4_t kZero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+
+// Fragment from row-major hi/lo LDS matrices (8 consecutive elements along K).
+__device__ __forceinline__ SFrag lds_sfrag(const _Float16* hi, const _Float16* lo, int pitch, int row, int k) {
+    SFrag f;
+    f.hi = *reinterpret_cast<const half8_t*>(hi + row * pitch + k);
+    f.lo = *reinterpret_cast<const half8_t*>(lo + row * pitch + k);
+    return f;
+}
+
+// Fragment whose K index runs down the rows of row-major hi/lo LDS matrices:
+// element e is M[k + e][col].
+__device__ __forceinline__ SFrag lds_sfrag_t(const _Float16* hi, const _Float16* lo, int pitch, int k, int col) {
+    SFrag f;
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+        f.hi[e] = hi[(k + e) * pitch + col];
+        f.lo[e] = lo[(k + e) * pitch + col];
+    }
+    return f;
+}
+
+// Operand fragment from two accumulator tiles that hold rows [32s, 32s+16) and
+// [32s+16, 32s+32) of a matrix X (lane l owns X[4*(l/16) + i][l%16] of each):
+// returns x[e] = X[32s + 8*(l/16) + e][l%16], the K-major operand layout.
+// permlane32_swap exchanges the upper half-wave of its first operand with the
+// lower half-wave of its second; permlane16_swap exchanges the odd 16-lane rows
+// of the first with the even rows of the second.
+__device__ __forceinline__ void acc_to_operand(const float4_t& t0, const float4_t& t1, float (&x)[8]) {
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(t0[e]), __float_as_uint(t1[e]), false, false);
+        const auto t = __builtin_amdgcn_permlane16_swap(s[0], s[1], false, false);
+        x[e] = __uint_as_float(t[0]);
+        x[e + 4] = __uint_as_float(t[1]);
+    }
+}
+
+}  // namespace gdn

@@ -1,0 +1,64 @@
+// Internal interface between the C-ABI front end (gdn_api.cpp) and the HIP
+// kernels.  Not installed; the public surface is include/gdn.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+// Everything the fused chunked-prefill kernel needs, passed by value.
+struct PrefillParams {
+    const void* q;              // [T][h_k][d_k]
+    const void* k;              // [T][h_k][d_k]
+    const void* v;              // [T][h_v][d_v]
+    const float* g;             // [T][h_v]
+    const float* beta;          // [T][h_v]
+    const int32_t* cu_seqlens;  // [N+1]
+    const void* conv_w;         // [C][4] or null
+    const void* conv_b;         // [C] or null
+    const void* conv_state_in;  // [N][C][3] or null
+    void* conv_state_out;       // [N][C][3] or null
+    const float* initial_state; // [N][h_v][d_k][d_v] or null
+    void* o;                    // [T][h_v][d_v]
+    float* final_state;         // [N][h_v][d_k][d_v] or null
+    const int32_t* order;       // [N] dispatch order (workspace)
+    int32_t num_seqs;
+    int32_t h_k, h_v;
+    int32_t conv_width;         // 0 or 4
+    int32_t qk_l2norm;
+    float l2_eps;
+    float scale;
+};
+
+struct DecodeParams {
+    const void* q;              // [N][h_k][d_k]
+    const void* k;              // [N][h_k][d_k]
+    const void* v;              // [N][h_v][d_v]
+    const float* g;             // [N][h_v]
+    const float* beta;          // [N][h_v]
+    const void* conv_w;         // [C][4] or null
+    const void* conv_b;         // [C] or null
+    void* conv_state_pool;      // [P][C][3] or null
+    float* state_pool;          // [P][h_v][d_k][d_v]
+    const int32_t* state_indices; // [N] or null
+    void* o;                    // [N][h_v][d_v]
+    int32_t num_seqs;
+    int32_t h_k, h_v;
+    int32_t conv_width;
+    int32_t qk_l2norm;
+    float l2_eps;
+    float scale;
+};
+
+// Launchers return hipSuccess or the launch error.  dtype codes follow gdn_dtype.
+hipError_t launch_prefill(const PrefillParams& p, int d_k, int d_v, int qkv_dtype, int out_dtype,
+                          hipStream_t stream);
+int prefill_supported(int d_k, int d_v, int qkv_dtype, int out_dtype);
+
+hipError_t launch_decode(const DecodeParams& p, int d_k, int d_v, int qkv_dtype, int out_dtype,
+                         hipStream_t stream);
+int decode_supported(int d_k, int d_v, int qkv_dtype, int out_dtype);
+
+}  // namespace gdn

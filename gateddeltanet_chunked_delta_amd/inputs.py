@@ -38,9 +38,14 @@ class Geometry:
 def bf16_round(x: np.ndarray) -> np.ndarray:
     """Round fp32 values to the nearest bf16 (ties to even); returns fp32."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    return rounded.astype(np.uint32).view(np.float32).reshape(x.shape)
+    if not np.all(np.isfinite(x)):
+        raise ValueError("bf16_round expects finite values")
+    u = x.view(np.uint32).copy()
+    lsb = (u >> 16) & np.uint32(1)
+    u += np.uint32(0x7FFF)  # no wrap: finite fp32 bit patterns stay below 0xFF800000
+    u += lsb
+    u &= np.uint32(0xFFFF0000)
+    return u.view(np.float32).reshape(x.shape)
 
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:

@@ -1,0 +1,173 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) GatedDeltaNet gated delta-rule library.
+ *
+ * Operation.  Per value head, the gated delta rule ("Qwen3.5-27B GPTQ Garbage
+ * Inference -- Root Cause Analysis", section "Why abliteration failed on
+ * Qwen3.5", item 3, with the delta read as the prediction error of the
+ * decayed state):
+ *     S_t = e^{g_t} S_{t-1} + beta_t (v_t - e^{g_t} S_{t-1} k_t) k_t^T
+ *     o_t = scale * S_t q_t              (scale = d_k^{-1/2} by default)
+ * where S is d_v x d_k.  The STORED state is H = S^T, fp32, laid out
+ * [seq][h_v][d_k][d_v] with d_v contiguous ("[Feature] Add batch invariance
+ * support to GDN_ATTN backend", review comment part "1. Recurrent state in
+ * fp32": shape (batch, v_heads, k_head_dim, v_head_dim), fp32).
+ *
+ * Prologue (same page, part "3. The chunked delta-rule scan itself", (a)):
+ * with conv_width = 4, every q|k|v channel c goes through a causal depthwise
+ * convolution y_t[c] = b[c] + sum_{j=0..3} w[c][j] x_{t-3+j}[c] (w[c][3] hits
+ * the newest token) followed by SiLU; history before a sequence start is the
+ * given conv state (3 raw inputs per channel, oldest first) or zero, never
+ * the previous packed sequence.  Then, with qk_l2norm = 1, q and k are
+ * normalised per head: x / sqrt(sum x^2 + l2_eps).  Channel order is q | k | v,
+ * each head-major: C = 2 h_k d_k + h_v d_v channels.
+ *
+ * GQA: value head h reads key head h / (h_v / h_k).
+ *
+ * Layout.  One layout only: time-first and packed ("Qwen3.5 FLA linear
+ * attention tensor format mismatch", section "Root Cause": [B, T, H, D], not
+ * head-first).  Sequences are concatenated and delimited by cu_seqlens, one
+ * entry per sequence start plus the total ("[Feature] Add batch invariance
+ * support to GDN_ATTN backend", commit messages: cu_seqlens = [0, len] per
+ * sequence).  There is no batch dimension and no layout heuristic.
+ *
+ * Conventions.
+ *  - All tensor pointers are DEVICE pointers, row-major, contiguous.  The
+ *    gdn_problem struct is HOST memory and is read during the call only.
+ *  - The caller owns every buffer.  The library never allocates, frees or
+ *    synchronises; work is enqueued on `stream` (a hipStream_t passed as
+ *    void*, NULL = the null stream) and the call returns without waiting.
+ *  - Argument errors return a negative status before any HIP call and leave
+ *    every output untouched.  A failed launch returns GDN_ERR_HIP.
+ *  - Device-side contents are preconditions, not checked: cu_seqlens
+ *    non-decreasing with cu_seqlens[0] = 0 and cu_seqlens[N] = total_tokens;
+ *    state indices in range and distinct (except -1).  NaN/Inf propagate.
+ *  - Batch invariance: a sequence's outputs and final states are bit-identical
+ *    whatever other sequences share the call; kernel choice depends only on
+ *    (d_k, d_v, qkv_dtype, out_dtype), never on N, lengths or totals.
+ *  - Exponentials are only taken of non-positive decay differences when
+ *    g <= 0 (a log decay); positive g is accepted with no overflow guarantee.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gdn_dtype {
+    GDN_F32 = 0,  /* IEEE fp32 */
+    GDN_BF16 = 1  /* bfloat16 (8-bit exponent, 7-bit mantissa) */
+} gdn_dtype;
+
+typedef enum gdn_status {
+    GDN_OK = 0,
+    GDN_ERR_NULL = -1,        /* a required pointer is NULL */
+    GDN_ERR_SHAPE = -2,       /* sizes inconsistent or out of range */
+    GDN_ERR_DTYPE = -3,       /* dtype value not in gdn_dtype */
+    GDN_ERR_UNSUPPORTED = -4, /* valid request this build has no kernel for */
+    GDN_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than required */
+    GDN_ERR_HIP = -6,         /* a kernel launch failed */
+    GDN_ERR_ALIAS = -7        /* an output overlaps a buffer it must not */
+} gdn_status;
+
+typedef struct gdn_problem {
+    int32_t num_seqs;      /* N >= 0: sequences (prefill) or slots (decode) */
+    int64_t total_tokens;  /* prefill: cu_seqlens[N]; decode: must equal N */
+    int32_t h_k, h_v;      /* key and value heads, h_k >= 1, h_v % h_k == 0 */
+    int32_t d_k, d_v;      /* head dims; this build: 64 or 128 each */
+    int32_t qkv_dtype;     /* gdn_dtype of q, k, v, conv weight, bias, conv states */
+    int32_t out_dtype;     /* gdn_dtype of o */
+    float scale;           /* multiplier of S q; 0 => d_k^{-1/2} */
+    int32_t qk_l2norm;     /* 1 => L2-normalise q and k per head; 0 => no */
+    float l2_eps;          /* eps of the L2 norm; 0 => 1e-6 */
+    int32_t conv_width;    /* 0 => no conv prologue (no SiLU); 4 => conv + SiLU */
+} gdn_problem;
+
+/* Bytes of device workspace gdn_prefill_varlen needs for this problem (the
+ * per-call dispatch map: an ordering of the sequences).  Returns 0 for a NULL
+ * problem.  Depends on num_seqs only. */
+size_t gdn_prefill_workspace_bytes(const gdn_problem* p);
+
+/*
+ * Chunked prefill over packed variable-length sequences.
+ *
+ * The recurrence is evaluated in chunks of 64 tokens aligned to each
+ * sequence start, with the recurrent state carried across chunks in fp32
+ * ("[Feature] Add batch invariance support to GDN_ATTN backend", part "3.
+ * The chunked delta-rule scan itself" (a): chunks are multiples of the
+ * 64-token delta-rule block, state carried across chunk boundaries).
+ *
+ *  q, k            [T][h_k][d_k]  qkv_dtype   raw (pre-prologue) inputs
+ *  v               [T][h_v][d_v]  qkv_dtype
+ *  g, beta         [T][h_v]       fp32        log decay, write strength
+ *  cu_seqlens      [N+1]          int32       sequence boundaries (device)
+ *  conv_w          [C][4]         qkv_dtype   required when conv_width = 4
+ *  conv_b          [C]            qkv_dtype   or NULL (no bias)
+ *  conv_state_in   [N][C][3]      qkv_dtype   or NULL (zero history)
+ *  conv_state_out  [N][C][3]      qkv_dtype   or NULL (not written); the last
+ *                                 3 raw inputs of each sequence (with history
+ *                                 from conv_state_in for sequences shorter
+ *                                 than 3).  May be the same pointer as
+ *                                 conv_state_in; no other overlap.
+ *  initial_state   [N][h_v][d_k][d_v] fp32    or NULL (zero state)
+ *  o               [T][h_v][d_v]  out_dtype   written for every token
+ *  final_state     [N][h_v][d_k][d_v] fp32    or NULL (not written); may be
+ *                                 the same pointer as initial_state.
+ *  workspace       >= gdn_prefill_workspace_bytes(p) bytes, 256-byte aligned
+ *
+ * Length-0 sequences are allowed (final state = initial state).  o must not
+ * overlap any input.  Supported: d_k = d_v in {64, 128}, bf16 or fp32 inputs.
+ * Matrix products use split-fp16 operands (about 21 significant bits each)
+ * with fp32 accumulation; intermediate magnitudes must stay below 65504.
+ */
+gdn_status gdn_prefill_varlen(const gdn_problem* p,
+                              const void* q, const void* k, const void* v,
+                              const float* g, const float* beta,
+                              const int32_t* cu_seqlens,
+                              const void* conv_w, const void* conv_b,
+                              const void* conv_state_in, void* conv_state_out,
+                              const float* initial_state,
+                              void* o, float* final_state,
+                              void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/*
+ * One decode step: one new token for each of N slots, updating a pooled
+ * state in place ("[Feature] Add batch invariance support to GDN_ATTN
+ * backend", commit messages: the decode update runs over the state pool
+ * addressed by ssm_state_indices, in place).
+ *
+ *  q, k             [N][h_k][d_k]  qkv_dtype
+ *  v                [N][h_v][d_v]  qkv_dtype
+ *  g, beta          [N][h_v]       fp32
+ *  conv_w, conv_b   as in prefill; conv_w required when conv_width = 4
+ *  conv_state_pool  [P][C][3]      qkv_dtype  read-modify-write (shifted to
+ *                                  hold the newest 3 raw inputs); required
+ *                                  when conv_width = 4, else ignored
+ *  state_pool       [P][h_v][d_k][d_v] fp32   read-modify-write
+ *  state_indices    [N] int32 or NULL (slot n uses pool entry n); entry -1
+ *                   skips the slot (its o row and pool entries untouched)
+ *  o                [N][h_v][d_v]  out_dtype
+ *
+ * p->total_tokens must equal p->num_seqs.  Each slot is computed alone, so
+ * results do not depend on N or on the other slots.  Supported: d_k, d_v in
+ * {64, 128}, any qkv dtype.
+ */
+gdn_status gdn_decode_step(const gdn_problem* p,
+                           const void* q, const void* k, const void* v,
+                           const float* g, const float* beta,
+                           const void* conv_w, const void* conv_b, void* conv_state_pool,
+                           float* state_pool, const int32_t* state_indices,
+                           void* o, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* gdn_status_string(gdn_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

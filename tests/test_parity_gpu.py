@@ -1,0 +1,311 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Bar: max|gpu - oracle| / rms(oracle) <= 1e-4 for fp32 inputs and <= 1e-2 for
+bf16 inputs, on outputs and on final states; conv states (raw values moved)
+bit-exact.  Sizes span several 64-token chunks with ragged tails; the full
+prefill workload (4 x 4096 tokens, 16 key / 32 value heads, d = 128, bf16) is
+checked on sampled (sequence, key head) units the oracle recomputes alone.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gateddeltanet_chunked_delta_amd import binding
+from gateddeltanet_chunked_delta_amd.inputs import (Geometry, bf16_round, conv_state_pool, conv_weights,
+                                                    decode_inputs, prefill_inputs, state_pool, uniform_lengths)
+from tests.gpu_util import TOL, TORCH_DT, dev, gpu_prefill, head_slice, oracle_prefill, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_prefill(oracle, x, **kw):
+    o, fs, cso = gpu_prefill(x, **kw)
+    kw.pop("out_dtype", None)
+    ro, rfs, rcso = oracle_prefill(oracle, x, **kw)
+    eo, ef = rel_err(o, ro), rel_err(fs, rfs)
+    print(f"  rel err o={eo:.3e} final_state={ef:.3e} (tol {TOL[x.dtype]:.0e})", flush=True)
+    assert np.all(np.isfinite(o))
+    assert eo <= TOL[x.dtype] and ef <= TOL[x.dtype]
+    if rcso is not None and cso is not None:
+        assert np.array_equal(cso, rcso)
+    return o, fs
+
+
+def test_single_sequence_fp32_T256(oracle_mod):
+    """1 x 256 tokens, 4 heads, d = 64, fp32, conv + SiLU + L2, zero state."""
+    x = prefill_inputs(0, [256], Geometry(4, 4, 64, 64), "f32")
+    _check_prefill(oracle_mod, x)
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_ragged_bf16(oracle_mod, d):
+    lengths = [1, 63, 64, 65, 200, 3, 130, 0, 2]
+    x = prefill_inputs(10 + d, lengths, Geometry(2, 4, d, d), "bf16", initial_state_std=0.02, conv_state=True)
+    _check_prefill(oracle_mod, x)
+
+
+def test_ragged_fp32_gqa3(oracle_mod):
+    x = prefill_inputs(20, [5, 64, 129, 70, 1], Geometry(2, 6, 64, 64), "f32", initial_state_std=0.02,
+                       conv_state=True)
+    _check_prefill(oracle_mod, x)
+
+
+def test_ragged_fp32_d128(oracle_mod):
+    x = prefill_inputs(24, [3, 64, 100], Geometry(1, 2, 128, 128), "f32", initial_state_std=0.02,
+                       conv_state=True)
+    _check_prefill(oracle_mod, x)
+
+
+def test_fp32_without_conv(oracle_mod):
+    x = prefill_inputs(21, [100, 37], Geometry(1, 2, 64, 64), "f32", initial_state_std=0.02)
+    _check_prefill(oracle_mod, x, conv=False)
+
+
+def test_fp32_without_l2norm(oracle_mod):
+    """qk_l2norm = 0 with inputs already scaled to unit-size heads."""
+    x = prefill_inputs(22, [90], Geometry(1, 1, 64, 64), "f32", initial_state_std=0.02)
+    x.q /= np.linalg.norm(x.q, axis=-1, keepdims=True)
+    x.k /= np.linalg.norm(x.k, axis=-1, keepdims=True)
+    _check_prefill(oracle_mod, x, conv=False, qk_l2norm=False)
+
+
+def test_custom_scale(oracle_mod):
+    x = prefill_inputs(23, [70], Geometry(2, 2, 128, 128), "bf16")
+    _check_prefill(oracle_mod, x, scale=0.5)
+
+
+def test_short_sequence_many_heads_is_time_first(oracle_mod):
+    """T = 12 with 32 value heads (fewer tokens than heads): one layout, no heuristic."""
+    x = prefill_inputs(30, [12], Geometry(16, 32, 128, 128), "bf16")
+    _check_prefill(oracle_mod, x)
+
+
+def test_29_packed_sequences(oracle_mod):
+    lengths = uniform_lengths(31, 29, 1, 300)
+    x = prefill_inputs(31, lengths, Geometry(2, 4, 128, 128), "bf16", initial_state_std=0.02, conv_state=True)
+    _check_prefill(oracle_mod, x)
+
+
+def test_bf16_output(oracle_mod):
+    """bf16 o is the kernel's fp32 o rounded to nearest even at the store (bit
+    for bit), so |o_bf16 - oracle| <= tol rms(oracle) + half a bf16 ulp (2^-8 |o|)."""
+    x = prefill_inputs(32, [150, 40], Geometry(2, 4, 128, 128), "bf16", initial_state_std=0.02)
+    o16, f16, _ = gpu_prefill(x, out_dtype=torch.bfloat16)
+    o32, f32, _ = gpu_prefill(x)
+    assert np.array_equal(o16, bf16_round(o32))
+    assert np.array_equal(f16, f32)
+    ro, _, _ = oracle_prefill(oracle_mod, x)
+    rms = np.sqrt(np.mean(ro ** 2))
+    assert np.all(np.abs(o16 - ro) <= TOL["bf16"] * rms + 2.0 ** -8 * np.abs(o32))
+
+
+def test_full_prefill_4x4096_sampled(oracle_mod):
+    """4 x 4096 tokens, h_k = 16, h_v = 32, d = 128, bf16: whole-run sanity plus
+    oracle parity on sampled (sequence, key head) units."""
+    geom = Geometry(16, 32, 128, 128)
+    x = prefill_inputs(1, [4096] * 4, geom, "bf16")
+    o, fs, _ = gpu_prefill(x)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(fs))
+    for n, hk in [(0, 0), (1, 9), (3, 15)]:
+        xs = head_slice(x, n, hk)
+        ro, rfs, _ = oracle_prefill(oracle_mod, xs)
+        s = slice(int(x.cu_seqlens[n]), int(x.cu_seqlens[n + 1]))
+        eo = rel_err(o[s, 2 * hk:2 * hk + 2], ro)
+        ef = rel_err(fs[n, 2 * hk:2 * hk + 2], rfs[0])
+        print(f"  seq {n} key head {hk}: rel err o={eo:.3e} final={ef:.3e}", flush=True)
+        assert eo <= TOL["bf16"] and ef <= TOL["bf16"]
+
+
+# ---------------------------------------------------------------- invariants
+
+def test_beta0_g0_keeps_state_bitwise():
+    geom = Geometry(2, 4, 128, 128)
+    x = prefill_inputs(40, [70, 130], geom, "bf16", initial_state_std=0.02)
+    x.beta[:] = 0.0
+    x.g[:] = 0.0
+    _, fs, _ = gpu_prefill(x)
+    assert np.array_equal(fs, x.initial_state)
+
+
+def test_run_to_run_bitwise():
+    x = prefill_inputs(41, [300, 5, 64], Geometry(2, 4, 128, 128), "bf16", initial_state_std=0.02)
+    o1, f1, _ = gpu_prefill(x)
+    o2, f2, _ = gpu_prefill(x)
+    assert np.array_equal(o1, o2) and np.array_equal(f1, f2)
+
+
+def test_batch_invariance_bitwise():
+    """Target sequences give bit-identical outputs and final states alone and
+    packed at different positions among seeded filler sequences."""
+    geom = Geometry(2, 4, 128, 128)
+    targets = [(500, 300), (501, 64), (502, 1)]  # (seq id, length)
+    alone = {}
+    for sid, L in targets:
+        x = prefill_inputs(42, [L], geom, "bf16", seq_ids=[sid], initial_state_std=0.02)
+        o, fs, _ = gpu_prefill(x)
+        alone[sid] = (o, fs[0])
+    rng = np.random.default_rng(42)
+    for batch in (4, 9):
+        fill = uniform_lengths(42 + batch, batch, 1, 400)
+        ids = list(range(batch))
+        pos = sorted(rng.choice(batch + len(targets), size=len(targets), replace=False))
+        lengths, seq_ids = list(fill), list(ids)
+        for (sid, L), p in zip(targets, pos):
+            lengths.insert(p, L)
+            seq_ids.insert(p, sid)
+        x = prefill_inputs(42, lengths, geom, "bf16", seq_ids=seq_ids, initial_state_std=0.02)
+        o, fs, _ = gpu_prefill(x)
+        for sid, _ in targets:
+            n = seq_ids.index(sid)
+            s = slice(int(x.cu_seqlens[n]), int(x.cu_seqlens[n + 1]))
+            assert np.array_equal(o[s], alone[sid][0]), (batch, sid)
+            assert np.array_equal(fs[n], alone[sid][1]), (batch, sid)
+
+
+@pytest.mark.parametrize("split", [64, 128])
+def test_split_and_resume_bitwise_at_64_multiples(split):
+    """Prefill of 300 tokens equals prefill of the first `split` tokens then of
+    the rest from the carried recurrent and conv states, bit for bit."""
+    geom = Geometry(2, 4, 128, 128)
+    x = prefill_inputs(43, [300], geom, "bf16", initial_state_std=0.02, conv_state=True)
+    dt = TORCH_DT["bf16"]
+    q, k, v, g, b = dev(x.q, dt), dev(x.k, dt), dev(x.v, dt), dev(x.g), dev(x.beta)
+    w, cs, h0 = dev(x.conv_w, dt), dev(x.conv_state_in, dt), dev(x.initial_state)
+    o, fs, cso = binding.gdn_prefill_varlen(q, k, v, g, b, [0, 300], conv_weight=w, conv_state=cs, initial_state=h0)
+    a = slice(0, split)
+    c = slice(split, 300)
+    o1, f1, c1 = binding.gdn_prefill_varlen(q[a].contiguous(), k[a].contiguous(), v[a].contiguous(),
+                                            g[a].contiguous(), b[a].contiguous(), [0, split], conv_weight=w,
+                                            conv_state=cs, initial_state=h0)
+    o2, f2, c2 = binding.gdn_prefill_varlen(q[c].contiguous(), k[c].contiguous(), v[c].contiguous(),
+                                            g[c].contiguous(), b[c].contiguous(), [0, 300 - split], conv_weight=w,
+                                            conv_state=c1, initial_state=f1)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([o1, o2]), o)
+    assert torch.equal(f2, fs)
+    assert torch.equal(c2, cso)
+
+
+def test_in_place_state_and_conv_state():
+    """final_state may alias initial_state and conv_state_out conv_state_in."""
+    geom = Geometry(2, 4, 128, 128)
+    x = prefill_inputs(44, [100, 7], geom, "bf16", initial_state_std=0.02, conv_state=True)
+    dt = TORCH_DT["bf16"]
+    args = (dev(x.q, dt), dev(x.k, dt), dev(x.v, dt), dev(x.g), dev(x.beta), x.cu_seqlens.astype(np.int32).tolist())
+    w = dev(x.conv_w, dt)
+    h0, cs = dev(x.initial_state), dev(x.conv_state_in, dt)
+    o, fs, cso = binding.gdn_prefill_varlen(*args, conv_weight=w, conv_state=cs.clone(), initial_state=h0.clone())
+    o2, fs2, cso2 = binding.gdn_prefill_varlen(*args, conv_weight=w, conv_state=cs, initial_state=h0,
+                                               final_state_out=h0, conv_state_out=cs)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(fs, h0) and torch.equal(cso, cs)
+
+
+def test_empty_and_zero_length():
+    geom = Geometry(2, 4, 128, 128)
+    x = prefill_inputs(45, [0, 0], geom, "bf16", initial_state_std=0.02)
+    o, fs, _ = gpu_prefill(x)
+    assert o.shape == (0, 4, 128)
+    assert np.array_equal(fs, x.initial_state)
+
+
+# -------------------------------------------------------------------- decode
+
+def _oracle_decode_steps(oracle, geom, pool64, steps, n_slots, slots, conv=None, cpool64=None, indices=None):
+    dims = oracle.Dims(geom.h_k, geom.h_v, geom.d_k, geom.d_v, conv_width=4 if conv is not None else 0)
+    outs = []
+    for d in steps:
+        sel = slots
+        q, k, v = d.q[sel], d.k[sel], d.v[sel]
+        idx = np.arange(len(sel)) if indices is None else indices
+        outs.append(oracle.decode(dims, q, k, v, d.g[sel], d.beta[sel], pool64, idx, conv, None, cpool64))
+    return outs
+
+
+def test_decode_256_slots_sampled(oracle_mod):
+    """256 slots x 32 value heads (16 key heads), d = 128, bf16 inputs, fp32
+    pool of 512 MiB updated in place for 3 steps; sampled slots vs the oracle."""
+    geom = Geometry(16, 32, 128, 128)
+    N = 256
+    pool = dev(state_pool(3, N, geom))
+    sample = [0, 77, 255]
+    ref_pool = pool[sample].double().cpu().numpy().copy()
+    steps = [decode_inputs(3, s, N, geom, "bf16") for s in range(3)]
+    gpu_out = []
+    for d in steps:
+        o = binding.gdn_decode_step(dev(d.q, torch.bfloat16), dev(d.k, torch.bfloat16), dev(d.v, torch.bfloat16),
+                                    dev(d.g), dev(d.beta), pool)
+        gpu_out.append(o.cpu().numpy())
+    ref = _oracle_decode_steps(oracle_mod, geom, ref_pool, steps, N, sample)
+    for s in range(3):
+        e = rel_err(gpu_out[s][sample], ref[s])
+        print(f"  step {s}: rel err o={e:.3e}", flush=True)
+        assert e <= TOL["bf16"]
+    ef = rel_err(pool[sample].cpu().numpy(), ref_pool)
+    assert ef <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128), ("bf16", 64)])
+def test_decode_conv_and_indices(oracle_mod, dtype, d):
+    """Conv update from the conv pool, a permuted index map and a skipped slot."""
+    geom = Geometry(2, 4, d, d)
+    P, N = 7, 5
+    dt = TORCH_DT[dtype]
+    pool_np = state_pool(50, P, geom)
+    cpool_np = conv_state_pool(50, P, geom, dtype)
+    w_np = conv_weights(50, geom, dtype)
+    idx = np.array([3, -1, 0, 6, 2], dtype=np.int32)
+    pool, cpool = dev(pool_np), dev(cpool_np, dt)
+    ref_pool, ref_cpool = pool_np.astype(np.float64), cpool_np.astype(np.float64)
+    dims = oracle_mod.Dims(2, 4, d, d, conv_width=4)
+    for s in range(3):
+        x = decode_inputs(50, s, N, geom, dtype)
+        o = binding.gdn_decode_step(dev(x.q, dt), dev(x.k, dt), dev(x.v, dt), dev(x.g), dev(x.beta), pool,
+                                    state_indices=dev(idx, torch.int32), conv_weight=dev(w_np, dt),
+                                    conv_state_pool=cpool)
+        ro = oracle_mod.decode(dims, x.q, x.k, x.v, x.g, x.beta, ref_pool, idx.astype(np.int64), w_np, None,
+                               ref_cpool)
+        used = idx >= 0
+        assert rel_err(o.cpu().numpy()[used], ro[used]) <= TOL[dtype]
+    assert rel_err(pool.cpu().numpy(), ref_pool) <= TOL[dtype]
+    assert np.array_equal(cpool.float().cpu().numpy(), ref_cpool.astype(np.float32))
+    assert np.array_equal(pool[1].cpu().numpy(), pool_np[1])  # untouched entries
+
+
+def test_decode_steps_match_prefill(oracle_mod):
+    """T decode steps from a pooled state equal one prefill of the T tokens (tolerance)."""
+    geom = Geometry(2, 4, 128, 128)
+    T = 40
+    x = prefill_inputs(51, [T], geom, "bf16", initial_state_std=0.02, conv_state=True)
+    o_pre, fs_pre, cso_pre = gpu_prefill(x)
+    dt = torch.bfloat16
+    pool = dev(x.initial_state)
+    cpool = dev(x.conv_state_in, dt)
+    w = dev(x.conv_w, dt)
+    outs = []
+    for t in range(T):
+        outs.append(binding.gdn_decode_step(dev(x.q[t:t + 1], dt), dev(x.k[t:t + 1], dt), dev(x.v[t:t + 1], dt),
+                                            dev(x.g[t:t + 1]), dev(x.beta[t:t + 1]), pool, conv_weight=w,
+                                            conv_state_pool=cpool))
+    o_dec = torch.cat(outs).cpu().numpy()
+    assert rel_err(o_dec, o_pre) <= TOL["bf16"]
+    assert rel_err(pool.cpu().numpy(), fs_pre) <= TOL["bf16"]
+    assert np.array_equal(cpool.float().cpu().numpy(), cso_pre)
+
+
+def test_decode_batch_invariance_bitwise():
+    """A slot's output and state do not depend on which other slots share the call."""
+    geom = Geometry(16, 32, 128, 128)
+    N = 64
+    pool0 = dev(state_pool(52, N, geom))
+    x = decode_inputs(52, 0, N, geom, "bf16")
+    dt = torch.bfloat16
+    pa = pool0.clone()
+    oa = binding.gdn_decode_step(dev(x.q, dt), dev(x.k, dt), dev(x.v, dt), dev(x.g), dev(x.beta), pa)
+    sub = [5, 40]
+    pb = pool0.clone()
+    ob = binding.gdn_decode_step(dev(x.q[sub], dt), dev(x.k[sub], dt), dev(x.v[sub], dt), dev(x.g[sub]),
+                                 dev(x.beta[sub]), pb, state_indices=dev(np.array(sub, np.int32), torch.int32))
+    torch.cuda.synchronize()
+    assert torch.equal(oa[sub], ob)
+    assert torch.equal(pa[sub], pb[sub])
