@@ -34,6 +34,15 @@ template <> struct Elem<float> {
         out[0] = x.x; out[1] = x.y; out[2] = x.z; out[3] = x.w;
     }
     __device__ __forceinline__ static void put(float* p, float x) { *p = x; }
+    __device__ __forceinline__ static void unpack16(const uint4& u, float* out) {
+        out[0] = __uint_as_float(u.x); out[1] = __uint_as_float(u.y);
+        out[2] = __uint_as_float(u.z); out[3] = __uint_as_float(u.w);
+    }
+    // element e of a 16-byte pack
+    __device__ __forceinline__ static void set16(uint4& u, int e, const float* p) {
+        const uint32_t b = __float_as_uint(*p);
+        if (e == 0) u.x = b; else if (e == 1) u.y = b; else if (e == 2) u.z = b; else u.w = b;
+    }
 };
 template <> struct Elem<bf16_t> {
     static constexpr int kVec = 8;
@@ -48,13 +57,28 @@ template <> struct Elem<bf16_t> {
         }
     }
     __device__ __forceinline__ static void put(bf16_t* p, float x) { *p = f32_to_bf16(x); }
+    __device__ __forceinline__ static void unpack16(const uint4& u, float* out) {
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            out[2 * i] = __uint_as_float(w[i] << 16);
+            out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+    __device__ __forceinline__ static void set16(uint4& u, int e, const bf16_t* p) {
+        const uint32_t b = *p;
+        uint32_t* w = (e < 4) ? ((e < 2) ? &u.x : &u.y) : ((e < 6) ? &u.z : &u.w);
+        *w = (e & 1) ? ((*w & 0x0000ffffu) | (b << 16)) : ((*w & 0xffff0000u) | b);
+    }
 };
 
 // Matrix-core lane layout (16x16 output tile, K-step 32): lane l supplies
 // A[l%16][8*(l/16) + e] and B[8*(l/16) + e][l%16], e = 0..7, and owns
 // D[4*(l/16) + i][l%16], i = 0..3.
 
-__device__ __forceinline__ float silu(float y) { return y / (1.0f + expf(-y)); }
+// y * sigmoid(y) with the hardware exp2 and reciprocal (a few ulp); large
+// negative y gives exp = inf and a zero reciprocal, so the result is -0.
+__device__ __forceinline__ float silu(float y) { return y * __builtin_amdgcn_rcpf(1.0f + __expf(-y)); }
 
 // ---- split-fp16 operands: x ~= hi + lo * 2^-11, hi = fp16(x), lo = fp16((x - hi) 2^11) ----
 // Scaling the residual by 2^11 keeps lo out of fp16's subnormal range (whose

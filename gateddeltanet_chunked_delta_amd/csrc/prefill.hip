@@ -12,27 +12,29 @@
 //
 // Per chunk of L <= 64 tokens, with gam_r = sum_{s<=r} g_s (chunk-local):
 //   prologue   causal conv(4) + SiLU of the raw q|k|v rows (3 rows of history
-//              from the previous chunk, the conv state, or zeros), then per
-//              head L2 norm of q and k.
+//              from the previous chunk, the conv state, or zeros); the per
+//              head L2 norms of q and k are row scales, applied to the fp32
+//              results of the products that read q and k.
 //   A[r][s]  = beta_r e^{gam_r - gam_s} (k_r . k_s)       s <  r
 //   P[r][s]  =        e^{gam_r - gam_s} (q_r . k_s)       s <= r
-//   T        = (I + A)^{-1}   (fp32, 16x16 diagonal blocks by substitution,
-//                              off-diagonal blocks T_ij = -T_ii sum_k A_ik T_kj)
 //   R        = diag(beta) (V - diag(e^gam) K H)
-//   D        = T R                       (the per-token deltas)
+//   D        = (I + A)^{-1} R            (the per-token deltas: inverses of
+//                                         the 16x16 diagonal blocks, then block
+//                                         forward substitution)
 //   o        = scale (diag(e^gam) Q H + P D)
 //   H       <- e^{gam_last} H + K^T diag(e^{gam_last - gam}) D
 // This is the delta rule S_t = e^{g_t} S_{t-1} + beta_t (v_t - e^{g_t}
 // S_{t-1} k_t) k_t^T unrolled over a chunk ("Qwen3.5-27B GPTQ Garbage
 // Inference -- Root Cause Analysis", section "Why abliteration failed on
-// Qwen3.5", item 3).  Forming R from the current state and applying T to it
-// (rather than precomputing W = T diag(beta e^gam) K) skips one 64x64xd_k
-// product per chunk, which suits a kernel that runs the chunks of one
-// sequence back to back.
+// Qwen3.5", item 3).  Solving for D from the current state's residuals R
+// (rather than precomputing W = (I + A)^{-1} diag(beta e^gam) K and
+// U = (I + A)^{-1} diag(beta) V) skips one 64x64xd_k product per chunk, which
+// suits a kernel that runs the chunks of one sequence back to back.
 //
-// Precision: every matrix product takes split-fp16 operands (x = hi +
-// lo 2^-11, three fp16 matrix-core steps, fp32 accumulation), about 22
-// significant bits per operand.  A single fp16 rounding of any operand would already cost up to
+// Precision: the products with d_k-long reductions take split-fp16 operands
+// (x = hi + lo 2^-11, three fp16 matrix-core steps, fp32 accumulation), about
+// 22 significant bits per operand; the 16-wide block products of the
+// substitution and of P D run on fp32 matrix-core steps.  A single fp16 rounding of any operand would already cost up to
 // ~1e-2 of rms(o) in the worst element, because the outputs and states are
 // sums of heavy-tailed products.  Operand magnitudes must stay below the fp16
 // limit (65504); with q/k L2-normalised they are O(1).
@@ -50,37 +52,36 @@ constexpr int kChunk = 64;
 constexpr int kThreads = 256;
 constexpr int kLdsLimit = 163840;  // gfx950: 160 KiB per workgroup
 
-// LDS carve-up for one workgroup.  Matrices shared by the four waves are held
-// as split-fp16 pairs (hi, lo); row pitches pad each row by 16 bytes so that
-// the 16-byte fragment reads of one wave spread over the banks.
-template <int DK, int VEC>
+// LDS carve-up for one workgroup.  K and Q (read by all four waves as
+// matrix operands) are split-fp16 pairs (hi, lo); A, P, V and the diagonal
+// inverse blocks are fp32.  Row pitches pad rows by 16 bytes so that the
+// 16-byte reads of one wave spread over the banks.
+template <int DK, int DVS, int VEC>
 struct Smem {
-    static constexpr int kPitchK = DK + 8;      // K, Q rows: [token][d_k]
-    static constexpr int kPitchT = kChunk + 8;  // A, T, P rows: [token][token]
+    static constexpr int kPitchK = DK + 8;      // K, Q rows: [token][d_k] (fp16)
+    static constexpr int kPitchF = kChunk + 4;  // A, P rows: [token][token] (fp32)
+    static constexpr int kPitchV = DVS + 4;     // V rows: [token][column] (fp32)
+    static constexpr int kPitchD = 20;          // diagonal inverse blocks: [4][16][kPitchD] (fp32)
     static constexpr int kRedCols = 2 * (DK / VEC);  // q|k partial sums of squares per row
 
     static constexpr size_t szKQ = size_t(kChunk) * kPitchK * sizeof(_Float16);
-    static constexpr size_t szTT = size_t(kChunk) * kPitchT * sizeof(_Float16);
     static constexpr size_t oKhi = 0;
     static constexpr size_t oKlo = oKhi + szKQ;
     static constexpr size_t oQhi = oKlo + szKQ;
     static constexpr size_t oQlo = oQhi + szKQ;
-    static constexpr size_t oAF = oQlo + szKQ;                 // A (fp32), later T (hi, lo)
-    static constexpr size_t oTf = oAF + 2 * szTT;              // T while it is built (fp32)
-    static constexpr size_t oPhi = oTf + 2 * szTT;
-    static constexpr size_t oPlo = oPhi + szTT;
-    static constexpr size_t oU1 = oPlo + szTT;                 // partial sums | off-diagonal blocks
-    static constexpr size_t szU1a = size_t(kChunk) * kRedCols * sizeof(float);
-    static constexpr size_t szU1b = size_t(3) * 256 * sizeof(float);
-    static constexpr size_t szU1 = szU1a > szU1b ? szU1a : szU1b;
-    static constexpr size_t oGam = oU1 + szU1;                 // gam (fp64)
-    static constexpr size_t oScal = oGam + kChunk * sizeof(double);  // e^gam, beta, e^{gam_last-gam}, e^{gam_last}
-    static constexpr size_t kBytes = oScal + (3 * kChunk + 4) * sizeof(float);
+    static constexpr size_t oA = oQlo + szKQ;
+    static constexpr size_t oP = oA + size_t(kChunk) * kPitchF * sizeof(float);
+    static constexpr size_t oV = oP + size_t(kChunk) * kPitchF * sizeof(float);
+    static constexpr size_t oTd = oV + size_t(kChunk) * kPitchV * sizeof(float);
+    static constexpr size_t oRed = oTd + size_t(4) * 16 * kPitchD * sizeof(float);
+    static constexpr size_t oGam = oRed + size_t(kChunk) * kRedCols * sizeof(float);  // gam (fp64)
+    // e^gam, beta, e^{gam_last-gam}, 1/|q|, 1/|k| per token, e^{gam_last}
+    static constexpr size_t oScal = oGam + kChunk * sizeof(double);
+    static constexpr size_t kBytes = oScal + (5 * kChunk + 4) * sizeof(float);
 
-    static_assert(size_t(kChunk) * kPitchT * sizeof(float) == 2 * szTT, "A (fp32) and T (hi, lo) share a region");
     static_assert(kBytes <= size_t(kLdsLimit), "LDS budget");
-    static_assert(oKlo % 16 == 0 && oQhi % 16 == 0 && oQlo % 16 == 0 && oAF % 16 == 0 && oTf % 16 == 0 &&
-                      oPhi % 16 == 0 && oPlo % 16 == 0 && oU1 % 16 == 0 && oGam % 16 == 0 && oScal % 16 == 0,
+    static_assert(oKlo % 16 == 0 && oQhi % 16 == 0 && oQlo % 16 == 0 && oA % 16 == 0 && oP % 16 == 0 &&
+                      oV % 16 == 0 && oTd % 16 == 0 && oRed % 16 == 0 && oGam % 16 == 0 && oScal % 16 == 0,
                   "16-byte aligned regions");
 };
 
@@ -89,16 +90,25 @@ __device__ __forceinline__ void lower_tile(int idx, int& ti, int& tj) {
     ti = (idx >= 1) + (idx >= 3) + (idx >= 6);
     tj = idx - ti * (ti + 1) / 2;
 }
-// Upper 16x16 tiles (ti < tj).
-__device__ __forceinline__ void upper_tile(int idx, int& ti, int& tj) {
-    ti = (idx >= 3) + (idx >= 5);
-    tj = idx - (idx >= 3 ? (idx >= 5 ? 2 : 1) : -1);
+
+// acc += A X for a 16x16 fp32 block A (row-major at `a`, row pitch `pitch`)
+// and a 16x16 X held in accumulator layout (lane l owns X[4*(l/16) + i][l%16]).
+// Four fp32 K=4 matrix-core steps; in step i, lane group g = l/16 contributes
+// k = 4g + i, which is exactly the element of X this lane already holds, so X
+// needs no lane exchange and no precision split.
+__device__ __forceinline__ void mma_blk_f32(float4_t& acc, const float* a, int pitch, const float4_t& x) {
+    const int l = threadIdx.x & 63;
+    const float4 av = *reinterpret_cast<const float4*>(a + (l & 15) * pitch + 4 * (l >> 4));
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.x, x[0], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.y, x[1], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.z, x[2], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.w, x[3], acc, 0, 0, 0);
 }
 
 // Workgroup = (sequence, value head, 64-column slice of d_v); wave w owns the
-// 16 state columns [16w, 16w + 16) of the slice.  The state slice, the
+// 16 state columns [16w, 16w + 16) of the slice.  The state slice and the
 // per-token residuals R and deltas D of those columns stay in registers in
-// matrix-core accumulator layout; K, Q, T and P are shared through LDS.
+// matrix-core accumulator layout; K, Q, A, P and V are shared through LDS.
 template <int DK, int DV, typename TIn, typename TOut>
 __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillParams p) {
     constexpr int DVS = 64;
@@ -106,32 +116,35 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillParam
     constexpr int VEC = Elem<TIn>::kVec;
     constexpr int NGQ = DK / VEC;           // 16-byte groups per q (or k) head row
     constexpr int NG = 2 * NGQ;
-    constexpr int IPT = kChunk * NG / kThreads;  // q|k prologue items per thread
+    constexpr int RB = kThreads / NG;       // q|k prologue: row blocks per chunk
+    constexpr int RPB = kChunk / RB;        // q|k rows per thread
+    constexpr int NGV = DVS / VEC;          // 16-byte groups of a v slice row
+    constexpr int VRPB = kChunk / (kThreads / NGV);  // v rows per thread
     constexpr int KT = DK / 16;             // 16-row tiles of the state column
     constexpr int KS = DK / 32;             // 32-wide steps over d_k
-    static_assert(kChunk * NG % kThreads == 0, "prologue items must split evenly");
+    static_assert(kThreads % NG == 0 && kChunk % RB == 0, "q|k prologue tiling");
+    static_assert(kThreads % NGV == 0 && kChunk % (kThreads / NGV) == 0, "v prologue tiling");
     static_assert(DV % DVS == 0, "d_v slices");
-    using S = Smem<DK, VEC>;
-    constexpr int PK = S::kPitchK, PT = S::kPitchT;
+    using S = Smem<DK, DVS, VEC>;
+    constexpr int PK = S::kPitchK, PF = S::kPitchF, PV = S::kPitchV, PD = S::kPitchD;
 
     __shared__ __attribute__((aligned(16))) char smem[S::kBytes];
     _Float16* Khi = reinterpret_cast<_Float16*>(smem + S::oKhi);
     _Float16* Klo = reinterpret_cast<_Float16*>(smem + S::oKlo);
     _Float16* Qhi = reinterpret_cast<_Float16*>(smem + S::oQhi);
     _Float16* Qlo = reinterpret_cast<_Float16*>(smem + S::oQlo);
-    float* Af = reinterpret_cast<float*>(smem + S::oAF);
-    _Float16* Thi = reinterpret_cast<_Float16*>(smem + S::oAF);
-    _Float16* Tlo = Thi + kChunk * PT;
-    float* Tf = reinterpret_cast<float*>(smem + S::oTf);
-    _Float16* Phi = reinterpret_cast<_Float16*>(smem + S::oPhi);
-    _Float16* Plo = reinterpret_cast<_Float16*>(smem + S::oPlo);
-    float* red = reinterpret_cast<float*>(smem + S::oU1);
-    float* Mb = reinterpret_cast<float*>(smem + S::oU1);
+    float* Af = reinterpret_cast<float*>(smem + S::oA);
+    float* Pf = reinterpret_cast<float*>(smem + S::oP);
+    float* Vf = reinterpret_cast<float*>(smem + S::oV);
+    float* Td = reinterpret_cast<float*>(smem + S::oTd);
+    float* red = reinterpret_cast<float*>(smem + S::oRed);
     double* gam = reinterpret_cast<double*>(smem + S::oGam);
     float* eg = reinterpret_cast<float*>(smem + S::oScal);
     float* bet = eg + kChunk;
     float* dl = bet + kChunk;
-    float* egl = dl + kChunk;
+    float* rq = dl + kChunk;
+    float* rk = rq + kChunk;
+    float* egl = rk + kChunk;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
@@ -140,7 +153,8 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillParam
     const int h = (u / NS) % p.h_v;
     const int n = p.order[u / (NS * p.h_v)];
     const int hk = h / (p.h_v / p.h_k);
-    const int col = slice * DVS + 16 * wave + lr;  // this lane's column of d_v
+    const int wcol = 16 * wave + lr;               // this lane's column within the slice
+    const int col = slice * DVS + wcol;            // ... and within d_v
     const int64_t bos = p.cu_seqlens[n], eos = p.cu_seqlens[n + 1];
     const int64_t nq = int64_t(p.h_k) * DK, nv = int64_t(p.h_v) * DV, C = 2 * nq + nv;
     const TIn* qin = static_cast<const TIn*>(p.q);
@@ -161,85 +175,121 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillParam
         for (int e = 0; e < 4; e++)
             hacc[it][e] = p.initial_state ? p.initial_state[state_base + int64_t(16 * it + 4 * lg + e) * DV] : 0.0f;
 
-    // Conv taps of this lane's v channel.
-    const int64_t vch = 2 * nq + int64_t(h) * DV + col;
-    float vw[4] = {0.0f, 0.0f, 0.0f, 0.0f}, vbias = 0.0f;
+    // Prologue assignments, fixed for the sequence: one 16-byte channel group
+    // of q|k (and one of the v slice) for a block of consecutive rows of every
+    // chunk.  The groups' conv taps stay in registers as raw 16-byte packs
+    // (w[4 e + tap]).
+    const int pg = tid % NG, prow0 = (tid / NG) * RPB;
+    const int pwhich = pg / NGQ, poff = (pg % NGQ) * VEC;
+    const TIn* pbase = (pwhich ? kin : qin) + hk * DK + poff;
+    const int64_t pch = (pwhich ? nq : 0) + int64_t(hk) * DK + poff;
+    const int vg = tid % NGV, vrow0 = (tid / NGV) * VRPB;
+    const TIn* vbase = vin + int64_t(h) * DV + slice * DVS + vg * VEC;
+    const int64_t vch = 2 * nq + int64_t(h) * DV + slice * DVS + vg * VEC;
+    uint4 pw[4] = {}, vwp[4] = {};
+    float pbias[VEC], vbias[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; e++) pbias[e] = vbias[e] = 0.0f;
     if (conv) {
 #pragma unroll
-        for (int j = 0; j < 4; j++) vw[j] = Elem<TIn>::get(cw + vch * 4 + j);
-        vbias = cb ? Elem<TIn>::get(cb + vch) : 0.0f;
+        for (int m = 0; m < 4; m++) {
+            pw[m] = *reinterpret_cast<const uint4*>(cw + pch * 4 + m * VEC);
+            vwp[m] = *reinterpret_cast<const uint4*>(cw + vch * 4 + m * VEC);
+        }
+        if (cb) {
+#pragma unroll
+            for (int e = 0; e < VEC; e++) {
+                pbias[e] = Elem<TIn>::get(cb + pch + e);
+                vbias[e] = Elem<TIn>::get(cb + vch + e);
+            }
+        }
     }
+
+    // conv(4) + SiLU of `rows` consecutive rows of one 16-byte channel group;
+    // xr holds the raw rows from 3 before the first (zero outside the data).
+    auto conv_rows = [&](const uint4* xr, const uint4 (&wp)[4], const float (&bias)[VEC], int i, float (&y)[VEC]) {
+        if (conv) {
+            float wv[4 * VEC], xs[4][VEC];
+#pragma unroll
+            for (int m = 0; m < 4; m++) Elem<TIn>::unpack16(wp[m], wv + m * VEC);
+#pragma unroll
+            for (int jj = 0; jj < 4; jj++) Elem<TIn>::unpack16(xr[i + jj], xs[jj]);
+#pragma unroll
+            for (int e = 0; e < VEC; e++) {
+                float acc = bias[e];
+#pragma unroll
+                for (int jj = 0; jj < 4; jj++) acc += wv[4 * e + jj] * xs[jj][e];
+                y[e] = silu(acc);
+            }
+        } else {
+            Elem<TIn>::unpack16(xr[i + 3], y);
+        }
+    };
 
     for (int64_t c0 = bos; c0 < eos; c0 += kChunk) {
         const int L = int(eos - c0 < kChunk ? eos - c0 : kChunk);
 
-        // ---- prologue, q|k: conv + SiLU into registers, partial sums of squares ----
-        float val[IPT][VEC];
+        // ---- prologue: conv + SiLU.  q|k are staged un-normalised as split
+        //      operands (the per-row L2 norms scale the fp32 products later);
+        //      v is staged in fp32.  All raw rows are loaded before any math. ----
+        {
+            uint4 xr[RPB + 3], xv[VRPB + 3];
 #pragma unroll
-        for (int j = 0; j < IPT; j++) {
-            const int item = tid + kThreads * j, r = item / NG, gi = item % NG;
-            const int which = gi / NGQ, off = (gi % NGQ) * VEC;
-            const TIn* base = (which ? kin : qin) + hk * DK + off;
-            const int64_t ch = (which ? nq : 0) + int64_t(hk) * DK + off;
-            float y[VEC];
-            if (r < L) {
-                const int64_t t = c0 + r;
-                if (conv) {
-#pragma unroll
-                    for (int e = 0; e < VEC; e++) y[e] = cb ? Elem<TIn>::get(cb + ch + e) : 0.0f;
-#pragma unroll
-                    for (int jj = 0; jj < 4; jj++) {
-                        const int64_t tt = t - 3 + jj;
-                        float x[VEC];
-                        if (tt >= bos) {
-                            Elem<TIn>::load16(base + tt * nq, x);
-                        } else if (csi) {
-#pragma unroll
-                            for (int e = 0; e < VEC; e++)
-                                x[e] = Elem<TIn>::get(csi + (int64_t(n) * C + ch + e) * 3 + (3 + (tt - bos)));
-                        } else {
-#pragma unroll
-                            for (int e = 0; e < VEC; e++) x[e] = 0.0f;
-                        }
-#pragma unroll
-                        for (int e = 0; e < VEC; e++) y[e] += Elem<TIn>::get(cw + (ch + e) * 4 + jj) * x[e];
-                    }
-#pragma unroll
-                    for (int e = 0; e < VEC; e++) y[e] = silu(y[e]);
-                } else {
-                    Elem<TIn>::load16(base + t * nq, y);
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < VEC; e++) y[e] = 0.0f;
-            }
-            float ss = 0.0f;
-#pragma unroll
-            for (int e = 0; e < VEC; e++) ss += y[e] * y[e];
-            red[r * NG + gi] = ss;
-#pragma unroll
-            for (int e = 0; e < VEC; e++) val[j][e] = y[e];
-        }
-        // ---- prologue, v: this lane's column for tokens 16 tb + 4 lg + e ----
-        float4_t vv[4];
-#pragma unroll
-        for (int tb = 0; tb < 4; tb++) {
-            const int rb = 16 * tb + 4 * lg;
-            float x[7];
-#pragma unroll
-            for (int j = 0; j < 7; j++) {
-                const int row = rb - 3 + j;
+            for (int j = 0; j < RPB + 3; j++) {
+                const int row = prow0 - 3 + j;
                 const int64_t tt = c0 + row;
-                if (row >= L || (!conv && j < 3)) x[j] = 0.0f;
-                else if (tt >= bos) x[j] = Elem<TIn>::get(vin + tt * nv + int64_t(h) * DV + col);
-                else if (csi) x[j] = Elem<TIn>::get(csi + (int64_t(n) * C + vch) * 3 + (3 + (tt - bos)));
-                else x[j] = 0.0f;
+                uint4 v = {0u, 0u, 0u, 0u};
+                if (row < L && (conv || j >= 3)) {
+                    if (tt >= bos) {
+                        v = *reinterpret_cast<const uint4*>(pbase + tt * nq);
+                    } else if (csi) {
+#pragma unroll
+                        for (int e = 0; e < VEC; e++)
+                            Elem<TIn>::set16(v, e, csi + (int64_t(n) * C + pch + e) * 3 + (3 + (tt - bos)));
+                    }
+                }
+                xr[j] = v;
             }
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-                float y = x[e + 3];
-                if (conv) y = silu(vbias + vw[0] * x[e] + vw[1] * x[e + 1] + vw[2] * x[e + 2] + vw[3] * x[e + 3]);
-                vv[tb][e] = (rb + e < L) ? y : 0.0f;
+            for (int j = 0; j < VRPB + 3; j++) {
+                const int row = vrow0 - 3 + j;
+                const int64_t tt = c0 + row;
+                uint4 v = {0u, 0u, 0u, 0u};
+                if (row < L && (conv || j >= 3)) {
+                    if (tt >= bos) {
+                        v = *reinterpret_cast<const uint4*>(vbase + tt * nv);
+                    } else if (csi) {
+#pragma unroll
+                        for (int e = 0; e < VEC; e++)
+                            Elem<TIn>::set16(v, e, csi + (int64_t(n) * C + vch + e) * 3 + (3 + (tt - bos)));
+                    }
+                }
+                xv[j] = v;
+            }
+#pragma unroll
+            for (int i = 0; i < RPB; i++) {
+                const int row = prow0 + i;
+                float y[VEC];
+                conv_rows(xr, pw, pbias, i, y);
+                float ss = 0.0f;
+#pragma unroll
+                for (int e = 0; e < VEC; e++) {
+                    if (row >= L) y[e] = 0.0f;
+                    ss += y[e] * y[e];
+                }
+                red[row * NG + pg] = ss;
+                _Float16* dhi = (pwhich ? Khi : Qhi) + row * PK + poff;
+                _Float16* dlo = (pwhich ? Klo : Qlo) + row * PK + poff;
+#pragma unroll
+                for (int e = 0; e < VEC; e++) split1(y[e], dhi[e], dlo[e]);
+            }
+#pragma unroll
+            for (int i = 0; i < VRPB; i++) {
+                const int row = vrow0 + i;
+                float y[VEC];
+                conv_rows(xv, vwp, vbias, i, y);
+#pragma unroll
+                for (int e = 0; e < VEC; e++) Vf[row * PV + vg * VEC + e] = (row < L) ? y[e] : 0.0f;
             }
         }
         // ---- chunk-local cumulative log decay and its exponentials (wave 0) ----
@@ -267,27 +317,19 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillParam
         }
         __syncthreads();
 
-        // ---- prologue, q|k: L2 norm, stage split operands ----
+        // ---- per-row 1/|q| and 1/|k| (fixed summation order) ----
+        if (tid < 2 * kChunk) {
+            const int r = tid & (kChunk - 1), which = tid / kChunk;
+            const float* rr = red + r * NG + which * NGQ;
+            float sum = 0.0f;
 #pragma unroll
-        for (int j = 0; j < IPT; j++) {
-            const int item = tid + kThreads * j, r = item / NG, gi = item % NG;
-            const int which = gi / NGQ, off = (gi % NGQ) * VEC;
-            float rn = 1.0f;
-            if (p.qk_l2norm) {
-                const float* rr = red + r * NG + which * NGQ;
-                float s = 0.0f;
-#pragma unroll
-                for (int q = 0; q < NGQ; q++) s += rr[q];
-                rn = 1.0f / sqrtf(s + p.l2_eps);
-            }
-            _Float16* dhi = (which ? Khi : Qhi) + r * PK + off;
-            _Float16* dlo = (which ? Klo : Qlo) + r * PK + off;
-#pragma unroll
-            for (int e = 0; e < VEC; e++) split1(val[j][e] * rn, dhi[e], dlo[e]);
+            for (int q = 0; q < NGQ; q++) sum += rr[q];
+            (which ? rk : rq)[r] = p.qk_l2norm ? 1.0f / sqrtf(sum + p.l2_eps) : 1.0f;
         }
         __syncthreads();
 
-        // ---- Gram tiles: A (strictly lower, fp32) and P (lower incl., split) ----
+        // ---- Gram tiles: A (strictly lower) and P (lower incl.), fp32.  Tiles
+        //      above the diagonal are never read. ----
         for (int job = wave; job < 20; job += 4) {
             const int which = job / 10;
             int ti, tj;
@@ -299,24 +341,16 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillParam
                      lds_sfrag(Khi, Klo, PK, 16 * tj + lr, 32 * ks + 8 * lg));
             const float4_t acc = combine(hh, xx);
             const int s = 16 * tj + lr;
+            const float* rrow = which ? rq : rk;
+            const float rks = rk[s];
 #pragma unroll
             for (int e = 0; e < 4; e++) {
                 const int r = 16 * ti + 4 * lg + e;
+                const float gram = acc[e] * rrow[r] * rks;
                 const float dec = (s <= r) ? expf(static_cast<float>(gam[r] - gam[s])) : 0.0f;
-                if (which == 0) {
-                    Af[r * PT + s] = (s < r) ? bet[r] * dec * acc[e] : 0.0f;
-                } else {
-                    const float pv = dec * acc[e];
-                    split1(pv, Phi[r * PT + s], Plo[r * PT + s]);
-                }
+                if (which == 0) Af[r * PF + s] = (s < r) ? bet[r] * dec * gram : 0.0f;
+                else Pf[r * PF + s] = dec * gram;
             }
-        }
-        for (int e = tid; e < 6 * 256; e += kThreads) {
-            int ti, tj;
-            upper_tile(e >> 8, ti, tj);
-            const int idx = (16 * ti + ((e & 255) >> 4)) * PT + 16 * tj + (e & 15);
-            Phi[idx] = _Float16(0.0f);
-            Plo[idx] = _Float16(0.0f);
         }
 
         // ---- K H and Q H on this wave's column; R = beta (V - e^gam K H) ----
@@ -342,13 +376,15 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillParam
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
                     const int r = 16 * tb + 4 * lg + e;
-                    rr[tb][e] = bet[r] * (vv[tb][e] - eg[r] * kh[e]);
+                    qh[tb][e] *= rq[r];
+                    rr[tb][e] = bet[r] * (Vf[r * PV + wcol] - eg[r] * rk[r] * kh[e]);
                 }
             }
         }
         __syncthreads();
 
-        // ---- T = (I + A)^{-1}: diagonal 16x16 blocks by forward substitution ----
+        // ---- inverses of the 16x16 diagonal blocks of (I + A), by forward
+        //      substitution, one column per lane (wave 0) ----
         if (wave == 0) {
             const int b = lane >> 4, c = lane & 15;
             float x[16];
@@ -356,96 +392,42 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillParam
             for (int r = 0; r < 16; r++) {
                 float acc = 0.0f;
 #pragma unroll
-                for (int s = 0; s < r; s++) acc += Af[(16 * b + r) * PT + 16 * b + s] * x[s];
+                for (int s = 0; s < r; s++) acc += Af[(16 * b + r) * PF + 16 * b + s] * x[s];
                 x[r] = (r < c) ? 0.0f : ((r == c) ? 1.0f : -acc);
             }
 #pragma unroll
-            for (int r = 0; r < 16; r++) Tf[(16 * b + r) * PT + 16 * b + c] = x[r];
-        } else {
-            for (int e = tid - 64; e < 6 * 256; e += kThreads - 64) {
-                int ti, tj;
-                upper_tile(e >> 8, ti, tj);
-                Tf[(16 * ti + ((e & 255) >> 4)) * PT + 16 * tj + (e & 15)] = 0.0f;
-            }
-        }
-        __syncthreads();
-        // ---- off-diagonal blocks by distance: T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj ----
-#pragma unroll 1
-        for (int d = 1; d <= 3; d++) {
-            const int nb = 4 - d;
-            for (int e = tid; e < nb * 256; e += kThreads) {
-                const int bi = d + (e >> 8), bj = bi - d, r = (e & 255) >> 4, c = e & 15;
-                float acc = 0.0f;
-                for (int kb = bj; kb < bi; kb++) {
-#pragma unroll
-                    for (int s = 0; s < 16; s++)
-                        acc += Af[(16 * bi + r) * PT + 16 * kb + s] * Tf[(16 * kb + s) * PT + 16 * bj + c];
-                }
-                Mb[e] = acc;
-            }
-            __syncthreads();
-            for (int e = tid; e < nb * 256; e += kThreads) {
-                const int bi = d + (e >> 8), bj = bi - d, r = (e & 255) >> 4, c = e & 15;
-                const float* m = Mb + (e & ~255);
-                float acc = 0.0f;
-#pragma unroll
-                for (int s = 0; s < 16; s++) acc += Tf[(16 * bi + r) * PT + 16 * bi + s] * m[s * 16 + c];
-                Tf[(16 * bi + r) * PT + 16 * bj + c] = -acc;
-            }
-            __syncthreads();
-        }
-        // T as split operand, over the (now dead) A region
-        for (int e = tid; e < kChunk * kChunk; e += kThreads) {
-            const int r = e >> 6, c = e & 63;
-            split1(Tf[r * PT + c], Thi[r * PT + c], Tlo[r * PT + c]);
+            for (int r = 0; r < 16; r++) Td[(16 * b + r) * PD + c] = x[r];
         }
         __syncthreads();
 
-        // ---- D = T R (T lower triangular: token block tb needs K steps <= tb/2) ----
+        // ---- D: block forward substitution of (I + A) D = R on this wave's
+        //      column, D_b = Tbb (R_b - sum_{k<b} A_bk D_k) ----
         float4_t dacc[4];
-        {
-            SFrag rb[2];
 #pragma unroll
-            for (int ks = 0; ks < 2; ks++) {
-                float x[8];
-                acc_to_operand(rr[2 * ks], rr[2 * ks + 1], x);
-                rb[ks] = split8(x);
+        for (int b = 0; b < 4; b++) {
+            float4_t x = rr[b];
+#pragma unroll
+            for (int k = 0; k < b; k++) {
+                const float4_t nd = -dacc[k];
+                mma_blk_f32(x, Af + 16 * b * PF + 16 * k, PF, nd);
             }
-#pragma unroll
-            for (int tb = 0; tb < 4; tb++) {
-                float4_t hh = kZero4, xx = kZero4;
-#pragma unroll
-                for (int ks = 0; ks <= (tb >> 1); ks++)
-                    mma3(hh, xx, lds_sfrag(Thi, Tlo, PT, 16 * tb + lr, 32 * ks + 8 * lg), rb[ks]);
-                dacc[tb] = combine(hh, xx);
-            }
+            dacc[b] = kZero4;
+            mma_blk_f32(dacc[b], Td + 16 * b * PD, PD, x);
         }
         // ---- o = scale (e^gam Q H + P D) ----
-        {
-            SFrag db[2];
 #pragma unroll
-            for (int ks = 0; ks < 2; ks++) {
-                float x[8];
-                acc_to_operand(dacc[2 * ks], dacc[2 * ks + 1], x);
-                db[ks] = split8(x);
-            }
+        for (int b = 0; b < 4; b++) {
+            float4_t oacc = kZero4;
 #pragma unroll
-            for (int tb = 0; tb < 4; tb++) {
-                float4_t hh = kZero4, xx = kZero4;
+            for (int k = 0; k <= b; k++) mma_blk_f32(oacc, Pf + 16 * b * PF + 16 * k, PF, dacc[k]);
 #pragma unroll
-                for (int ks = 0; ks <= (tb >> 1); ks++)
-                    mma3(hh, xx, lds_sfrag(Phi, Plo, PT, 16 * tb + lr, 32 * ks + 8 * lg), db[ks]);
-                const float4_t oacc = combine(hh, xx);
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    const int r = 16 * tb + 4 * lg + e;
-                    if (r < L)
-                        Elem<TOut>::put(out + ((c0 + r) * p.h_v + h) * DV + col,
-                                        p.scale * (eg[r] * qh[tb][e] + oacc[e]));
-                }
+            for (int e = 0; e < 4; e++) {
+                const int r = 16 * b + 4 * lg + e;
+                if (r < L)
+                    Elem<TOut>::put(out + ((c0 + r) * p.h_v + h) * DV + col, p.scale * (eg[r] * qh[b][e] + oacc[e]));
             }
         }
-        // ---- H <- e^{gam_last} H + K^T diag(e^{gam_last - gam}) D ----
+        // ---- H <- e^{gam_last} H + K^T diag(e^{gam_last - gam} / |k|) D ----
         {
             SFrag tb2[2];
 #pragma unroll
@@ -453,8 +435,9 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillParam
                 float4_t a0, a1;
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
-                    a0[e] = dl[32 * ks + 4 * lg + e] * dacc[2 * ks][e];
-                    a1[e] = dl[32 * ks + 16 + 4 * lg + e] * dacc[2 * ks + 1][e];
+                    const int r0 = 32 * ks + 4 * lg + e, r1 = r0 + 16;
+                    a0[e] = dl[r0] * rk[r0] * dacc[2 * ks][e];
+                    a1[e] = dl[r1] * rk[r1] * dacc[2 * ks + 1][e];
                 }
                 float x[8];
                 acc_to_operand(a0, a1, x);
