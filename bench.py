@@ -45,6 +45,26 @@ def decode_algorithmic(N, h_k, h_v, d, in_bytes=2, out_bytes=4):
     return bytes_, flops
 
 
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when the kernel's sources changed since the counters were taken."""
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    try:
+        with open(os.path.join(root, "profiles", "traffic.json")) as f:
+            t = json.load(f)
+        k = t[kernel]
+        h = hashlib.sha256()
+        for src in k["sources"]:
+            with open(os.path.join(root, src), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest()[:16] != k["src_sha256_16"]:
+            return None
+        return (k["fetch_kib"] * t["fetch_scale"] + k["write_kib"] * t["write_scale"]) * 1024.0
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(x, nthreads):
     """The fp64 oracle on the same seeded inputs (all sequences, all heads), wall clock."""
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
@@ -68,6 +88,9 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also time a plain 1 GiB device-to-device copy (the reference for measured "
+                         "HBM bandwidth and for scaling FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -141,7 +164,8 @@ def main():
                                "d_k=d_v=128, bf16 q/k/v, fp32 g/beta/state/o, conv4+SiLU+L2, chunk 64",
                    "num_seqs": B, "seq_len": Tseq, "h_k": 16, "h_v": 32, "d": 128},
         "roofline": {"bound": "hbm", "achieved": pbytes / avg_call_s / 1e9, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": pbytes / avg_call_s / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                     "unit": "GB/s", "frac": pbytes / avg_call_s / 1e9 / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(PREFILL_KERNEL),
                      "kernel": PREFILL_KERNEL, "algorithmic_bytes": pbytes, "avg_call_us": avg_call_s * 1e6},
         "mfma_util": pflops / avg_call_s / (MFMA_F16_PEAK_TFLOPS * 1e12),
         "algorithmic_tflops": pflops / avg_call_s / 1e12,
@@ -174,9 +198,30 @@ def main():
                                         "bf16 q/k/v, fp32 512 MiB state pool in place",
                             "steps": nsteps, "us_per_step": us, "GB/s": gbs,
                             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                         "frac": gbs / HBM_PEAK_GBS, "traffic": None, "kernel": DECODE_KERNEL,
+                                         "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic(DECODE_KERNEL),
+                                         "kernel": DECODE_KERNEL,
                                          "algorithmic_bytes": dbytes}}
         print(f"[bench] decode: {us:.1f} us/step, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
+
+    if args.copy_calibration:
+        nbytes = 1 << 30
+        src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 10
+        e0.record(stream)
+        for _ in range(reps):
+            dst.copy_(src)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        result["copy_calibration"] = {"bytes_read": nbytes, "bytes_written": nbytes, "us_per_copy": us,
+                                      "GB/s": 2 * nbytes / (us * 1e-6) / 1e9}
+        print(f"[bench] copy 1 GiB: {us:.1f} us, {2 * nbytes / (us * 1e-6) / 1e9:.0f} GB/s", file=sys.stderr, flush=True)
+        del src, dst
 
     if not args.no_cpu_baseline:
         n = len(os.sched_getaffinity(0))
