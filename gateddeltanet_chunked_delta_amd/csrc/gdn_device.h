@@ -72,6 +72,15 @@ template <> struct Elem<bf16_t> {
     }
 };
 
+// Workgroup barrier that orders LDS only: each wave waits for its own LDS
+// accesses, not for its outstanding global loads and stores, so loads of later
+// data and stores of finished outputs stay in flight across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Matrix-core lane layout (16x16 output tile, K-step 32): lane l supplies
 // A[l%16][8*(l/16) + e] and B[8*(l/16) + e][l%16], e = 0..7, and owns
 // D[4*(l/16) + i][l%16], i = 0..3.

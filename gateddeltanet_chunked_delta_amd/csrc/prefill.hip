@@ -73,7 +73,7 @@ struct Smem {
     static constexpr size_t oP = oA + size_t(kChunk) * kPitchF * sizeof(float);
     static constexpr size_t oV = oP + size_t(kChunk) * kPitchF * sizeof(float);
     static constexpr size_t oTd = oV + size_t(kChunk) * kPitchV * sizeof(float);
-    static constexpr size_t oRed = oTd + size_t(4) * 16 * kPitchD * sizeof(float);
+    static constexpr size_t oRed = oTd + size_t(4) * 16 * kPitchD * sizeof(float);  // q|k partial sums of squares
     static constexpr size_t oGam = oRed + size_t(kChunk) * kRedCols * sizeof(float);  // gam (fp64)
     // e^gam, beta, e^{gam_last-gam}, 1/|q|, 1/|k| per token, e^{gam_last}
     static constexpr size_t oScal = oGam + kChunk * sizeof(double);
@@ -81,14 +81,36 @@ struct Smem {
 
     static_assert(kBytes <= size_t(kLdsLimit), "LDS budget");
     static_assert(oKlo % 16 == 0 && oQhi % 16 == 0 && oQlo % 16 == 0 && oA % 16 == 0 && oP % 16 == 0 &&
-                      oV % 16 == 0 && oTd % 16 == 0 && oRed % 16 == 0 && oGam % 16 == 0 && oScal % 16 == 0,
+                      oV % 16 == 0 && oTd % 16 == 0 && oRed % 16 == 0 &&
+                      oGam % 16 == 0 && oScal % 16 == 0,
                   "16-byte aligned regions");
 };
 
-// Lower 16x16 tiles (ti >= tj) of a 64x64 matrix, row by row.
-__device__ __forceinline__ void lower_tile(int idx, int& ti, int& tj) {
-    ti = (idx >= 1) + (idx >= 3) + (idx >= 6);
-    tj = idx - ti * (ti + 1) / 2;
+// Gram tiles of two tile-rows R0 < R1 of A B^T (A = K or Q rows, B = K rows),
+// all lower tiles (R0, 0..R0) and (R1, 0..R1): R0 + R1 + 2 tiles that share
+// their operand fragments, accumulated as independent split pairs.
+template <int R0, int R1, int KS, int PK>
+__device__ __forceinline__ void gram_two_rows(const _Float16* Ahi, const _Float16* Alo, const _Float16* Khi,
+                                              const _Float16* Klo, int lr, int lg, float4_t (&acc)[R0 + R1 + 2]) {
+    constexpr int NT = R0 + R1 + 2;
+    float4_t hh[NT], xx[NT];
+#pragma unroll
+    for (int j = 0; j < NT; j++) hh[j] = xx[j] = kZero4;
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++) {
+        const int k = 32 * ks + 8 * lg;
+        const SFrag a0 = lds_sfrag(Ahi, Alo, PK, 16 * R0 + lr, k);
+        const SFrag a1 = lds_sfrag(Ahi, Alo, PK, 16 * R1 + lr, k);
+        SFrag b[R1 + 1];
+#pragma unroll
+        for (int t = 0; t <= R1; t++) b[t] = lds_sfrag(Khi, Klo, PK, 16 * t + lr, k);
+#pragma unroll
+        for (int t = 0; t <= R0; t++) mma3(hh[t], xx[t], a0, b[t]);
+#pragma unroll
+        for (int t = 0; t <= R1; t++) mma3(hh[R0 + 1 + t], xx[R0 + 1 + t], a1, b[t]);
+    }
+#pragma unroll
+    for (int j = 0; j < NT; j++) acc[j] = combine(hh[j], xx[j]);
 }
 
 // acc += A X for a 16x16 fp32 block A (row-major at `a`, row pitch `pitch`)
@@ -226,46 +248,53 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillParam
         }
     };
 
+    // Raw 16-byte rows of this thread's channel groups for the chunk at cs
+    // (3 rows of history from the previous chunk, the conv state or zeros;
+    // rows past the chunk are zero).  All raw rows are loaded before any math.
+    uint4 xr[RPB + 3], xv[VRPB + 3];
+    auto load_raw = [&](int64_t cs) {
+        const int Lc = int(eos - cs < kChunk ? eos - cs : kChunk);
+#pragma unroll
+        for (int j = 0; j < RPB + 3; j++) {
+            const int row = prow0 - 3 + j;
+            const int64_t tt = cs + row;
+            uint4 v = {0u, 0u, 0u, 0u};
+            if (row < Lc && (conv || j >= 3)) {
+                if (tt >= bos) {
+                    v = *reinterpret_cast<const uint4*>(pbase + tt * nq);
+                } else if (csi) {
+#pragma unroll
+                    for (int e = 0; e < VEC; e++)
+                        Elem<TIn>::set16(v, e, csi + (int64_t(n) * C + pch + e) * 3 + (3 + (tt - bos)));
+                }
+            }
+            xr[j] = v;
+        }
+#pragma unroll
+        for (int j = 0; j < VRPB + 3; j++) {
+            const int row = vrow0 - 3 + j;
+            const int64_t tt = cs + row;
+            uint4 v = {0u, 0u, 0u, 0u};
+            if (row < Lc && (conv || j >= 3)) {
+                if (tt >= bos) {
+                    v = *reinterpret_cast<const uint4*>(vbase + tt * nv);
+                } else if (csi) {
+#pragma unroll
+                    for (int e = 0; e < VEC; e++)
+                        Elem<TIn>::set16(v, e, csi + (int64_t(n) * C + vch + e) * 3 + (3 + (tt - bos)));
+                }
+            }
+            xv[j] = v;
+        }
+    };
     for (int64_t c0 = bos; c0 < eos; c0 += kChunk) {
         const int L = int(eos - c0 < kChunk ? eos - c0 : kChunk);
+        load_raw(c0);
 
         // ---- prologue: conv + SiLU.  q|k are staged un-normalised as split
         //      operands (the per-row L2 norms scale the fp32 products later);
-        //      v is staged in fp32.  All raw rows are loaded before any math. ----
+        //      v is staged in fp32. ----
         {
-            uint4 xr[RPB + 3], xv[VRPB + 3];
-#pragma unroll
-            for (int j = 0; j < RPB + 3; j++) {
-                const int row = prow0 - 3 + j;
-                const int64_t tt = c0 + row;
-                uint4 v = {0u, 0u, 0u, 0u};
-                if (row < L && (conv || j >= 3)) {
-                    if (tt >= bos) {
-                        v = *reinterpret_cast<const uint4*>(pbase + tt * nq);
-                    } else if (csi) {
-#pragma unroll
-                        for (int e = 0; e < VEC; e++)
-                            Elem<TIn>::set16(v, e, csi + (int64_t(n) * C + pch + e) * 3 + (3 + (tt - bos)));
-                    }
-                }
-                xr[j] = v;
-            }
-#pragma unroll
-            for (int j = 0; j < VRPB + 3; j++) {
-                const int row = vrow0 - 3 + j;
-                const int64_t tt = c0 + row;
-                uint4 v = {0u, 0u, 0u, 0u};
-                if (row < L && (conv || j >= 3)) {
-                    if (tt >= bos) {
-                        v = *reinterpret_cast<const uint4*>(vbase + tt * nv);
-                    } else if (csi) {
-#pragma unroll
-                        for (int e = 0; e < VEC; e++)
-                            Elem<TIn>::set16(v, e, csi + (int64_t(n) * C + vch + e) * 3 + (3 + (tt - bos)));
-                    }
-                }
-                xv[j] = v;
-            }
 #pragma unroll
             for (int i = 0; i < RPB; i++) {
                 const int row = prow0 + i;
@@ -315,7 +344,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillParam
             dl[lane] = static_cast<float>(exp(gl - x));
             if (lane == 0) egl[0] = static_cast<float>(exp(gl));
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- per-row 1/|q| and 1/|k| (fixed summation order) ----
         if (tid < 2 * kChunk) {
@@ -326,30 +355,47 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillParam
             for (int q = 0; q < NGQ; q++) sum += rr[q];
             (which ? rk : rq)[r] = p.qk_l2norm ? 1.0f / sqrtf(sum + p.l2_eps) : 1.0f;
         }
-        __syncthreads();
+        lds_barrier();
 
-        // ---- Gram tiles: A (strictly lower) and P (lower incl.), fp32.  Tiles
-        //      above the diagonal are never read. ----
-        for (int job = wave; job < 20; job += 4) {
-            const int which = job / 10;
-            int ti, tj;
-            lower_tile(job % 10, ti, tj);
-            float4_t hh = kZero4, xx = kZero4;
+        // ---- Gram tiles: A (strictly lower) and P (lower incl.), fp32.  Waves
+        //      0, 1 take K K^T, waves 2, 3 take Q K^T; each wave two tile-rows
+        //      ({0, 3} or {1, 2}: 5 tiles).  Tiles above the diagonal are never read. ----
+        {
+            const int which = wave >> 1;
+            const _Float16* Ahi = which ? Qhi : Khi;
+            const _Float16* Alo = which ? Qlo : Klo;
+            const float* rnorm = which ? rq : rk;
+            auto store_tile = [&](const float4_t& acc, int ti, int tj) {
+                const int s = 16 * tj + lr, r0 = 16 * ti + 4 * lg;
+                const float4 rn = *reinterpret_cast<const float4*>(rnorm + r0);
+                const float4 bt = *reinterpret_cast<const float4*>(bet + r0);
+                const double2 g01 = *reinterpret_cast<const double2*>(gam + r0);
+                const double2 g23 = *reinterpret_cast<const double2*>(gam + r0 + 2);
+                const double gs = gam[s];
+                const float rks = rk[s];
+                const float rnv[4] = {rn.x, rn.y, rn.z, rn.w}, btv[4] = {bt.x, bt.y, bt.z, bt.w};
+                const double grv[4] = {g01.x, g01.y, g23.x, g23.y};
 #pragma unroll
-            for (int ks = 0; ks < KS; ks++)
-                mma3(hh, xx, lds_sfrag(which ? Qhi : Khi, which ? Qlo : Klo, PK, 16 * ti + lr, 32 * ks + 8 * lg),
-                     lds_sfrag(Khi, Klo, PK, 16 * tj + lr, 32 * ks + 8 * lg));
-            const float4_t acc = combine(hh, xx);
-            const int s = 16 * tj + lr;
-            const float* rrow = which ? rq : rk;
-            const float rks = rk[s];
+                for (int e = 0; e < 4; e++) {
+                    const int r = r0 + e;
+                    const float gram = acc[e] * rnv[e] * rks;
+                    const float dec = (s <= r) ? __expf(static_cast<float>(grv[e] - gs)) : 0.0f;
+                    if (which == 0) Af[r * PF + s] = (s < r) ? btv[e] * dec * gram : 0.0f;
+                    else Pf[r * PF + s] = dec * gram;
+                }
+            };
+            float4_t acc[5];
+            if ((wave & 1) == 0) {
+                gram_two_rows<0, 3, KS, PK>(Ahi, Alo, Khi, Klo, lr, lg, acc);
+                store_tile(acc[0], 0, 0);
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const int r = 16 * ti + 4 * lg + e;
-                const float gram = acc[e] * rrow[r] * rks;
-                const float dec = (s <= r) ? expf(static_cast<float>(gam[r] - gam[s])) : 0.0f;
-                if (which == 0) Af[r * PF + s] = (s < r) ? bet[r] * dec * gram : 0.0f;
-                else Pf[r * PF + s] = dec * gram;
+                for (int t = 0; t < 4; t++) store_tile(acc[1 + t], 3, t);
+            } else {
+                gram_two_rows<1, 2, KS, PK>(Ahi, Alo, Khi, Klo, lr, lg, acc);
+                store_tile(acc[0], 1, 0);
+                store_tile(acc[1], 1, 1);
+#pragma unroll
+                for (int t = 0; t < 3; t++) store_tile(acc[2 + t], 2, t);
             }
         }
 
@@ -381,7 +427,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillParam
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- inverses of the 16x16 diagonal blocks of (I + A), by forward
         //      substitution, one column per lane (wave 0) ----
@@ -398,33 +444,39 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillParam
 #pragma unroll
             for (int r = 0; r < 16; r++) Td[(16 * b + r) * PD + c] = x[r];
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- D: block forward substitution of (I + A) D = R on this wave's
         //      column, D_b = Tbb (R_b - sum_{k<b} A_bk D_k) ----
         float4_t dacc[4];
 #pragma unroll
         for (int b = 0; b < 4; b++) {
-            float4_t x = rr[b];
-#pragma unroll
-            for (int k = 0; k < b; k++) {
-                const float4_t nd = -dacc[k];
-                mma_blk_f32(x, Af + 16 * b * PF + 16 * k, PF, nd);
-            }
             dacc[b] = kZero4;
-            mma_blk_f32(dacc[b], Td + 16 * b * PD, PD, x);
+            mma_blk_f32(dacc[b], Td + 16 * b * PD, PD, rr[b]);
+            const float4_t nd = -dacc[b];
+#pragma unroll
+            for (int c = b + 1; c < 4; c++) mma_blk_f32(rr[c], Af + 16 * c * PF + 16 * b, PF, nd);
         }
         // ---- o = scale (e^gam Q H + P D) ----
+        {
+            float4_t oacc[4];
 #pragma unroll
-        for (int b = 0; b < 4; b++) {
-            float4_t oacc = kZero4;
+            for (int b = 0; b < 4; b++) oacc[b] = kZero4;
 #pragma unroll
-            for (int k = 0; k <= b; k++) mma_blk_f32(oacc, Pf + 16 * b * PF + 16 * k, PF, dacc[k]);
+            for (int k = 0; k < 4; k++)
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const int r = 16 * b + 4 * lg + e;
-                if (r < L)
-                    Elem<TOut>::put(out + ((c0 + r) * p.h_v + h) * DV + col, p.scale * (eg[r] * qh[b][e] + oacc[e]));
+                for (int b = k; b < 4; b++) mma_blk_f32(oacc[b], Pf + 16 * b * PF + 16 * k, PF, dacc[k]);
+#pragma unroll
+            for (int b = 0; b < 4; b++) {
+                const float4 egv = *reinterpret_cast<const float4*>(eg + 16 * b + 4 * lg);
+                const float egr[4] = {egv.x, egv.y, egv.z, egv.w};
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const int r = 16 * b + 4 * lg + e;
+                    if (r < L)
+                        Elem<TOut>::put(out + ((c0 + r) * p.h_v + h) * DV + col,
+                                        p.scale * (egr[e] * qh[b][e] + oacc[b][e]));
+                }
             }
         }
         // ---- H <- e^{gam_last} H + K^T diag(e^{gam_last - gam} / |k|) D ----
@@ -453,7 +505,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillParam
                 hacc[it] = combine(hh, xx);
             }
         }
-        __syncthreads();
+        lds_barrier();
     }
 
     if (p.final_state) {
