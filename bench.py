@@ -37,10 +37,15 @@ def prefill_algorithmic(T, N, h_k, h_v, d, in_bytes=2, out_bytes=4, chunk=64):
     return bytes_, flops
 
 
-def decode_algorithmic(N, h_k, h_v, d, in_bytes=2, out_bytes=4):
-    """State read + write, q/k/v/g/beta read, o written; ~ (6 d^2 + O(d)) flops per (slot, head)."""
+def decode_algorithmic(N, h_k, h_v, d, in_bytes=2, out_bytes=4, conv=True):
+    """State read + write, q/k/v/g/beta read, o written, and with the conv
+    prologue the conv history read + written and the conv weights read;
+    ~ (6 d^2 + O(d)) flops per (slot, head)."""
     state = N * h_v * d * d * 4
-    bytes_ = 2 * state + N * (2 * h_k * d + h_v * d) * in_bytes + N * h_v * 2 * 4 + N * h_v * d * out_bytes
+    C = 2 * h_k * d + h_v * d
+    bytes_ = 2 * state + N * C * in_bytes + N * h_v * 2 * 4 + N * h_v * d * out_bytes
+    if conv:
+        bytes_ += 2 * N * C * 3 * in_bytes + C * 4 * in_bytes
     flops = N * h_v * 7.0 * d * d
     return bytes_, flops
 
@@ -100,7 +105,8 @@ def main():
 
     import torch
     import gateddeltanet_chunked_delta_amd as gdn
-    from gateddeltanet_chunked_delta_amd.inputs import Geometry, decode_inputs, prefill_inputs, state_pool
+    from gateddeltanet_chunked_delta_amd.inputs import (Geometry, conv_state_pool, conv_weights, decode_inputs,
+                                                        prefill_inputs, state_pool)
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -173,8 +179,16 @@ def main():
 
     if not args.no_decode:
         N = 256
-        print("[bench] decode: 256 slots, 512 MiB pool", file=sys.stderr, flush=True)
-        pool = torch.from_numpy(state_pool(3, N, geom)).to(dev)
+        # Four pools in rotation: a pool comes back only after 1.5 GiB of other
+        # state traffic, so no cache (256 MiB of last-level cache) holds it
+        # between its steps, as in a model where every layer has its own pool.
+        NPOOL = 4
+        print(f"[bench] decode: 256 slots, {NPOOL} rotating 512 MiB pools", file=sys.stderr, flush=True)
+        pools = [torch.from_numpy(state_pool(3, N, geom)).to(dev) for _ in range(1)]
+        pools += [pools[0].clone() for _ in range(NPOOL - 1)]
+        cpools = [torch.from_numpy(conv_state_pool(3, N, geom, "bf16")).to(dev, bf) for _ in range(1)]
+        cpools += [cpools[0].clone() for _ in range(NPOOL - 1)]
+        cw = torch.from_numpy(conv_weights(3, geom, "bf16")).to(dev, bf)
         nsteps = args.decode_steps
         dins = []
         for s in range(nsteps):
@@ -182,20 +196,26 @@ def main():
             dins.append(tuple(torch.from_numpy(a).to(dev, dt) for a, dt in
                               ((d.q, bf), (d.k, bf), (d.v, bf), (d.g, torch.float32), (d.beta, torch.float32))))
         od = torch.empty((N, 32, 128), dtype=torch.float32, device=dev)
-        for s in range(min(5, nsteps)):
-            gdn.gdn_decode_step(*dins[s], pool, out=od, validate=False)
+
+        def dstep(s):
+            gdn.gdn_decode_step(*dins[s], pools[s % NPOOL], out=od, conv_weight=cw,
+                                conv_state_pool=cpools[s % NPOOL], validate=False)
+
+        for s in range(min(2 * NPOOL, nsteps)):
+            dstep(s)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for s in range(nsteps):
-            gdn.gdn_decode_step(*dins[s], pool, out=od, validate=False)
+            dstep(s)
         e1.record(stream)
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / nsteps
         dbytes, dflops = decode_algorithmic(N, 16, 32, 128)
         gbs = dbytes / (us * 1e-6) / 1e9
         result["decode"] = {"workload": "decode step, 256 slots x 32 value heads (16 key heads), d=128, "
-                                        "bf16 q/k/v, fp32 512 MiB state pool in place",
+                                        "bf16 q/k/v, conv4+SiLU+L2, fp32 512 MiB state pool in place, "
+                                        f"{NPOOL} pools in rotation",
                             "steps": nsteps, "us_per_step": us, "GB/s": gbs,
                             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                          "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic(DECODE_KERNEL),

@@ -272,6 +272,35 @@ def test_decode_conv_and_indices(oracle_mod, dtype, d):
     assert np.array_equal(pool[1].cpu().numpy(), pool_np[1])  # untouched entries
 
 
+@pytest.mark.parametrize("h_k,h_v,d_k,d_v", [(3, 3, 64, 64), (2, 6, 128, 64), (1, 4, 64, 128)])
+def test_decode_gqa_groups(oracle_mod, h_k, h_v, d_k, d_v):
+    """Value heads per key head 1, 3 and 4 (one workgroup serves the group and
+    shifts its conv history), with d_k != d_v, conv and an index map."""
+    geom = Geometry(h_k, h_v, d_k, d_v)
+    P, N = 6, 4
+    dt = torch.bfloat16
+    pool_np = state_pool(53, P, geom)
+    cpool_np = conv_state_pool(53, P, geom, "bf16")
+    w_np = conv_weights(53, geom, "bf16")
+    idx = np.array([5, 1, -1, 2], dtype=np.int32)
+    pool, cpool = dev(pool_np), dev(cpool_np, dt)
+    ref_pool, ref_cpool = pool_np.astype(np.float64), cpool_np.astype(np.float64)
+    dims = oracle_mod.Dims(h_k, h_v, d_k, d_v, conv_width=4)
+    for s in range(2):
+        x = decode_inputs(53, s, N, geom, "bf16")
+        o = binding.gdn_decode_step(dev(x.q, dt), dev(x.k, dt), dev(x.v, dt), dev(x.g), dev(x.beta), pool,
+                                    state_indices=dev(idx, torch.int32), conv_weight=dev(w_np, dt),
+                                    conv_state_pool=cpool)
+        ro = oracle_mod.decode(dims, x.q, x.k, x.v, x.g, x.beta, ref_pool, idx.astype(np.int64), w_np, None,
+                               ref_cpool)
+        used = idx >= 0
+        assert rel_err(o.cpu().numpy()[used], ro[used]) <= TOL["bf16"]
+    assert rel_err(pool.cpu().numpy(), ref_pool) <= TOL["bf16"]
+    assert np.array_equal(cpool.float().cpu().numpy(), ref_cpool.astype(np.float32))
+    for e in (0, 3, 4):  # entries no index names stay untouched
+        assert np.array_equal(pool[e].cpu().numpy(), pool_np[e])
+
+
 def test_decode_steps_match_prefill(oracle_mod):
     """T decode steps from a pooled state equal one prefill of the T tokens (tolerance)."""
     geom = Geometry(2, 4, 128, 128)
