@@ -126,7 +126,8 @@ def main():
     o = torch.empty((T, 32, 128), dtype=torch.float32, device=dev)
     fs = torch.empty((B, 32, 128, 128), dtype=torch.float32, device=dev)
     cso = torch.empty((B, geom.channels, 3), dtype=bf, device=dev)
-    ws = torch.empty(4096, dtype=torch.uint8, device=dev)
+    prob = gdn.binding.make_problem(B, T, 16, 32, 128, 128, gdn.GDN_BF16, gdn.GDN_F32)
+    ws = torch.empty(gdn.binding.gdn_prefill_workspace_bytes(prob), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def step():

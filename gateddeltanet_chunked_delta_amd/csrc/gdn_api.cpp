@@ -53,8 +53,8 @@ gdn_status from_hip(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_HI
 extern "C" {
 
 size_t gdn_prefill_workspace_bytes(const gdn_problem* p) {
-    if (!p || p->num_seqs <= 0) return 0;
-    return (static_cast<size_t>(p->num_seqs) * sizeof(int32_t) + 255) / 256 * 256;
+    if (!p || p->num_seqs <= 0 || p->total_tokens < 0) return 0;
+    return gdn::prefill_layout(p->num_seqs, p->total_tokens, p->h_k, p->h_v, p->d_k, p->d_v).bytes;
 }
 
 gdn_status gdn_prefill_varlen(const gdn_problem* p, const void* q, const void* k, const void* v,
@@ -71,7 +71,10 @@ gdn_status gdn_prefill_varlen(const gdn_problem* p, const void* q, const void* k
     if (T > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL;
     if (p->conv_width == 4 && !conv_w) return GDN_ERR_NULL;
     if (!gdn::prefill_supported(p->d_k, p->d_v, p->qkv_dtype, p->out_dtype)) return GDN_ERR_UNSUPPORTED;
-    if (N > 0 && (!workspace || workspace_bytes < gdn_prefill_workspace_bytes(p))) return GDN_ERR_WORKSPACE;
+    const gdn::PrefillLayout lay = gdn::prefill_layout(N, T, p->h_k, p->h_v, p->d_k, p->d_v);
+    if (N > 0 && (lay.prep_blocks >= (int64_t(1) << 31) || lay.carry_blocks >= (int64_t(1) << 31)))
+        return GDN_ERR_SHAPE;
+    if (N > 0 && (!workspace || workspace_bytes < lay.bytes)) return GDN_ERR_WORKSPACE;
     if (N == 0) return GDN_OK;
 
     const int64_t eb = elem_bytes(p->qkv_dtype), ob = elem_bytes(p->out_dtype);
@@ -109,8 +112,16 @@ gdn_status gdn_prefill_varlen(const gdn_problem* p, const void* q, const void* k
     prm.q = q; prm.k = k; prm.v = v; prm.g = g; prm.beta = beta; prm.cu_seqlens = cu_seqlens;
     prm.conv_w = conv_w; prm.conv_b = conv_b; prm.conv_state_in = conv_state_in;
     prm.conv_state_out = conv_state_out; prm.initial_state = initial_state; prm.o = o;
-    prm.final_state = final_state; prm.order = static_cast<const int32_t*>(workspace);
-    prm.num_seqs = p->num_seqs; prm.h_k = p->h_k; prm.h_v = p->h_v; prm.conv_width = p->conv_width;
+    prm.final_state = final_state;
+    char* ws = static_cast<char*>(workspace);
+    prm.order = reinterpret_cast<int32_t*>(ws + lay.order);
+    prm.chunk_base = reinterpret_cast<int32_t*>(ws + lay.chunk_base);
+    prm.kq_img = ws + lay.kq_img;
+    prm.tp_img = ws + lay.tp_img;
+    prm.scal_img = reinterpret_cast<float*>(ws + lay.scal_img);
+    prm.slots = lay.slots;
+    prm.num_seqs = p->num_seqs; prm.h_k = p->h_k; prm.h_v = p->h_v; prm.d_v = p->d_v;
+    prm.conv_width = p->conv_width;
     prm.qk_l2norm = p->qk_l2norm; prm.l2_eps = eff_eps(p); prm.scale = eff_scale(p);
     return from_hip(gdn::launch_prefill(prm, p->d_k, p->d_v, p->qkv_dtype, p->out_dtype,
                                         static_cast<hipStream_t>(stream)));

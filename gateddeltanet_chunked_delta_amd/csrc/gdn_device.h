@@ -9,6 +9,12 @@ namespace gdn {
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
+// 16 raw bytes as a native vector (kept in registers across loop iterations,
+// where a struct-typed uint4 array can end up in scratch memory).
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 to_uint4(const u32x4_t& v) { return uint4{v[0], v[1], v[2], v[3]}; }
+__device__ __forceinline__ u32x4_t to_u32x4(const uint4& v) { return u32x4_t{v.x, v.y, v.z, v.w}; }
 
 // bf16 is carried as its uint16_t bit pattern.
 typedef uint16_t bf16_t;
@@ -154,14 +160,28 @@ __device__ __forceinline__ SFrag lds_sfrag(const _Float16* hi, const _Float16* l
 }
 
 // Fragment whose K index runs down the rows of row-major hi/lo LDS matrices:
-// element e is M[k + e][col].
-__device__ __forceinline__ SFrag lds_sfrag_t(const _Float16* hi, const _Float16* lo, int pitch, int k, int col) {
+// element e is M[k + e][col0 + l%16], read with the gfx950 LDS transpose load
+// (ds_read_b64_tr_b16), 4 instructions.  Within each 16-lane group the load treats
+// the 8-byte chunks addressed by lanes 0..15 as a 16x4 matrix M and returns
+// M[j/4 + 4m][j%4], m = 0..3, to lane j.  So lane j addresses 4 consecutive
+// columns col0 + 4 (j%4) .. of row k + j/4 and receives column col0 + j of
+// rows k .. k+3; a second load covers rows k+4 .. k+7.  col0 is a multiple of
+// 16 and the rows must be 8-byte aligned.
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4_t lds_short4_t;
+// The loaded vectors are reinterpreted whole and joined with a shuffle: with
+// ROCm 7.2's clang, extracting their 16-bit elements one by one produced code
+// that kept only the first two elements of each load (checked on the GPU).
+__device__ __forceinline__ half4_t lds_tr16(const _Float16* p) {
+    return __builtin_bit_cast(half4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(p)));
+}
+__device__ __forceinline__ SFrag lds_sfrag_tr(const _Float16* hi, const _Float16* lo, int pitch, int k, int col0) {
+    const int j = threadIdx.x & 15;
+    const int off = (k + (j >> 2)) * pitch + col0 + 4 * (j & 3);
     SFrag f;
-#pragma unroll
-    for (int e = 0; e < 8; e++) {
-        f.hi[e] = hi[(k + e) * pitch + col];
-        f.lo[e] = lo[(k + e) * pitch + col];
-    }
+    f.hi = __builtin_shufflevector(lds_tr16(hi + off), lds_tr16(hi + off + 4 * pitch), 0, 1, 2, 3, 4, 5, 6, 7);
+    f.lo = __builtin_shufflevector(lds_tr16(lo + off), lds_tr16(lo + off + 4 * pitch), 0, 1, 2, 3, 4, 5, 6, 7);
     return f;
 }
 

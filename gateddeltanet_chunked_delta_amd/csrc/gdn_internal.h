@@ -8,7 +8,7 @@
 
 namespace gdn {
 
-// Everything the fused chunked-prefill kernel needs, passed by value.
+// Everything the chunked-prefill kernels need, passed by value.
 struct PrefillParams {
     const void* q;              // [T][h_k][d_k]
     const void* k;              // [T][h_k][d_k]
@@ -23,14 +23,30 @@ struct PrefillParams {
     const float* initial_state; // [N][h_v][d_k][d_v] or null
     void* o;                    // [T][h_v][d_v]
     float* final_state;         // [N][h_v][d_k][d_v] or null
-    const int32_t* order;       // [N] dispatch order (workspace)
+    // workspace (see PrefillLayout)
+    int32_t* order;             // [N] sequences, longest first
+    int32_t* chunk_base;        // [N+1] chunks before each sequence
+    void* kq_img;               // [slots][h_k] K|Q split-fp16 images
+    void* tp_img;               // [slots][h_v] T|P split-fp16 images
+    float* scal_img;            // [slots][h_v][4][64] per-token scalars
+    int64_t slots;              // chunk slots: >= sum_n ceil(len_n / 64)
     int32_t num_seqs;
     int32_t h_k, h_v;
+    int32_t d_v;
     int32_t conv_width;         // 0 or 4
     int32_t qk_l2norm;
     float l2_eps;
     float scale;
 };
+
+// Byte offsets of the prefill workspace regions (each 256-byte aligned) and
+// the grid sizes the launches will use.
+struct PrefillLayout {
+    size_t order, chunk_base, kq_img, tp_img, scal_img, bytes;
+    int64_t slots, prep_blocks, carry_blocks;
+};
+PrefillLayout prefill_layout(int64_t num_seqs, int64_t total_tokens, int64_t h_k, int64_t h_v, int64_t d_k,
+                             int64_t d_v);
 
 struct DecodeParams {
     const void* q;              // [N][h_k][d_k]

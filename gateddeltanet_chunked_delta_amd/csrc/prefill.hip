@@ -1,47 +1,46 @@
 // Chunked varlen prefill of the gated delta rule on gfx950.
 //
-// One workgroup owns one (sequence, value head, 64-column slice of d_v) and
-// walks that sequence's 64-token chunks in order, keeping its slice of the
-// fp32 state H (d_k x 64) in matrix-core accumulators for the whole sequence.
-// Chunks are aligned to the sequence start and padded with zero rows, so a
-// sequence's arithmetic never depends on the rest of the batch ("[Feature] Add
-// batch invariance support to GDN_ATTN backend", commit messages: one
-// cu_seqlens = [0, len] and fresh chunk indices per sequence; review part
-// "3. The chunked delta-rule scan itself" (a): 64-token blocks, state carried
-// across chunk boundaries).
+// The recurrence S_t = e^{g_t} S_{t-1} + beta_t (v_t - e^{g_t} S_{t-1} k_t)
+// k_t^T ("Qwen3.5-27B GPTQ Garbage Inference -- Root Cause Analysis", section
+// "Why abliteration failed on Qwen3.5", item 3) is evaluated in 64-token
+// chunks aligned to each sequence start, zero-padded at the tail, with the
+// fp32 state carried across chunks ("[Feature] Add batch invariance support
+// to GDN_ATTN backend", review part "3. The chunked delta-rule scan itself"
+// (a); commit messages: one cu_seqlens = [0, len] and fresh chunk indices per
+// sequence).  With gam_r = sum_{s<=r} g_s inside a chunk, H = S^T and q, k
+// L2-normalised:
+//   A[r][s] = beta_r e^{gam_r - gam_s} (k_r . k_s)   s <  r
+//   T       = (I + A)^{-1}
+//   P[r][s] =        e^{gam_r - gam_s} (q_r . k_s)   s <= r
+//   R       = diag(beta) (V - diag(e^gam) K H)
+//   D       = T R                       (the per-token deltas)
+//   o       = scale (diag(e^gam) Q H + P D)
+//   H      <- e^{gam_last} H + K^T diag(e^{gam_last - gam}) D
+// Everything but the last four lines is independent of H, so it runs in
+// parallel over all chunks; only R, D, o and the update form the dependent
+// chain over a sequence's chunks.  The launches:
+//   chunk_map_kernel  chunk_base[n] = chunks before sequence n
+//   order_kernel      sequences by descending chunk count (longest first)
+//   prep_kernel       per (chunk, key head): conv(4) + SiLU + L2 norm of q
+//                     and k; K K^T and Q K^T; then per value head of the
+//                     group: the decays, T and P.  Writes split-fp16 images
+//                     of K, Q, T, P and the per-token scalars to the workspace.
+//   carry_kernel      per (sequence, value head, 64 columns of d_v): conv of
+//                     v, then the chain above with the state slice held in
+//                     matrix-core accumulators.  The next chunk's images are
+//                     loaded into registers while the current chunk computes.
+//   conv_state_kernel the final conv states.
 //
-// Per chunk of L <= 64 tokens, with gam_r = sum_{s<=r} g_s (chunk-local):
-//   prologue   causal conv(4) + SiLU of the raw q|k|v rows (3 rows of history
-//              from the previous chunk, the conv state, or zeros); the per
-//              head L2 norms of q and k are row scales, applied to the fp32
-//              results of the products that read q and k.
-//   A[r][s]  = beta_r e^{gam_r - gam_s} (k_r . k_s)       s <  r
-//   P[r][s]  =        e^{gam_r - gam_s} (q_r . k_s)       s <= r
-//   R        = diag(beta) (V - diag(e^gam) K H)
-//   D        = (I + A)^{-1} R            (the per-token deltas: inverses of
-//                                         the 16x16 diagonal blocks, then block
-//                                         forward substitution)
-//   o        = scale (diag(e^gam) Q H + P D)
-//   H       <- e^{gam_last} H + K^T diag(e^{gam_last - gam}) D
-// This is the delta rule S_t = e^{g_t} S_{t-1} + beta_t (v_t - e^{g_t}
-// S_{t-1} k_t) k_t^T unrolled over a chunk ("Qwen3.5-27B GPTQ Garbage
-// Inference -- Root Cause Analysis", section "Why abliteration failed on
-// Qwen3.5", item 3).  Solving for D from the current state's residuals R
-// (rather than precomputing W = (I + A)^{-1} diag(beta e^gam) K and
-// U = (I + A)^{-1} diag(beta) V) skips one 64x64xd_k product per chunk, which
-// suits a kernel that runs the chunks of one sequence back to back.
+// Precision: every product takes split-fp16 operands (x = hi + lo 2^-11,
+// three fp16 matrix-core steps, fp32 accumulation), about 22 significant bits
+// per operand; the diagonal blocks of T come from an fp32 forward
+// substitution and the off-diagonal blocks from fp32 matrix-core steps; the
+// decays are scanned and exponentiated in fp64.  Operand magnitudes must stay
+// below the fp16 limit (65504).
 //
-// Precision: the products with d_k-long reductions take split-fp16 operands
-// (x = hi + lo 2^-11, three fp16 matrix-core steps, fp32 accumulation), about
-// 22 significant bits per operand; the 16-wide block products of the
-// substitution and of P D run on fp32 matrix-core steps.  A single fp16 rounding of any operand would already cost up to
-// ~1e-2 of rms(o) in the worst element, because the outputs and states are
-// sums of heavy-tailed products.  Operand magnitudes must stay below the fp16
-// limit (65504); with q/k L2-normalised they are O(1).
-//
-// All reductions run in a fixed order inside one workgroup: no atomics and
-// no batch-dependent split, so results are bit-reproducible and
-// batch-invariant.
+// All reductions run in a fixed order inside one workgroup, with no atomics
+// and no batch-dependent split: a sequence's results are bit-identical
+// whatever else shares the call.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -51,40 +50,114 @@ namespace {
 constexpr int kChunk = 64;
 constexpr int kThreads = 256;
 constexpr int kLdsLimit = 163840;  // gfx950: 160 KiB per workgroup
+constexpr int kDvs = 64;           // d_v columns per carry workgroup
 
-// LDS carve-up for one workgroup.  K and Q (read by all four waves as
-// matrix operands) are split-fp16 pairs (hi, lo); A, P, V and the diagonal
-// inverse blocks are fp32.  Row pitches pad rows by 16 bytes so that the
-// 16-byte reads of one wave spread over the banks.
-template <int DK, int DVS, int VEC>
-struct Smem {
-    static constexpr int kPitchK = DK + 8;      // K, Q rows: [token][d_k] (fp16)
-    static constexpr int kPitchF = kChunk + 4;  // A, P rows: [token][token] (fp32)
-    static constexpr int kPitchV = DVS + 4;     // V rows: [token][column] (fp32)
-    static constexpr int kPitchD = 20;          // diagonal inverse blocks: [4][16][kPitchD] (fp32)
-    static constexpr int kRedCols = 2 * (DK / VEC);  // q|k partial sums of squares per row
-
-    static constexpr size_t szKQ = size_t(kChunk) * kPitchK * sizeof(_Float16);
-    static constexpr size_t oKhi = 0;
-    static constexpr size_t oKlo = oKhi + szKQ;
-    static constexpr size_t oQhi = oKlo + szKQ;
-    static constexpr size_t oQlo = oQhi + szKQ;
-    static constexpr size_t oA = oQlo + szKQ;
-    static constexpr size_t oP = oA + size_t(kChunk) * kPitchF * sizeof(float);
-    static constexpr size_t oV = oP + size_t(kChunk) * kPitchF * sizeof(float);
-    static constexpr size_t oTd = oV + size_t(kChunk) * kPitchV * sizeof(float);
-    static constexpr size_t oRed = oTd + size_t(4) * 16 * kPitchD * sizeof(float);  // q|k partial sums of squares
-    static constexpr size_t oGam = oRed + size_t(kChunk) * kRedCols * sizeof(float);  // gam (fp64)
-    // e^gam, beta, e^{gam_last-gam}, 1/|q|, 1/|k| per token, e^{gam_last}
-    static constexpr size_t oScal = oGam + kChunk * sizeof(double);
-    static constexpr size_t kBytes = oScal + (5 * kChunk + 4) * sizeof(float);
-
-    static_assert(kBytes <= size_t(kLdsLimit), "LDS budget");
-    static_assert(oKlo % 16 == 0 && oQhi % 16 == 0 && oQlo % 16 == 0 && oA % 16 == 0 && oP % 16 == 0 &&
-                      oV % 16 == 0 && oTd % 16 == 0 && oRed % 16 == 0 &&
-                      oGam % 16 == 0 && oScal % 16 == 0,
-                  "16-byte aligned regions");
+// Workspace images, per chunk slot: [h_k] K|Q images, each a hi and a lo
+// fp16 plane of [64][d_k]; [h_v] T|P images, each a hi and a lo plane of the
+// 10 lower 16x16 blocks of a 64x64 matrix (TriPack); [h_v] scalar rows beta,
+// e^gam, e^{gam_last - gam}, e^{gam_last}.
+// A TriPack plane stores row r's columns [0, 16 (r/16 + 1)) as 16-byte
+// pieces, rows in order: 320 pieces.
+struct TriPack {
+    static constexpr int kPieces = 320;
+    // first piece of row r
+    __device__ __forceinline__ static int row_start(int r) {
+        const int b = r >> 4;
+        return 16 * b * (b + 1) + 2 * (b + 1) * (r & 15);
+    }
+    // row and 8-column group of piece q
+    __device__ __forceinline__ static void locate(int q, int& r, int& c8) {
+        const int b = q < 32 ? 0 : (q < 96 ? 1 : (q < 192 ? 2 : 3));
+        const int w = 2 * (b + 1), q0 = q - 16 * b * (b + 1);
+        r = 16 * b + q0 / w;
+        c8 = q0 % w;
+    }
 };
+
+template <int DK>
+struct Img {
+    static constexpr int kKQ = 2 * 2 * kChunk * DK;            // halves per (slot, key head)
+    static constexpr int kTP = 2 * 2 * TriPack::kPieces * 8;   // halves per (slot, value head)
+    static constexpr int kScal = 4 * kChunk;                   // floats per (slot, value head)
+};
+
+// ---------------------------------------------------------------- prologue
+
+// conv(4) + SiLU of row i of one 16-byte channel group: xr[i .. i+3] hold the
+// raw rows from 3 before it; wp the taps as raw packs (w[4 e + tap]).
+template <typename TIn>
+__device__ __forceinline__ void conv_row(bool conv, const u32x4_t* xr, const u32x4_t (&wp)[4],
+                                         const float (&bias)[Elem<TIn>::kVec], int i,
+                                         float (&y)[Elem<TIn>::kVec]) {
+    constexpr int VEC = Elem<TIn>::kVec;
+    if (conv) {
+        float wv[4 * VEC], xs[4][VEC];
+#pragma unroll
+        for (int m = 0; m < 4; m++) Elem<TIn>::unpack16(to_uint4(wp[m]), wv + m * VEC);
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++) Elem<TIn>::unpack16(to_uint4(xr[i + jj]), xs[jj]);
+#pragma unroll
+        for (int e = 0; e < VEC; e++) {
+            float acc = bias[e];
+#pragma unroll
+            for (int jj = 0; jj < 4; jj++) acc += wv[4 * e + jj] * xs[jj][e];
+            y[e] = silu(acc);
+        }
+    } else {
+        Elem<TIn>::unpack16(to_uint4(xr[i + 3]), y);
+    }
+}
+
+// Raw 16-byte rows r0-3 .. r0+R-1 of one channel group for the chunk starting
+// at token c0 (L valid rows; the sequence starts at bos).  Rows before the
+// sequence start come from the conv state `hist` (3 inputs per channel,
+// oldest first; channel e of the group at hist + 3 e) or are zero; rows at or
+// past L are zero.  Without the conv only rows r0.. are read.
+template <typename TIn, int R>
+__device__ __forceinline__ void load_rows(u32x4_t (&x)[R + 3], const TIn* base, int64_t stride, int64_t c0,
+                                          int r0, int L, int64_t bos, bool conv, const TIn* hist) {
+#pragma unroll
+    for (int j = 0; j < R + 3; j++) {
+        const int row = r0 - 3 + j;
+        const int64_t tt = c0 + row;
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        if (row < L && (conv || j >= 3)) {
+            if (tt >= bos) {
+                v = *reinterpret_cast<const u32x4_t*>(base + tt * stride);
+            } else if (hist) {
+                uint4 u = {0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int e = 0; e < Elem<TIn>::kVec; e++) Elem<TIn>::set16(u, e, hist + 3 * e + (3 + (tt - bos)));
+                v = to_u32x4(u);
+            }
+        }
+        x[j] = v;
+    }
+}
+
+// The 4 conv taps and the bias of one 16-byte channel group starting at
+// channel ch, kept in registers by the workgroup.
+template <typename TIn>
+__device__ __forceinline__ void conv_params(const PrefillParams& p, int64_t ch, u32x4_t (&wp)[4],
+                                            float (&bias)[Elem<TIn>::kVec]) {
+    constexpr int VEC = Elem<TIn>::kVec;
+    const TIn* cw = static_cast<const TIn*>(p.conv_w);
+    const TIn* cb = static_cast<const TIn*>(p.conv_b);
+#pragma unroll
+    for (int m = 0; m < 4; m++) wp[m] = u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < VEC; e++) bias[e] = 0.0f;
+    if (p.conv_width == 4) {
+#pragma unroll
+        for (int m = 0; m < 4; m++) wp[m] = *reinterpret_cast<const u32x4_t*>(cw + ch * 4 + m * VEC);
+        if (cb) {
+#pragma unroll
+            for (int e = 0; e < VEC; e++) bias[e] = Elem<TIn>::get(cb + ch + e);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- products
 
 // Gram tiles of two tile-rows R0 < R1 of A B^T (A = K or Q rows, B = K rows),
 // all lower tiles (R0, 0..R0) and (R1, 0..R1): R0 + R1 + 2 tiles that share
@@ -127,201 +200,262 @@ __device__ __forceinline__ void mma_blk_f32(float4_t& acc, const float* a, int p
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.w, x[3], acc, 0, 0, 0);
 }
 
-// Workgroup = (sequence, value head, 64-column slice of d_v); wave w owns the
-// 16 state columns [16w, 16w + 16) of the slice.  The state slice and the
-// per-token residuals R and deltas D of those columns stay in registers in
-// matrix-core accumulator layout; K, Q, A, P and V are shared through LDS.
-template <int DK, int DV, typename TIn, typename TOut>
-__global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillParams p) {
-    constexpr int DVS = 64;
-    constexpr int NS = DV / DVS;
+// Column block J of T = (I + A)^{-1} below the diagonal:
+//   T_iJ = -T_ii sum_{k=J}^{i-1} A_ik T_kJ,  i = J+1 .. 3,
+// from the diagonal inverses in Td; blocks (J..3, J) are written to Tf.
+// Block products on fp32 matrix-core steps, in a fixed order.
+template <int J, int PF, int PD>
+__device__ __forceinline__ void inverse_column(const float* Af, const float* Td, float* Tf, int lr, int lg) {
+    float4_t tc[4];
+#pragma unroll
+    for (int e = 0; e < 4; e++) tc[J][e] = Td[(16 * J + 4 * lg + e) * PD + lr];
+#pragma unroll
+    for (int i = J + 1; i < 4; i++) {
+        float4_t s = kZero4;
+#pragma unroll
+        for (int k = J; k < i; k++) mma_blk_f32(s, Af + 16 * i * PF + 16 * k, PF, tc[k]);
+        float4_t t = kZero4;
+        mma_blk_f32(t, Td + 16 * i * PD, PD, s);
+        tc[i] = -t;
+    }
+#pragma unroll
+    for (int i = J; i < 4; i++)
+#pragma unroll
+        for (int e = 0; e < 4; e++) Tf[(16 * i + 4 * lg + e) * PF + 16 * J + lr] = tc[i][e];
+}
+
+// Split 8 consecutive fp32 values into 16-byte hi and lo packs.
+__device__ __forceinline__ void split_pack(const float (&x)[8], uint4& hi, uint4& lo) {
+    const SFrag f = split8(x);
+    hi = *reinterpret_cast<const uint4*>(&f.hi);
+    lo = *reinterpret_cast<const uint4*>(&f.lo);
+}
+
+// ---------------------------------------------------------------- chunk map
+
+// chunk_base[n] = sum_{m<n} ceil(len_m / 64), chunk_base[N] = total chunks.
+// One workgroup scans the sequences in tiles of 256.
+__global__ void __launch_bounds__(256) chunk_map_kernel(const int32_t* __restrict__ cu, int32_t n,
+                                                         int32_t* __restrict__ base) {
+    __shared__ int32_t s[256];
+    const int t = threadIdx.x;
+    int32_t carry = 0;
+    for (int t0 = 0; t0 < n; t0 += 256) {
+        const int i = t0 + t;
+        const int32_t c = i < n ? int32_t((int64_t(cu[i + 1]) - cu[i] + kChunk - 1) / kChunk) : 0;
+        s[t] = c;
+        __syncthreads();
+        for (int o = 1; o < 256; o <<= 1) {
+            const int32_t x = t >= o ? s[t - o] : 0;
+            __syncthreads();
+            s[t] += x;
+            __syncthreads();
+        }
+        if (i < n) base[i] = carry + s[t] - c;
+        carry += s[255];
+        __syncthreads();
+    }
+    if (t == 0) base[n] = carry;
+}
+
+// Sequences ordered by descending chunk count (ties by index), so that the
+// longest dependent chains start first.  Ranks are unique, so the map is a
+// permutation for any cu_seqlens contents.  The order only schedules work:
+// results do not depend on it.  Beyond kMaxRanked sequences the quadratic
+// ranking is skipped and the identity order used.
+constexpr int kMaxRanked = 8192;
+__global__ void __launch_bounds__(256) order_kernel(const int32_t* __restrict__ cu, int32_t n,
+                                                     int32_t* __restrict__ order) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    if (n > kMaxRanked) {
+        order[i] = i;
+        return;
+    }
+    const int64_t ci = (int64_t(cu[i + 1]) - cu[i] + kChunk - 1) / kChunk;
+    int rank = 0;
+    for (int j = 0; j < n; j++) {
+        const int64_t cj = (int64_t(cu[j + 1]) - cu[j] + kChunk - 1) / kChunk;
+        rank += (cj > ci) || (cj == ci && j < i);
+    }
+    order[rank] = i;
+}
+
+// ---------------------------------------------------------------- prep: q|k prologue and chunk-local terms
+
+template <int DK, int VEC>
+struct PrepSmem {
+    static constexpr int kPitchK = DK + 8;      // K, Q rows: [token][d_k] (fp16)
+    static constexpr int kPitchF = kChunk + 4;  // [token][token] (fp32)
+    static constexpr int kPitchD = 20;          // diagonal inverse blocks: [4][16][kPitchD]
+    static constexpr int kNG = 2 * (DK / VEC);  // q|k 16-byte groups per row
+
+    static constexpr size_t szKQ = size_t(kChunk) * kPitchK * sizeof(_Float16);
+    static constexpr size_t szF = size_t(kChunk) * kPitchF * sizeof(float);
+    static constexpr size_t oKhi = 0, oKlo = szKQ, oQhi = 2 * szKQ, oQlo = 3 * szKQ;
+    static constexpr size_t oKK = 4 * szKQ;
+    static constexpr size_t oQK = oKK + szF;
+    static constexpr size_t oA = oQK + szF;  // also the q|k partial sums of squares during the prologue
+    static constexpr size_t oT = oA + szF;
+    static constexpr size_t oTd = oT + szF;
+    static constexpr size_t oGam = oTd + size_t(4) * 16 * kPitchD * sizeof(float);
+    static constexpr size_t oScal = oGam + kChunk * sizeof(double);  // eg, bet, rq, rk [64]
+    static constexpr size_t kBytes = oScal + 4 * kChunk * sizeof(float);
+
+    static_assert(size_t(kChunk) * kNG * sizeof(float) <= szF, "partial sums fit the A region");
+    static_assert(kBytes <= size_t(kLdsLimit), "LDS budget");
+    static_assert(oKK % 16 == 0 && oQK % 16 == 0 && oA % 16 == 0 && oT % 16 == 0 && oTd % 16 == 0 &&
+                      oGam % 16 == 0 && oScal % 16 == 0,
+                  "16-byte aligned regions");
+};
+
+// Workgroup = (chunk slot, key head).  Slots past the last chunk exit.
+template <int DK, typename TIn>
+__global__ void __launch_bounds__(kThreads, 1) prep_kernel(const PrefillParams p) {
     constexpr int VEC = Elem<TIn>::kVec;
-    constexpr int NGQ = DK / VEC;           // 16-byte groups per q (or k) head row
+    constexpr int NGQ = DK / VEC;       // 16-byte groups per q (or k) head row
     constexpr int NG = 2 * NGQ;
-    constexpr int RB = kThreads / NG;       // q|k prologue: row blocks per chunk
-    constexpr int RPB = kChunk / RB;        // q|k rows per thread
-    constexpr int NGV = DVS / VEC;          // 16-byte groups of a v slice row
-    constexpr int VRPB = kChunk / (kThreads / NGV);  // v rows per thread
-    constexpr int KT = DK / 16;             // 16-row tiles of the state column
-    constexpr int KS = DK / 32;             // 32-wide steps over d_k
+    constexpr int RB = kThreads / NG;   // row blocks per chunk
+    constexpr int RPB = kChunk / RB;    // rows per thread
+    constexpr int KS = DK / 32;
     static_assert(kThreads % NG == 0 && kChunk % RB == 0, "q|k prologue tiling");
-    static_assert(kThreads % NGV == 0 && kChunk % (kThreads / NGV) == 0, "v prologue tiling");
-    static_assert(DV % DVS == 0, "d_v slices");
-    using S = Smem<DK, DVS, VEC>;
-    constexpr int PK = S::kPitchK, PF = S::kPitchF, PV = S::kPitchV, PD = S::kPitchD;
+    using S = PrepSmem<DK, VEC>;
+    constexpr int PK = S::kPitchK, PF = S::kPitchF, PD = S::kPitchD;
 
     __shared__ __attribute__((aligned(16))) char smem[S::kBytes];
     _Float16* Khi = reinterpret_cast<_Float16*>(smem + S::oKhi);
     _Float16* Klo = reinterpret_cast<_Float16*>(smem + S::oKlo);
     _Float16* Qhi = reinterpret_cast<_Float16*>(smem + S::oQhi);
     _Float16* Qlo = reinterpret_cast<_Float16*>(smem + S::oQlo);
+    float* KK = reinterpret_cast<float*>(smem + S::oKK);
+    float* QK = reinterpret_cast<float*>(smem + S::oQK);
     float* Af = reinterpret_cast<float*>(smem + S::oA);
-    float* Pf = reinterpret_cast<float*>(smem + S::oP);
-    float* Vf = reinterpret_cast<float*>(smem + S::oV);
+    float* red = Af;
+    float* Tf = reinterpret_cast<float*>(smem + S::oT);
     float* Td = reinterpret_cast<float*>(smem + S::oTd);
-    float* red = reinterpret_cast<float*>(smem + S::oRed);
     double* gam = reinterpret_cast<double*>(smem + S::oGam);
-    float* eg = reinterpret_cast<float*>(smem + S::oScal);
-    float* bet = eg + kChunk;
-    float* dl = bet + kChunk;
-    float* rq = dl + kChunk;
+    float* bet = reinterpret_cast<float*>(smem + S::oScal);
+    float* rq = bet + kChunk;
     float* rk = rq + kChunk;
-    float* egl = rk + kChunk;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
-    const int u = blockIdx.x;
-    const int slice = u % NS;
-    const int h = (u / NS) % p.h_v;
-    const int n = p.order[u / (NS * p.h_v)];
-    const int hk = h / (p.h_v / p.h_k);
-    const int wcol = 16 * wave + lr;               // this lane's column within the slice
-    const int col = slice * DVS + wcol;            // ... and within d_v
+    const int cs = int(blockIdx.x / unsigned(p.h_k)), hk = int(blockIdx.x % unsigned(p.h_k));
+    if (cs >= p.chunk_base[p.num_seqs]) return;
+    // the sequence of this slot: the last n with chunk_base[n] <= cs
+    int lo = 0, hi = p.num_seqs - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (p.chunk_base[mid] <= cs) lo = mid;
+        else hi = mid - 1;
+    }
+    const int n = lo;
+    const int G = p.h_v / p.h_k;
     const int64_t bos = p.cu_seqlens[n], eos = p.cu_seqlens[n + 1];
-    const int64_t nq = int64_t(p.h_k) * DK, nv = int64_t(p.h_v) * DV, C = 2 * nq + nv;
-    const TIn* qin = static_cast<const TIn*>(p.q);
-    const TIn* kin = static_cast<const TIn*>(p.k);
-    const TIn* vin = static_cast<const TIn*>(p.v);
-    const TIn* cw = static_cast<const TIn*>(p.conv_w);
-    const TIn* cb = static_cast<const TIn*>(p.conv_b);
-    const TIn* csi = static_cast<const TIn*>(p.conv_state_in);
-    TOut* out = static_cast<TOut*>(p.o);
+    const int64_t c0 = bos + int64_t(cs - p.chunk_base[n]) * kChunk;
+    const int L = int(eos - c0 < kChunk ? eos - c0 : kChunk);
+    const int64_t nq = int64_t(p.h_k) * DK, C = 2 * nq + int64_t(p.h_v) * p.d_v;
     const bool conv = p.conv_width == 4;
-    const int64_t state_base = (int64_t(n) * p.h_v + h) * DK * DV + col;
 
-    // State column: hacc[it][e] = H[16 it + 4 lg + e][col].
-    float4_t hacc[KT];
-#pragma unroll
-    for (int it = 0; it < KT; it++)
-#pragma unroll
-        for (int e = 0; e < 4; e++)
-            hacc[it][e] = p.initial_state ? p.initial_state[state_base + int64_t(16 * it + 4 * lg + e) * DV] : 0.0f;
-
-    // Prologue assignments, fixed for the sequence: one 16-byte channel group
-    // of q|k (and one of the v slice) for a block of consecutive rows of every
-    // chunk.  The groups' conv taps stay in registers as raw 16-byte packs
-    // (w[4 e + tap]).
+    // ---- prologue: one 16-byte channel group of q|k for RPB consecutive rows ----
     const int pg = tid % NG, prow0 = (tid / NG) * RPB;
     const int pwhich = pg / NGQ, poff = (pg % NGQ) * VEC;
-    const TIn* pbase = (pwhich ? kin : qin) + hk * DK + poff;
     const int64_t pch = (pwhich ? nq : 0) + int64_t(hk) * DK + poff;
-    const int vg = tid % NGV, vrow0 = (tid / NGV) * VRPB;
-    const TIn* vbase = vin + int64_t(h) * DV + slice * DVS + vg * VEC;
-    const int64_t vch = 2 * nq + int64_t(h) * DV + slice * DVS + vg * VEC;
-    uint4 pw[4] = {}, vwp[4] = {};
-    float pbias[VEC], vbias[VEC];
+    float y[RPB][VEC];
+    {
+        u32x4_t pw[4];
+        float pbias[VEC];
+        conv_params<TIn>(p, pch, pw, pbias);
+        const TIn* pbase = static_cast<const TIn*>(pwhich ? p.k : p.q) + hk * DK + poff;
+        const TIn* hist = p.conv_state_in ? static_cast<const TIn*>(p.conv_state_in) + (int64_t(n) * C + pch) * 3
+                                          : nullptr;
+        u32x4_t xr[RPB + 3];
+        load_rows<TIn, RPB>(xr, pbase, nq, c0, prow0, L, bos, conv, hist);
 #pragma unroll
-    for (int e = 0; e < VEC; e++) pbias[e] = vbias[e] = 0.0f;
-    if (conv) {
-#pragma unroll
-        for (int m = 0; m < 4; m++) {
-            pw[m] = *reinterpret_cast<const uint4*>(cw + pch * 4 + m * VEC);
-            vwp[m] = *reinterpret_cast<const uint4*>(cw + vch * 4 + m * VEC);
-        }
-        if (cb) {
+        for (int i = 0; i < RPB; i++) {
+            conv_row<TIn>(conv, xr, pw, pbias, i, y[i]);
+            float ss = 0.0f;
 #pragma unroll
             for (int e = 0; e < VEC; e++) {
-                pbias[e] = Elem<TIn>::get(cb + pch + e);
-                vbias[e] = Elem<TIn>::get(cb + vch + e);
+                if (prow0 + i >= L) y[i][e] = 0.0f;
+                ss += y[i][e] * y[i][e];
+            }
+            red[(prow0 + i) * NG + pg] = ss;
+        }
+    }
+    lds_barrier();
+    // per-row 1/|q| and 1/|k| (fixed summation order)
+    if (tid < 2 * kChunk) {
+        const int r = tid & (kChunk - 1), which = tid / kChunk;
+        const float* rr = red + r * NG + which * NGQ;
+        float sum = 0.0f;
+#pragma unroll
+        for (int q = 0; q < NGQ; q++) sum += rr[q];
+        (which ? rk : rq)[r] = p.qk_l2norm ? 1.0f / sqrtf(sum + p.l2_eps) : 1.0f;
+    }
+    lds_barrier();
+    // normalised rows as split-fp16 pairs, into LDS and the K|Q image
+    {
+        // K image first, then Q
+        _Float16* img = static_cast<_Float16*>(p.kq_img) + (int64_t(cs) * p.h_k + hk) * Img<DK>::kKQ +
+                        (pwhich ? 0 : 2 * kChunk * DK);
+        _Float16* dhi = pwhich ? Khi : Qhi;
+        _Float16* dlo = pwhich ? Klo : Qlo;
+        const float* rn = pwhich ? rk : rq;
+#pragma unroll
+        for (int i = 0; i < RPB; i++) {
+            const int row = prow0 + i;
+            const float s = rn[row];
+            _Float16 h16[VEC], l16[VEC];
+#pragma unroll
+            for (int e = 0; e < VEC; e++) split1(y[i][e] * s, h16[e], l16[e]);
+            if constexpr (VEC == 8) {
+                const uint4 hv = *reinterpret_cast<const uint4*>(h16), lv = *reinterpret_cast<const uint4*>(l16);
+                *reinterpret_cast<uint4*>(dhi + row * PK + poff) = hv;
+                *reinterpret_cast<uint4*>(dlo + row * PK + poff) = lv;
+                *reinterpret_cast<uint4*>(img + row * DK + poff) = hv;
+                *reinterpret_cast<uint4*>(img + kChunk * DK + row * DK + poff) = lv;
+            } else {
+                const uint2 hv = *reinterpret_cast<const uint2*>(h16), lv = *reinterpret_cast<const uint2*>(l16);
+                *reinterpret_cast<uint2*>(dhi + row * PK + poff) = hv;
+                *reinterpret_cast<uint2*>(dlo + row * PK + poff) = lv;
+                *reinterpret_cast<uint2*>(img + row * DK + poff) = hv;
+                *reinterpret_cast<uint2*>(img + kChunk * DK + row * DK + poff) = lv;
             }
         }
     }
+    lds_barrier();
 
-    // conv(4) + SiLU of `rows` consecutive rows of one 16-byte channel group;
-    // xr holds the raw rows from 3 before the first (zero outside the data).
-    auto conv_rows = [&](const uint4* xr, const uint4 (&wp)[4], const float (&bias)[VEC], int i, float (&y)[VEC]) {
-        if (conv) {
-            float wv[4 * VEC], xs[4][VEC];
+    // ---- Gram tiles K K^T (waves 0, 1) and Q K^T (waves 2, 3), lower tiles
+    //      only, raw fp32; each wave two tile-rows ({0, 3} or {1, 2}). ----
+    {
+        const int which = wave >> 1;
+        const _Float16* Ahi = which ? Qhi : Khi;
+        const _Float16* Alo = which ? Qlo : Klo;
+        float* dst = which ? QK : KK;
+        auto store_tile = [&](const float4_t& acc, int ti, int tj) {
 #pragma unroll
-            for (int m = 0; m < 4; m++) Elem<TIn>::unpack16(wp[m], wv + m * VEC);
+            for (int e = 0; e < 4; e++) dst[(16 * ti + 4 * lg + e) * PF + 16 * tj + lr] = acc[e];
+        };
+        float4_t acc[5];
+        if ((wave & 1) == 0) {
+            gram_two_rows<0, 3, KS, PK>(Ahi, Alo, Khi, Klo, lr, lg, acc);
+            store_tile(acc[0], 0, 0);
 #pragma unroll
-            for (int jj = 0; jj < 4; jj++) Elem<TIn>::unpack16(xr[i + jj], xs[jj]);
-#pragma unroll
-            for (int e = 0; e < VEC; e++) {
-                float acc = bias[e];
-#pragma unroll
-                for (int jj = 0; jj < 4; jj++) acc += wv[4 * e + jj] * xs[jj][e];
-                y[e] = silu(acc);
-            }
+            for (int t = 0; t < 4; t++) store_tile(acc[1 + t], 3, t);
         } else {
-            Elem<TIn>::unpack16(xr[i + 3], y);
+            gram_two_rows<1, 2, KS, PK>(Ahi, Alo, Khi, Klo, lr, lg, acc);
+            store_tile(acc[0], 1, 0);
+            store_tile(acc[1], 1, 1);
+#pragma unroll
+            for (int t = 0; t < 3; t++) store_tile(acc[2 + t], 2, t);
         }
-    };
+    }
 
-    // Raw 16-byte rows of this thread's channel groups for the chunk at cs
-    // (3 rows of history from the previous chunk, the conv state or zeros;
-    // rows past the chunk are zero).  All raw rows are loaded before any math.
-    uint4 xr[RPB + 3], xv[VRPB + 3];
-    auto load_raw = [&](int64_t cs) {
-        const int Lc = int(eos - cs < kChunk ? eos - cs : kChunk);
-#pragma unroll
-        for (int j = 0; j < RPB + 3; j++) {
-            const int row = prow0 - 3 + j;
-            const int64_t tt = cs + row;
-            uint4 v = {0u, 0u, 0u, 0u};
-            if (row < Lc && (conv || j >= 3)) {
-                if (tt >= bos) {
-                    v = *reinterpret_cast<const uint4*>(pbase + tt * nq);
-                } else if (csi) {
-#pragma unroll
-                    for (int e = 0; e < VEC; e++)
-                        Elem<TIn>::set16(v, e, csi + (int64_t(n) * C + pch + e) * 3 + (3 + (tt - bos)));
-                }
-            }
-            xr[j] = v;
-        }
-#pragma unroll
-        for (int j = 0; j < VRPB + 3; j++) {
-            const int row = vrow0 - 3 + j;
-            const int64_t tt = cs + row;
-            uint4 v = {0u, 0u, 0u, 0u};
-            if (row < Lc && (conv || j >= 3)) {
-                if (tt >= bos) {
-                    v = *reinterpret_cast<const uint4*>(vbase + tt * nv);
-                } else if (csi) {
-#pragma unroll
-                    for (int e = 0; e < VEC; e++)
-                        Elem<TIn>::set16(v, e, csi + (int64_t(n) * C + vch + e) * 3 + (3 + (tt - bos)));
-                }
-            }
-            xv[j] = v;
-        }
-    };
-    for (int64_t c0 = bos; c0 < eos; c0 += kChunk) {
-        const int L = int(eos - c0 < kChunk ? eos - c0 : kChunk);
-        load_raw(c0);
-
-        // ---- prologue: conv + SiLU.  q|k are staged un-normalised as split
-        //      operands (the per-row L2 norms scale the fp32 products later);
-        //      v is staged in fp32. ----
-        {
-#pragma unroll
-            for (int i = 0; i < RPB; i++) {
-                const int row = prow0 + i;
-                float y[VEC];
-                conv_rows(xr, pw, pbias, i, y);
-                float ss = 0.0f;
-#pragma unroll
-                for (int e = 0; e < VEC; e++) {
-                    if (row >= L) y[e] = 0.0f;
-                    ss += y[e] * y[e];
-                }
-                red[row * NG + pg] = ss;
-                _Float16* dhi = (pwhich ? Khi : Qhi) + row * PK + poff;
-                _Float16* dlo = (pwhich ? Klo : Qlo) + row * PK + poff;
-#pragma unroll
-                for (int e = 0; e < VEC; e++) split1(y[e], dhi[e], dlo[e]);
-            }
-#pragma unroll
-            for (int i = 0; i < VRPB; i++) {
-                const int row = vrow0 + i;
-                float y[VEC];
-                conv_rows(xv, vwp, vbias, i, y);
-#pragma unroll
-                for (int e = 0; e < VEC; e++) Vf[row * PV + vg * VEC + e] = (row < L) ? y[e] : 0.0f;
-            }
-        }
-        // ---- chunk-local cumulative log decay and its exponentials (wave 0) ----
+    // ---- per value head of the group: decays, A, P, T ----
+    for (int gi = 0; gi < G; gi++) {
+        const int h = hk * G + gi;
+        const int64_t ih = int64_t(cs) * p.h_v + h;
         // gam reaches about -50 over a chunk; in fp32 its rounding (~4e-6
         // absolute) would become a relative error of every decay factor, which
         // the inter- and intra-chunk terms amplify.  Scan and exponentiate in fp64.
@@ -339,98 +473,45 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillParam
             }
             const double gl = __shfl(x, 63);
             gam[lane] = x;
-            eg[lane] = static_cast<float>(exp(x));
             bet[lane] = bv;
-            dl[lane] = static_cast<float>(exp(gl - x));
-            if (lane == 0) egl[0] = static_cast<float>(exp(gl));
+            float* sc = p.scal_img + ih * Img<DK>::kScal;
+            sc[lane] = bv;
+            sc[kChunk + lane] = static_cast<float>(exp(x));
+            sc[2 * kChunk + lane] = static_cast<float>(exp(gl - x));
+            sc[3 * kChunk + lane] = lane == 0 ? static_cast<float>(exp(gl)) : 0.0f;
         }
         lds_barrier();
-
-        // ---- per-row 1/|q| and 1/|k| (fixed summation order) ----
-        if (tid < 2 * kChunk) {
-            const int r = tid & (kChunk - 1), which = tid / kChunk;
-            const float* rr = red + r * NG + which * NGQ;
-            float sum = 0.0f;
-#pragma unroll
-            for (int q = 0; q < NGQ; q++) sum += rr[q];
-            (which ? rk : rq)[r] = p.qk_l2norm ? 1.0f / sqrtf(sum + p.l2_eps) : 1.0f;
-        }
-        lds_barrier();
-
-        // ---- Gram tiles: A (strictly lower) and P (lower incl.), fp32.  Waves
-        //      0, 1 take K K^T, waves 2, 3 take Q K^T; each wave two tile-rows
-        //      ({0, 3} or {1, 2}: 5 tiles).  Tiles above the diagonal are never read. ----
+        // A (fp32, LDS) and P (split, image): 8 consecutive columns per item
         {
-            const int which = wave >> 1;
-            const _Float16* Ahi = which ? Qhi : Khi;
-            const _Float16* Alo = which ? Qlo : Klo;
-            const float* rnorm = which ? rq : rk;
-            auto store_tile = [&](const float4_t& acc, int ti, int tj) {
-                const int s = 16 * tj + lr, r0 = 16 * ti + 4 * lg;
-                const float4 rn = *reinterpret_cast<const float4*>(rnorm + r0);
-                const float4 bt = *reinterpret_cast<const float4*>(bet + r0);
-                const double2 g01 = *reinterpret_cast<const double2*>(gam + r0);
-                const double2 g23 = *reinterpret_cast<const double2*>(gam + r0 + 2);
-                const double gs = gam[s];
-                const float rks = rk[s];
-                const float rnv[4] = {rn.x, rn.y, rn.z, rn.w}, btv[4] = {bt.x, bt.y, bt.z, bt.w};
-                const double grv[4] = {g01.x, g01.y, g23.x, g23.y};
+            _Float16* pimg = static_cast<_Float16*>(p.tp_img) + ih * Img<DK>::kTP + 2 * TriPack::kPieces * 8;
 #pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    const int r = r0 + e;
-                    const float gram = acc[e] * rnv[e] * rks;
-                    const float dec = (s <= r) ? __expf(static_cast<float>(grv[e] - gs)) : 0.0f;
-                    if (which == 0) Af[r * PF + s] = (s < r) ? btv[e] * dec * gram : 0.0f;
-                    else Pf[r * PF + s] = dec * gram;
+            for (int it = 0; it < 2; it++) {
+                const int item = tid + kThreads * it;
+                const int r = item >> 3, s0 = (item & 7) * 8;
+                const double gr = gam[r];
+                const float br = bet[r];
+                float a[8], pp[8];
+#pragma unroll
+                for (int e = 0; e < 8; e++) {
+                    const int s = s0 + e;
+                    const float dec = (s <= r) ? __expf(static_cast<float>(gr - gam[s])) : 0.0f;
+                    a[e] = (s < r) ? br * dec * KK[r * PF + s] : 0.0f;
+                    pp[e] = (s <= r) ? dec * QK[r * PF + s] : 0.0f;
                 }
-            };
-            float4_t acc[5];
-            if ((wave & 1) == 0) {
-                gram_two_rows<0, 3, KS, PK>(Ahi, Alo, Khi, Klo, lr, lg, acc);
-                store_tile(acc[0], 0, 0);
-#pragma unroll
-                for (int t = 0; t < 4; t++) store_tile(acc[1 + t], 3, t);
-            } else {
-                gram_two_rows<1, 2, KS, PK>(Ahi, Alo, Khi, Klo, lr, lg, acc);
-                store_tile(acc[0], 1, 0);
-                store_tile(acc[1], 1, 1);
-#pragma unroll
-                for (int t = 0; t < 3; t++) store_tile(acc[2 + t], 2, t);
-            }
-        }
-
-        // ---- K H and Q H on this wave's column; R = beta (V - e^gam K H) ----
-        float4_t qh[4], rr[4];
-        {
-            SFrag hb[KS];
-#pragma unroll
-            for (int ks = 0; ks < KS; ks++) {
-                float x[8];
-                acc_to_operand(hacc[2 * ks], hacc[2 * ks + 1], x);
-                hb[ks] = split8(x);
-            }
-#pragma unroll
-            for (int tb = 0; tb < 4; tb++) {
-                float4_t khh = kZero4, khx = kZero4, qhh = kZero4, qhx = kZero4;
-#pragma unroll
-                for (int ks = 0; ks < KS; ks++) {
-                    mma3(khh, khx, lds_sfrag(Khi, Klo, PK, 16 * tb + lr, 32 * ks + 8 * lg), hb[ks]);
-                    mma3(qhh, qhx, lds_sfrag(Qhi, Qlo, PK, 16 * tb + lr, 32 * ks + 8 * lg), hb[ks]);
-                }
-                const float4_t kh = combine(khh, khx);
-                qh[tb] = combine(qhh, qhx);
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    const int r = 16 * tb + 4 * lg + e;
-                    qh[tb][e] *= rq[r];
-                    rr[tb][e] = bet[r] * (Vf[r * PV + wcol] - eg[r] * rk[r] * kh[e]);
+                *reinterpret_cast<float4*>(Af + r * PF + s0) = make_float4(a[0], a[1], a[2], a[3]);
+                *reinterpret_cast<float4*>(Af + r * PF + s0 + 4) = make_float4(a[4], a[5], a[6], a[7]);
+                if ((s0 >> 4) <= (r >> 4)) {
+                    uint4 hv, lv;
+                    split_pack(pp, hv, lv);
+                    const int q = TriPack::row_start(r) + (s0 >> 3);
+                    *reinterpret_cast<uint4*>(pimg + 8 * q) = hv;
+                    *reinterpret_cast<uint4*>(pimg + 8 * (TriPack::kPieces + q)) = lv;
                 }
             }
         }
         lds_barrier();
-
-        // ---- inverses of the 16x16 diagonal blocks of (I + A), by forward
-        //      substitution, one column per lane (wave 0) ----
+        // inverses of the 16x16 diagonal blocks of (I + A) by forward
+        // substitution, one column per lane (wave 0)
         if (wave == 0) {
             const int b = lane >> 4, c = lane & 15;
             float x[16];
@@ -445,63 +526,292 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillParam
             for (int r = 0; r < 16; r++) Td[(16 * b + r) * PD + c] = x[r];
         }
         lds_barrier();
+        if (wave == 0) {
+            inverse_column<0, PF, PD>(Af, Td, Tf, lr, lg);
+        } else if (wave == 1) {
+            inverse_column<1, PF, PD>(Af, Td, Tf, lr, lg);
+        } else if (wave == 2) {
+            inverse_column<2, PF, PD>(Af, Td, Tf, lr, lg);
+        } else if (lane < 16) {  // block (3, 3) is its diagonal inverse
+#pragma unroll
+            for (int r = 0; r < 16; r++) Tf[(48 + r) * PF + 48 + lane] = Td[(48 + r) * PD + lane];
+        }
+        lds_barrier();
+        // T image (blocks above the diagonal are zero)
+        {
+            _Float16* timg = static_cast<_Float16*>(p.tp_img) + ih * Img<DK>::kTP;
+#pragma unroll
+            for (int it = 0; it < 2; it++) {
+                const int item = tid + kThreads * it;
+                const int r = item >> 3, s0 = (item & 7) * 8;
+                float t[8];
+#pragma unroll
+                for (int e = 0; e < 8; e++) {
+                    const int s = s0 + e;
+                    t[e] = ((s >> 4) <= (r >> 4)) ? Tf[r * PF + s] : 0.0f;
+                }
+                if ((s0 >> 4) <= (r >> 4)) {
+                    uint4 hv, lv;
+                    split_pack(t, hv, lv);
+                    const int q = TriPack::row_start(r) + (s0 >> 3);
+                    *reinterpret_cast<uint4*>(timg + 8 * q) = hv;
+                    *reinterpret_cast<uint4*>(timg + 8 * (TriPack::kPieces + q)) = lv;
+                }
+            }
+        }
+        lds_barrier();
+    }
+}
 
-        // ---- D: block forward substitution of (I + A) D = R on this wave's
-        //      column, D_b = Tbb (R_b - sum_{k<b} A_bk D_k) ----
-        float4_t dacc[4];
+// ---------------------------------------------------------------- carry: v prologue, state chain, outputs
+
+template <int DK>
+struct CarrySmem {
+    static constexpr int kPitchK = DK + 8;      // K, Q image rows (fp16)
+    static constexpr int kPitchT = kChunk + 8;  // T, P image rows (fp16)
+    static constexpr int kPitchV = kDvs + 4;    // V rows (fp32)
+    static constexpr size_t szKQ = size_t(kChunk) * kPitchK * sizeof(_Float16);
+    static constexpr size_t szTP = size_t(kChunk) * kPitchT * sizeof(_Float16);
+    static constexpr size_t oKQ = 0;         // K hi, K lo, Q hi, Q lo
+    static constexpr size_t oTP = 4 * szKQ;  // T hi, T lo, P hi, P lo
+    static constexpr size_t oV = oTP + 4 * szTP;
+    static constexpr size_t oScal = oV + size_t(kChunk) * kPitchV * sizeof(float);
+    static constexpr size_t kBytes = oScal + Img<DK>::kScal * sizeof(float);
+    static_assert(kBytes <= size_t(kLdsLimit), "LDS budget");
+    static_assert(oTP % 16 == 0 && oV % 16 == 0 && oScal % 16 == 0, "16-byte aligned regions");
+};
+
+// Workgroup = (sequence, value head, 64-column slice of d_v); wave w owns the
+// 16 state columns [16w, 16w + 16) of the slice in accumulator layout.  The
+// workgroups of one (sequence, key head) group are mapped to the same XCD, so
+// their shared K and Q images are read through one L2.
+template <int DK, int DV, typename TIn, typename TOut>
+__global__ void __launch_bounds__(kThreads, 1) carry_kernel(const PrefillParams p) {
+    constexpr int NS = DV / kDvs;
+    constexpr int VEC = Elem<TIn>::kVec;
+    constexpr int NGV = kDvs / VEC;                    // 16-byte groups of a v slice row
+    constexpr int VRPB = kChunk / (kThreads / NGV);    // v rows per thread
+    constexpr int KT = DK / 16, KS = DK / 32;
+    constexpr int NKQ = Img<DK>::kKQ / 8 / kThreads;   // 16-byte image pieces per thread
+    constexpr int NTP = Img<DK>::kTP / 8 / kThreads;
+    static_assert(Img<DK>::kKQ % (8 * kThreads) == 0 && Img<DK>::kTP % (8 * kThreads) == 0, "image pieces");
+    static_assert(NTP * kThreads == 4 * TriPack::kPieces, "T|P pieces");
+    static_assert(Img<DK>::kScal == kThreads, "one scalar per thread");
+    static_assert(kThreads % NGV == 0 && kChunk % (kThreads / NGV) == 0, "v prologue tiling");
+    static_assert(DV % kDvs == 0, "d_v slices");
+    using S = CarrySmem<DK>;
+    constexpr int PK = S::kPitchK, PT = S::kPitchT, PV = S::kPitchV;
+
+    __shared__ __attribute__((aligned(16))) char smem[S::kBytes];
+    _Float16* kq = reinterpret_cast<_Float16*>(smem + S::oKQ);
+    _Float16* tp = reinterpret_cast<_Float16*>(smem + S::oTP);
+    const _Float16* Khi = kq;
+    const _Float16* Klo = kq + kChunk * PK;
+    const _Float16* Qhi = kq + 2 * kChunk * PK;
+    const _Float16* Qlo = kq + 3 * kChunk * PK;
+    const _Float16* Thi = tp;
+    const _Float16* Tlo = tp + kChunk * PT;
+    const _Float16* Phi = tp + 2 * kChunk * PT;
+    const _Float16* Plo = tp + 3 * kChunk * PT;
+    float* Vf = reinterpret_cast<float*>(smem + S::oV);
+    float* scal = reinterpret_cast<float*>(smem + S::oScal);
+    const float* bet = scal;
+    const float* eg = scal + kChunk;
+    const float* dl = scal + 2 * kChunk;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
+    // XCD-aware unit map: workgroup b runs on XCD b % 8; the M = G * NS
+    // members of group g = (order index, key head) share XCD g % 8.
+    const int G = p.h_v / p.h_k, M = G * NS;
+    const int ngroups = p.num_seqs * p.h_k;
+    const int xcd = int(blockIdx.x & 7u), kx = int(blockIdx.x >> 3);
+    const int grp = (kx / M) * 8 + xcd, mem = kx % M;
+    if (grp >= ngroups) return;
+    const int hk = grp % p.h_k, gi = mem / NS, slice = mem % NS;
+    const int n = p.order[grp / p.h_k];
+    const int h = hk * G + gi;
+    const int wcol = 16 * wave + lr;      // this lane's column within the slice
+    const int col = slice * kDvs + wcol;  // ... and within d_v
+    const int64_t bos = p.cu_seqlens[n], eos = p.cu_seqlens[n + 1];
+    const int nch = int((eos - bos + kChunk - 1) / kChunk);
+    const int cb = p.chunk_base[n];
+    const int64_t nq = int64_t(p.h_k) * DK, nv = int64_t(p.h_v) * DV, C = 2 * nq + nv;
+    const bool conv = p.conv_width == 4;
+    TOut* out = static_cast<TOut*>(p.o);
+    const int64_t state_base = (int64_t(n) * p.h_v + h) * DK * DV + col;
+
+    // State column: hacc[it][e] = H[16 it + 4 lg + e][col].
+    float4_t hacc[KT];
 #pragma unroll
-        for (int b = 0; b < 4; b++) {
-            dacc[b] = kZero4;
-            mma_blk_f32(dacc[b], Td + 16 * b * PD, PD, rr[b]);
-            const float4_t nd = -dacc[b];
+    for (int it = 0; it < KT; it++)
 #pragma unroll
-            for (int c = b + 1; c < 4; c++) mma_blk_f32(rr[c], Af + 16 * c * PF + 16 * b, PF, nd);
+        for (int e = 0; e < 4; e++)
+            hacc[it][e] = p.initial_state ? p.initial_state[state_base + int64_t(16 * it + 4 * lg + e) * DV] : 0.0f;
+
+    // v prologue: one 16-byte channel group of the slice for VRPB rows
+    const int vg = tid % NGV, vrow0 = (tid / NGV) * VRPB;
+    const int64_t vch = 2 * nq + int64_t(h) * DV + slice * kDvs + vg * VEC;
+    const TIn* vbase = static_cast<const TIn*>(p.v) + int64_t(h) * DV + slice * kDvs + vg * VEC;
+    const TIn* vhist = p.conv_state_in ? static_cast<const TIn*>(p.conv_state_in) + (int64_t(n) * C + vch) * 3
+                                       : nullptr;
+    u32x4_t vwp[4];
+    float vbias[VEC];
+    conv_params<TIn>(p, vch, vwp, vbias);
+
+    // The next chunk's images and raw v rows, in registers.
+    u32x4_t pkq[NKQ], ptp[NTP], xv[VRPB + 3];
+    float psc;
+    auto fetch = [&](int j) {
+        const int64_t slot = int64_t(cb) + j;
+        const u32x4_t* skq = reinterpret_cast<const u32x4_t*>(static_cast<const _Float16*>(p.kq_img) +
+                                                              (slot * p.h_k + hk) * Img<DK>::kKQ);
+        const u32x4_t* stp = reinterpret_cast<const u32x4_t*>(static_cast<const _Float16*>(p.tp_img) +
+                                                              (slot * p.h_v + h) * Img<DK>::kTP);
+#pragma unroll
+        for (int i = 0; i < NKQ; i++) pkq[i] = skq[tid + kThreads * i];
+#pragma unroll
+        for (int i = 0; i < NTP; i++) ptp[i] = stp[tid + kThreads * i];
+        psc = p.scal_img[(slot * p.h_v + h) * Img<DK>::kScal + tid];
+        const int64_t c0 = bos + int64_t(j) * kChunk;
+        const int L = int(eos - c0 < kChunk ? eos - c0 : kChunk);
+        load_rows<TIn, VRPB>(xv, vbase, nv, c0, vrow0, L, bos, conv, vhist);
+    };
+    // Blocks (0, 1) and (2, 3) of the T and P planes are read by the products
+    // (k-steps of 32 columns) but never staged: zero them once.
+    for (int i = tid; i < 4 * 2 * 16 * 2; i += kThreads) {
+        const int plane = i >> 6, blk = (i >> 5) & 1, rr = (i >> 1) & 15, half = i & 1;
+        const int r = 32 * blk + rr, c = 32 * blk + 16 + 8 * half;
+        *reinterpret_cast<u32x4_t*>(tp + plane * kChunk * PT + r * PT + c) = u32x4_t{0u, 0u, 0u, 0u};
+    }
+    if (nch > 0) fetch(0);
+
+    for (int j = 0; j < nch; j++) {
+        const int64_t c0 = bos + int64_t(j) * kChunk;
+        const int L = int(eos - c0 < kChunk ? eos - c0 : kChunk);
+
+        // ---- stage the chunk (every wave is done with the previous one) ----
+#pragma unroll
+        for (int i = 0; i < NKQ; i++) {
+            const int pc = tid + kThreads * i;  // piece: plane, row, 8 columns
+            const int plane = pc / (kChunk * DK / 8), rem = pc % (kChunk * DK / 8);
+            *reinterpret_cast<u32x4_t*>(kq + plane * kChunk * PK + (rem / (DK / 8)) * PK + 8 * (rem % (DK / 8))) =
+                pkq[i];
+        }
+#pragma unroll
+        for (int i = 0; i < NTP; i++) {
+            const int pc = tid + kThreads * i;
+            const int plane = pc / TriPack::kPieces;
+            int r, c8;
+            TriPack::locate(pc % TriPack::kPieces, r, c8);
+            *reinterpret_cast<u32x4_t*>(tp + plane * kChunk * PT + r * PT + 8 * c8) = ptp[i];
+        }
+        scal[tid] = psc;
+#pragma unroll
+        for (int i = 0; i < VRPB; i++) {
+            const int row = vrow0 + i;
+            float y[VEC];
+            conv_row<TIn>(conv, xv, vwp, vbias, i, y);
+#pragma unroll
+            for (int e = 0; e < VEC; e++) Vf[row * PV + vg * VEC + e] = (row < L) ? y[e] : 0.0f;
+        }
+        lds_barrier();
+        if (j + 1 < nch) fetch(j + 1);
+
+        // ---- the state as the B operand of this chunk's products ----
+        SFrag hb[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++) {
+            float x[8];
+            acc_to_operand(hacc[2 * ks], hacc[2 * ks + 1], x);
+            hb[ks] = split8(x);
+        }
+        // ---- R = beta (V - e^gam K H) ----
+        float4_t rr[4];
+#pragma unroll
+        for (int tb = 0; tb < 4; tb++) {
+            float4_t hh = kZero4, xx = kZero4;
+#pragma unroll
+            for (int ks = 0; ks < KS; ks++)
+                mma3(hh, xx, lds_sfrag(Khi, Klo, PK, 16 * tb + lr, 32 * ks + 8 * lg), hb[ks]);
+            const float4_t kh = combine(hh, xx);
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int r = 16 * tb + 4 * lg + e;
+                rr[tb][e] = bet[r] * (Vf[r * PV + wcol] - eg[r] * kh[e]);
+            }
+        }
+        // ---- D = T R (T lower triangular: row block tb needs k-steps <= tb/2) ----
+        float4_t dd[4];
+        {
+            SFrag rb[2];
+#pragma unroll
+            for (int s = 0; s < 2; s++) {
+                float x[8];
+                acc_to_operand(rr[2 * s], rr[2 * s + 1], x);
+                rb[s] = split8(x);
+            }
+#pragma unroll
+            for (int tb = 0; tb < 4; tb++) {
+                float4_t hh = kZero4, xx = kZero4;
+#pragma unroll
+                for (int ks = 0; ks <= tb / 2; ks++)
+                    mma3(hh, xx, lds_sfrag(Thi, Tlo, PT, 16 * tb + lr, 32 * ks + 8 * lg), rb[ks]);
+                dd[tb] = combine(hh, xx);
+            }
         }
         // ---- o = scale (e^gam Q H + P D) ----
         {
-            float4_t oacc[4];
+            SFrag db[2];
 #pragma unroll
-            for (int b = 0; b < 4; b++) oacc[b] = kZero4;
+            for (int s = 0; s < 2; s++) {
+                float x[8];
+                acc_to_operand(dd[2 * s], dd[2 * s + 1], x);
+                db[s] = split8(x);
+            }
 #pragma unroll
-            for (int k = 0; k < 4; k++)
+            for (int tb = 0; tb < 4; tb++) {
+                float4_t qhh = kZero4, qhx = kZero4, phh = kZero4, phx = kZero4;
 #pragma unroll
-                for (int b = k; b < 4; b++) mma_blk_f32(oacc[b], Pf + 16 * b * PF + 16 * k, PF, dacc[k]);
+                for (int ks = 0; ks < KS; ks++)
+                    mma3(qhh, qhx, lds_sfrag(Qhi, Qlo, PK, 16 * tb + lr, 32 * ks + 8 * lg), hb[ks]);
 #pragma unroll
-            for (int b = 0; b < 4; b++) {
-                const float4 egv = *reinterpret_cast<const float4*>(eg + 16 * b + 4 * lg);
+                for (int ks = 0; ks <= tb / 2; ks++)
+                    mma3(phh, phx, lds_sfrag(Phi, Plo, PT, 16 * tb + lr, 32 * ks + 8 * lg), db[ks]);
+                const float4_t qh = combine(qhh, qhx), pd = combine(phh, phx);
+                const float4 egv = *reinterpret_cast<const float4*>(eg + 16 * tb + 4 * lg);
                 const float egr[4] = {egv.x, egv.y, egv.z, egv.w};
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
-                    const int r = 16 * b + 4 * lg + e;
+                    const int r = 16 * tb + 4 * lg + e;
                     if (r < L)
-                        Elem<TOut>::put(out + ((c0 + r) * p.h_v + h) * DV + col,
-                                        p.scale * (egr[e] * qh[b][e] + oacc[b][e]));
+                        Elem<TOut>::put(out + ((c0 + r) * p.h_v + h) * DV + col, p.scale * (egr[e] * qh[e] + pd[e]));
                 }
             }
         }
-        // ---- H <- e^{gam_last} H + K^T diag(e^{gam_last - gam} / |k|) D ----
+        // ---- H <- e^{gam_last} H + K^T diag(e^{gam_last - gam}) D ----
         {
-            SFrag tb2[2];
+            SFrag ab[2];
 #pragma unroll
-            for (int ks = 0; ks < 2; ks++) {
+            for (int s = 0; s < 2; s++) {
                 float4_t a0, a1;
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
-                    const int r0 = 32 * ks + 4 * lg + e, r1 = r0 + 16;
-                    a0[e] = dl[r0] * rk[r0] * dacc[2 * ks][e];
-                    a1[e] = dl[r1] * rk[r1] * dacc[2 * ks + 1][e];
+                    const int r0 = 32 * s + 4 * lg + e, r1 = r0 + 16;
+                    a0[e] = dl[r0] * dd[2 * s][e];
+                    a1[e] = dl[r1] * dd[2 * s + 1][e];
                 }
                 float x[8];
                 acc_to_operand(a0, a1, x);
-                tb2[ks] = split8(x);
+                ab[s] = split8(x);
             }
-            const float decay = egl[0];
+            const float decay = scal[3 * kChunk];
 #pragma unroll
             for (int it = 0; it < KT; it++) {
                 float4_t hh = hacc[it] * decay, xx = kZero4;
 #pragma unroll
-                for (int ks = 0; ks < 2; ks++)
-                    mma3(hh, xx, lds_sfrag_t(Khi, Klo, PK, 32 * ks + 8 * lg, 16 * it + lr), tb2[ks]);
+                for (int s = 0; s < 2; s++)
+                    mma3(hh, xx, lds_sfrag_tr(Khi, Klo, PK, 32 * s + 8 * lg, 16 * it), ab[s]);
                 hacc[it] = combine(hh, xx);
             }
         }
@@ -515,22 +825,6 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillParam
             for (int e = 0; e < 4; e++)
                 p.final_state[state_base + int64_t(16 * it + 4 * lg + e) * DV] = hacc[it][e];
     }
-}
-
-// Dispatch map: sequences ordered by descending chunk count (ties by index),
-// so the longest dependent chains start first.  Ranks are unique, so the map
-// is a permutation for any cu_seqlens contents.
-__global__ void __launch_bounds__(256) order_kernel(const int32_t* __restrict__ cu, int32_t n,
-                                                     int32_t* __restrict__ order) {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n) return;
-    const int ci = (cu[i + 1] - cu[i] + kChunk - 1) / kChunk;
-    int rank = 0;
-    for (int j = 0; j < n; j++) {
-        const int cj = (cu[j + 1] - cu[j] + kChunk - 1) / kChunk;
-        rank += (cj > ci) || (cj == ci && j < i);
-    }
-    order[rank] = i;
 }
 
 // Final conv state of every sequence: its last 3 raw inputs per channel,
@@ -564,10 +858,20 @@ __global__ void __launch_bounds__(256) conv_state_kernel(const PrefillParams p, 
     for (int j = 0; j < 3; j++) cso[e * 3 + j] = vals[j];
 }
 
+int64_t carry_blocks(int64_t num_seqs, int64_t h_k, int64_t h_v, int64_t d_v) {
+    const int64_t groups = num_seqs * h_k, members = (h_v / h_k) * (d_v / kDvs);
+    return (groups + 7) / 8 * 8 * members;
+}
+
 template <int DK, int DV, typename TIn, typename TOut>
 hipError_t run(const PrefillParams& p, hipStream_t stream) {
-    const int64_t blocks = int64_t(p.num_seqs) * p.h_v * (DV / 64);
-    prefill_kernel<DK, DV, TIn, TOut><<<dim3(unsigned(blocks)), dim3(kThreads), 0, stream>>>(p);
+    if (p.slots > 0) {
+        prep_kernel<DK, TIn><<<dim3(unsigned(p.slots * p.h_k)), dim3(kThreads), 0, stream>>>(p);
+        const hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    carry_kernel<DK, DV, TIn, TOut>
+        <<<dim3(unsigned(carry_blocks(p.num_seqs, p.h_k, p.h_v, DV))), dim3(kThreads), 0, stream>>>(p);
     return hipGetLastError();
 }
 
@@ -578,6 +882,8 @@ hipError_t run_dtype(const PrefillParams& p, int d_k, int d_v, hipStream_t strea
     return hipErrorInvalidValue;
 }
 
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
 }  // namespace
 
 int prefill_supported(int d_k, int d_v, int qkv_dtype, int out_dtype) {
@@ -586,12 +892,37 @@ int prefill_supported(int d_k, int d_v, int qkv_dtype, int out_dtype) {
     return (d_k == 128 && d_v == 128) || (d_k == 64 && d_v == 64);
 }
 
+PrefillLayout prefill_layout(int64_t num_seqs, int64_t total_tokens, int64_t h_k, int64_t h_v, int64_t d_k,
+                             int64_t d_v) {
+    PrefillLayout l{};
+    if (num_seqs <= 0 || h_k <= 0 || h_v <= 0 || d_k <= 0 || d_v <= 0) return l;
+    // sum_n ceil(len_n / 64) <= (T + 63 N) / 64 for any split of T tokens into N sequences
+    l.slots = (total_tokens + 63 * num_seqs) / kChunk;
+    size_t off = 0;
+    l.order = off;
+    off = align256(off + size_t(num_seqs) * sizeof(int32_t));
+    l.chunk_base = off;
+    off = align256(off + size_t(num_seqs + 1) * sizeof(int32_t));
+    l.kq_img = off;
+    off = align256(off + size_t(l.slots) * size_t(h_k) * (4 * kChunk * size_t(d_k)) * sizeof(_Float16));
+    l.tp_img = off;
+    off = align256(off + size_t(l.slots) * size_t(h_v) * (4 * TriPack::kPieces * 8) * sizeof(_Float16));
+    l.scal_img = off;
+    off = align256(off + size_t(l.slots) * size_t(h_v) * (4 * kChunk) * sizeof(float));
+    l.bytes = off;
+    l.prep_blocks = l.slots * h_k;
+    l.carry_blocks = carry_blocks(num_seqs, h_k, h_v, d_v);
+    return l;
+}
+
 hipError_t launch_prefill(const PrefillParams& p, int d_k, int d_v, int qkv_dtype, int out_dtype,
                           hipStream_t stream) {
     if (p.num_seqs <= 0) return hipSuccess;
-    int32_t* order = const_cast<int32_t*>(p.order);
-    order_kernel<<<dim3((p.num_seqs + 255) / 256), dim3(256), 0, stream>>>(p.cu_seqlens, p.num_seqs, order);
+    chunk_map_kernel<<<dim3(1), dim3(256), 0, stream>>>(p.cu_seqlens, p.num_seqs, p.chunk_base);
     hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    order_kernel<<<dim3((p.num_seqs + 255) / 256), dim3(256), 0, stream>>>(p.cu_seqlens, p.num_seqs, p.order);
+    err = hipGetLastError();
     if (err != hipSuccess) return err;
     if (qkv_dtype == 1)
         err = out_dtype == 1 ? run_dtype<bf16_t, bf16_t>(p, d_k, d_v, stream) : run_dtype<bf16_t, float>(p, d_k, d_v, stream);

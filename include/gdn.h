@@ -86,9 +86,15 @@ typedef struct gdn_problem {
     int32_t conv_width;    /* 0 => no conv prologue (no SiLU); 4 => conv + SiLU */
 } gdn_problem;
 
-/* Bytes of device workspace gdn_prefill_varlen needs for this problem (the
- * per-call dispatch map: an ordering of the sequences).  Returns 0 for a NULL
- * problem.  Depends on num_seqs only. */
+/* Bytes of device workspace gdn_prefill_varlen needs for this problem: the
+ * chunk map (chunks before each sequence), a dispatch order of the sequences,
+ * and the chunk-local terms computed in parallel over all 64-token chunks
+ * (split-fp16 images of the normalised K and Q per key head, of
+ * T = (I + A)^{-1} and of the decayed Q K^T per value head, and per-token
+ * decay scalars).  That is about (T + 63 N) / 64 chunk slots of
+ * 512 d_k h_k + 21504 h_v bytes each, e.g. 27 KB per token for h_k = 16,
+ * h_v = 32, d_k = 128.  Depends on num_seqs, total_tokens, h_k, h_v, d_k and
+ * d_v; returns 0 for a NULL problem or num_seqs <= 0. */
 size_t gdn_prefill_workspace_bytes(const gdn_problem* p);
 
 /*
