@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(_PKG, "libgdn.so")
 GDN_F32, GDN_BF16 = 0, 1
 _STATUS = {0: "GDN_OK", -1: "GDN_ERR_NULL", -2: "GDN_ERR_SHAPE", -3: "GDN_ERR_DTYPE",
            -4: "GDN_ERR_UNSUPPORTED", -5: "GDN_ERR_WORKSPACE", -6: "GDN_ERR_HIP", -7: "GDN_ERR_ALIAS"}
-EXPORTED = ("gdn_prefill_workspace_bytes", "gdn_prefill_varlen", "gdn_decode_step", "gdn_status_string")
+EXPORTED = ("gdn_prefill_workspace_bytes", "gdn_prefill_varlen", "gdn_prefill_varlen_timed", "gdn_decode_step",
+            "gdn_status_string")
 
 
 class GdnProblem(ctypes.Structure):
@@ -52,6 +53,9 @@ def load() -> ctypes.CDLL:
         lib.gdn_prefill_workspace_bytes.restype = c64
         lib.gdn_prefill_varlen.argtypes = [ctypes.POINTER(GdnProblem)] + [vp] * 14 + [c64, vp]
         lib.gdn_prefill_varlen.restype = ctypes.c_int
+        lib.gdn_prefill_varlen_timed.argtypes = [ctypes.POINTER(GdnProblem)] + [vp] * 14 + [c64, vp,
+                                                                                           ctypes.POINTER(vp)]
+        lib.gdn_prefill_varlen_timed.restype = ctypes.c_int
         lib.gdn_decode_step.argtypes = [ctypes.POINTER(GdnProblem)] + [vp] * 11 + [vp]
         lib.gdn_decode_step.restype = ctypes.c_int
         lib.gdn_status_string.argtypes = [ctypes.c_int]
@@ -115,13 +119,15 @@ def gdn_prefill_varlen(q, k, v, g, beta, cu_seqlens=None, *, conv_weight=None, c
                        conv_state=None, initial_state=None, output_final_state=True,
                        output_conv_state=True, use_qk_l2norm=True, scale=None, l2_eps=1e-6,
                        out_dtype=torch.float32, validate=True, out=None, final_state_out=None,
-                       conv_state_out=None, workspace=None, stream=None):
+                       conv_state_out=None, workspace=None, stream=None, events=None):
     """Chunked varlen prefill (C ABI ``gdn_prefill_varlen``).
 
     q, k: ``[T, h_k, d_k]`` (or ``[B, T, h_k, d_k]`` with equal lengths and no
     cu_seqlens); v: ``[T, h_v, d_v]``; g, beta: ``[T, h_v]`` fp32; cu_seqlens:
     int32 ``[N+1]`` on the device (or a CPU tensor / list, copied).  Returns
-    ``(o, final_state or None, conv_state_out or None)``.
+    ``(o, final_state or None, conv_state_out or None)``.  With ``events`` (four
+    ``torch.cuda.Event(enable_timing=True)``) the call goes through
+    ``gdn_prefill_varlen_timed``, which records them around its stages.
     """
     if q.dim() == 4:
         if cu_seqlens is not None:
@@ -187,10 +193,22 @@ def gdn_prefill_varlen(q, k, v, g, beta, cu_seqlens=None, *, conv_weight=None, c
         raise ValueError("workspace too small")
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
-    st = load().gdn_prefill_varlen(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                   _ptr(cu_seqlens), _ptr(conv_weight), _ptr(conv_bias), _ptr(conv_state),
-                                   _ptr(cso), _ptr(initial_state), _ptr(o), _ptr(fs), _ptr(workspace),
-                                   ctypes.c_size_t(workspace.numel()), ctypes.c_void_p(stream))
+    args = (ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+            _ptr(cu_seqlens), _ptr(conv_weight), _ptr(conv_bias), _ptr(conv_state),
+            _ptr(cso), _ptr(initial_state), _ptr(o), _ptr(fs), _ptr(workspace),
+            ctypes.c_size_t(workspace.numel()), ctypes.c_void_p(stream))
+    if events is None:
+        st = load().gdn_prefill_varlen(*args)
+    else:
+        if len(events) != 4:
+            raise ValueError("events must be four torch.cuda.Event")
+        handles = []
+        for e in events:
+            if e.cuda_event == 0:  # torch creates the event at its first record
+                e.record()
+            handles.append(e.cuda_event)
+        arr = (ctypes.c_void_p * 4)(*handles)
+        st = load().gdn_prefill_varlen_timed(*args, arr)
     if st != 0:
         raise GdnError(st, "gdn_prefill_varlen")
     return o, fs, cso

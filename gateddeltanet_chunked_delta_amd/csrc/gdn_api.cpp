@@ -57,12 +57,13 @@ size_t gdn_prefill_workspace_bytes(const gdn_problem* p) {
     return gdn::prefill_layout(p->num_seqs, p->total_tokens, p->h_k, p->h_v, p->d_k, p->d_v).bytes;
 }
 
-gdn_status gdn_prefill_varlen(const gdn_problem* p, const void* q, const void* k, const void* v,
-                              const float* g, const float* beta, const int32_t* cu_seqlens,
-                              const void* conv_w, const void* conv_b, const void* conv_state_in,
-                              void* conv_state_out, const float* initial_state, void* o,
-                              float* final_state, void* workspace, size_t workspace_bytes,
-                              void* stream) {
+namespace {
+
+gdn_status prefill(const gdn_problem* p, const void* q, const void* k, const void* v, const float* g,
+                   const float* beta, const int32_t* cu_seqlens, const void* conv_w, const void* conv_b,
+                   const void* conv_state_in, void* conv_state_out, const float* initial_state, void* o,
+                   float* final_state, void* workspace, size_t workspace_bytes, void* stream,
+                   void* const* events) {
     gdn_status st = check_problem(p);
     if (st != GDN_OK) return st;
     const int64_t T = p->total_tokens, N = p->num_seqs;
@@ -124,7 +125,30 @@ gdn_status gdn_prefill_varlen(const gdn_problem* p, const void* q, const void* k
     prm.conv_width = p->conv_width;
     prm.qk_l2norm = p->qk_l2norm; prm.l2_eps = eff_eps(p); prm.scale = eff_scale(p);
     return from_hip(gdn::launch_prefill(prm, p->d_k, p->d_v, p->qkv_dtype, p->out_dtype,
-                                        static_cast<hipStream_t>(stream)));
+                                        static_cast<hipStream_t>(stream), events));
+}
+
+}  // namespace
+
+gdn_status gdn_prefill_varlen(const gdn_problem* p, const void* q, const void* k, const void* v,
+                              const float* g, const float* beta, const int32_t* cu_seqlens,
+                              const void* conv_w, const void* conv_b, const void* conv_state_in,
+                              void* conv_state_out, const float* initial_state, void* o,
+                              float* final_state, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+    return prefill(p, q, k, v, g, beta, cu_seqlens, conv_w, conv_b, conv_state_in, conv_state_out,
+                   initial_state, o, final_state, workspace, workspace_bytes, stream, nullptr);
+}
+
+gdn_status gdn_prefill_varlen_timed(const gdn_problem* p, const void* q, const void* k, const void* v,
+                                    const float* g, const float* beta, const int32_t* cu_seqlens,
+                                    const void* conv_w, const void* conv_b, const void* conv_state_in,
+                                    void* conv_state_out, const float* initial_state, void* o,
+                                    float* final_state, void* workspace, size_t workspace_bytes,
+                                    void* stream, void* const* events) {
+    if (!events || !events[0] || !events[1] || !events[2] || !events[3]) return GDN_ERR_NULL;
+    return prefill(p, q, k, v, g, beta, cu_seqlens, conv_w, conv_b, conv_state_in, conv_state_out,
+                   initial_state, o, final_state, workspace, workspace_bytes, stream, events);
 }
 
 gdn_status gdn_decode_step(const gdn_problem* p, const void* q, const void* k, const void* v,

@@ -108,28 +108,23 @@ struct SFrag {
     half8_t hi, lo;
 };
 
-// hi is x rounded to fp16's 11 significant bits (ties to even) in integer
-// arithmetic, so it is exactly representable in fp16 and the value stored as
-// hi is the value the residual is taken from, whatever instruction the
-// compiler picks for the conversion (converters that break ties differently
-// would otherwise leave the pair one fp16 ulp off on exact ties).  Values
-// below fp16's normal range (2^-14) go entirely into lo.
+// hi is x converted to fp16 by the hardware converter; the residual x - hi is
+// then exact in fp32 (hi is converted back, so the pair always refers to the
+// stored hi whatever rounding the converter applied) and is scaled by 2^11
+// before its own conversion.  Values below fp16's normal range (2^-14) keep
+// their precision in lo.
 __device__ __forceinline__ void split1(float x, _Float16& hi, _Float16& lo) {
-    const uint32_t u = __float_as_uint(x);
-    float h = __uint_as_float((u + 0x0FFFu + ((u >> 13) & 1u)) & 0xFFFFE000u);
-    if (fabsf(x) < 6.103515625e-05f) h = 0.0f;
-    hi = static_cast<_Float16>(h);
-    lo = static_cast<_Float16>((x - h) * kLoScale);
+    hi = static_cast<_Float16>(x);
+    lo = static_cast<_Float16>((x - static_cast<float>(hi)) * kLoScale);
 }
 
 __device__ __forceinline__ SFrag split8(const float (&x)[8]) {
     SFrag f;
 #pragma unroll
     for (int e = 0; e < 8; e++) {
-        _Float16 h, l;
-        split1(x[e], h, l);
+        const _Float16 h = static_cast<_Float16>(x[e]);
         f.hi[e] = h;
-        f.lo[e] = l;
+        f.lo[e] = static_cast<_Float16>((x[e] - static_cast<float>(h)) * kLoScale);
     }
     return f;
 }

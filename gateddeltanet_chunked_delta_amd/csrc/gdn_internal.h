@@ -69,8 +69,10 @@ struct DecodeParams {
 };
 
 // Launchers return hipSuccess or the launch error.  dtype codes follow gdn_dtype.
+// events: null, or 4 hipEvent_t recorded on `stream` before the chunk-local
+// kernel, before the carry kernel, after it and after the last launch.
 hipError_t launch_prefill(const PrefillParams& p, int d_k, int d_v, int qkv_dtype, int out_dtype,
-                          hipStream_t stream);
+                          hipStream_t stream, void* const* events);
 int prefill_supported(int d_k, int d_v, int qkv_dtype, int out_dtype);
 
 hipError_t launch_decode(const DecodeParams& p, int d_k, int d_v, int qkv_dtype, int out_dtype,

@@ -863,22 +863,32 @@ int64_t carry_blocks(int64_t num_seqs, int64_t h_k, int64_t h_v, int64_t d_v) {
     return (groups + 7) / 8 * 8 * members;
 }
 
+hipError_t record(void* const* events, int i, hipStream_t stream) {
+    return events ? hipEventRecord(static_cast<hipEvent_t>(events[i]), stream) : hipSuccess;
+}
+
 template <int DK, int DV, typename TIn, typename TOut>
-hipError_t run(const PrefillParams& p, hipStream_t stream) {
+hipError_t run(const PrefillParams& p, hipStream_t stream, void* const* events) {
+    hipError_t err = record(events, 0, stream);
+    if (err != hipSuccess) return err;
     if (p.slots > 0) {
         prep_kernel<DK, TIn><<<dim3(unsigned(p.slots * p.h_k)), dim3(kThreads), 0, stream>>>(p);
-        const hipError_t err = hipGetLastError();
+        err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
+    err = record(events, 1, stream);
+    if (err != hipSuccess) return err;
     carry_kernel<DK, DV, TIn, TOut>
         <<<dim3(unsigned(carry_blocks(p.num_seqs, p.h_k, p.h_v, DV))), dim3(kThreads), 0, stream>>>(p);
-    return hipGetLastError();
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    return record(events, 2, stream);
 }
 
 template <typename TIn, typename TOut>
-hipError_t run_dtype(const PrefillParams& p, int d_k, int d_v, hipStream_t stream) {
-    if (d_k == 128 && d_v == 128) return run<128, 128, TIn, TOut>(p, stream);
-    if (d_k == 64 && d_v == 64) return run<64, 64, TIn, TOut>(p, stream);
+hipError_t run_dtype(const PrefillParams& p, int d_k, int d_v, hipStream_t stream, void* const* events) {
+    if (d_k == 128 && d_v == 128) return run<128, 128, TIn, TOut>(p, stream, events);
+    if (d_k == 64 && d_v == 64) return run<64, 64, TIn, TOut>(p, stream, events);
     return hipErrorInvalidValue;
 }
 
@@ -916,8 +926,14 @@ PrefillLayout prefill_layout(int64_t num_seqs, int64_t total_tokens, int64_t h_k
 }
 
 hipError_t launch_prefill(const PrefillParams& p, int d_k, int d_v, int qkv_dtype, int out_dtype,
-                          hipStream_t stream) {
-    if (p.num_seqs <= 0) return hipSuccess;
+                          hipStream_t stream, void* const* events) {
+    if (p.num_seqs <= 0) {
+        for (int i = 0; i < 4 && events; i++) {
+            const hipError_t err = record(events, i, stream);
+            if (err != hipSuccess) return err;
+        }
+        return hipSuccess;
+    }
     chunk_map_kernel<<<dim3(1), dim3(256), 0, stream>>>(p.cu_seqlens, p.num_seqs, p.chunk_base);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
@@ -925,9 +941,11 @@ hipError_t launch_prefill(const PrefillParams& p, int d_k, int d_v, int qkv_dtyp
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     if (qkv_dtype == 1)
-        err = out_dtype == 1 ? run_dtype<bf16_t, bf16_t>(p, d_k, d_v, stream) : run_dtype<bf16_t, float>(p, d_k, d_v, stream);
+        err = out_dtype == 1 ? run_dtype<bf16_t, bf16_t>(p, d_k, d_v, stream, events)
+                             : run_dtype<bf16_t, float>(p, d_k, d_v, stream, events);
     else
-        err = out_dtype == 1 ? run_dtype<float, bf16_t>(p, d_k, d_v, stream) : run_dtype<float, float>(p, d_k, d_v, stream);
+        err = out_dtype == 1 ? run_dtype<float, bf16_t>(p, d_k, d_v, stream, events)
+                             : run_dtype<float, float>(p, d_k, d_v, stream, events);
     if (err != hipSuccess) return err;
     if (p.conv_state_out && p.conv_width == 4) {
         const int64_t total = int64_t(p.num_seqs) * (2 * int64_t(p.h_k) * d_k + int64_t(p.h_v) * d_v);
@@ -935,8 +953,9 @@ hipError_t launch_prefill(const PrefillParams& p, int d_k, int d_v, int qkv_dtyp
         if (qkv_dtype == 1) conv_state_kernel<bf16_t><<<dim3(grid), dim3(256), 0, stream>>>(p, d_k, d_v);
         else conv_state_kernel<float><<<dim3(grid), dim3(256), 0, stream>>>(p, d_k, d_v);
         err = hipGetLastError();
+        if (err != hipSuccess) return err;
     }
-    return err;
+    return record(events, 3, stream);
 }
 
 }  // namespace gdn

@@ -141,6 +141,25 @@ gdn_status gdn_prefill_varlen(const gdn_problem* p,
                               void* stream);
 
 /*
+ * gdn_prefill_varlen with stage timing, for measurement: identical work and
+ * results, plus four caller-created hipEvent_t (passed as void*) recorded on
+ * `stream`: events[0] before the chunk-local kernel (norms, K K^T, T, P),
+ * events[1] before the cross-chunk carry kernel, events[2] after it and
+ * events[3] after the last launch.  GDN_ERR_NULL if events or any of the four
+ * is NULL.  Argument errors record nothing.
+ */
+gdn_status gdn_prefill_varlen_timed(const gdn_problem* p,
+                                    const void* q, const void* k, const void* v,
+                                    const float* g, const float* beta,
+                                    const int32_t* cu_seqlens,
+                                    const void* conv_w, const void* conv_b,
+                                    const void* conv_state_in, void* conv_state_out,
+                                    const float* initial_state,
+                                    void* o, float* final_state,
+                                    void* workspace, size_t workspace_bytes,
+                                    void* stream, void* const* events);
+
+/*
  * One decode step: one new token for each of N slots, updating a pooled
  * state in place ("[Feature] Add batch invariance support to GDN_ATTN
  * backend", commit messages: the decode update runs over the state pool

@@ -129,6 +129,28 @@ def test_prefill_workspace(lib):
     assert binding.gdn_prefill_workspace_bytes(_prob(num_seqs=0, total_tokens=0)) == 0
 
 
+def test_prefill_workspace_size_formula(lib):
+    """(T + 63 N) / 64 chunk slots of 512 d_k h_k + 21504 h_v bytes, plus the
+    256-byte aligned order and chunk-base arrays, as the header states."""
+    for N, T, h_k, h_v, d in [(4, 16384, 16, 32, 128), (60, 250000, 16, 48, 128), (3, 7, 2, 6, 64), (1, 0, 1, 1, 64)]:
+        need = binding.gdn_prefill_workspace_bytes(_prob(num_seqs=N, total_tokens=T, h_k=h_k, h_v=h_v, d_k=d, d_v=d))
+        slots = (T + 63 * N) // 64
+        body = slots * (512 * d * h_k + 21504 * h_v)
+        assert body <= need <= body + 4 * 256 + 8 * (N + 1) + 256, (N, T, need, body)
+
+
+def test_prefill_timed_needs_four_events(lib):
+    prob = _prob(conv_width=0)
+    f = lambda x: None if x is None else _fake(x)
+    args = [ctypes.byref(prob)] + [f(i) for i in (1, 2, 3, 4, 5, 6)] + [None] * 3 + [None, None, f(7), None, f(8),
+                                                                                    ctypes.c_size_t(1 << 30), None]
+    assert lib.gdn_prefill_varlen_timed(*args, None) == -1
+    ev = (ctypes.c_void_p * 4)(_fake(20).value, _fake(21).value, None, _fake(23).value)
+    assert lib.gdn_prefill_varlen_timed(*args, ev) == -1
+    ev = (ctypes.c_void_p * 4)(*[_fake(20 + i).value for i in range(4)])
+    assert lib.gdn_prefill_varlen_timed(*args[:1], None, *args[2:], ev) == -1  # q missing: no event recorded
+
+
 def test_prefill_alias_and_alignment(lib):
     prob = _prob(conv_width=0)
     assert _prefill(lib, prob, o=1) == -7                       # o == q
