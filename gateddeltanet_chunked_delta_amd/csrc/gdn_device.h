@@ -111,10 +111,16 @@ struct SFrag {
 // hi is x converted to fp16 by the hardware converter; the residual x - hi is
 // then exact in fp32 (hi is converted back, so the pair always refers to the
 // stored hi whatever rounding the converter applied) and is scaled by 2^11
-// before its own conversion.  Values below fp16's normal range (2^-14) keep
-// their precision in lo.
+// before its own conversion.  Values below fp16's normal range (2^-14) go
+// entirely into lo: the matrix cores treat fp16 subnormal inputs as zero
+// (seen as a 2e-4 relative error in the outputs when subnormal hi parts were
+// allowed).
+__device__ __forceinline__ _Float16 split_hi(float x) {
+    return fabsf(x) < 6.103515625e-05f ? static_cast<_Float16>(0.0f) : static_cast<_Float16>(x);
+}
+
 __device__ __forceinline__ void split1(float x, _Float16& hi, _Float16& lo) {
-    hi = static_cast<_Float16>(x);
+    hi = split_hi(x);
     lo = static_cast<_Float16>((x - static_cast<float>(hi)) * kLoScale);
 }
 
@@ -122,7 +128,7 @@ __device__ __forceinline__ SFrag split8(const float (&x)[8]) {
     SFrag f;
 #pragma unroll
     for (int e = 0; e < 8; e++) {
-        const _Float16 h = static_cast<_Float16>(x[e]);
+        const _Float16 h = split_hi(x[e]);
         f.hi[e] = h;
         f.lo[e] = static_cast<_Float16>((x[e] - static_cast<float>(h)) * kLoScale);
     }
