@@ -283,6 +283,8 @@ __global__ void __launch_bounds__(256) order_kernel(const int32_t* __restrict__ 
 
 // ---------------------------------------------------------------- prep: q|k prologue and chunk-local terms
 
+constexpr int kPrepThreads = 512;  // 8 waves: two groups of 4 take two value heads at a time
+
 template <int DK, int VEC>
 struct PrepSmem {
     static constexpr int kPitchK = DK + 8;      // K, Q rows: [token][d_k] (fp16)
@@ -292,33 +294,54 @@ struct PrepSmem {
 
     static constexpr size_t szKQ = size_t(kChunk) * kPitchK * sizeof(_Float16);
     static constexpr size_t szF = size_t(kChunk) * kPitchF * sizeof(float);
+    // K and Q split planes; once the Gram tiles are done the same bytes hold
+    // A and T of the two value heads in flight.
     static constexpr size_t oKhi = 0, oKlo = szKQ, oQhi = 2 * szKQ, oQlo = 3 * szKQ;
-    static constexpr size_t oKK = 4 * szKQ;
+    static constexpr size_t oA0 = 0, oT0 = szF, oA1 = 2 * szF, oT1 = 3 * szF;
+    static constexpr size_t szShared = 4 * szKQ > 4 * szF ? 4 * szKQ : 4 * szF;
+    static constexpr size_t oKK = szShared;  // also the q|k partial sums of squares during the prologue
     static constexpr size_t oQK = oKK + szF;
-    static constexpr size_t oA = oQK + szF;  // also the q|k partial sums of squares during the prologue
-    static constexpr size_t oT = oA + szF;
-    static constexpr size_t oTd = oT + szF;
-    static constexpr size_t oGam = oTd + size_t(4) * 16 * kPitchD * sizeof(float);
-    static constexpr size_t oScal = oGam + kChunk * sizeof(double);  // eg, bet, rq, rk [64]
+    static constexpr size_t oTd = oQK + szF;                             // [2][4][16][kPitchD]
+    static constexpr size_t oGam = oTd + size_t(2) * 4 * 16 * kPitchD * sizeof(float);  // [2][64] fp64
+    static constexpr size_t oScal = oGam + 2 * kChunk * sizeof(double);  // bet[2][64], rq, rk [64]
     static constexpr size_t kBytes = oScal + 4 * kChunk * sizeof(float);
 
-    static_assert(size_t(kChunk) * kNG * sizeof(float) <= szF, "partial sums fit the A region");
+    static_assert(size_t(kChunk) * kNG * sizeof(float) <= szF, "partial sums fit the K K^T region");
     static_assert(kBytes <= size_t(kLdsLimit), "LDS budget");
-    static_assert(oKK % 16 == 0 && oQK % 16 == 0 && oA % 16 == 0 && oT % 16 == 0 && oTd % 16 == 0 &&
-                      oGam % 16 == 0 && oScal % 16 == 0,
+    static_assert(oKK % 16 == 0 && oQK % 16 == 0 && oTd % 16 == 0 && oGam % 16 == 0 && oScal % 16 == 0 &&
+                      oA1 % 16 == 0 && oT0 % 16 == 0 && oT1 % 16 == 0,
                   "16-byte aligned regions");
 };
 
+// Gram tiles (R, 0..R) of one tile-row of A B^T (A = K or Q rows, B = K rows),
+// accumulated as independent split pairs.
+template <int R, int KS, int PK>
+__device__ __forceinline__ void gram_row(const _Float16* Ahi, const _Float16* Alo, const _Float16* Khi,
+                                         const _Float16* Klo, int lr, int lg, float4_t (&acc)[R + 1]) {
+    float4_t hh[R + 1], xx[R + 1];
+#pragma unroll
+    for (int j = 0; j <= R; j++) hh[j] = xx[j] = kZero4;
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++) {
+        const int k = 32 * ks + 8 * lg;
+        const SFrag a = lds_sfrag(Ahi, Alo, PK, 16 * R + lr, k);
+#pragma unroll
+        for (int t = 0; t <= R; t++) mma3(hh[t], xx[t], a, lds_sfrag(Khi, Klo, PK, 16 * t + lr, k));
+    }
+#pragma unroll
+    for (int j = 0; j <= R; j++) acc[j] = combine(hh[j], xx[j]);
+}
+
 // Workgroup = (chunk slot, key head).  Slots past the last chunk exit.
 template <int DK, typename TIn>
-__global__ void __launch_bounds__(kThreads, 1) prep_kernel(const PrefillParams p) {
+__global__ void __launch_bounds__(kPrepThreads, 1) prep_kernel(const PrefillParams p) {
     constexpr int VEC = Elem<TIn>::kVec;
-    constexpr int NGQ = DK / VEC;       // 16-byte groups per q (or k) head row
+    constexpr int NGQ = DK / VEC;          // 16-byte groups per q (or k) head row
     constexpr int NG = 2 * NGQ;
-    constexpr int RB = kThreads / NG;   // row blocks per chunk
-    constexpr int RPB = kChunk / RB;    // rows per thread
+    constexpr int RB = kPrepThreads / NG;  // row blocks per chunk
+    constexpr int RPB = kChunk / RB;       // rows per thread
     constexpr int KS = DK / 32;
-    static_assert(kThreads % NG == 0 && kChunk % RB == 0, "q|k prologue tiling");
+    static_assert(kPrepThreads % NG == 0 && kChunk % RB == 0, "q|k prologue tiling");
     using S = PrepSmem<DK, VEC>;
     constexpr int PK = S::kPitchK, PF = S::kPitchF, PD = S::kPitchD;
 
@@ -329,13 +352,8 @@ __global__ void __launch_bounds__(kThreads, 1) prep_kernel(const PrefillParams p
     _Float16* Qlo = reinterpret_cast<_Float16*>(smem + S::oQlo);
     float* KK = reinterpret_cast<float*>(smem + S::oKK);
     float* QK = reinterpret_cast<float*>(smem + S::oQK);
-    float* Af = reinterpret_cast<float*>(smem + S::oA);
-    float* red = Af;
-    float* Tf = reinterpret_cast<float*>(smem + S::oT);
-    float* Td = reinterpret_cast<float*>(smem + S::oTd);
-    double* gam = reinterpret_cast<double*>(smem + S::oGam);
-    float* bet = reinterpret_cast<float*>(smem + S::oScal);
-    float* rq = bet + kChunk;
+    float* red = KK;
+    float* rq = reinterpret_cast<float*>(smem + S::oScal) + 2 * kChunk;
     float* rk = rq + kChunk;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -405,10 +423,10 @@ __global__ void __launch_bounds__(kThreads, 1) prep_kernel(const PrefillParams p
 #pragma unroll
         for (int i = 0; i < RPB; i++) {
             const int row = prow0 + i;
-            const float s = rn[row];
+            const float sc = rn[row];
             _Float16 h16[VEC], l16[VEC];
 #pragma unroll
-            for (int e = 0; e < VEC; e++) split1(y[i][e] * s, h16[e], l16[e]);
+            for (int e = 0; e < VEC; e++) split1(y[i][e] * sc, h16[e], l16[e]);
             if constexpr (VEC == 8) {
                 const uint4 hv = *reinterpret_cast<const uint4*>(h16), lv = *reinterpret_cast<const uint4*>(l16);
                 *reinterpret_cast<uint4*>(dhi + row * PK + poff) = hv;
@@ -426,40 +444,57 @@ __global__ void __launch_bounds__(kThreads, 1) prep_kernel(const PrefillParams p
     }
     lds_barrier();
 
-    // ---- Gram tiles K K^T (waves 0, 1) and Q K^T (waves 2, 3), lower tiles
-    //      only, raw fp32; each wave two tile-rows ({0, 3} or {1, 2}). ----
+    // ---- Gram tiles K K^T (waves 0-3) and Q K^T (waves 4-7), lower tiles
+    //      only, raw fp32; wave w takes tile-row w % 4. ----
     {
-        const int which = wave >> 1;
+        const int which = wave >> 2, tr = wave & 3;
         const _Float16* Ahi = which ? Qhi : Khi;
         const _Float16* Alo = which ? Qlo : Klo;
         float* dst = which ? QK : KK;
-        auto store_tile = [&](const float4_t& acc, int ti, int tj) {
+        auto store_row = [&](const float4_t* acc, int ntiles) {
 #pragma unroll
-            for (int e = 0; e < 4; e++) dst[(16 * ti + 4 * lg + e) * PF + 16 * tj + lr] = acc[e];
+            for (int t = 0; t < 4; t++)
+                if (t < ntiles)
+#pragma unroll
+                    for (int e = 0; e < 4; e++) dst[(16 * tr + 4 * lg + e) * PF + 16 * t + lr] = acc[t][e];
         };
-        float4_t acc[5];
-        if ((wave & 1) == 0) {
-            gram_two_rows<0, 3, KS, PK>(Ahi, Alo, Khi, Klo, lr, lg, acc);
-            store_tile(acc[0], 0, 0);
-#pragma unroll
-            for (int t = 0; t < 4; t++) store_tile(acc[1 + t], 3, t);
+        if (tr == 0) {
+            float4_t acc[1];
+            gram_row<0, KS, PK>(Ahi, Alo, Khi, Klo, lr, lg, acc);
+            store_row(acc, 1);
+        } else if (tr == 1) {
+            float4_t acc[2];
+            gram_row<1, KS, PK>(Ahi, Alo, Khi, Klo, lr, lg, acc);
+            store_row(acc, 2);
+        } else if (tr == 2) {
+            float4_t acc[3];
+            gram_row<2, KS, PK>(Ahi, Alo, Khi, Klo, lr, lg, acc);
+            store_row(acc, 3);
         } else {
-            gram_two_rows<1, 2, KS, PK>(Ahi, Alo, Khi, Klo, lr, lg, acc);
-            store_tile(acc[0], 1, 0);
-            store_tile(acc[1], 1, 1);
-#pragma unroll
-            for (int t = 0; t < 3; t++) store_tile(acc[2 + t], 2, t);
+            float4_t acc[4];
+            gram_row<3, KS, PK>(Ahi, Alo, Khi, Klo, lr, lg, acc);
+            store_row(acc, 4);
         }
     }
+    lds_barrier();
 
-    // ---- per value head of the group: decays, A, P, T ----
-    for (int gi = 0; gi < G; gi++) {
+    // ---- per value head: decays, A, P, T; wave group grp (4 waves) takes
+    //      value heads grp, grp + 2, ... of the key head's group ----
+    const int grp = wave >> 2, gw = wave & 3, gt = tid & 255;
+    float* Af = reinterpret_cast<float*>(smem + (grp ? S::oA1 : S::oA0));
+    float* Tf = reinterpret_cast<float*>(smem + (grp ? S::oT1 : S::oT0));
+    float* Td = reinterpret_cast<float*>(smem + S::oTd) + grp * 4 * 16 * PD;
+    double* gam = reinterpret_cast<double*>(smem + S::oGam) + grp * kChunk;
+    float* bet = reinterpret_cast<float*>(smem + S::oScal) + grp * kChunk;
+    for (int g0 = 0; g0 < G; g0 += 2) {
+        const int gi = g0 + grp;
+        const bool act = gi < G;  // both groups run every barrier
         const int h = hk * G + gi;
         const int64_t ih = int64_t(cs) * p.h_v + h;
         // gam reaches about -50 over a chunk; in fp32 its rounding (~4e-6
         // absolute) would become a relative error of every decay factor, which
         // the inter- and intra-chunk terms amplify.  Scan and exponentiate in fp64.
-        if (wave == 0) {
+        if (act && gw == 0) {
             float gv = 0.0f, bv = 0.0f;
             if (lane < L) {
                 gv = p.g[(c0 + lane) * p.h_v + h];
@@ -482,21 +517,21 @@ __global__ void __launch_bounds__(kThreads, 1) prep_kernel(const PrefillParams p
         }
         lds_barrier();
         // A (fp32, LDS) and P (split, image): 8 consecutive columns per item
-        {
+        if (act) {
             _Float16* pimg = static_cast<_Float16*>(p.tp_img) + ih * Img<DK>::kTP + 2 * TriPack::kPieces * 8;
 #pragma unroll
             for (int it = 0; it < 2; it++) {
-                const int item = tid + kThreads * it;
+                const int item = gt + 256 * it;
                 const int r = item >> 3, s0 = (item & 7) * 8;
                 const double gr = gam[r];
                 const float br = bet[r];
                 float a[8], pp[8];
 #pragma unroll
                 for (int e = 0; e < 8; e++) {
-                    const int s = s0 + e;
-                    const float dec = (s <= r) ? __expf(static_cast<float>(gr - gam[s])) : 0.0f;
-                    a[e] = (s < r) ? br * dec * KK[r * PF + s] : 0.0f;
-                    pp[e] = (s <= r) ? dec * QK[r * PF + s] : 0.0f;
+                    const int sidx = s0 + e;
+                    const float dec = (sidx <= r) ? __expf(static_cast<float>(gr - gam[sidx])) : 0.0f;
+                    a[e] = (sidx < r) ? br * dec * KK[r * PF + sidx] : 0.0f;
+                    pp[e] = (sidx <= r) ? dec * QK[r * PF + sidx] : 0.0f;
                 }
                 *reinterpret_cast<float4*>(Af + r * PF + s0) = make_float4(a[0], a[1], a[2], a[3]);
                 *reinterpret_cast<float4*>(Af + r * PF + s0 + 4) = make_float4(a[4], a[5], a[6], a[7]);
@@ -511,46 +546,45 @@ __global__ void __launch_bounds__(kThreads, 1) prep_kernel(const PrefillParams p
         }
         lds_barrier();
         // inverses of the 16x16 diagonal blocks of (I + A) by forward
-        // substitution, one column per lane (wave 0)
-        if (wave == 0) {
+        // substitution, one column per lane (the group's first wave)
+        if (act && gw == 0) {
             const int b = lane >> 4, c = lane & 15;
             float x[16];
 #pragma unroll
             for (int r = 0; r < 16; r++) {
                 float acc = 0.0f;
 #pragma unroll
-                for (int s = 0; s < r; s++) acc += Af[(16 * b + r) * PF + 16 * b + s] * x[s];
+                for (int sidx = 0; sidx < r; sidx++) acc += Af[(16 * b + r) * PF + 16 * b + sidx] * x[sidx];
                 x[r] = (r < c) ? 0.0f : ((r == c) ? 1.0f : -acc);
             }
 #pragma unroll
             for (int r = 0; r < 16; r++) Td[(16 * b + r) * PD + c] = x[r];
         }
         lds_barrier();
-        if (wave == 0) {
-            inverse_column<0, PF, PD>(Af, Td, Tf, lr, lg);
-        } else if (wave == 1) {
-            inverse_column<1, PF, PD>(Af, Td, Tf, lr, lg);
-        } else if (wave == 2) {
-            inverse_column<2, PF, PD>(Af, Td, Tf, lr, lg);
-        } else if (lane < 16) {  // block (3, 3) is its diagonal inverse
+        if (act) {
+            if (gw == 0) {
+                inverse_column<0, PF, PD>(Af, Td, Tf, lr, lg);
+            } else if (gw == 1) {
+                inverse_column<1, PF, PD>(Af, Td, Tf, lr, lg);
+            } else if (gw == 2) {
+                inverse_column<2, PF, PD>(Af, Td, Tf, lr, lg);
+            } else if (lane < 16) {  // block (3, 3) is its diagonal inverse
 #pragma unroll
-            for (int r = 0; r < 16; r++) Tf[(48 + r) * PF + 48 + lane] = Td[(48 + r) * PD + lane];
+                for (int r = 0; r < 16; r++) Tf[(48 + r) * PF + 48 + lane] = Td[(48 + r) * PD + lane];
+            }
         }
         lds_barrier();
-        // T image (blocks above the diagonal are zero)
-        {
+        // T image (lower blocks)
+        if (act) {
             _Float16* timg = static_cast<_Float16*>(p.tp_img) + ih * Img<DK>::kTP;
 #pragma unroll
             for (int it = 0; it < 2; it++) {
-                const int item = tid + kThreads * it;
+                const int item = gt + 256 * it;
                 const int r = item >> 3, s0 = (item & 7) * 8;
-                float t[8];
-#pragma unroll
-                for (int e = 0; e < 8; e++) {
-                    const int s = s0 + e;
-                    t[e] = ((s >> 4) <= (r >> 4)) ? Tf[r * PF + s] : 0.0f;
-                }
                 if ((s0 >> 4) <= (r >> 4)) {
+                    float t[8];
+#pragma unroll
+                    for (int e = 0; e < 8; e++) t[e] = ((s0 + e) >> 4 <= (r >> 4)) ? Tf[r * PF + s0 + e] : 0.0f;
                     uint4 hv, lv;
                     split_pack(t, hv, lv);
                     const int q = TriPack::row_start(r) + (s0 >> 3);
@@ -872,7 +906,7 @@ hipError_t run(const PrefillParams& p, hipStream_t stream, void* const* events) 
     hipError_t err = record(events, 0, stream);
     if (err != hipSuccess) return err;
     if (p.slots > 0) {
-        prep_kernel<DK, TIn><<<dim3(unsigned(p.slots * p.h_k)), dim3(kThreads), 0, stream>>>(p);
+        prep_kernel<DK, TIn><<<dim3(unsigned(p.slots * p.h_k)), dim3(kPrepThreads), 0, stream>>>(p);
         err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
