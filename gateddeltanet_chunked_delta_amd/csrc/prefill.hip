@@ -696,20 +696,37 @@ __global__ void __launch_bounds__(kThreads, 1) carry_kernel(const PrefillParams 
     // The next chunk's images and raw v rows, in registers.
     u32x4_t pkq[NKQ], ptp[NTP], xv[VRPB + 3];
     float psc;
-    auto fetch = [&](int j) {
+    // The next chunk's loads are spread over the phases of the current one
+    // (part 0..4), so that their issue overlaps the matrix-core work instead
+    // of stalling the waves in one block.
+    auto fetch = [&](int j, int part) {
         const int64_t slot = int64_t(cb) + j;
         const u32x4_t* skq = reinterpret_cast<const u32x4_t*>(static_cast<const _Float16*>(p.kq_img) +
                                                               (slot * p.h_k + hk) * Img<DK>::kKQ);
         const u32x4_t* stp = reinterpret_cast<const u32x4_t*>(static_cast<const _Float16*>(p.tp_img) +
                                                               (slot * p.h_v + h) * Img<DK>::kTP);
+        // part 0: raw v rows and scalars; parts 1-4: a quarter of the K|Q
+        // pieces each, parts 1-3 also a third of the T|P pieces
+        constexpr int Q4 = NKQ / 4, T3 = (NTP + 2) / 3;
+        static_assert(NKQ % 4 == 0, "K|Q pieces in four parts");
+        if (part == 0) {
+            psc = p.scal_img[(slot * p.h_v + h) * Img<DK>::kScal + tid];
+            const int64_t c0 = bos + int64_t(j) * kChunk;
+            const int L = int(eos - c0 < kChunk ? eos - c0 : kChunk);
+            load_rows<TIn, VRPB>(xv, vbase, nv, c0, vrow0, L, bos, conv, vhist);
+        } else {
 #pragma unroll
-        for (int i = 0; i < NKQ; i++) pkq[i] = skq[tid + kThreads * i];
+            for (int i = 0; i < Q4; i++) pkq[(part - 1) * Q4 + i] = skq[tid + kThreads * ((part - 1) * Q4 + i)];
 #pragma unroll
-        for (int i = 0; i < NTP; i++) ptp[i] = stp[tid + kThreads * i];
-        psc = p.scal_img[(slot * p.h_v + h) * Img<DK>::kScal + tid];
-        const int64_t c0 = bos + int64_t(j) * kChunk;
-        const int L = int(eos - c0 < kChunk ? eos - c0 : kChunk);
-        load_rows<TIn, VRPB>(xv, vbase, nv, c0, vrow0, L, bos, conv, vhist);
+            for (int i = 0; i < T3; i++) {
+                const int t = (part - 1) * T3 + i;
+                if (t < NTP) ptp[t] = stp[tid + kThreads * t];
+            }
+        }
+    };
+    auto fetch_all = [&](int j) {
+#pragma unroll
+        for (int part = 0; part < 5; part++) fetch(j, part);
     };
     // Blocks (0, 1) and (2, 3) of the T and P planes are read by the products
     // (k-steps of 32 columns) but never staged: zero them once.
@@ -718,7 +735,7 @@ __global__ void __launch_bounds__(kThreads, 1) carry_kernel(const PrefillParams 
         const int r = 32 * blk + rr, c = 32 * blk + 16 + 8 * half;
         *reinterpret_cast<u32x4_t*>(tp + plane * kChunk * PT + r * PT + c) = u32x4_t{0u, 0u, 0u, 0u};
     }
-    if (nch > 0) fetch(0);
+    if (nch > 0) fetch_all(0);
 
     for (int j = 0; j < nch; j++) {
         const int64_t c0 = bos + int64_t(j) * kChunk;
@@ -750,7 +767,8 @@ __global__ void __launch_bounds__(kThreads, 1) carry_kernel(const PrefillParams 
             for (int e = 0; e < VEC; e++) Vf[row * PV + vg * VEC + e] = (row < L) ? y[e] : 0.0f;
         }
         lds_barrier();
-        if (j + 1 < nch) fetch(j + 1);
+        const bool more = j + 1 < nch;
+        if (more) fetch(j + 1, 0);
 
         // ---- the state as the B operand of this chunk's products ----
         SFrag hb[KS];
@@ -775,6 +793,7 @@ __global__ void __launch_bounds__(kThreads, 1) carry_kernel(const PrefillParams 
                 rr[tb][e] = bet[r] * (Vf[r * PV + wcol] - eg[r] * kh[e]);
             }
         }
+        if (more) fetch(j + 1, 1);
         // ---- D = T R (T lower triangular: row block tb needs k-steps <= tb/2) ----
         float4_t dd[4];
         {
@@ -794,6 +813,7 @@ __global__ void __launch_bounds__(kThreads, 1) carry_kernel(const PrefillParams 
                 dd[tb] = combine(hh, xx);
             }
         }
+        if (more) fetch(j + 1, 2);
         // ---- o = scale (e^gam Q H + P D) ----
         {
             SFrag db[2];
@@ -823,6 +843,7 @@ __global__ void __launch_bounds__(kThreads, 1) carry_kernel(const PrefillParams 
                 }
             }
         }
+        if (more) fetch(j + 1, 3);
         // ---- H <- e^{gam_last} H + K^T diag(e^{gam_last - gam}) D ----
         {
             SFrag ab[2];
@@ -849,6 +870,7 @@ __global__ void __launch_bounds__(kThreads, 1) carry_kernel(const PrefillParams 
                 hacc[it] = combine(hh, xx);
             }
         }
+        if (more) fetch(j + 1, 4);
         lds_barrier();
     }
 
