@@ -17,9 +17,16 @@ values plus its bf16 bit pattern).
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass
 
 import numpy as np
+
+
+def _workers() -> int:
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    return max(1, min(n, int(os.environ.get("OMP_NUM_THREADS", n)), 16))
 
 
 @dataclass(frozen=True)
@@ -35,17 +42,27 @@ class Geometry:
         return 2 * self.h_k * self.d_k + self.h_v * self.d_v
 
 
+def _bf16_round_inplace(x: np.ndarray, block: int = 1 << 18) -> np.ndarray:
+    """Round a contiguous fp32 array to bf16 values (ties to even) in place, in
+    cache-sized blocks."""
+    u = x.reshape(-1).view(np.uint32)
+    lsb = np.empty(min(block, u.size), dtype=np.uint32)
+    for i in range(0, u.size, block):
+        b = u[i:i + block]
+        if not np.all(np.isfinite(b.view(np.float32))):
+            raise ValueError("bf16_round expects finite values")
+        t = lsb[:b.size]
+        np.right_shift(b, 16, out=t)
+        np.bitwise_and(t, np.uint32(1), out=t)
+        b += np.uint32(0x7FFF)  # no wrap: finite fp32 bit patterns stay below 0xFF800000
+        b += t
+        b &= np.uint32(0xFFFF0000)
+    return x
+
+
 def bf16_round(x: np.ndarray) -> np.ndarray:
     """Round fp32 values to the nearest bf16 (ties to even); returns fp32."""
-    x = np.ascontiguousarray(x, dtype=np.float32)
-    if not np.all(np.isfinite(x)):
-        raise ValueError("bf16_round expects finite values")
-    u = x.view(np.uint32).copy()
-    lsb = (u >> 16) & np.uint32(1)
-    u += np.uint32(0x7FFF)  # no wrap: finite fp32 bit patterns stay below 0xFF800000
-    u += lsb
-    u &= np.uint32(0xFFFF0000)
-    return u.view(np.float32).reshape(x.shape)
+    return _bf16_round_inplace(np.array(x, dtype=np.float32, order="C", copy=True))
 
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -73,7 +90,7 @@ def sequence_draw(workload_id: int, seq_id: int, length: int, geom: Geometry, dt
     b_raw = r.standard_normal((length, geom.h_v))
     a_raw = r.standard_normal((length, geom.h_v))
     if dtype == "bf16":
-        x = bf16_round(x)
+        x = _bf16_round_inplace(x)
     beta = _sigmoid(b_raw).astype(np.float32)
     g = (-_softplus(a_raw)).astype(np.float32)
     return x, g, beta
@@ -133,7 +150,8 @@ def prefill_inputs(workload_id: int, lengths, geom: Geometry, dtype: str, *,
     v = np.empty((T, geom.h_v, geom.d_v), np.float32)
     g = np.empty((T, geom.h_v), np.float32)
     beta = np.empty((T, geom.h_v), np.float32)
-    for n, (sid, L) in enumerate(zip(seq_ids, lengths)):
+    def fill(n):
+        sid, L = seq_ids[n], lengths[n]
         x, gg, bb = sequence_draw(workload_id, sid, L, geom, dtype)
         s = slice(cu[n], cu[n + 1])
         q[s] = x[:, :nq].reshape(L, geom.h_k, geom.d_k)
@@ -141,6 +159,16 @@ def prefill_inputs(workload_id: int, lengths, geom: Geometry, dtype: str, *,
         v[s] = x[:, 2 * nq:].reshape(L, geom.h_v, geom.d_v)
         g[s] = gg
         beta[s] = bb
+
+    # Sequences are independent draws (one generator each), so they are
+    # filled by a thread pool; numpy releases the GIL in these loops.
+    workers = min(len(lengths), _workers())
+    if workers > 1 and T * geom.channels > (1 << 22):
+        with ThreadPoolExecutor(workers) as ex:
+            list(ex.map(fill, range(len(lengths))))
+    else:
+        for n in range(len(lengths)):
+            fill(n)
     conv_w = conv_weights(workload_id, geom, dtype) if conv else None
     init = None
     if initial_state_std is not None:
