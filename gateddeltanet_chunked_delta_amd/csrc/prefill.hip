@@ -778,19 +778,25 @@ __global__ void __launch_bounds__(kThreads, 1) carry_kernel(const PrefillParams 
             acc_to_operand(hacc[2 * ks], hacc[2 * ks + 1], x);
             hb[ks] = split8(x);
         }
-        // ---- R = beta (V - e^gam K H) ----
-        float4_t rr[4];
+        // ---- R = beta (V - e^gam K H) and e^gam Q H, sharing the state operand ----
+        float4_t rr[4], eqh[4];
 #pragma unroll
         for (int tb = 0; tb < 4; tb++) {
-            float4_t hh = kZero4, xx = kZero4;
+            float4_t khh = kZero4, khx = kZero4, qhh = kZero4, qhx = kZero4;
 #pragma unroll
-            for (int ks = 0; ks < KS; ks++)
-                mma3(hh, xx, lds_sfrag(Khi, Klo, PK, 16 * tb + lr, 32 * ks + 8 * lg), hb[ks]);
-            const float4_t kh = combine(hh, xx);
+            for (int ks = 0; ks < KS; ks++) {
+                mma3(khh, khx, lds_sfrag(Khi, Klo, PK, 16 * tb + lr, 32 * ks + 8 * lg), hb[ks]);
+                mma3(qhh, qhx, lds_sfrag(Qhi, Qlo, PK, 16 * tb + lr, 32 * ks + 8 * lg), hb[ks]);
+            }
+            const float4_t kh = combine(khh, khx), qh = combine(qhh, qhx);
+            const float4 egv = *reinterpret_cast<const float4*>(eg + 16 * tb + 4 * lg);
+            const float4 btv = *reinterpret_cast<const float4*>(bet + 16 * tb + 4 * lg);
+            const float egr[4] = {egv.x, egv.y, egv.z, egv.w}, btr[4] = {btv.x, btv.y, btv.z, btv.w};
 #pragma unroll
             for (int e = 0; e < 4; e++) {
                 const int r = 16 * tb + 4 * lg + e;
-                rr[tb][e] = bet[r] * (Vf[r * PV + wcol] - eg[r] * kh[e]);
+                rr[tb][e] = btr[e] * (Vf[r * PV + wcol] - egr[e] * kh[e]);
+                eqh[tb][e] = egr[e] * qh[e];
             }
         }
         if (more) fetch(j + 1, 1);
@@ -825,21 +831,16 @@ __global__ void __launch_bounds__(kThreads, 1) carry_kernel(const PrefillParams 
             }
 #pragma unroll
             for (int tb = 0; tb < 4; tb++) {
-                float4_t qhh = kZero4, qhx = kZero4, phh = kZero4, phx = kZero4;
-#pragma unroll
-                for (int ks = 0; ks < KS; ks++)
-                    mma3(qhh, qhx, lds_sfrag(Qhi, Qlo, PK, 16 * tb + lr, 32 * ks + 8 * lg), hb[ks]);
+                float4_t phh = kZero4, phx = kZero4;
 #pragma unroll
                 for (int ks = 0; ks <= tb / 2; ks++)
                     mma3(phh, phx, lds_sfrag(Phi, Plo, PT, 16 * tb + lr, 32 * ks + 8 * lg), db[ks]);
-                const float4_t qh = combine(qhh, qhx), pd = combine(phh, phx);
-                const float4 egv = *reinterpret_cast<const float4*>(eg + 16 * tb + 4 * lg);
-                const float egr[4] = {egv.x, egv.y, egv.z, egv.w};
+                const float4_t pd = combine(phh, phx);
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
                     const int r = 16 * tb + 4 * lg + e;
                     if (r < L)
-                        Elem<TOut>::put(out + ((c0 + r) * p.h_v + h) * DV + col, p.scale * (egr[e] * qh[e] + pd[e]));
+                        Elem<TOut>::put(out + ((c0 + r) * p.h_v + h) * DV + col, p.scale * (eqh[tb][e] + pd[e]));
                 }
             }
         }
