@@ -712,8 +712,15 @@ __global__ void __launch_bounds__(kThreads, 1) carry_kernel(const PrefillParams 
         if (part == 0) {
             psc = p.scal_img[(slot * p.h_v + h) * Img<DK>::kScal + tid];
             const int64_t c0 = bos + int64_t(j) * kChunk;
-            const int L = int(eos - c0 < kChunk ? eos - c0 : kChunk);
-            load_rows<TIn, VRPB>(xv, vbase, nv, c0, vrow0, L, bos, conv, vhist);
+            if (c0 - 3 >= bos && c0 + kChunk <= eos) {
+                // interior chunk: every row, history included, is in the sequence
+#pragma unroll
+                for (int jj = 0; jj < VRPB + 3; jj++)
+                    xv[jj] = *reinterpret_cast<const u32x4_t*>(vbase + (c0 + vrow0 - 3 + jj) * nv);
+            } else {
+                const int L = int(eos - c0 < kChunk ? eos - c0 : kChunk);
+                load_rows<TIn, VRPB>(xv, vbase, nv, c0, vrow0, L, bos, conv, vhist);
+            }
         } else {
 #pragma unroll
             for (int i = 0; i < Q4; i++) pkq[(part - 1) * Q4 + i] = skq[tid + kThreads * ((part - 1) * Q4 + i)];
