@@ -224,6 +224,16 @@ __device__ __forceinline__ void inverse_column(const float* Af, const float* Td,
         for (int e = 0; e < 4; e++) Tf[(16 * i + 4 * lg + e) * PF + 16 * J + lr] = tc[i][e];
 }
 
+// e^x rounded to fp32 for an fp64 argument: x log2(e) is reduced in fp64 to an
+// integer n and a fraction |f| <= 1/2, 2^f comes from the hardware exp2 and
+// 2^n is applied exactly.  Relative error ~1.5e-7, against ~4e-6 for the fp32
+// exponential of an fp32-rounded argument near -50.
+__device__ __forceinline__ float exp_of_f64(double x) {
+    const double t = x * 1.4426950408889634;
+    const double n = rint(t);
+    return ldexpf(__builtin_amdgcn_exp2f(static_cast<float>(t - n)), static_cast<int>(n));
+}
+
 // Split 8 consecutive fp32 values into 16-byte hi and lo packs.
 __device__ __forceinline__ void split_pack(const float (&x)[8], uint4& hi, uint4& lo) {
     const SFrag f = split8(x);
@@ -375,6 +385,19 @@ __global__ void __launch_bounds__(kPrepThreads, 1) prep_kernel(const PrefillPara
     const int64_t nq = int64_t(p.h_k) * DK, C = 2 * nq + int64_t(p.h_v) * p.d_v;
     const bool conv = p.conv_width == 4;
 
+    // Value heads are taken two at a time by wave groups grp = 0 (waves 0-3)
+    // and 1 (waves 4-7).  g and beta of a group's next value head are loaded
+    // ahead of use, the first ones before the prologue.
+    const int grp = wave >> 2, gw = wave & 3;
+    float gpre = 0.0f, bpre = 0.0f;
+    auto load_gb = [&](int gi) {
+        if (gw == 0 && gi < G && lane < L) {
+            gpre = p.g[(c0 + lane) * p.h_v + hk * G + gi];
+            bpre = p.beta[(c0 + lane) * p.h_v + hk * G + gi];
+        }
+    };
+    load_gb(grp);
+
     // ---- prologue: one 16-byte channel group of q|k for RPB consecutive rows ----
     const int pg = tid % NG, prow0 = (tid / NG) * RPB;
     const int pwhich = pg / NGQ, poff = (pg % NGQ) * VEC;
@@ -480,7 +503,7 @@ __global__ void __launch_bounds__(kPrepThreads, 1) prep_kernel(const PrefillPara
 
     // ---- per value head: decays, A, P, T; wave group grp (4 waves) takes
     //      value heads grp, grp + 2, ... of the key head's group ----
-    const int grp = wave >> 2, gw = wave & 3, gt = tid & 255;
+    const int gt = tid & 255;
     float* Af = reinterpret_cast<float*>(smem + (grp ? S::oA1 : S::oA0));
     float* Tf = reinterpret_cast<float*>(smem + (grp ? S::oT1 : S::oT0));
     float* Td = reinterpret_cast<float*>(smem + S::oTd) + grp * 4 * 16 * PD;
@@ -493,13 +516,10 @@ __global__ void __launch_bounds__(kPrepThreads, 1) prep_kernel(const PrefillPara
         const int64_t ih = int64_t(cs) * p.h_v + h;
         // gam reaches about -50 over a chunk; in fp32 its rounding (~4e-6
         // absolute) would become a relative error of every decay factor, which
-        // the inter- and intra-chunk terms amplify.  Scan and exponentiate in fp64.
+        // the inter- and intra-chunk terms amplify.  Scan in fp64.
         if (act && gw == 0) {
-            float gv = 0.0f, bv = 0.0f;
-            if (lane < L) {
-                gv = p.g[(c0 + lane) * p.h_v + h];
-                bv = p.beta[(c0 + lane) * p.h_v + h];
-            }
+            const float gv = gpre, bv = bpre;
+            load_gb(gi + 2);
             double x = gv;
 #pragma unroll
             for (int o = 1; o < 64; o <<= 1) {
@@ -509,11 +529,13 @@ __global__ void __launch_bounds__(kPrepThreads, 1) prep_kernel(const PrefillPara
             const double gl = __shfl(x, 63);
             gam[lane] = x;
             bet[lane] = bv;
+            const float ex = exp_of_f64(x);
             float* sc = p.scal_img + ih * Img<DK>::kScal;
             sc[lane] = bv;
-            sc[kChunk + lane] = static_cast<float>(exp(x));
-            sc[2 * kChunk + lane] = static_cast<float>(exp(gl - x));
-            sc[3 * kChunk + lane] = lane == 0 ? static_cast<float>(exp(gl)) : 0.0f;
+            sc[kChunk + lane] = ex;
+            sc[2 * kChunk + lane] = exp_of_f64(gl - x);
+            const float exl = __shfl(ex, 63);
+            sc[3 * kChunk + lane] = lane == 0 ? exl : 0.0f;
         }
         lds_barrier();
         // A (fp32, LDS) and P (split, image): 8 consecutive columns per item
