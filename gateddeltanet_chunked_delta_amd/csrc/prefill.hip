@@ -368,50 +368,78 @@ __global__ void __launch_bounds__(kPrepThreads, 1) prep_kernel(const PrefillPara
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
-    const int cs = int(blockIdx.x / unsigned(p.h_k)), hk = int(blockIdx.x % unsigned(p.h_k));
-    if (cs >= p.chunk_base[p.num_seqs]) return;
-    // the sequence of this slot: the last n with chunk_base[n] <= cs
-    int lo = 0, hi = p.num_seqs - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (p.chunk_base[mid] <= cs) lo = mid;
-        else hi = mid - 1;
-    }
-    const int n = lo;
     const int G = p.h_v / p.h_k;
-    const int64_t bos = p.cu_seqlens[n], eos = p.cu_seqlens[n + 1];
-    const int64_t c0 = bos + int64_t(cs - p.chunk_base[n]) * kChunk;
-    const int L = int(eos - c0 < kChunk ? eos - c0 : kChunk);
     const int64_t nq = int64_t(p.h_k) * DK, C = 2 * nq + int64_t(p.h_v) * p.d_v;
     const bool conv = p.conv_width == 4;
+    const int nunits = p.chunk_base[p.num_seqs] * p.h_k;  // (chunk, key head) units, chunk-major
+
+    // Unit u = (chunk slot cs, key head hk); its sequence is the last n with
+    // chunk_base[n] <= cs.
+    struct Unit {
+        int cs, hk, n, L;
+        int64_t bos, c0;
+    };
+    auto locate = [&](int u, Unit& U) {
+        U.cs = u / p.h_k;
+        U.hk = u % p.h_k;
+        int lo = 0, hi = p.num_seqs - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (p.chunk_base[mid] <= U.cs) lo = mid;
+            else hi = mid - 1;
+        }
+        U.n = lo;
+        U.bos = p.cu_seqlens[lo];
+        const int64_t eos = p.cu_seqlens[lo + 1];
+        U.c0 = U.bos + int64_t(U.cs - p.chunk_base[lo]) * kChunk;
+        U.L = int(eos - U.c0 < kChunk ? eos - U.c0 : kChunk);
+    };
 
     // Value heads are taken two at a time by wave groups grp = 0 (waves 0-3)
-    // and 1 (waves 4-7).  g and beta of a group's next value head are loaded
-    // ahead of use, the first ones before the prologue.
+    // and 1 (waves 4-7).
     const int grp = wave >> 2, gw = wave & 3;
-    float gpre = 0.0f, bpre = 0.0f;
-    auto load_gb = [&](int gi) {
-        if (gw == 0 && gi < G && lane < L) {
-            gpre = p.g[(c0 + lane) * p.h_v + hk * G + gi];
-            bpre = p.beta[(c0 + lane) * p.h_v + hk * G + gi];
-        }
-    };
-    load_gb(grp);
-
-    // ---- prologue: one 16-byte channel group of q|k for RPB consecutive rows ----
+    // prologue assignment: one 16-byte channel group of q|k, RPB consecutive rows
     const int pg = tid % NG, prow0 = (tid / NG) * RPB;
     const int pwhich = pg / NGQ, poff = (pg % NGQ) * VEC;
-    const int64_t pch = (pwhich ? nq : 0) + int64_t(hk) * DK + poff;
-    float y[RPB][VEC];
-    {
-        u32x4_t pw[4];
-        float pbias[VEC];
+
+    // The workgroup walks units blockIdx.x, blockIdx.x + gridDim.x, ...; the
+    // raw q|k rows, conv taps and first g/beta of the next unit are loaded
+    // while the current one computes.
+    u32x4_t xr[RPB + 3], pw[4];
+    float pbias[VEC];
+    float gpre = 0.0f, bpre = 0.0f;
+    // (rows past the chunk's end take g = beta = 0)
+    auto load_gb = [&](const Unit& U, int gi) {
+        if (gw == 0 && gi < G) {
+            const bool in = lane < U.L;
+            const int64_t at = (U.c0 + (in ? lane : 0)) * p.h_v + U.hk * G + gi;
+            const float gv = p.g[at], bv = p.beta[at];
+            gpre = in ? gv : 0.0f;
+            bpre = in ? bv : 0.0f;
+        }
+    };
+    auto load_unit = [&](const Unit& U) {
+        const int64_t pch = (pwhich ? nq : 0) + int64_t(U.hk) * DK + poff;
         conv_params<TIn>(p, pch, pw, pbias);
-        const TIn* pbase = static_cast<const TIn*>(pwhich ? p.k : p.q) + hk * DK + poff;
-        const TIn* hist = p.conv_state_in ? static_cast<const TIn*>(p.conv_state_in) + (int64_t(n) * C + pch) * 3
+        const TIn* pbase = static_cast<const TIn*>(pwhich ? p.k : p.q) + U.hk * DK + poff;
+        const TIn* hist = p.conv_state_in ? static_cast<const TIn*>(p.conv_state_in) + (int64_t(U.n) * C + pch) * 3
                                           : nullptr;
-        u32x4_t xr[RPB + 3];
-        load_rows<TIn, RPB>(xr, pbase, nq, c0, prow0, L, bos, conv, hist);
+        load_rows<TIn, RPB>(xr, pbase, nq, U.c0, prow0, U.L, U.bos, conv, hist);
+    };
+
+    Unit U;
+    int u = blockIdx.x;
+    if (u < nunits) {
+        locate(u, U);
+        load_unit(U);
+        load_gb(U, grp);
+    }
+    for (; u < nunits; u += gridDim.x) {
+        const int cs = U.cs, hk = U.hk, L = U.L;
+        const int64_t c0 = U.c0;
+
+        // ---- prologue: conv + SiLU of this thread's rows, partial sums of squares ----
+        float y[RPB][VEC];
 #pragma unroll
         for (int i = 0; i < RPB; i++) {
             conv_row<TIn>(conv, xr, pw, pbias, i, y[i]);
@@ -423,199 +451,209 @@ __global__ void __launch_bounds__(kPrepThreads, 1) prep_kernel(const PrefillPara
             }
             red[(prow0 + i) * NG + pg] = ss;
         }
-    }
-    lds_barrier();
-    // per-row 1/|q| and 1/|k| (fixed summation order)
-    if (tid < 2 * kChunk) {
-        const int r = tid & (kChunk - 1), which = tid / kChunk;
-        const float* rr = red + r * NG + which * NGQ;
-        float sum = 0.0f;
+        Unit N;
+        const bool more = u + int(gridDim.x) < nunits;
+        if (more) {
+            locate(u + gridDim.x, N);
+            load_unit(N);
+        }
+        lds_barrier();
+        // per-row 1/|q| and 1/|k| (fixed summation order)
+        if (tid < 2 * kChunk) {
+            const int r = tid & (kChunk - 1), which = tid / kChunk;
+            const float* rr = red + r * NG + which * NGQ;
+            float sum = 0.0f;
 #pragma unroll
-        for (int q = 0; q < NGQ; q++) sum += rr[q];
-        (which ? rk : rq)[r] = p.qk_l2norm ? 1.0f / sqrtf(sum + p.l2_eps) : 1.0f;
-    }
-    lds_barrier();
-    // normalised rows as split-fp16 pairs, into LDS and the K|Q image
-    {
-        // K image first, then Q
-        _Float16* img = static_cast<_Float16*>(p.kq_img) + (int64_t(cs) * p.h_k + hk) * Img<DK>::kKQ +
-                        (pwhich ? 0 : 2 * kChunk * DK);
-        _Float16* dhi = pwhich ? Khi : Qhi;
-        _Float16* dlo = pwhich ? Klo : Qlo;
-        const float* rn = pwhich ? rk : rq;
+            for (int q = 0; q < NGQ; q++) sum += rr[q];
+            (which ? rk : rq)[r] = p.qk_l2norm ? 1.0f / sqrtf(sum + p.l2_eps) : 1.0f;
+        }
+        lds_barrier();
+        // normalised rows as split-fp16 pairs, into LDS and the K|Q image
+        {
+            // K image first, then Q
+            _Float16* img = static_cast<_Float16*>(p.kq_img) + (int64_t(cs) * p.h_k + hk) * Img<DK>::kKQ +
+                            (pwhich ? 0 : 2 * kChunk * DK);
+            _Float16* dhi = pwhich ? Khi : Qhi;
+            _Float16* dlo = pwhich ? Klo : Qlo;
+            const float* rn = pwhich ? rk : rq;
 #pragma unroll
-        for (int i = 0; i < RPB; i++) {
-            const int row = prow0 + i;
-            const float sc = rn[row];
-            _Float16 h16[VEC], l16[VEC];
+            for (int i = 0; i < RPB; i++) {
+                const int row = prow0 + i;
+                const float sc = rn[row];
+                _Float16 h16[VEC], l16[VEC];
 #pragma unroll
-            for (int e = 0; e < VEC; e++) split1(y[i][e] * sc, h16[e], l16[e]);
-            if constexpr (VEC == 8) {
-                const uint4 hv = *reinterpret_cast<const uint4*>(h16), lv = *reinterpret_cast<const uint4*>(l16);
-                *reinterpret_cast<uint4*>(dhi + row * PK + poff) = hv;
-                *reinterpret_cast<uint4*>(dlo + row * PK + poff) = lv;
-                *reinterpret_cast<uint4*>(img + row * DK + poff) = hv;
-                *reinterpret_cast<uint4*>(img + kChunk * DK + row * DK + poff) = lv;
+                for (int e = 0; e < VEC; e++) split1(y[i][e] * sc, h16[e], l16[e]);
+                if constexpr (VEC == 8) {
+                    const uint4 hv = *reinterpret_cast<const uint4*>(h16), lv = *reinterpret_cast<const uint4*>(l16);
+                    *reinterpret_cast<uint4*>(dhi + row * PK + poff) = hv;
+                    *reinterpret_cast<uint4*>(dlo + row * PK + poff) = lv;
+                    *reinterpret_cast<uint4*>(img + row * DK + poff) = hv;
+                    *reinterpret_cast<uint4*>(img + kChunk * DK + row * DK + poff) = lv;
+                } else {
+                    const uint2 hv = *reinterpret_cast<const uint2*>(h16), lv = *reinterpret_cast<const uint2*>(l16);
+                    *reinterpret_cast<uint2*>(dhi + row * PK + poff) = hv;
+                    *reinterpret_cast<uint2*>(dlo + row * PK + poff) = lv;
+                    *reinterpret_cast<uint2*>(img + row * DK + poff) = hv;
+                    *reinterpret_cast<uint2*>(img + kChunk * DK + row * DK + poff) = lv;
+                }
+            }
+        }
+        lds_barrier();
+
+        // ---- Gram tiles K K^T (waves 0-3) and Q K^T (waves 4-7), lower tiles
+        //      only, raw fp32; wave w takes tile-row w % 4. ----
+        {
+            const int which = wave >> 2, tr = wave & 3;
+            const _Float16* Ahi = which ? Qhi : Khi;
+            const _Float16* Alo = which ? Qlo : Klo;
+            float* dst = which ? QK : KK;
+            auto store_row = [&](const float4_t* acc, int ntiles) {
+#pragma unroll
+                for (int t = 0; t < 4; t++)
+                    if (t < ntiles)
+#pragma unroll
+                        for (int e = 0; e < 4; e++) dst[(16 * tr + 4 * lg + e) * PF + 16 * t + lr] = acc[t][e];
+            };
+            if (tr == 0) {
+                float4_t acc[1];
+                gram_row<0, KS, PK>(Ahi, Alo, Khi, Klo, lr, lg, acc);
+                store_row(acc, 1);
+            } else if (tr == 1) {
+                float4_t acc[2];
+                gram_row<1, KS, PK>(Ahi, Alo, Khi, Klo, lr, lg, acc);
+                store_row(acc, 2);
+            } else if (tr == 2) {
+                float4_t acc[3];
+                gram_row<2, KS, PK>(Ahi, Alo, Khi, Klo, lr, lg, acc);
+                store_row(acc, 3);
             } else {
-                const uint2 hv = *reinterpret_cast<const uint2*>(h16), lv = *reinterpret_cast<const uint2*>(l16);
-                *reinterpret_cast<uint2*>(dhi + row * PK + poff) = hv;
-                *reinterpret_cast<uint2*>(dlo + row * PK + poff) = lv;
-                *reinterpret_cast<uint2*>(img + row * DK + poff) = hv;
-                *reinterpret_cast<uint2*>(img + kChunk * DK + row * DK + poff) = lv;
+                float4_t acc[4];
+                gram_row<3, KS, PK>(Ahi, Alo, Khi, Klo, lr, lg, acc);
+                store_row(acc, 4);
             }
         }
-    }
-    lds_barrier();
+        lds_barrier();
 
-    // ---- Gram tiles K K^T (waves 0-3) and Q K^T (waves 4-7), lower tiles
-    //      only, raw fp32; wave w takes tile-row w % 4. ----
-    {
-        const int which = wave >> 2, tr = wave & 3;
-        const _Float16* Ahi = which ? Qhi : Khi;
-        const _Float16* Alo = which ? Qlo : Klo;
-        float* dst = which ? QK : KK;
-        auto store_row = [&](const float4_t* acc, int ntiles) {
+        // ---- per value head: decays, A, P, T; wave group grp (4 waves) takes
+        //      value heads grp, grp + 2, ... of the key head's group ----
+        const int gt = tid & 255;
+        float* Af = reinterpret_cast<float*>(smem + (grp ? S::oA1 : S::oA0));
+        float* Tf = reinterpret_cast<float*>(smem + (grp ? S::oT1 : S::oT0));
+        float* Td = reinterpret_cast<float*>(smem + S::oTd) + grp * 4 * 16 * PD;
+        double* gam = reinterpret_cast<double*>(smem + S::oGam) + grp * kChunk;
+        float* bet = reinterpret_cast<float*>(smem + S::oScal) + grp * kChunk;
+        for (int g0 = 0; g0 < G; g0 += 2) {
+            const int gi = g0 + grp;
+            const bool act = gi < G;  // both groups run every barrier
+            const int h = hk * G + gi;
+            const int64_t ih = int64_t(cs) * p.h_v + h;
+            // gam reaches about -50 over a chunk; in fp32 its rounding (~4e-6
+            // absolute) would become a relative error of every decay factor, which
+            // the inter- and intra-chunk terms amplify.  Scan in fp64.
+            if (act && gw == 0) {
+                const float gv = gpre, bv = bpre;
+                load_gb(U, gi + 2);
+                double x = gv;
 #pragma unroll
-            for (int t = 0; t < 4; t++)
-                if (t < ntiles)
-#pragma unroll
-                    for (int e = 0; e < 4; e++) dst[(16 * tr + 4 * lg + e) * PF + 16 * t + lr] = acc[t][e];
-        };
-        if (tr == 0) {
-            float4_t acc[1];
-            gram_row<0, KS, PK>(Ahi, Alo, Khi, Klo, lr, lg, acc);
-            store_row(acc, 1);
-        } else if (tr == 1) {
-            float4_t acc[2];
-            gram_row<1, KS, PK>(Ahi, Alo, Khi, Klo, lr, lg, acc);
-            store_row(acc, 2);
-        } else if (tr == 2) {
-            float4_t acc[3];
-            gram_row<2, KS, PK>(Ahi, Alo, Khi, Klo, lr, lg, acc);
-            store_row(acc, 3);
-        } else {
-            float4_t acc[4];
-            gram_row<3, KS, PK>(Ahi, Alo, Khi, Klo, lr, lg, acc);
-            store_row(acc, 4);
-        }
-    }
-    lds_barrier();
-
-    // ---- per value head: decays, A, P, T; wave group grp (4 waves) takes
-    //      value heads grp, grp + 2, ... of the key head's group ----
-    const int gt = tid & 255;
-    float* Af = reinterpret_cast<float*>(smem + (grp ? S::oA1 : S::oA0));
-    float* Tf = reinterpret_cast<float*>(smem + (grp ? S::oT1 : S::oT0));
-    float* Td = reinterpret_cast<float*>(smem + S::oTd) + grp * 4 * 16 * PD;
-    double* gam = reinterpret_cast<double*>(smem + S::oGam) + grp * kChunk;
-    float* bet = reinterpret_cast<float*>(smem + S::oScal) + grp * kChunk;
-    for (int g0 = 0; g0 < G; g0 += 2) {
-        const int gi = g0 + grp;
-        const bool act = gi < G;  // both groups run every barrier
-        const int h = hk * G + gi;
-        const int64_t ih = int64_t(cs) * p.h_v + h;
-        // gam reaches about -50 over a chunk; in fp32 its rounding (~4e-6
-        // absolute) would become a relative error of every decay factor, which
-        // the inter- and intra-chunk terms amplify.  Scan in fp64.
-        if (act && gw == 0) {
-            const float gv = gpre, bv = bpre;
-            load_gb(gi + 2);
-            double x = gv;
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const double t = __shfl_up(x, o);
-                if (lane >= o) x += t;
-            }
-            const double gl = __shfl(x, 63);
-            gam[lane] = x;
-            bet[lane] = bv;
-            const float ex = exp_of_f64(x);
-            float* sc = p.scal_img + ih * Img<DK>::kScal;
-            sc[lane] = bv;
-            sc[kChunk + lane] = ex;
-            sc[2 * kChunk + lane] = exp_of_f64(gl - x);
-            const float exl = __shfl(ex, 63);
-            sc[3 * kChunk + lane] = lane == 0 ? exl : 0.0f;
-        }
-        lds_barrier();
-        // A (fp32, LDS) and P (split, image): 8 consecutive columns per item
-        if (act) {
-            _Float16* pimg = static_cast<_Float16*>(p.tp_img) + ih * Img<DK>::kTP + 2 * TriPack::kPieces * 8;
-#pragma unroll
-            for (int it = 0; it < 2; it++) {
-                const int item = gt + 256 * it;
-                const int r = item >> 3, s0 = (item & 7) * 8;
-                const double gr = gam[r];
-                const float br = bet[r];
-                float a[8], pp[8];
-#pragma unroll
-                for (int e = 0; e < 8; e++) {
-                    const int sidx = s0 + e;
-                    const float dec = (sidx <= r) ? __expf(static_cast<float>(gr - gam[sidx])) : 0.0f;
-                    a[e] = (sidx < r) ? br * dec * KK[r * PF + sidx] : 0.0f;
-                    pp[e] = (sidx <= r) ? dec * QK[r * PF + sidx] : 0.0f;
+                for (int o = 1; o < 64; o <<= 1) {
+                    const double t = __shfl_up(x, o);
+                    if (lane >= o) x += t;
                 }
-                *reinterpret_cast<float4*>(Af + r * PF + s0) = make_float4(a[0], a[1], a[2], a[3]);
-                *reinterpret_cast<float4*>(Af + r * PF + s0 + 4) = make_float4(a[4], a[5], a[6], a[7]);
-                if ((s0 >> 4) <= (r >> 4)) {
-                    uint4 hv, lv;
-                    split_pack(pp, hv, lv);
-                    const int q = TriPack::row_start(r) + (s0 >> 3);
-                    *reinterpret_cast<uint4*>(pimg + 8 * q) = hv;
-                    *reinterpret_cast<uint4*>(pimg + 8 * (TriPack::kPieces + q)) = lv;
+                const double gl = __shfl(x, 63);
+                gam[lane] = x;
+                bet[lane] = bv;
+                const float ex = exp_of_f64(x);
+                float* sc = p.scal_img + ih * Img<DK>::kScal;
+                sc[lane] = bv;
+                sc[kChunk + lane] = ex;
+                sc[2 * kChunk + lane] = exp_of_f64(gl - x);
+                const float exl = __shfl(ex, 63);
+                sc[3 * kChunk + lane] = lane == 0 ? exl : 0.0f;
+            }
+            lds_barrier();
+            // A (fp32, LDS) and P (split, image): 8 consecutive columns per item
+            if (act) {
+                _Float16* pimg = static_cast<_Float16*>(p.tp_img) + ih * Img<DK>::kTP + 2 * TriPack::kPieces * 8;
+#pragma unroll
+                for (int it = 0; it < 2; it++) {
+                    const int item = gt + 256 * it;
+                    const int r = item >> 3, s0 = (item & 7) * 8;
+                    const double gr = gam[r];
+                    const float br = bet[r];
+                    float a[8], pp[8];
+#pragma unroll
+                    for (int e = 0; e < 8; e++) {
+                        const int sidx = s0 + e;
+                        const float dec = (sidx <= r) ? __expf(static_cast<float>(gr - gam[sidx])) : 0.0f;
+                        a[e] = (sidx < r) ? br * dec * KK[r * PF + sidx] : 0.0f;
+                        pp[e] = (sidx <= r) ? dec * QK[r * PF + sidx] : 0.0f;
+                    }
+                    *reinterpret_cast<float4*>(Af + r * PF + s0) = make_float4(a[0], a[1], a[2], a[3]);
+                    *reinterpret_cast<float4*>(Af + r * PF + s0 + 4) = make_float4(a[4], a[5], a[6], a[7]);
+                    if ((s0 >> 4) <= (r >> 4)) {
+                        uint4 hv, lv;
+                        split_pack(pp, hv, lv);
+                        const int q = TriPack::row_start(r) + (s0 >> 3);
+                        *reinterpret_cast<uint4*>(pimg + 8 * q) = hv;
+                        *reinterpret_cast<uint4*>(pimg + 8 * (TriPack::kPieces + q)) = lv;
+                    }
                 }
             }
-        }
-        lds_barrier();
-        // inverses of the 16x16 diagonal blocks of (I + A) by forward
-        // substitution, one column per lane (the group's first wave)
-        if (act && gw == 0) {
-            const int b = lane >> 4, c = lane & 15;
-            float x[16];
+            lds_barrier();
+            // inverses of the 16x16 diagonal blocks of (I + A) by forward
+            // substitution, one column per lane (the group's first wave)
+            if (act && gw == 0) {
+                const int b = lane >> 4, c = lane & 15;
+                float x[16];
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                float acc = 0.0f;
+                for (int r = 0; r < 16; r++) {
+                    float acc = 0.0f;
 #pragma unroll
-                for (int sidx = 0; sidx < r; sidx++) acc += Af[(16 * b + r) * PF + 16 * b + sidx] * x[sidx];
-                x[r] = (r < c) ? 0.0f : ((r == c) ? 1.0f : -acc);
+                    for (int sidx = 0; sidx < r; sidx++) acc += Af[(16 * b + r) * PF + 16 * b + sidx] * x[sidx];
+                    x[r] = (r < c) ? 0.0f : ((r == c) ? 1.0f : -acc);
+                }
+#pragma unroll
+                for (int r = 0; r < 16; r++) Td[(16 * b + r) * PD + c] = x[r];
             }
+            lds_barrier();
+            if (act) {
+                if (gw == 0) {
+                    inverse_column<0, PF, PD>(Af, Td, Tf, lr, lg);
+                } else if (gw == 1) {
+                    inverse_column<1, PF, PD>(Af, Td, Tf, lr, lg);
+                } else if (gw == 2) {
+                    inverse_column<2, PF, PD>(Af, Td, Tf, lr, lg);
+                } else if (lane < 16) {  // block (3, 3) is its diagonal inverse
 #pragma unroll
-            for (int r = 0; r < 16; r++) Td[(16 * b + r) * PD + c] = x[r];
-        }
-        lds_barrier();
-        if (act) {
-            if (gw == 0) {
-                inverse_column<0, PF, PD>(Af, Td, Tf, lr, lg);
-            } else if (gw == 1) {
-                inverse_column<1, PF, PD>(Af, Td, Tf, lr, lg);
-            } else if (gw == 2) {
-                inverse_column<2, PF, PD>(Af, Td, Tf, lr, lg);
-            } else if (lane < 16) {  // block (3, 3) is its diagonal inverse
-#pragma unroll
-                for (int r = 0; r < 16; r++) Tf[(48 + r) * PF + 48 + lane] = Td[(48 + r) * PD + lane];
-            }
-        }
-        lds_barrier();
-        // T image (lower blocks)
-        if (act) {
-            _Float16* timg = static_cast<_Float16*>(p.tp_img) + ih * Img<DK>::kTP;
-#pragma unroll
-            for (int it = 0; it < 2; it++) {
-                const int item = gt + 256 * it;
-                const int r = item >> 3, s0 = (item & 7) * 8;
-                if ((s0 >> 4) <= (r >> 4)) {
-                    float t[8];
-#pragma unroll
-                    for (int e = 0; e < 8; e++) t[e] = ((s0 + e) >> 4 <= (r >> 4)) ? Tf[r * PF + s0 + e] : 0.0f;
-                    uint4 hv, lv;
-                    split_pack(t, hv, lv);
-                    const int q = TriPack::row_start(r) + (s0 >> 3);
-                    *reinterpret_cast<uint4*>(timg + 8 * q) = hv;
-                    *reinterpret_cast<uint4*>(timg + 8 * (TriPack::kPieces + q)) = lv;
+                    for (int r = 0; r < 16; r++) Tf[(48 + r) * PF + 48 + lane] = Td[(48 + r) * PD + lane];
                 }
             }
+            lds_barrier();
+            // T image (lower blocks)
+            if (act) {
+                _Float16* timg = static_cast<_Float16*>(p.tp_img) + ih * Img<DK>::kTP;
+#pragma unroll
+                for (int it = 0; it < 2; it++) {
+                    const int item = gt + 256 * it;
+                    const int r = item >> 3, s0 = (item & 7) * 8;
+                    if ((s0 >> 4) <= (r >> 4)) {
+                        float t[8];
+#pragma unroll
+                        for (int e = 0; e < 8; e++) t[e] = ((s0 + e) >> 4 <= (r >> 4)) ? Tf[r * PF + s0 + e] : 0.0f;
+                        uint4 hv, lv;
+                        split_pack(t, hv, lv);
+                        const int q = TriPack::row_start(r) + (s0 >> 3);
+                        *reinterpret_cast<uint4*>(timg + 8 * q) = hv;
+                        *reinterpret_cast<uint4*>(timg + 8 * (TriPack::kPieces + q)) = lv;
+                    }
+                }
+            }
+            lds_barrier();
         }
-        lds_barrier();
+        if (more) {
+            load_gb(N, grp);
+            U = N;
+        }
     }
 }
 
@@ -949,6 +987,19 @@ int64_t carry_blocks(int64_t num_seqs, int64_t h_k, int64_t h_v, int64_t d_v) {
     return (groups + 7) / 8 * 8 * members;
 }
 
+// Compute units of the current device (cached per device).
+int64_t compute_units() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] <= 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
 hipError_t record(void* const* events, int i, hipStream_t stream) {
     return events ? hipEventRecord(static_cast<hipEvent_t>(events[i]), stream) : hipSuccess;
 }
@@ -958,7 +1009,10 @@ hipError_t run(const PrefillParams& p, hipStream_t stream, void* const* events) 
     hipError_t err = record(events, 0, stream);
     if (err != hipSuccess) return err;
     if (p.slots > 0) {
-        prep_kernel<DK, TIn><<<dim3(unsigned(p.slots * p.h_k)), dim3(kPrepThreads), 0, stream>>>(p);
+        // one resident workgroup per CU walks the (chunk, key head) units
+        const int64_t units = p.slots * p.h_k;
+        const int64_t grid = units < compute_units() ? units : compute_units();
+        prep_kernel<DK, TIn><<<dim3(unsigned(grid)), dim3(kPrepThreads), 0, stream>>>(p);
         err = hipGetLastError();
         if (err != hipSuccess) return err;
     }

@@ -99,6 +99,17 @@ def test_bf16_output(oracle_mod):
     assert np.all(np.abs(o16 - ro) <= TOL["bf16"] * rms + 2.0 ** -8 * np.abs(o32))
 
 
+def test_many_short_ragged_sequences(oracle_mod):
+    """600 sequences of 1..130 tokens (about 900 chunks, most with a ragged
+    tail): more (chunk, key head) units than the chunk-local kernel has
+    resident workgroups, so each workgroup walks several units of different
+    sequences; the whole run is compared with the oracle."""
+    geom = Geometry(1, 2, 64, 64)
+    lengths = uniform_lengths(44, 600, 1, 130)
+    x = prefill_inputs(44, lengths, geom, "bf16", initial_state_std=0.02, conv_state=True)
+    _check_prefill(oracle_mod, x)
+
+
 def test_full_prefill_4x4096_sampled(oracle_mod):
     """4 x 4096 tokens, h_k = 16, h_v = 32, d = 128, bf16: whole-run sanity plus
     oracle parity on sampled (sequence, key head) units."""
