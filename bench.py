@@ -193,7 +193,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "chunked varlen prefill, 4 sequences x 4096 tokens, h_k=16, h_v=32, "
                                "d_k=d_v=128, bf16 q/k/v, fp32 g/beta/state/o, conv4+SiLU+L2, chunk 64",

@@ -95,68 +95,113 @@ __device__ __forceinline__ void lds_barrier() {
 // negative y gives exp = inf and a zero reciprocal, so the result is -0.
 __device__ __forceinline__ float silu(float y) { return y * __builtin_amdgcn_rcpf(1.0f + __expf(-y)); }
 
-// ---- split-fp16 operands: x ~= hi + lo * 2^-11, hi = fp16(x), lo = fp16((x - hi) 2^11) ----
-// Scaling the residual by 2^11 keeps lo out of fp16's subnormal range (whose
-// fixed 2^-24 grid would cap the precision of small operands), so each operand
-// keeps about 22 significant bits for |x| >= 2^-14.  A product takes three
-// fp16 matrix-core steps: hi*hi into one accumulator, lo*hi + hi*lo into a
-// second one that is scaled by 2^-11 when the sum is complete (lo*lo dropped).
+// ---- split operands: x ~= hi + lo, both halves 16-bit matrix-core inputs ----
+// A product of two split operands takes three 16-bit matrix-core steps,
+// lo*hi + hi*lo + hi*hi (lo*lo is dropped), accumulated in fp32.  Two element
+// types are used:
+//  * bf16 (operands of bf16-input calls): hi = bf16(x), lo = bf16(x - hi),
+//    both rounded to nearest even.  The pair keeps about 16 significant bits
+//    (|x - hi - lo| <= 2^-16 |x|) over the whole fp32 range, and costs three
+//    vector instructions per value (two values per packed conversion).
+//  * fp16 (operands of fp32-input calls): hi = fp16(x), lo = fp16((x - hi) 2^11).
+//    Scaling the residual by 2^11 keeps lo out of fp16's subnormal range, so
+//    the pair keeps about 22 significant bits for 2^-14 <= |x| < 65504; the
+//    cross terms go into a second accumulator that is scaled by 2^-11 at the end.
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
+template <typename E> struct OpVec;
+template <> struct OpVec<_Float16> { typedef half8_t v8; typedef half4_t v4; };
+template <> struct OpVec<__bf16> { typedef bf16x8_t v8; typedef bf16x4_t v4; };
+
+// Operand element type for each input element type.
+template <typename TIn> struct OpFor;
+template <> struct OpFor<float> { typedef _Float16 type; };
+template <> struct OpFor<bf16_t> { typedef __bf16 type; };
+
+template <typename E>
+struct SFrag {
+    typename OpVec<E>::v8 hi, lo;
+};
+
 constexpr float kLoScale = 2048.0f;
 constexpr float kLoUnscale = 1.0f / 2048.0f;
 
-struct SFrag {
-    half8_t hi, lo;
-};
-
-// hi is x converted to fp16 by the hardware converter; the residual x - hi is
+// fp16: hi is x converted by the hardware converter; the residual x - hi is
 // then exact in fp32 (hi is converted back, so the pair always refers to the
 // stored hi whatever rounding the converter applied) and is scaled by 2^11
 // before its own conversion.  Values below fp16's normal range (2^-14) go
-// entirely into lo: the matrix cores treat fp16 subnormal inputs as zero
-// (seen as a 2e-4 relative error in the outputs when subnormal hi parts were
-// allowed).
+// entirely into lo: the matrix cores treat fp16 subnormal inputs as zero.
 __device__ __forceinline__ _Float16 split_hi(float x) {
     return fabsf(x) < 6.103515625e-05f ? static_cast<_Float16>(0.0f) : static_cast<_Float16>(x);
 }
 
-__device__ __forceinline__ void split1(float x, _Float16& hi, _Float16& lo) {
-    hi = split_hi(x);
-    lo = static_cast<_Float16>((x - static_cast<float>(hi)) * kLoScale);
+// Splits of the value pair (x0, x1); element 0 of each result belongs to x0.
+__device__ __forceinline__ void split2(float x0, float x1, half2_t& hi, half2_t& lo) {
+    hi = half2_t{split_hi(x0), split_hi(x1)};
+    lo = half2_t{static_cast<_Float16>((x0 - static_cast<float>(hi[0])) * kLoScale),
+                 static_cast<_Float16>((x1 - static_cast<float>(hi[1])) * kLoScale)};
+}
+// bf16: the residual x - hi is exact in fp32 (hi keeps the leading 8 bits of x).
+__device__ __forceinline__ void split2(float x0, float x1, bf16x2_t& hi, bf16x2_t& lo) {
+    const float2_t v = {x0, x1};
+    hi = __builtin_convertvector(v, bf16x2_t);
+    const float2_t b = __builtin_convertvector(hi, float2_t);
+    lo = __builtin_convertvector(float2_t{x0 - b[0], x1 - b[1]}, bf16x2_t);
 }
 
-__device__ __forceinline__ SFrag split8(const float (&x)[8]) {
-    SFrag f;
+template <typename E>
+__device__ __forceinline__ SFrag<E> split8(const float (&x)[8]) {
+    typedef typename OpVec<E>::v8 V8;
+    typedef E V2 __attribute__((ext_vector_type(2)));
+    V2 h[4], l[4];
 #pragma unroll
-    for (int e = 0; e < 8; e++) {
-        const _Float16 h = split_hi(x[e]);
-        f.hi[e] = h;
-        f.lo[e] = static_cast<_Float16>((x[e] - static_cast<float>(h)) * kLoScale);
-    }
+    for (int i = 0; i < 4; i++) split2(x[2 * i], x[2 * i + 1], h[i], l[i]);
+    SFrag<E> f;
+    f.hi = V8{h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
+    f.lo = V8{l[0][0], l[0][1], l[1][0], l[1][1], l[2][0], l[2][1], l[3][0], l[3][1]};
     return f;
 }
 
-// Split accumulation: hh += A.hi B.hi, xx += A.lo B.hi + A.hi B.lo.
-__device__ __forceinline__ void mma3(float4_t& hh, float4_t& xx, const SFrag& a, const SFrag& b) {
+// hh += A.hi B.hi; xx += A.lo B.hi + A.hi B.lo (the fp16 cross terms carry the
+// 2^11 scale; the bf16 ones do not and go straight into hh).
+__device__ __forceinline__ void mma3(float4_t& hh, float4_t& xx, const SFrag<_Float16>& a, const SFrag<_Float16>& b) {
     xx = __builtin_amdgcn_mfma_f32_16x16x32_f16(a.lo, b.hi, xx, 0, 0, 0);
     xx = __builtin_amdgcn_mfma_f32_16x16x32_f16(a.hi, b.lo, xx, 0, 0, 0);
     hh = __builtin_amdgcn_mfma_f32_16x16x32_f16(a.hi, b.hi, hh, 0, 0, 0);
 }
+__device__ __forceinline__ void mma3(float4_t& hh, float4_t&, const SFrag<__bf16>& a, const SFrag<__bf16>& b) {
+    hh = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b.hi, hh, 0, 0, 0);
+    hh = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.lo, hh, 0, 0, 0);
+    hh = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, hh, 0, 0, 0);
+}
 
-// The finished product: hh + xx 2^-11.
+// The finished product.
+template <typename E>
 __device__ __forceinline__ float4_t combine(const float4_t& hh, const float4_t& xx) {
-    float4_t r;
+    if constexpr (__is_same(E, __bf16)) {
+        return hh;
+    } else {
+        float4_t r;
 #pragma unroll
-    for (int i = 0; i < 4; i++) r[i] = hh[i] + xx[i] * kLoUnscale;
-    return r;
+        for (int i = 0; i < 4; i++) r[i] = hh[i] + xx[i] * kLoUnscale;
+        return r;
+    }
 }
 
 constexpr float4_t kZero4 = {0.0f, 0.0f, 0.0f, 0.0f};
 
 // Fragment from row-major hi/lo LDS matrices (8 consecutive elements along K).
-__device__ __forceinline__ SFrag lds_sfrag(const _Float16* hi, const _Float16* lo, int pitch, int row, int k) {
-    SFrag f;
-    f.hi = *reinterpret_cast<const half8_t*>(hi + row * pitch + k);
-    f.lo = *reinterpret_cast<const half8_t*>(lo + row * pitch + k);
+template <typename E>
+__device__ __forceinline__ SFrag<E> lds_sfrag(const E* hi, const E* lo, int pitch, int row, int k) {
+    typedef typename OpVec<E>::v8 V8;
+    SFrag<E> f;
+    f.hi = *reinterpret_cast<const V8*>(hi + row * pitch + k);
+    f.lo = *reinterpret_cast<const V8*>(lo + row * pitch + k);
     return f;
 }
 
@@ -169,18 +214,19 @@ __device__ __forceinline__ SFrag lds_sfrag(const _Float16* hi, const _Float16* l
 // rows k .. k+3; a second load covers rows k+4 .. k+7.  col0 is a multiple of
 // 16 and the rows must be 8-byte aligned.
 typedef short short4_t __attribute__((ext_vector_type(4)));
-typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4_t lds_short4_t;
 // The loaded vectors are reinterpreted whole and joined with a shuffle: with
 // ROCm 7.2's clang, extracting their 16-bit elements one by one produced code
 // that kept only the first two elements of each load (checked on the GPU).
-__device__ __forceinline__ half4_t lds_tr16(const _Float16* p) {
-    return __builtin_bit_cast(half4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(p)));
+template <typename E>
+__device__ __forceinline__ typename OpVec<E>::v4 lds_tr16(const E* p) {
+    return __builtin_bit_cast(typename OpVec<E>::v4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(p)));
 }
-__device__ __forceinline__ SFrag lds_sfrag_tr(const _Float16* hi, const _Float16* lo, int pitch, int k, int col0) {
+template <typename E>
+__device__ __forceinline__ SFrag<E> lds_sfrag_tr(const E* hi, const E* lo, int pitch, int k, int col0) {
     const int j = threadIdx.x & 15;
     const int off = (k + (j >> 2)) * pitch + col0 + 4 * (j & 3);
-    SFrag f;
+    SFrag<E> f;
     f.hi = __builtin_shufflevector(lds_tr16(hi + off), lds_tr16(hi + off + 4 * pitch), 0, 1, 2, 3, 4, 5, 6, 7);
     f.lo = __builtin_shufflevector(lds_tr16(lo + off), lds_tr16(lo + off + 4 * pitch), 0, 1, 2, 3, 4, 5, 6, 7);
     return f;

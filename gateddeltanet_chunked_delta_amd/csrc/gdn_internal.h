@@ -26,8 +26,8 @@ struct PrefillParams {
     // workspace (see PrefillLayout)
     int32_t* order;             // [N] sequences, longest first
     int32_t* chunk_base;        // [N+1] chunks before each sequence
-    void* kq_img;               // [slots][h_k] K|Q split-fp16 images
-    void* tp_img;               // [slots][h_v] T|P split-fp16 images
+    void* kq_img;               // [slots][h_k] K|Q split images (16-bit hi, lo planes)
+    void* tp_img;               // [slots][h_v] T|P split images
     float* scal_img;            // [slots][h_v][4][64] per-token scalars
     int64_t slots;              // chunk slots: >= sum_n ceil(len_n / 64)
     int32_t num_seqs;

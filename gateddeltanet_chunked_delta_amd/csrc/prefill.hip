@@ -23,20 +23,20 @@
 //   order_kernel      sequences by descending chunk count (longest first)
 //   prep_kernel       per (chunk, key head): conv(4) + SiLU + L2 norm of q
 //                     and k; K K^T and Q K^T; then per value head of the
-//                     group: the decays, T and P.  Writes split-fp16 images
-//                     of K, Q, T, P and the per-token scalars to the workspace.
+//                     group: the decays, T and P.  Writes split images (hi
+//                     and lo planes) of K, Q, T, P and the per-token scalars to the workspace.
 //   carry_kernel      per (sequence, value head, 64 columns of d_v): conv of
 //                     v, then the chain above with the state slice held in
 //                     matrix-core accumulators.  The next chunk's images are
 //                     loaded into registers while the current chunk computes.
 //   conv_state_kernel the final conv states.
 //
-// Precision: every product takes split-fp16 operands (x = hi + lo 2^-11,
-// three fp16 matrix-core steps, fp32 accumulation), about 22 significant bits
-// per operand; the diagonal blocks of T come from an fp32 forward
-// substitution and the off-diagonal blocks from fp32 matrix-core steps; the
-// decays are scanned and exponentiated in fp64.  Operand magnitudes must stay
-// below the fp16 limit (65504).
+// Precision: every product takes split operands (x = hi + lo, three 16-bit
+// matrix-core steps, fp32 accumulation): bf16 pairs (about 16 significant
+// bits, full fp32 range) for bf16 inputs, fp16 pairs (about 22 significant
+// bits, magnitudes below 65504) for fp32 inputs.  The diagonal blocks of T
+// come from an fp32 forward substitution and the off-diagonal blocks from
+// fp32 matrix-core steps; the decays are scanned and exponentiated in fp64.
 //
 // All reductions run in a fixed order inside one workgroup, with no atomics
 // and no batch-dependent split: a sequence's results are bit-identical
@@ -53,7 +53,7 @@ constexpr int kLdsLimit = 163840;  // gfx950: 160 KiB per workgroup
 constexpr int kDvs = 64;           // d_v columns per carry workgroup
 
 // Workspace images, per chunk slot: [h_k] K|Q images, each a hi and a lo
-// fp16 plane of [64][d_k]; [h_v] T|P images, each a hi and a lo plane of the
+// 16-bit plane (bf16 or fp16, as the operands) of [64][d_k]; [h_v] T|P images, each a hi and a lo plane of the
 // 10 lower 16x16 blocks of a 64x64 matrix (TriPack); [h_v] scalar rows beta,
 // e^gam, e^{gam_last - gam}, e^{gam_last}.
 // A TriPack plane stores row r's columns [0, 16 (r/16 + 1)) as 16-byte
@@ -159,33 +159,6 @@ __device__ __forceinline__ void conv_params(const PrefillParams& p, int64_t ch, 
 
 // ---------------------------------------------------------------- products
 
-// Gram tiles of two tile-rows R0 < R1 of A B^T (A = K or Q rows, B = K rows),
-// all lower tiles (R0, 0..R0) and (R1, 0..R1): R0 + R1 + 2 tiles that share
-// their operand fragments, accumulated as independent split pairs.
-template <int R0, int R1, int KS, int PK>
-__device__ __forceinline__ void gram_two_rows(const _Float16* Ahi, const _Float16* Alo, const _Float16* Khi,
-                                              const _Float16* Klo, int lr, int lg, float4_t (&acc)[R0 + R1 + 2]) {
-    constexpr int NT = R0 + R1 + 2;
-    float4_t hh[NT], xx[NT];
-#pragma unroll
-    for (int j = 0; j < NT; j++) hh[j] = xx[j] = kZero4;
-#pragma unroll
-    for (int ks = 0; ks < KS; ks++) {
-        const int k = 32 * ks + 8 * lg;
-        const SFrag a0 = lds_sfrag(Ahi, Alo, PK, 16 * R0 + lr, k);
-        const SFrag a1 = lds_sfrag(Ahi, Alo, PK, 16 * R1 + lr, k);
-        SFrag b[R1 + 1];
-#pragma unroll
-        for (int t = 0; t <= R1; t++) b[t] = lds_sfrag(Khi, Klo, PK, 16 * t + lr, k);
-#pragma unroll
-        for (int t = 0; t <= R0; t++) mma3(hh[t], xx[t], a0, b[t]);
-#pragma unroll
-        for (int t = 0; t <= R1; t++) mma3(hh[R0 + 1 + t], xx[R0 + 1 + t], a1, b[t]);
-    }
-#pragma unroll
-    for (int j = 0; j < NT; j++) acc[j] = combine(hh[j], xx[j]);
-}
-
 // acc += A X for a 16x16 fp32 block A (row-major at `a`, row pitch `pitch`)
 // and a 16x16 X held in accumulator layout (lane l owns X[4*(l/16) + i][l%16]).
 // Four fp32 K=4 matrix-core steps; in step i, lane group g = l/16 contributes
@@ -235,8 +208,9 @@ __device__ __forceinline__ float exp_of_f64(double x) {
 }
 
 // Split 8 consecutive fp32 values into 16-byte hi and lo packs.
+template <typename E>
 __device__ __forceinline__ void split_pack(const float (&x)[8], uint4& hi, uint4& lo) {
-    const SFrag f = split8(x);
+    const SFrag<E> f = split8<E>(x);
     hi = *reinterpret_cast<const uint4*>(&f.hi);
     lo = *reinterpret_cast<const uint4*>(&f.lo);
 }
@@ -297,12 +271,12 @@ constexpr int kPrepThreads = 512;  // 8 waves: two groups of 4 take two value he
 
 template <int DK, int VEC>
 struct PrepSmem {
-    static constexpr int kPitchK = DK + 8;      // K, Q rows: [token][d_k] (fp16)
+    static constexpr int kPitchK = DK + 8;      // K, Q rows: [token][d_k] (16-bit)
     static constexpr int kPitchF = kChunk + 4;  // [token][token] (fp32)
     static constexpr int kPitchD = 20;          // diagonal inverse blocks: [4][16][kPitchD]
     static constexpr int kNG = 2 * (DK / VEC);  // q|k 16-byte groups per row
 
-    static constexpr size_t szKQ = size_t(kChunk) * kPitchK * sizeof(_Float16);
+    static constexpr size_t szKQ = size_t(kChunk) * kPitchK * sizeof(uint16_t);
     static constexpr size_t szF = size_t(kChunk) * kPitchF * sizeof(float);
     // K and Q split planes; once the Gram tiles are done the same bytes hold
     // A and T of the two value heads in flight.
@@ -325,21 +299,21 @@ struct PrepSmem {
 
 // Gram tiles (R, 0..R) of one tile-row of A B^T (A = K or Q rows, B = K rows),
 // accumulated as independent split pairs.
-template <int R, int KS, int PK>
-__device__ __forceinline__ void gram_row(const _Float16* Ahi, const _Float16* Alo, const _Float16* Khi,
-                                         const _Float16* Klo, int lr, int lg, float4_t (&acc)[R + 1]) {
+template <int R, int KS, int PK, typename E>
+__device__ __forceinline__ void gram_row(const E* Ahi, const E* Alo, const E* Khi, const E* Klo, int lr, int lg,
+                                         float4_t (&acc)[R + 1]) {
     float4_t hh[R + 1], xx[R + 1];
 #pragma unroll
     for (int j = 0; j <= R; j++) hh[j] = xx[j] = kZero4;
 #pragma unroll
     for (int ks = 0; ks < KS; ks++) {
         const int k = 32 * ks + 8 * lg;
-        const SFrag a = lds_sfrag(Ahi, Alo, PK, 16 * R + lr, k);
+        const SFrag<E> a = lds_sfrag(Ahi, Alo, PK, 16 * R + lr, k);
 #pragma unroll
         for (int t = 0; t <= R; t++) mma3(hh[t], xx[t], a, lds_sfrag(Khi, Klo, PK, 16 * t + lr, k));
     }
 #pragma unroll
-    for (int j = 0; j <= R; j++) acc[j] = combine(hh[j], xx[j]);
+    for (int j = 0; j <= R; j++) acc[j] = combine<E>(hh[j], xx[j]);
 }
 
 // Workgroup = (chunk slot, key head).  Slots past the last chunk exit.
@@ -353,13 +327,14 @@ __global__ void __launch_bounds__(kPrepThreads, 1) prep_kernel(const PrefillPara
     constexpr int KS = DK / 32;
     static_assert(kPrepThreads % NG == 0 && kChunk % RB == 0, "q|k prologue tiling");
     using S = PrepSmem<DK, VEC>;
+    using E = typename OpFor<TIn>::type;
     constexpr int PK = S::kPitchK, PF = S::kPitchF, PD = S::kPitchD;
 
     __shared__ __attribute__((aligned(16))) char smem[S::kBytes];
-    _Float16* Khi = reinterpret_cast<_Float16*>(smem + S::oKhi);
-    _Float16* Klo = reinterpret_cast<_Float16*>(smem + S::oKlo);
-    _Float16* Qhi = reinterpret_cast<_Float16*>(smem + S::oQhi);
-    _Float16* Qlo = reinterpret_cast<_Float16*>(smem + S::oQlo);
+    E* Khi = reinterpret_cast<E*>(smem + S::oKhi);
+    E* Klo = reinterpret_cast<E*>(smem + S::oKlo);
+    E* Qhi = reinterpret_cast<E*>(smem + S::oQhi);
+    E* Qlo = reinterpret_cast<E*>(smem + S::oQlo);
     float* KK = reinterpret_cast<float*>(smem + S::oKK);
     float* QK = reinterpret_cast<float*>(smem + S::oQK);
     float* red = KK;
@@ -468,21 +443,22 @@ __global__ void __launch_bounds__(kPrepThreads, 1) prep_kernel(const PrefillPara
             (which ? rk : rq)[r] = p.qk_l2norm ? 1.0f / sqrtf(sum + p.l2_eps) : 1.0f;
         }
         lds_barrier();
-        // normalised rows as split-fp16 pairs, into LDS and the K|Q image
+        // normalised rows as split pairs, into LDS and the K|Q image
         {
             // K image first, then Q
-            _Float16* img = static_cast<_Float16*>(p.kq_img) + (int64_t(cs) * p.h_k + hk) * Img<DK>::kKQ +
+            E* img = static_cast<E*>(p.kq_img) + (int64_t(cs) * p.h_k + hk) * Img<DK>::kKQ +
                             (pwhich ? 0 : 2 * kChunk * DK);
-            _Float16* dhi = pwhich ? Khi : Qhi;
-            _Float16* dlo = pwhich ? Klo : Qlo;
+            E* dhi = pwhich ? Khi : Qhi;
+            E* dlo = pwhich ? Klo : Qlo;
             const float* rn = pwhich ? rk : rq;
 #pragma unroll
             for (int i = 0; i < RPB; i++) {
                 const int row = prow0 + i;
                 const float sc = rn[row];
-                _Float16 h16[VEC], l16[VEC];
+                typedef E E2 __attribute__((ext_vector_type(2)));
+                E2 h16[VEC / 2], l16[VEC / 2];
 #pragma unroll
-                for (int e = 0; e < VEC; e++) split1(y[i][e] * sc, h16[e], l16[e]);
+                for (int e = 0; e < VEC / 2; e++) split2(y[i][2 * e] * sc, y[i][2 * e + 1] * sc, h16[e], l16[e]);
                 if constexpr (VEC == 8) {
                     const uint4 hv = *reinterpret_cast<const uint4*>(h16), lv = *reinterpret_cast<const uint4*>(l16);
                     *reinterpret_cast<uint4*>(dhi + row * PK + poff) = hv;
@@ -504,8 +480,8 @@ __global__ void __launch_bounds__(kPrepThreads, 1) prep_kernel(const PrefillPara
         //      only, raw fp32; wave w takes tile-row w % 4. ----
         {
             const int which = wave >> 2, tr = wave & 3;
-            const _Float16* Ahi = which ? Qhi : Khi;
-            const _Float16* Alo = which ? Qlo : Klo;
+            const E* Ahi = which ? Qhi : Khi;
+            const E* Alo = which ? Qlo : Klo;
             float* dst = which ? QK : KK;
             auto store_row = [&](const float4_t* acc, int ntiles) {
 #pragma unroll
@@ -573,7 +549,7 @@ __global__ void __launch_bounds__(kPrepThreads, 1) prep_kernel(const PrefillPara
             lds_barrier();
             // A (fp32, LDS) and P (split, image): 8 consecutive columns per item
             if (act) {
-                _Float16* pimg = static_cast<_Float16*>(p.tp_img) + ih * Img<DK>::kTP + 2 * TriPack::kPieces * 8;
+                E* pimg = static_cast<E*>(p.tp_img) + ih * Img<DK>::kTP + 2 * TriPack::kPieces * 8;
 #pragma unroll
                 for (int it = 0; it < 2; it++) {
                     const int item = gt + 256 * it;
@@ -592,7 +568,7 @@ __global__ void __launch_bounds__(kPrepThreads, 1) prep_kernel(const PrefillPara
                     *reinterpret_cast<float4*>(Af + r * PF + s0 + 4) = make_float4(a[4], a[5], a[6], a[7]);
                     if ((s0 >> 4) <= (r >> 4)) {
                         uint4 hv, lv;
-                        split_pack(pp, hv, lv);
+                        split_pack<E>(pp, hv, lv);
                         const int q = TriPack::row_start(r) + (s0 >> 3);
                         *reinterpret_cast<uint4*>(pimg + 8 * q) = hv;
                         *reinterpret_cast<uint4*>(pimg + 8 * (TriPack::kPieces + q)) = lv;
@@ -631,7 +607,7 @@ __global__ void __launch_bounds__(kPrepThreads, 1) prep_kernel(const PrefillPara
             lds_barrier();
             // T image (lower blocks)
             if (act) {
-                _Float16* timg = static_cast<_Float16*>(p.tp_img) + ih * Img<DK>::kTP;
+                E* timg = static_cast<E*>(p.tp_img) + ih * Img<DK>::kTP;
 #pragma unroll
                 for (int it = 0; it < 2; it++) {
                     const int item = gt + 256 * it;
@@ -641,7 +617,7 @@ __global__ void __launch_bounds__(kPrepThreads, 1) prep_kernel(const PrefillPara
 #pragma unroll
                         for (int e = 0; e < 8; e++) t[e] = ((s0 + e) >> 4 <= (r >> 4)) ? Tf[r * PF + s0 + e] : 0.0f;
                         uint4 hv, lv;
-                        split_pack(t, hv, lv);
+                        split_pack<E>(t, hv, lv);
                         const int q = TriPack::row_start(r) + (s0 >> 3);
                         *reinterpret_cast<uint4*>(timg + 8 * q) = hv;
                         *reinterpret_cast<uint4*>(timg + 8 * (TriPack::kPieces + q)) = lv;
@@ -661,11 +637,11 @@ __global__ void __launch_bounds__(kPrepThreads, 1) prep_kernel(const PrefillPara
 
 template <int DK>
 struct CarrySmem {
-    static constexpr int kPitchK = DK + 8;      // K, Q image rows (fp16)
-    static constexpr int kPitchT = kChunk + 8;  // T, P image rows (fp16)
+    static constexpr int kPitchK = DK + 8;      // K, Q image rows (16-bit)
+    static constexpr int kPitchT = kChunk + 8;  // T, P image rows (16-bit)
     static constexpr int kPitchV = kDvs + 4;    // V rows (fp32)
-    static constexpr size_t szKQ = size_t(kChunk) * kPitchK * sizeof(_Float16);
-    static constexpr size_t szTP = size_t(kChunk) * kPitchT * sizeof(_Float16);
+    static constexpr size_t szKQ = size_t(kChunk) * kPitchK * sizeof(uint16_t);
+    static constexpr size_t szTP = size_t(kChunk) * kPitchT * sizeof(uint16_t);
     static constexpr size_t oKQ = 0;         // K hi, K lo, Q hi, Q lo
     static constexpr size_t oTP = 4 * szKQ;  // T hi, T lo, P hi, P lo
     static constexpr size_t oV = oTP + 4 * szTP;
@@ -694,19 +670,20 @@ __global__ void __launch_bounds__(kThreads, 1) carry_kernel(const PrefillParams 
     static_assert(kThreads % NGV == 0 && kChunk % (kThreads / NGV) == 0, "v prologue tiling");
     static_assert(DV % kDvs == 0, "d_v slices");
     using S = CarrySmem<DK>;
+    using E = typename OpFor<TIn>::type;
     constexpr int PK = S::kPitchK, PT = S::kPitchT, PV = S::kPitchV;
 
     __shared__ __attribute__((aligned(16))) char smem[S::kBytes];
-    _Float16* kq = reinterpret_cast<_Float16*>(smem + S::oKQ);
-    _Float16* tp = reinterpret_cast<_Float16*>(smem + S::oTP);
-    const _Float16* Khi = kq;
-    const _Float16* Klo = kq + kChunk * PK;
-    const _Float16* Qhi = kq + 2 * kChunk * PK;
-    const _Float16* Qlo = kq + 3 * kChunk * PK;
-    const _Float16* Thi = tp;
-    const _Float16* Tlo = tp + kChunk * PT;
-    const _Float16* Phi = tp + 2 * kChunk * PT;
-    const _Float16* Plo = tp + 3 * kChunk * PT;
+    E* kq = reinterpret_cast<E*>(smem + S::oKQ);
+    E* tp = reinterpret_cast<E*>(smem + S::oTP);
+    const E* Khi = kq;
+    const E* Klo = kq + kChunk * PK;
+    const E* Qhi = kq + 2 * kChunk * PK;
+    const E* Qlo = kq + 3 * kChunk * PK;
+    const E* Thi = tp;
+    const E* Tlo = tp + kChunk * PT;
+    const E* Phi = tp + 2 * kChunk * PT;
+    const E* Plo = tp + 3 * kChunk * PT;
     float* Vf = reinterpret_cast<float*>(smem + S::oV);
     float* scal = reinterpret_cast<float*>(smem + S::oScal);
     const float* bet = scal;
@@ -761,9 +738,9 @@ __global__ void __launch_bounds__(kThreads, 1) carry_kernel(const PrefillParams 
     // of stalling the waves in one block.
     auto fetch = [&](int j, int part) {
         const int64_t slot = int64_t(cb) + j;
-        const u32x4_t* skq = reinterpret_cast<const u32x4_t*>(static_cast<const _Float16*>(p.kq_img) +
+        const u32x4_t* skq = reinterpret_cast<const u32x4_t*>(static_cast<const E*>(p.kq_img) +
                                                               (slot * p.h_k + hk) * Img<DK>::kKQ);
-        const u32x4_t* stp = reinterpret_cast<const u32x4_t*>(static_cast<const _Float16*>(p.tp_img) +
+        const u32x4_t* stp = reinterpret_cast<const u32x4_t*>(static_cast<const E*>(p.tp_img) +
                                                               (slot * p.h_v + h) * Img<DK>::kTP);
         // part 0: raw v rows and scalars; parts 1-4: a quarter of the K|Q
         // pieces each, parts 1-3 also a third of the T|P pieces
@@ -838,12 +815,12 @@ __global__ void __launch_bounds__(kThreads, 1) carry_kernel(const PrefillParams 
         if (more) fetch(j + 1, 0);
 
         // ---- the state as the B operand of this chunk's products ----
-        SFrag hb[KS];
+        SFrag<E> hb[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ks++) {
             float x[8];
             acc_to_operand(hacc[2 * ks], hacc[2 * ks + 1], x);
-            hb[ks] = split8(x);
+            hb[ks] = split8<E>(x);
         }
         // ---- R = beta (V - e^gam K H) and e^gam Q H, sharing the state operand ----
         float4_t rr[4], eqh[4];
@@ -855,7 +832,7 @@ __global__ void __launch_bounds__(kThreads, 1) carry_kernel(const PrefillParams 
                 mma3(khh, khx, lds_sfrag(Khi, Klo, PK, 16 * tb + lr, 32 * ks + 8 * lg), hb[ks]);
                 mma3(qhh, qhx, lds_sfrag(Qhi, Qlo, PK, 16 * tb + lr, 32 * ks + 8 * lg), hb[ks]);
             }
-            const float4_t kh = combine(khh, khx), qh = combine(qhh, qhx);
+            const float4_t kh = combine<E>(khh, khx), qh = combine<E>(qhh, qhx);
             const float4 egv = *reinterpret_cast<const float4*>(eg + 16 * tb + 4 * lg);
             const float4 btv = *reinterpret_cast<const float4*>(bet + 16 * tb + 4 * lg);
             const float egr[4] = {egv.x, egv.y, egv.z, egv.w}, btr[4] = {btv.x, btv.y, btv.z, btv.w};
@@ -870,12 +847,12 @@ __global__ void __launch_bounds__(kThreads, 1) carry_kernel(const PrefillParams 
         // ---- D = T R (T lower triangular: row block tb needs k-steps <= tb/2) ----
         float4_t dd[4];
         {
-            SFrag rb[2];
+            SFrag<E> rb[2];
 #pragma unroll
             for (int s = 0; s < 2; s++) {
                 float x[8];
                 acc_to_operand(rr[2 * s], rr[2 * s + 1], x);
-                rb[s] = split8(x);
+                rb[s] = split8<E>(x);
             }
 #pragma unroll
             for (int tb = 0; tb < 4; tb++) {
@@ -883,18 +860,18 @@ __global__ void __launch_bounds__(kThreads, 1) carry_kernel(const PrefillParams 
 #pragma unroll
                 for (int ks = 0; ks <= tb / 2; ks++)
                     mma3(hh, xx, lds_sfrag(Thi, Tlo, PT, 16 * tb + lr, 32 * ks + 8 * lg), rb[ks]);
-                dd[tb] = combine(hh, xx);
+                dd[tb] = combine<E>(hh, xx);
             }
         }
         if (more) fetch(j + 1, 2);
         // ---- o = scale (e^gam Q H + P D) ----
         {
-            SFrag db[2];
+            SFrag<E> db[2];
 #pragma unroll
             for (int s = 0; s < 2; s++) {
                 float x[8];
                 acc_to_operand(dd[2 * s], dd[2 * s + 1], x);
-                db[s] = split8(x);
+                db[s] = split8<E>(x);
             }
 #pragma unroll
             for (int tb = 0; tb < 4; tb++) {
@@ -902,7 +879,7 @@ __global__ void __launch_bounds__(kThreads, 1) carry_kernel(const PrefillParams 
 #pragma unroll
                 for (int ks = 0; ks <= tb / 2; ks++)
                     mma3(phh, phx, lds_sfrag(Phi, Plo, PT, 16 * tb + lr, 32 * ks + 8 * lg), db[ks]);
-                const float4_t pd = combine(phh, phx);
+                const float4_t pd = combine<E>(phh, phx);
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
                     const int r = 16 * tb + 4 * lg + e;
@@ -914,7 +891,7 @@ __global__ void __launch_bounds__(kThreads, 1) carry_kernel(const PrefillParams 
         if (more) fetch(j + 1, 3);
         // ---- H <- e^{gam_last} H + K^T diag(e^{gam_last - gam}) D ----
         {
-            SFrag ab[2];
+            SFrag<E> ab[2];
 #pragma unroll
             for (int s = 0; s < 2; s++) {
                 float4_t a0, a1;
@@ -926,7 +903,7 @@ __global__ void __launch_bounds__(kThreads, 1) carry_kernel(const PrefillParams 
                 }
                 float x[8];
                 acc_to_operand(a0, a1, x);
-                ab[s] = split8(x);
+                ab[s] = split8<E>(x);
             }
             const float decay = scal[3 * kChunk];
 #pragma unroll
@@ -935,7 +912,7 @@ __global__ void __launch_bounds__(kThreads, 1) carry_kernel(const PrefillParams 
 #pragma unroll
                 for (int s = 0; s < 2; s++)
                     mma3(hh, xx, lds_sfrag_tr(Khi, Klo, PK, 32 * s + 8 * lg, 16 * it), ab[s]);
-                hacc[it] = combine(hh, xx);
+                hacc[it] = combine<E>(hh, xx);
             }
         }
         if (more) fetch(j + 1, 4);
@@ -1054,9 +1031,9 @@ PrefillLayout prefill_layout(int64_t num_seqs, int64_t total_tokens, int64_t h_k
     l.chunk_base = off;
     off = align256(off + size_t(num_seqs + 1) * sizeof(int32_t));
     l.kq_img = off;
-    off = align256(off + size_t(l.slots) * size_t(h_k) * (4 * kChunk * size_t(d_k)) * sizeof(_Float16));
+    off = align256(off + size_t(l.slots) * size_t(h_k) * (4 * kChunk * size_t(d_k)) * sizeof(uint16_t));
     l.tp_img = off;
-    off = align256(off + size_t(l.slots) * size_t(h_v) * (4 * TriPack::kPieces * 8) * sizeof(_Float16));
+    off = align256(off + size_t(l.slots) * size_t(h_v) * (4 * TriPack::kPieces * 8) * sizeof(uint16_t));
     l.scal_img = off;
     off = align256(off + size_t(l.slots) * size_t(h_v) * (4 * kChunk) * sizeof(float));
     l.bytes = off;

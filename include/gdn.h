@@ -89,7 +89,7 @@ typedef struct gdn_problem {
 /* Bytes of device workspace gdn_prefill_varlen needs for this problem: the
  * chunk map (chunks before each sequence), a dispatch order of the sequences,
  * and the chunk-local terms computed in parallel over all 64-token chunks
- * (split-fp16 images of the normalised K and Q per key head, of
+ * (split 16-bit images of the normalised K and Q per key head, of
  * T = (I + A)^{-1} and of the decayed Q K^T per value head, and per-token
  * decay scalars).  That is about (T + 63 N) / 64 chunk slots of
  * 512 d_k h_k + 21504 h_v bytes each, e.g. 27 KB per token for h_k = 16,
@@ -126,8 +126,10 @@ size_t gdn_prefill_workspace_bytes(const gdn_problem* p);
  *
  * Length-0 sequences are allowed (final state = initial state).  o must not
  * overlap any input.  Supported: d_k = d_v in {64, 128}, bf16 or fp32 inputs.
- * Matrix products use split-fp16 operands (about 21 significant bits each)
- * with fp32 accumulation; intermediate magnitudes must stay below 65504.
+ * Matrix products use split 16-bit operands with fp32 accumulation: bf16
+ * pairs (about 16 significant bits each) for bf16 inputs, fp16 pairs (about
+ * 21 significant bits) for fp32 inputs, whose intermediate magnitudes must
+ * then stay below 65504.
  */
 gdn_status gdn_prefill_varlen(const gdn_problem* p,
                               const void* q, const void* k, const void* v,
