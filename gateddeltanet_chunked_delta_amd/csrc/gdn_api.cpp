@@ -117,6 +117,7 @@ gdn_status prefill(const gdn_problem* p, const void* q, const void* k, const voi
     char* ws = static_cast<char*>(workspace);
     prm.order = reinterpret_cast<int32_t*>(ws + lay.order);
     prm.chunk_base = reinterpret_cast<int32_t*>(ws + lay.chunk_base);
+    prm.slot_desc = reinterpret_cast<int32_t*>(ws + lay.slot_desc);
     prm.kq_img = ws + lay.kq_img;
     prm.tp_img = ws + lay.tp_img;
     prm.scal_img = reinterpret_cast<float*>(ws + lay.scal_img);

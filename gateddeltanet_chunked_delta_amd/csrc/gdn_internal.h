@@ -26,6 +26,7 @@ struct PrefillParams {
     // workspace (see PrefillLayout)
     int32_t* order;             // [N] sequences, longest first
     int32_t* chunk_base;        // [N+1] chunks before each sequence
+    int32_t* slot_desc;         // [slots][4] per chunk slot: sequence, first token, length, sequence start
     void* kq_img;               // [slots][h_k] K|Q split images (16-bit hi, lo planes)
     void* tp_img;               // [slots][h_v] T|P split images
     float* scal_img;            // [slots][h_v][4][64] per-token scalars
@@ -42,7 +43,7 @@ struct PrefillParams {
 // Byte offsets of the prefill workspace regions (each 256-byte aligned) and
 // the grid sizes the launches will use.
 struct PrefillLayout {
-    size_t order, chunk_base, kq_img, tp_img, scal_img, bytes;
+    size_t order, chunk_base, slot_desc, kq_img, tp_img, scal_img, bytes;
     int64_t slots, prep_blocks, carry_blocks;
 };
 PrefillLayout prefill_layout(int64_t num_seqs, int64_t total_tokens, int64_t h_k, int64_t h_v, int64_t d_k,

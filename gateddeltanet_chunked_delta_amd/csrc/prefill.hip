@@ -20,6 +20,7 @@
 // parallel over all chunks; only R, D, o and the update form the dependent
 // chain over a sequence's chunks.  The launches:
 //   chunk_map_kernel  chunk_base[n] = chunks before sequence n
+//   slot_map_kernel   per chunk slot: its sequence, first token and length
 //   order_kernel      sequences by descending chunk count (longest first)
 //   prep_kernel       per (chunk, key head): conv(4) + SiLU + L2 norm of q
 //                     and k; K K^T and Q K^T; then per value head of the
@@ -242,6 +243,25 @@ __global__ void __launch_bounds__(256) chunk_map_kernel(const int32_t* __restric
     if (t == 0) base[n] = carry;
 }
 
+// Descriptor of every chunk slot s < chunk_base[N]: {n, first token, length,
+// first token of n}, n being the last sequence with chunk_base[n] <= s (the
+// sequence that owns the slot; empty sequences own none).
+__global__ void __launch_bounds__(256) slot_map_kernel(const int32_t* __restrict__ cu, int32_t n,
+                                                        const int32_t* __restrict__ base,
+                                                        int4* __restrict__ desc) {
+    const int64_t s = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (s >= base[n]) return;
+    int lo = 0, hi = n - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (base[mid] <= s) lo = mid;
+        else hi = mid - 1;
+    }
+    const int32_t bos = cu[lo], c0 = bos + int32_t(s - base[lo]) * kChunk;
+    const int32_t left = cu[lo + 1] - c0;
+    desc[s] = int4{lo, c0, left < kChunk ? left : kChunk, bos};
+}
+
 // Sequences ordered by descending chunk count (ties by index), so that the
 // longest dependent chains start first.  Ranks are unique, so the map is a
 // permutation for any cu_seqlens contents.  The order only schedules work:
@@ -348,26 +368,21 @@ __global__ void __launch_bounds__(kPrepThreads, 1) prep_kernel(const PrefillPara
     const bool conv = p.conv_width == 4;
     const int nunits = p.chunk_base[p.num_seqs] * p.h_k;  // (chunk, key head) units, chunk-major
 
-    // Unit u = (chunk slot cs, key head hk); its sequence is the last n with
-    // chunk_base[n] <= cs.
+    // Unit u = (chunk slot cs, key head hk), described by the slot's
+    // descriptor {sequence, first token, length, sequence start}.
     struct Unit {
         int cs, hk, n, L;
         int64_t bos, c0;
     };
-    auto locate = [&](int u, Unit& U) {
+    const int4* slot_desc = reinterpret_cast<const int4*>(p.slot_desc);
+    auto desc_of = [&](int u) { return u < nunits ? slot_desc[u / p.h_k] : int4{0, 0, 0, 0}; };
+    auto unit_of = [&](int u, const int4& d, Unit& U) {
         U.cs = u / p.h_k;
         U.hk = u % p.h_k;
-        int lo = 0, hi = p.num_seqs - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (p.chunk_base[mid] <= U.cs) lo = mid;
-            else hi = mid - 1;
-        }
-        U.n = lo;
-        U.bos = p.cu_seqlens[lo];
-        const int64_t eos = p.cu_seqlens[lo + 1];
-        U.c0 = U.bos + int64_t(U.cs - p.chunk_base[lo]) * kChunk;
-        U.L = int(eos - U.c0 < kChunk ? eos - U.c0 : kChunk);
+        U.n = d.x;
+        U.c0 = d.y;
+        U.L = d.z;
+        U.bos = d.w;
     };
 
     // Value heads are taken two at a time by wave groups grp = 0 (waves 0-3)
@@ -402,10 +417,12 @@ __global__ void __launch_bounds__(kPrepThreads, 1) prep_kernel(const PrefillPara
         load_rows<TIn, RPB>(xr, pbase, nq, U.c0, prow0, U.L, U.bos, conv, hist);
     };
 
+    // The descriptor of the unit after next is loaded one unit ahead.
     Unit U;
     int u = blockIdx.x;
+    int4 dnext = desc_of(u + int(gridDim.x));
     if (u < nunits) {
-        locate(u, U);
+        unit_of(u, desc_of(u), U);
         load_unit(U);
         load_gb(U, grp);
     }
@@ -429,7 +446,8 @@ __global__ void __launch_bounds__(kPrepThreads, 1) prep_kernel(const PrefillPara
         Unit N;
         const bool more = u + int(gridDim.x) < nunits;
         if (more) {
-            locate(u + gridDim.x, N);
+            unit_of(u + gridDim.x, dnext, N);
+            dnext = desc_of(u + 2 * int(gridDim.x));
             load_unit(N);
         }
         lds_barrier();
@@ -1030,6 +1048,8 @@ PrefillLayout prefill_layout(int64_t num_seqs, int64_t total_tokens, int64_t h_k
     off = align256(off + size_t(num_seqs) * sizeof(int32_t));
     l.chunk_base = off;
     off = align256(off + size_t(num_seqs + 1) * sizeof(int32_t));
+    l.slot_desc = off;
+    off = align256(off + size_t(l.slots) * 4 * sizeof(int32_t));
     l.kq_img = off;
     off = align256(off + size_t(l.slots) * size_t(h_k) * (4 * kChunk * size_t(d_k)) * sizeof(uint16_t));
     l.tp_img = off;
@@ -1057,6 +1077,12 @@ hipError_t launch_prefill(const PrefillParams& p, int d_k, int d_v, int qkv_dtyp
     order_kernel<<<dim3((p.num_seqs + 255) / 256), dim3(256), 0, stream>>>(p.cu_seqlens, p.num_seqs, p.order);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
+    if (p.slots > 0) {
+        slot_map_kernel<<<dim3(unsigned((p.slots + 255) / 256)), dim3(256), 0, stream>>>(
+            p.cu_seqlens, p.num_seqs, p.chunk_base, reinterpret_cast<int4*>(p.slot_desc));
+        err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
     if (qkv_dtype == 1)
         err = out_dtype == 1 ? run_dtype<bf16_t, bf16_t>(p, d_k, d_v, stream, events)
                              : run_dtype<bf16_t, float>(p, d_k, d_v, stream, events);

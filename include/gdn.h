@@ -91,10 +91,11 @@ typedef struct gdn_problem {
  * and the chunk-local terms computed in parallel over all 64-token chunks
  * (split 16-bit images of the normalised K and Q per key head, of
  * T = (I + A)^{-1} and of the decayed Q K^T per value head, and per-token
- * decay scalars).  That is about (T + 63 N) / 64 chunk slots of
- * 512 d_k h_k + 21504 h_v bytes each, e.g. 27 KB per token for h_k = 16,
- * h_v = 32, d_k = 128.  Depends on num_seqs, total_tokens, h_k, h_v, d_k and
- * d_v; returns 0 for a NULL problem or num_seqs <= 0. */
+ * decay scalars), and a 16-byte descriptor per chunk slot.  That is about
+ * (T + 63 N) / 64 chunk slots of 512 d_k h_k + 21504 h_v + 16 bytes each,
+ * e.g. 27 KB per token for h_k = 16, h_v = 32, d_k = 128.  Depends on
+ * num_seqs, total_tokens, h_k, h_v, d_k and d_v; returns 0 for a NULL
+ * problem or num_seqs <= 0. */
 size_t gdn_prefill_workspace_bytes(const gdn_problem* p);
 
 /*

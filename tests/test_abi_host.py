@@ -130,13 +130,13 @@ def test_prefill_workspace(lib):
 
 
 def test_prefill_workspace_size_formula(lib):
-    """(T + 63 N) / 64 chunk slots of 512 d_k h_k + 21504 h_v bytes, plus the
+    """(T + 63 N) / 64 chunk slots of 512 d_k h_k + 21504 h_v + 16 bytes, plus the
     256-byte aligned order and chunk-base arrays, as the header states."""
     for N, T, h_k, h_v, d in [(4, 16384, 16, 32, 128), (60, 250000, 16, 48, 128), (3, 7, 2, 6, 64), (1, 0, 1, 1, 64)]:
         need = binding.gdn_prefill_workspace_bytes(_prob(num_seqs=N, total_tokens=T, h_k=h_k, h_v=h_v, d_k=d, d_v=d))
         slots = (T + 63 * N) // 64
-        body = slots * (512 * d * h_k + 21504 * h_v)
-        assert body <= need <= body + 4 * 256 + 8 * (N + 1) + 256, (N, T, need, body)
+        body = slots * (512 * d * h_k + 21504 * h_v + 16)
+        assert body <= need <= body + 5 * 256 + 8 * (N + 1) + 256, (N, T, need, body)
 
 
 def test_prefill_timed_needs_four_events(lib):
