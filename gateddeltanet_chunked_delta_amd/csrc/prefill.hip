@@ -52,6 +52,9 @@ constexpr int kChunk = 64;
 constexpr int kThreads = 256;
 constexpr int kLdsLimit = 163840;  // gfx950: 160 KiB per workgroup
 constexpr int kDvs = 64;           // d_v columns per carry workgroup
+// s_waitcnt immediate that waits for every outstanding vector memory
+// operation of the wave (vmcnt = 0; expcnt and lgkmcnt left at their maxima).
+constexpr int kVmcnt0 = 0x0f70;
 
 // Workspace images, per chunk slot: [h_k] K|Q images, each a hi and a lo
 // 16-bit plane (bf16 or fp16, as the operands) of [64][d_k]; [h_v] T|P images, each a hi and a lo plane of the
@@ -425,6 +428,7 @@ __global__ void __launch_bounds__(kPrepThreads, 1) prep_kernel(const PrefillPara
         unit_of(u, desc_of(u), U);
         load_unit(U);
         load_gb(U, grp);
+        __builtin_amdgcn_s_waitcnt(kVmcnt0);  // (see the wait in the loop)
     }
     for (; u < nunits; u += gridDim.x) {
         const int cs = U.cs, hk = U.hk, L = U.L;
@@ -574,13 +578,27 @@ __global__ void __launch_bounds__(kPrepThreads, 1) prep_kernel(const PrefillPara
                     const int r = item >> 3, s0 = (item & 7) * 8;
                     const double gr = gam[r];
                     const float br = bet[r];
+                    // All operands are loaded unconditionally (every index is in
+                    // bounds) and masked by selects: conditional loads compiled
+                    // into one branch and one LDS round trip per element.
+                    float kk[8], qk[8];
+                    double gs[8];
+#pragma unroll
+                    for (int h4 = 0; h4 < 2; h4++) {
+                        *reinterpret_cast<float4*>(kk + 4 * h4) = *reinterpret_cast<const float4*>(KK + r * PF + s0 + 4 * h4);
+                        *reinterpret_cast<float4*>(qk + 4 * h4) = *reinterpret_cast<const float4*>(QK + r * PF + s0 + 4 * h4);
+                    }
+#pragma unroll
+                    for (int h2 = 0; h2 < 4; h2++)
+                        *reinterpret_cast<double2*>(gs + 2 * h2) = *reinterpret_cast<const double2*>(gam + s0 + 2 * h2);
                     float a[8], pp[8];
 #pragma unroll
                     for (int e = 0; e < 8; e++) {
                         const int sidx = s0 + e;
-                        const float dec = (sidx <= r) ? __expf(static_cast<float>(gr - gam[sidx])) : 0.0f;
-                        a[e] = (sidx < r) ? br * dec * KK[r * PF + sidx] : 0.0f;
-                        pp[e] = (sidx <= r) ? dec * QK[r * PF + sidx] : 0.0f;
+                        const float ex = __expf(static_cast<float>(gr - gs[e]));
+                        const float dec = (sidx <= r) ? ex : 0.0f;
+                        a[e] = (sidx < r) ? br * dec * kk[e] : 0.0f;
+                        pp[e] = (sidx <= r) ? dec * qk[e] : 0.0f;
                     }
                     *reinterpret_cast<float4*>(Af + r * PF + s0) = make_float4(a[0], a[1], a[2], a[3]);
                     *reinterpret_cast<float4*>(Af + r * PF + s0 + 4) = make_float4(a[4], a[5], a[6], a[7]);
@@ -609,6 +627,12 @@ __global__ void __launch_bounds__(kPrepThreads, 1) prep_kernel(const PrefillPara
 #pragma unroll
                 for (int r = 0; r < 16; r++) Td[(16 * b + r) * PD + c] = x[r];
             }
+            // The next unit's raw rows and taps (loaded after this unit's
+            // prologue) have long arrived; waiting for them here, where only
+            // older stores are outstanding, tells the compiler so.  Otherwise the
+            // in-order vector memory counter makes their first use wait for
+            // this unit's last image stores too.
+            __builtin_amdgcn_s_waitcnt(kVmcnt0);
             lds_barrier();
             if (act) {
                 if (gw == 0) {
@@ -630,10 +654,13 @@ __global__ void __launch_bounds__(kPrepThreads, 1) prep_kernel(const PrefillPara
                 for (int it = 0; it < 2; it++) {
                     const int item = gt + 256 * it;
                     const int r = item >> 3, s0 = (item & 7) * 8;
+                    float tl[8];  // loaded unconditionally, masked below
+                    *reinterpret_cast<float4*>(tl) = *reinterpret_cast<const float4*>(Tf + r * PF + s0);
+                    *reinterpret_cast<float4*>(tl + 4) = *reinterpret_cast<const float4*>(Tf + r * PF + s0 + 4);
                     if ((s0 >> 4) <= (r >> 4)) {
                         float t[8];
 #pragma unroll
-                        for (int e = 0; e < 8; e++) t[e] = ((s0 + e) >> 4 <= (r >> 4)) ? Tf[r * PF + s0 + e] : 0.0f;
+                        for (int e = 0; e < 8; e++) t[e] = ((s0 + e) >> 4 <= (r >> 4)) ? tl[e] : 0.0f;
                         uint4 hv, lv;
                         split_pack<E>(t, hv, lv);
                         const int q = TriPack::row_start(r) + (s0 >> 3);
