@@ -139,6 +139,23 @@ __device__ __forceinline__ void load_rows(u32x4_t (&x)[R + 3], const TIn* base, 
     }
 }
 
+// Bias of one 16-byte channel group as raw element bits (0 without a bias):
+// converted only where it is used, so that the load does not have to be
+// waited for right away.
+template <typename TIn>
+__device__ __forceinline__ void conv_bias_raw(const PrefillParams& p, int64_t ch, uint32_t (&braw)[Elem<TIn>::kVec]) {
+    const TIn* cb = static_cast<const TIn*>(p.conv_b);
+#pragma unroll
+    for (int e = 0; e < Elem<TIn>::kVec; e++) braw[e] = 0u;
+    if (p.conv_width == 4 && cb) {
+#pragma unroll
+        for (int e = 0; e < Elem<TIn>::kVec; e++) {
+            if constexpr (sizeof(TIn) == 2) braw[e] = uint32_t(cb[ch + e]) << 16;
+            else braw[e] = __float_as_uint(cb[ch + e]);
+        }
+    }
+}
+
 // The 4 conv taps and the bias of one 16-byte channel group starting at
 // channel ch, kept in registers by the workgroup.
 template <typename TIn>
@@ -399,7 +416,7 @@ __global__ void __launch_bounds__(kPrepThreads, 1) prep_kernel(const PrefillPara
     // raw q|k rows, conv taps and first g/beta of the next unit are loaded
     // while the current one computes.
     u32x4_t xr[RPB + 3], pw[4];
-    float pbias[VEC];
+    uint32_t pbraw[VEC];
     float gpre = 0.0f, bpre = 0.0f;
     // (rows past the chunk's end take g = beta = 0)
     auto load_gb = [&](const Unit& U, int gi) {
@@ -413,11 +430,21 @@ __global__ void __launch_bounds__(kPrepThreads, 1) prep_kernel(const PrefillPara
     };
     auto load_unit = [&](const Unit& U) {
         const int64_t pch = (pwhich ? nq : 0) + int64_t(U.hk) * DK + poff;
-        conv_params<TIn>(p, pch, pw, pbias);
+        float unused[VEC];
+        conv_params<TIn>(p, pch, pw, unused);
+        conv_bias_raw<TIn>(p, pch, pbraw);
         const TIn* pbase = static_cast<const TIn*>(pwhich ? p.k : p.q) + U.hk * DK + poff;
-        const TIn* hist = p.conv_state_in ? static_cast<const TIn*>(p.conv_state_in) + (int64_t(U.n) * C + pch) * 3
-                                          : nullptr;
-        load_rows<TIn, RPB>(xr, pbase, nq, U.c0, prow0, U.L, U.bos, conv, hist);
+        if (U.c0 - 3 >= U.bos && U.L == kChunk) {
+            // interior chunk: every row, history included, is in the sequence
+#pragma unroll
+            for (int jj = 0; jj < RPB + 3; jj++)
+                xr[jj] = *reinterpret_cast<const u32x4_t*>(pbase + (U.c0 + prow0 - 3 + jj) * nq);
+        } else {
+            const TIn* hist = p.conv_state_in
+                                  ? static_cast<const TIn*>(p.conv_state_in) + (int64_t(U.n) * C + pch) * 3
+                                  : nullptr;
+            load_rows<TIn, RPB>(xr, pbase, nq, U.c0, prow0, U.L, U.bos, conv, hist);
+        }
     };
 
     // The descriptor of the unit after next is loaded one unit ahead.
@@ -435,6 +462,9 @@ __global__ void __launch_bounds__(kPrepThreads, 1) prep_kernel(const PrefillPara
         const int64_t c0 = U.c0;
 
         // ---- prologue: conv + SiLU of this thread's rows, partial sums of squares ----
+        float pbias[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; e++) pbias[e] = __uint_as_float(pbraw[e]);
         float y[RPB][VEC];
 #pragma unroll
         for (int i = 0; i < RPB; i++) {

@@ -101,6 +101,12 @@ def conv_weights(workload_id: int, geom: Geometry, dtype: str) -> np.ndarray:
     return bf16_round(w) if dtype == "bf16" else w
 
 
+def conv_bias(workload_id: int, geom: Geometry, dtype: str) -> np.ndarray:
+    """Conv bias [C] = 0.5 * N(0, 1) from key (workload_id, 1001)."""
+    b = (0.5 * _rng(workload_id, 1001).standard_normal(geom.channels)).astype(np.float32)
+    return bf16_round(b) if dtype == "bf16" else b
+
+
 def state_draw(workload_id: int, seq_id: int, geom: Geometry, std: float = 0.02) -> np.ndarray:
     r = _rng(workload_id, seq_id, 7)
     return (std * r.standard_normal((geom.h_v, geom.d_k, geom.d_v))).astype(np.float32)

@@ -11,7 +11,7 @@ import pytest
 import torch
 
 from gateddeltanet_chunked_delta_amd import binding
-from gateddeltanet_chunked_delta_amd.inputs import (Geometry, bf16_round, conv_state_pool, conv_weights,
+from gateddeltanet_chunked_delta_amd.inputs import (Geometry, bf16_round, conv_bias, conv_state_pool, conv_weights,
                                                     decode_inputs, prefill_inputs, state_pool, uniform_lengths)
 from tests.gpu_util import TOL, TORCH_DT, dev, gpu_prefill, head_slice, oracle_prefill, rel_err
 
@@ -67,6 +67,28 @@ def test_fp32_without_l2norm(oracle_mod):
     x.q /= np.linalg.norm(x.q, axis=-1, keepdims=True)
     x.k /= np.linalg.norm(x.k, axis=-1, keepdims=True)
     _check_prefill(oracle_mod, x, conv=False, qk_l2norm=False)
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
+def test_conv_bias(oracle_mod, dtype, d):
+    """Conv with a bias, ragged sequences (interior and boundary chunks),
+    carried conv states and initial states."""
+    geom = Geometry(2, 4, d, d)
+    x = prefill_inputs(25, [1, 64, 200, 130, 3], geom, dtype, initial_state_std=0.02, conv_state=True)
+    bias = conv_bias(25, geom, dtype)
+    dt = TORCH_DT[dtype]
+    o, fs, cso = binding.gdn_prefill_varlen(
+        dev(x.q, dt), dev(x.k, dt), dev(x.v, dt), dev(x.g), dev(x.beta), torch.from_numpy(x.cu_seqlens.astype(np.int32)),
+        conv_weight=dev(x.conv_w, dt), conv_bias=dev(bias, dt), conv_state=dev(x.conv_state_in, dt),
+        initial_state=dev(x.initial_state))
+    torch.cuda.synchronize()
+    dims = oracle_mod.Dims(2, 4, d, d, conv_width=4)
+    ro, rfs, rcso = oracle_mod.prefill(dims, x.cu_seqlens, x.q, x.k, x.v, x.g, x.beta, x.conv_w, bias,
+                                       x.conv_state_in, x.initial_state)
+    eo, ef = rel_err(o.cpu().numpy(), ro), rel_err(fs.cpu().numpy(), rfs)
+    print(f"  rel err o={eo:.3e} final_state={ef:.3e} (tol {TOL[dtype]:.0e})", flush=True)
+    assert eo <= TOL[dtype] and ef <= TOL[dtype]
+    assert np.array_equal(cso.float().cpu().numpy(), rcso)
 
 
 def test_custom_scale(oracle_mod):
@@ -281,6 +303,29 @@ def test_decode_conv_and_indices(oracle_mod, dtype, d):
     assert rel_err(pool.cpu().numpy(), ref_pool) <= TOL[dtype]
     assert np.array_equal(cpool.float().cpu().numpy(), ref_cpool.astype(np.float32))
     assert np.array_equal(pool[1].cpu().numpy(), pool_np[1])  # untouched entries
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_conv_bias(oracle_mod, dtype):
+    """Decode with a conv bias, two steps, in place."""
+    geom = Geometry(2, 4, 128, 128)
+    P = 4
+    dt = TORCH_DT[dtype]
+    pool_np = state_pool(51, P, geom)
+    cpool_np = conv_state_pool(51, P, geom, dtype)
+    w_np, b_np = conv_weights(51, geom, dtype), conv_bias(51, geom, dtype)
+    pool, cpool = dev(pool_np), dev(cpool_np, dt)
+    ref_pool, ref_cpool = pool_np.astype(np.float64), cpool_np.astype(np.float64)
+    dims = oracle_mod.Dims(2, 4, 128, 128, conv_width=4)
+    idx = np.arange(P, dtype=np.int64)
+    for s in range(2):
+        x = decode_inputs(51, s, P, geom, dtype)
+        o = binding.gdn_decode_step(dev(x.q, dt), dev(x.k, dt), dev(x.v, dt), dev(x.g), dev(x.beta), pool,
+                                    conv_weight=dev(w_np, dt), conv_bias=dev(b_np, dt), conv_state_pool=cpool)
+        ro = oracle_mod.decode(dims, x.q, x.k, x.v, x.g, x.beta, ref_pool, idx, w_np, b_np, ref_cpool)
+        assert rel_err(o.cpu().numpy(), ro) <= TOL[dtype]
+    assert rel_err(pool.cpu().numpy(), ref_pool) <= TOL[dtype]
+    assert np.array_equal(cpool.float().cpu().numpy(), ref_cpool.astype(np.float32))
 
 
 @pytest.mark.parametrize("h_k,h_v,d_k,d_v", [(3, 3, 64, 64), (2, 6, 128, 64), (1, 4, 64, 128)])
