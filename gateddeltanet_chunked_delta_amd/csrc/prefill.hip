@@ -710,6 +710,19 @@ __global__ void __launch_bounds__(kPrepThreads, 1) prep_kernel(const PrefillPara
 
 // ---------------------------------------------------------------- carry: v prologue, state chain, outputs
 
+// Raw buffer resources: word 3 of the descriptor for untyped 32-bit accesses
+// on gfx9-family parts.  A raw access at or past num_records bytes is out of
+// range: a store is dropped, a load returns zero.
+constexpr int kBufferFlags = 0x00020000;
+
+template <typename T> __device__ __forceinline__ void buf_put(__amdgpu_buffer_rsrc_t r, int off, float x);
+template <> __device__ __forceinline__ void buf_put<float>(__amdgpu_buffer_rsrc_t r, int off, float x) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, off, 0, 0);
+}
+template <> __device__ __forceinline__ void buf_put<bf16_t>(__amdgpu_buffer_rsrc_t r, int off, float x) {
+    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(x), r, off, 0, 0);
+}
+
 template <int DK>
 struct CarrySmem {
     static constexpr int kPitchK = DK + 8;      // K, Q image rows (16-bit)
@@ -941,6 +954,11 @@ __global__ void __launch_bounds__(kThreads, 1) carry_kernel(const PrefillParams 
         if (more) fetch(j + 1, 2);
         // ---- o = scale (e^gam Q H + P D) ----
         {
+            // The chunk's rows of o through a buffer resource whose extent ends
+            // after row L - 1: the hardware drops the stores of rows past the
+            // sequence's end, so no store needs a branch of its own.
+            const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+                out + c0 * p.h_v * DV, short(0), L * p.h_v * DV * int(sizeof(TOut)), kBufferFlags);
             SFrag<E> db[2];
 #pragma unroll
             for (int s = 0; s < 2; s++) {
@@ -958,8 +976,8 @@ __global__ void __launch_bounds__(kThreads, 1) carry_kernel(const PrefillParams 
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
                     const int r = 16 * tb + 4 * lg + e;
-                    if (r < L)
-                        Elem<TOut>::put(out + ((c0 + r) * p.h_v + h) * DV + col, p.scale * (eqh[tb][e] + pd[e]));
+                    buf_put<TOut>(orsrc, ((r * p.h_v + h) * DV + col) * int(sizeof(TOut)),
+                                  p.scale * (eqh[tb][e] + pd[e]));
                 }
             }
         }
