@@ -18,8 +18,8 @@ LIB_PATH = os.path.join(_PKG, "libgdn.so")
 GDN_F32, GDN_BF16 = 0, 1
 _STATUS = {0: "GDN_OK", -1: "GDN_ERR_NULL", -2: "GDN_ERR_SHAPE", -3: "GDN_ERR_DTYPE",
            -4: "GDN_ERR_UNSUPPORTED", -5: "GDN_ERR_WORKSPACE", -6: "GDN_ERR_HIP", -7: "GDN_ERR_ALIAS"}
-EXPORTED = ("gdn_prefill_workspace_bytes", "gdn_prefill_varlen", "gdn_prefill_varlen_timed", "gdn_decode_step",
-            "gdn_status_string")
+EXPORTED = ("gdn_prefill_workspace_bytes", "gdn_prefill_varlen", "gdn_prefill_varlen_timed",
+            "gdn_prefill_varlen_pooled", "gdn_decode_step", "gdn_status_string")
 
 
 class GdnProblem(ctypes.Structure):
@@ -56,6 +56,8 @@ def load() -> ctypes.CDLL:
         lib.gdn_prefill_varlen_timed.argtypes = [ctypes.POINTER(GdnProblem)] + [vp] * 14 + [c64, vp,
                                                                                            ctypes.POINTER(vp)]
         lib.gdn_prefill_varlen_timed.restype = ctypes.c_int
+        lib.gdn_prefill_varlen_pooled.argtypes = [ctypes.POINTER(GdnProblem)] + [vp] * 14 + [c64, vp]
+        lib.gdn_prefill_varlen_pooled.restype = ctypes.c_int
         lib.gdn_decode_step.argtypes = [ctypes.POINTER(GdnProblem)] + [vp] * 11 + [vp]
         lib.gdn_decode_step.restype = ctypes.c_int
         lib.gdn_status_string.argtypes = [ctypes.c_int]
@@ -214,6 +216,99 @@ def gdn_prefill_varlen(q, k, v, g, beta, cu_seqlens=None, *, conv_weight=None, c
     return o, fs, cso
 
 
+def _check_indices(state_indices, N, P, Pc, dev, validate):
+    """state_indices: int32 [N] on dev, each -1 or a distinct entry below P (and Pc)."""
+    if state_indices is None:
+        if validate and (N > P or (Pc is not None and N > Pc)):
+            raise ValueError("without state_indices the pools need at least N entries")
+        return
+    _check(state_indices, "state_indices", (N,), torch.int32, dev)
+    if validate and N:
+        idx = state_indices.cpu()
+        used = idx[idx >= 0]
+        if bool((idx < -1).any()) or bool((used >= P).any()) or (Pc is not None and bool((used >= Pc).any())):
+            raise ValueError("state_indices out of range")
+        if used.numel() != torch.unique(used).numel():
+            raise ValueError("state_indices must be distinct")
+
+
+def gdn_prefill_varlen_pooled(q, k, v, g, beta, cu_seqlens, state_pool, *, state_indices=None,
+                              has_initial_state=None, conv_weight=None, conv_bias=None, conv_state_pool=None,
+                              use_qk_l2norm=True, scale=None, l2_eps=1e-6, out_dtype=torch.float32,
+                              validate=True, out=None, workspace=None, stream=None):
+    """Chunked varlen prefill over pooled states, in place (C ABI
+    ``gdn_prefill_varlen_pooled``).
+
+    q, k: ``[T, h_k, d_k]``; v: ``[T, h_v, d_v]``; g, beta: ``[T, h_v]`` fp32;
+    cu_seqlens: int32 ``[N+1]`` (device, or CPU tensor / list, copied);
+    state_pool: fp32 ``[P, h_v, d_k, d_v]``; conv_state_pool: ``[P, C, 3]``
+    (with conv_weight); state_indices: int32 ``[N]`` or None (entry n), -1 =
+    no entry; has_initial_state: int32 ``[N]`` or None (all 1).  Sequence n
+    starts from entry state_indices[n] (zero if -1 or has_initial_state[n] = 0)
+    and leaves its final states there.  Returns o.
+    """
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, v must be packed [T, H, D]")
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on the GPU")
+    T, h_k, d_k = q.shape
+    h_v, d_v = v.shape[1], v.shape[2]
+    qdt = q.dtype
+    qcode = _dtype_code(qdt, "q")
+    ocode = _dtype_code(out_dtype, "out_dtype")
+    _check(q, "q", (T, h_k, d_k), qdt, dev)
+    _check(k, "k", (T, h_k, d_k), qdt, dev)
+    _check(v, "v", (T, h_v, d_v), qdt, dev)
+    _check(g, "g", (T, h_v), torch.float32, dev)
+    _check(beta, "beta", (T, h_v), torch.float32, dev)
+    if not isinstance(cu_seqlens, torch.Tensor):
+        cu_seqlens = torch.tensor(list(cu_seqlens), dtype=torch.int32)
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+        raise ValueError("cu_seqlens must be a 1-D int32 tensor")
+    if validate:
+        _validate_cu(cu_seqlens.cpu(), T)
+    cu_seqlens = cu_seqlens.to(dev).contiguous()
+    N = cu_seqlens.numel() - 1
+    if state_pool.dim() != 4:
+        raise ValueError("state_pool must be [P, h_v, d_k, d_v]")
+    P = state_pool.shape[0]
+    _check(state_pool, "state_pool", (P, h_v, d_k, d_v), torch.float32, dev)
+    C = 2 * h_k * d_k + h_v * d_v
+    conv_width = 4 if conv_weight is not None else 0
+    Pc = None
+    if conv_weight is not None:
+        _check(conv_weight, "conv_weight", (C, 4), qdt, dev)
+        _check(conv_bias, "conv_bias", (C,), qdt, dev)
+        if conv_state_pool is None or conv_state_pool.dim() != 3:
+            raise ValueError("conv_weight needs conv_state_pool [P, C, 3]")
+        Pc = conv_state_pool.shape[0]
+        _check(conv_state_pool, "conv_state_pool", (Pc, C, 3), qdt, dev)
+    elif conv_bias is not None or conv_state_pool is not None:
+        raise ValueError("conv_bias/conv_state_pool given without conv_weight")
+    _check_indices(state_indices, N, P, Pc, dev, validate)
+    if has_initial_state is not None:
+        _check(has_initial_state, "has_initial_state", (N,), torch.int32, dev)
+    o = out if out is not None else torch.empty((T, h_v, d_v), dtype=out_dtype, device=dev)
+    _check(o, "out", (T, h_v, d_v), out_dtype, dev)
+    prob = make_problem(N, T, h_k, h_v, d_k, d_v, qcode, ocode, scale, use_qk_l2norm, l2_eps, conv_width)
+    ws_bytes = gdn_prefill_workspace_bytes(prob)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    elif workspace.numel() < ws_bytes:
+        raise ValueError("workspace too small")
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    st = load().gdn_prefill_varlen_pooled(
+        ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
+        _ptr(conv_weight), _ptr(conv_bias), _ptr(conv_state_pool), _ptr(state_pool), _ptr(state_indices),
+        _ptr(has_initial_state), _ptr(o), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
+        ctypes.c_void_p(stream))
+    if st != 0:
+        raise GdnError(st, "gdn_prefill_varlen_pooled")
+    return o
+
+
 def gdn_decode_step(q, k, v, g, beta, state_pool, *, state_indices=None, conv_weight=None,
                     conv_bias=None, conv_state_pool=None, use_qk_l2norm=True, scale=None, l2_eps=1e-6,
                     out_dtype=torch.float32, validate=True, out=None, stream=None):
@@ -252,19 +347,7 @@ def gdn_decode_step(q, k, v, g, beta, state_pool, *, state_indices=None, conv_we
         if conv_state_pool.dim() != 3:
             raise ValueError("conv_state_pool must be [P, C, 3]")
         _check(conv_state_pool, "conv_state_pool", (conv_state_pool.shape[0], C, 3), qdt, dev)
-    if state_indices is not None:
-        _check(state_indices, "state_indices", (N,), torch.int32, dev)
-        if validate and N:
-            idx = state_indices.cpu()
-            used = idx[idx >= 0]
-            if bool((idx < -1).any()) or bool((used >= P).any()):
-                raise ValueError("state_indices out of range")
-            if conv_width and bool((used >= conv_state_pool.shape[0]).any()):
-                raise ValueError("state_indices out of range of conv_state_pool")
-            if used.numel() != torch.unique(used).numel():
-                raise ValueError("state_indices must be distinct")
-    elif validate and (N > P or (conv_width and N > conv_state_pool.shape[0])):
-        raise ValueError("without state_indices the pools need at least N entries")
+    _check_indices(state_indices, N, P, conv_state_pool.shape[0] if conv_width else None, dev, validate)
     o = out if out is not None else torch.empty((N, h_v, d_v), dtype=out_dtype, device=dev)
     _check(o, "out", (N, h_v, d_v), out_dtype, dev)
     prob = make_problem(N, N, h_k, h_v, d_k, d_v, qcode, ocode, scale, use_qk_l2norm, l2_eps, conv_width)

@@ -59,6 +59,33 @@ size_t gdn_prefill_workspace_bytes(const gdn_problem* p) {
 
 namespace {
 
+// Launches a validated prefill.
+gdn_status launch(const gdn_problem* p, const gdn::PrefillLayout& lay, const void* q, const void* k,
+                  const void* v, const float* g, const float* beta, const int32_t* cu_seqlens,
+                  const void* conv_w, const void* conv_b, const void* conv_state_in, void* conv_state_out,
+                  const float* initial_state, void* o, float* final_state, const int32_t* state_indices,
+                  const int32_t* has_initial, void* workspace, void* stream, void* const* events) {
+    gdn::PrefillParams prm;
+    prm.q = q; prm.k = k; prm.v = v; prm.g = g; prm.beta = beta; prm.cu_seqlens = cu_seqlens;
+    prm.conv_w = conv_w; prm.conv_b = conv_b; prm.conv_state_in = conv_state_in;
+    prm.conv_state_out = conv_state_out; prm.initial_state = initial_state; prm.o = o;
+    prm.final_state = final_state;
+    prm.state_indices = state_indices; prm.has_initial = has_initial;
+    char* ws = static_cast<char*>(workspace);
+    prm.order = reinterpret_cast<int32_t*>(ws + lay.order);
+    prm.chunk_base = reinterpret_cast<int32_t*>(ws + lay.chunk_base);
+    prm.slot_desc = reinterpret_cast<int32_t*>(ws + lay.slot_desc);
+    prm.kq_img = ws + lay.kq_img;
+    prm.tp_img = ws + lay.tp_img;
+    prm.scal_img = reinterpret_cast<float*>(ws + lay.scal_img);
+    prm.slots = lay.slots;
+    prm.num_seqs = p->num_seqs; prm.h_k = p->h_k; prm.h_v = p->h_v; prm.d_v = p->d_v;
+    prm.conv_width = p->conv_width;
+    prm.qk_l2norm = p->qk_l2norm; prm.l2_eps = eff_eps(p); prm.scale = eff_scale(p);
+    return from_hip(gdn::launch_prefill(prm, p->d_k, p->d_v, p->qkv_dtype, p->out_dtype,
+                                        static_cast<hipStream_t>(stream), events));
+}
+
 gdn_status prefill(const gdn_problem* p, const void* q, const void* k, const void* v, const float* g,
                    const float* beta, const int32_t* cu_seqlens, const void* conv_w, const void* conv_b,
                    const void* conv_state_in, void* conv_state_out, const float* initial_state, void* o,
@@ -109,24 +136,59 @@ gdn_status prefill(const gdn_problem* p, const void* q, const void* k, const voi
         overlaps(rc, rw))
         return GDN_ERR_ALIAS;
 
-    gdn::PrefillParams prm;
-    prm.q = q; prm.k = k; prm.v = v; prm.g = g; prm.beta = beta; prm.cu_seqlens = cu_seqlens;
-    prm.conv_w = conv_w; prm.conv_b = conv_b; prm.conv_state_in = conv_state_in;
-    prm.conv_state_out = conv_state_out; prm.initial_state = initial_state; prm.o = o;
-    prm.final_state = final_state;
-    char* ws = static_cast<char*>(workspace);
-    prm.order = reinterpret_cast<int32_t*>(ws + lay.order);
-    prm.chunk_base = reinterpret_cast<int32_t*>(ws + lay.chunk_base);
-    prm.slot_desc = reinterpret_cast<int32_t*>(ws + lay.slot_desc);
-    prm.kq_img = ws + lay.kq_img;
-    prm.tp_img = ws + lay.tp_img;
-    prm.scal_img = reinterpret_cast<float*>(ws + lay.scal_img);
-    prm.slots = lay.slots;
-    prm.num_seqs = p->num_seqs; prm.h_k = p->h_k; prm.h_v = p->h_v; prm.d_v = p->d_v;
-    prm.conv_width = p->conv_width;
-    prm.qk_l2norm = p->qk_l2norm; prm.l2_eps = eff_eps(p); prm.scale = eff_scale(p);
-    return from_hip(gdn::launch_prefill(prm, p->d_k, p->d_v, p->qkv_dtype, p->out_dtype,
-                                        static_cast<hipStream_t>(stream), events));
+    return launch(p, lay, q, k, v, g, beta, cu_seqlens, conv_w, conv_b, conv_state_in, conv_state_out,
+                  initial_state, o, final_state, nullptr, nullptr, workspace, stream, events);
+}
+
+gdn_status prefill_pooled(const gdn_problem* p, const void* q, const void* k, const void* v, const float* g,
+                          const float* beta, const int32_t* cu_seqlens, const void* conv_w, const void* conv_b,
+                          void* conv_state_pool, float* state_pool, const int32_t* state_indices,
+                          const int32_t* has_initial, void* o, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+    gdn_status st = check_problem(p);
+    if (st != GDN_OK) return st;
+    const int64_t T = p->total_tokens, N = p->num_seqs;
+    if (N == 0 && T != 0) return GDN_ERR_SHAPE;
+    if (N > 0 && (!cu_seqlens || !state_pool)) return GDN_ERR_NULL;
+    if (T > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL;
+    if (p->conv_width == 4 && (!conv_w || !conv_state_pool)) return GDN_ERR_NULL;
+    if (!gdn::prefill_supported(p->d_k, p->d_v, p->qkv_dtype, p->out_dtype)) return GDN_ERR_UNSUPPORTED;
+    const gdn::PrefillLayout lay = gdn::prefill_layout(N, T, p->h_k, p->h_v, p->d_k, p->d_v);
+    if (N > 0 && (lay.prep_blocks >= (int64_t(1) << 31) || lay.carry_blocks >= (int64_t(1) << 31)))
+        return GDN_ERR_SHAPE;
+    if (N > 0 && (!workspace || workspace_bytes < lay.bytes)) return GDN_ERR_WORKSPACE;
+    if (N == 0) return GDN_OK;
+
+    const int64_t eb = elem_bytes(p->qkv_dtype), ob = elem_bytes(p->out_dtype);
+    const int64_t nq = int64_t(p->h_k) * p->d_k, nv = int64_t(p->h_v) * p->d_v, C = 2 * nq + nv;
+    const void* ptrs16[] = {q, k, v, o, state_pool, workspace};
+    for (const void* ptr : ptrs16)
+        if (ptr && !aligned(ptr, 16)) return GDN_ERR_UNSUPPORTED;
+    const void* ptrs4[] = {g, beta, cu_seqlens, state_indices, has_initial};
+    for (const void* ptr : ptrs4)
+        if (ptr && !aligned(ptr, 4)) return GDN_ERR_UNSUPPORTED;
+    const void* ptrse[] = {conv_w, conv_b, conv_state_pool};
+    for (const void* ptr : ptrse)
+        if (ptr && !aligned(ptr, size_t(eb))) return GDN_ERR_UNSUPPORTED;
+    // The pool sizes are not known here: o and the workspace are checked
+    // against the per-call inputs, and must not start at a pool.
+    const Range in[] = {range_of(q, T * nq * eb), range_of(k, T * nq * eb), range_of(v, T * nv * eb),
+                        range_of(g, T * p->h_v * 4), range_of(beta, T * p->h_v * 4),
+                        range_of(cu_seqlens, (N + 1) * 4), range_of(conv_w, C * 4 * eb),
+                        range_of(conv_b, C * eb), range_of(state_indices, N * 4), range_of(has_initial, N * 4)};
+    const Range ro = range_of(o, T * nv * ob), rw = range_of(workspace, int64_t(workspace_bytes));
+    for (const Range& r : in)
+        if (overlaps(ro, r) || overlaps(rw, r)) return GDN_ERR_ALIAS;
+    if (overlaps(ro, rw)) return GDN_ERR_ALIAS;
+    const uintptr_t pools[] = {reinterpret_cast<uintptr_t>(state_pool), reinterpret_cast<uintptr_t>(conv_state_pool)};
+    for (uintptr_t pool : pools)
+        if (pool && (pool == reinterpret_cast<uintptr_t>(o) || pool == reinterpret_cast<uintptr_t>(workspace)))
+            return GDN_ERR_ALIAS;
+    if (conv_state_pool && reinterpret_cast<uintptr_t>(conv_state_pool) == reinterpret_cast<uintptr_t>(state_pool))
+        return GDN_ERR_ALIAS;
+    void* cpool = p->conv_width == 4 ? conv_state_pool : nullptr;
+    return launch(p, lay, q, k, v, g, beta, cu_seqlens, conv_w, conv_b, cpool, cpool, state_pool, o, state_pool,
+                  state_indices ? state_indices : nullptr, has_initial, workspace, stream, nullptr);
 }
 
 }  // namespace
@@ -150,6 +212,16 @@ gdn_status gdn_prefill_varlen_timed(const gdn_problem* p, const void* q, const v
     if (!events || !events[0] || !events[1] || !events[2] || !events[3]) return GDN_ERR_NULL;
     return prefill(p, q, k, v, g, beta, cu_seqlens, conv_w, conv_b, conv_state_in, conv_state_out,
                    initial_state, o, final_state, workspace, workspace_bytes, stream, events);
+}
+
+gdn_status gdn_prefill_varlen_pooled(const gdn_problem* p, const void* q, const void* k, const void* v,
+                                     const float* g, const float* beta, const int32_t* cu_seqlens,
+                                     const void* conv_w, const void* conv_b, void* conv_state_pool,
+                                     float* state_pool, const int32_t* state_indices,
+                                     const int32_t* has_initial_state, void* o, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+    return prefill_pooled(p, q, k, v, g, beta, cu_seqlens, conv_w, conv_b, conv_state_pool, state_pool,
+                          state_indices, has_initial_state, o, workspace, workspace_bytes, stream);
 }
 
 gdn_status gdn_decode_step(const gdn_problem* p, const void* q, const void* k, const void* v,

@@ -20,9 +20,15 @@ struct PrefillParams {
     const void* conv_b;         // [C] or null
     const void* conv_state_in;  // [N][C][3] or null
     void* conv_state_out;       // [N][C][3] or null
-    const float* initial_state; // [N][h_v][d_k][d_v] or null
+    const float* initial_state; // [N][h_v][d_k][d_v] or null (or a pool, see state_indices)
     void* o;                    // [T][h_v][d_v]
     float* final_state;         // [N][h_v][d_k][d_v] or null
+    // Pooled states: with state_indices, sequence n's initial/final recurrent
+    // state and conv history live in pool entry state_indices[n] of the
+    // arrays above (-1: none, zero start and nothing written back); the
+    // entry's stored contents are its initial ones unless has_initial[n] = 0.
+    const int32_t* state_indices;  // [N] or null (entry n)
+    const int32_t* has_initial;    // [N] or null (all 1)
     // workspace (see PrefillLayout)
     int32_t* order;             // [N] sequences, longest first
     int32_t* chunk_base;        // [N+1] chunks before each sequence

@@ -139,6 +139,16 @@ __device__ __forceinline__ void load_rows(u32x4_t (&x)[R + 3], const TIn* base, 
     }
 }
 
+// Pool entry holding sequence n's states: state_indices[n] (-1: none), or n
+// itself without an index map.  Its stored states are the sequence's initial
+// ones unless has_initial[n] is 0.
+__device__ __forceinline__ int state_slot(const PrefillParams& p, int n) {
+    return p.state_indices ? p.state_indices[n] : n;
+}
+__device__ __forceinline__ bool slot_has_initial(const PrefillParams& p, int n, int slot) {
+    return slot >= 0 && (!p.has_initial || p.has_initial[n] != 0);
+}
+
 // Bias of one 16-byte channel group as raw element bits (0 without a bias):
 // converted only where it is used, so that the load does not have to be
 // waited for right away.
@@ -440,8 +450,9 @@ __global__ void __launch_bounds__(kPrepThreads, 1) prep_kernel(const PrefillPara
             for (int jj = 0; jj < RPB + 3; jj++)
                 xr[jj] = *reinterpret_cast<const u32x4_t*>(pbase + (U.c0 + prow0 - 3 + jj) * nq);
         } else {
-            const TIn* hist = p.conv_state_in
-                                  ? static_cast<const TIn*>(p.conv_state_in) + (int64_t(U.n) * C + pch) * 3
+            const int sl = state_slot(p, U.n);
+            const TIn* hist = (p.conv_state_in && slot_has_initial(p, U.n, sl))
+                                  ? static_cast<const TIn*>(p.conv_state_in) + (int64_t(sl) * C + pch) * 3
                                   : nullptr;
             load_rows<TIn, RPB>(xr, pbase, nq, U.c0, prow0, U.L, U.bos, conv, hist);
         }
@@ -798,7 +809,9 @@ __global__ void __launch_bounds__(kThreads, 1) carry_kernel(const PrefillParams 
     const int64_t nq = int64_t(p.h_k) * DK, nv = int64_t(p.h_v) * DV, C = 2 * nq + nv;
     const bool conv = p.conv_width == 4;
     TOut* out = static_cast<TOut*>(p.o);
-    const int64_t state_base = (int64_t(n) * p.h_v + h) * DK * DV + col;
+    const int slot = state_slot(p, n);
+    const bool has_init = slot_has_initial(p, n, slot);
+    const int64_t state_base = (int64_t(slot) * p.h_v + h) * DK * DV + col;  // used only when slot >= 0
 
     // State column: hacc[it][e] = H[16 it + 4 lg + e][col].
     float4_t hacc[KT];
@@ -806,14 +819,15 @@ __global__ void __launch_bounds__(kThreads, 1) carry_kernel(const PrefillParams 
     for (int it = 0; it < KT; it++)
 #pragma unroll
         for (int e = 0; e < 4; e++)
-            hacc[it][e] = p.initial_state ? p.initial_state[state_base + int64_t(16 * it + 4 * lg + e) * DV] : 0.0f;
+            hacc[it][e] = (p.initial_state && has_init)
+                              ? p.initial_state[state_base + int64_t(16 * it + 4 * lg + e) * DV] : 0.0f;
 
     // v prologue: one 16-byte channel group of the slice for VRPB rows
     const int vg = tid % NGV, vrow0 = (tid / NGV) * VRPB;
     const int64_t vch = 2 * nq + int64_t(h) * DV + slice * kDvs + vg * VEC;
     const TIn* vbase = static_cast<const TIn*>(p.v) + int64_t(h) * DV + slice * kDvs + vg * VEC;
-    const TIn* vhist = p.conv_state_in ? static_cast<const TIn*>(p.conv_state_in) + (int64_t(n) * C + vch) * 3
-                                       : nullptr;
+    const TIn* vhist = (p.conv_state_in && has_init)
+                           ? static_cast<const TIn*>(p.conv_state_in) + (int64_t(slot) * C + vch) * 3 : nullptr;
     u32x4_t vwp[4];
     float vbias[VEC];
     conv_params<TIn>(p, vch, vwp, vbias);
@@ -1012,7 +1026,7 @@ __global__ void __launch_bounds__(kThreads, 1) carry_kernel(const PrefillParams 
         lds_barrier();
     }
 
-    if (p.final_state) {
+    if (p.final_state && slot >= 0) {
 #pragma unroll
         for (int it = 0; it < KT; it++)
 #pragma unroll
@@ -1022,15 +1036,20 @@ __global__ void __launch_bounds__(kThreads, 1) carry_kernel(const PrefillParams 
 }
 
 // Final conv state of every sequence: its last 3 raw inputs per channel,
-// reaching into conv_state_in for sequences shorter than 3.  One thread per
-// (sequence, channel) reads all three values before writing, so the output
-// may be the input buffer itself.
+// reaching into its conv history for sequences shorter than 3; both are
+// entry state_slot(n) of their arrays (no write without an entry).  One
+// thread per (sequence, channel) reads all three values before writing, so
+// the output may be the input buffer itself.
 template <typename TIn>
 __global__ void __launch_bounds__(256) conv_state_kernel(const PrefillParams p, int dk, int dv) {
     const int64_t nq = int64_t(p.h_k) * dk, nv = int64_t(p.h_v) * dv, C = 2 * nq + nv;
     const int64_t e = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     if (e >= int64_t(p.num_seqs) * C) return;
     const int64_t n = e / C, c = e % C;
+    const int sl = state_slot(p, int(n));
+    if (sl < 0) return;  // no pool entry: nothing to write
+    const bool hist = slot_has_initial(p, int(n), sl);
+    const int64_t at = (int64_t(sl) * C + c) * 3;
     const int64_t bos = p.cu_seqlens[n], len = p.cu_seqlens[n + 1] - bos;
     const TIn* qin = static_cast<const TIn*>(p.q);
     const TIn* kin = static_cast<const TIn*>(p.k);
@@ -1045,11 +1064,11 @@ __global__ void __launch_bounds__(256) conv_state_kernel(const PrefillParams p, 
             const int64_t t = bos + pos;
             vals[j] = c < nq ? qin[t * nq + c] : (c < 2 * nq ? kin[t * nq + c - nq] : vin[t * nv + c - 2 * nq]);
         } else {
-            vals[j] = csi ? csi[e * 3 + 3 + pos] : TIn(0);
+            vals[j] = (csi && hist) ? csi[at + 3 + pos] : TIn(0);
         }
     }
 #pragma unroll
-    for (int j = 0; j < 3; j++) cso[e * 3 + j] = vals[j];
+    for (int j = 0; j < 3; j++) cso[at + j] = vals[j];
 }
 
 int64_t carry_blocks(int64_t num_seqs, int64_t h_k, int64_t h_v, int64_t d_v) {

@@ -163,6 +163,46 @@ gdn_status gdn_prefill_varlen_timed(const gdn_problem* p,
                                     void* stream, void* const* events);
 
 /*
+ * Chunked prefill whose recurrent and conv states live in caller pools, as a
+ * serving engine keeps them ("[Feature] Add batch invariance support to
+ * GDN_ATTN backend": review comment part "3. The chunked delta-rule scan
+ * itself" (a), where a continued prefill starts the scan from the stored
+ * recurrent state, a new one from none, and the conv state is kept per cache
+ * slot; commit messages, where the whole state pool is passed and addressed
+ * by state indices, also for mixed batches).  Sequence n continues from pool
+ * entry i = state_indices[n] and leaves its final states there, in place:
+ *
+ *  state_pool       [P][h_v][d_k][d_v] fp32  read-modify-write
+ *  conv_state_pool  [P][C][3]      qkv_dtype read-modify-write (the last 3
+ *                                  raw inputs, oldest first); required when
+ *                                  conv_width = 4, else ignored
+ *  state_indices    [N] int32 or NULL (sequence n uses entry n).  Entry -1:
+ *                   the sequence starts from zero state and history, its o
+ *                   rows are written and no pool entry is touched.
+ *  has_initial_state [N] int32 or NULL (all 1).  0: the sequence starts from
+ *                   zero state and history whatever entry i holds (a new
+ *                   request); its final states still go to entry i.
+ *
+ * Everything else (q, k, v, g, beta, cu_seqlens, conv_w, conv_b, o,
+ * workspace, stream) is as in gdn_prefill_varlen; the results equal those of
+ * gdn_prefill_varlen with initial_state / conv_state_in gathered from the
+ * entries, bit for bit.  A decode token is a length-1 sequence, so one call
+ * can serve a mixed batch of prefills and decodes.  Indices must be in range
+ * and distinct (except -1), as in gdn_decode_step; the pool sizes are not
+ * passed, so o and the workspace are only checked not to start at a pool.
+ */
+gdn_status gdn_prefill_varlen_pooled(const gdn_problem* p,
+                                     const void* q, const void* k, const void* v,
+                                     const float* g, const float* beta,
+                                     const int32_t* cu_seqlens,
+                                     const void* conv_w, const void* conv_b,
+                                     void* conv_state_pool, float* state_pool,
+                                     const int32_t* state_indices,
+                                     const int32_t* has_initial_state,
+                                     void* o, void* workspace, size_t workspace_bytes,
+                                     void* stream);
+
+/*
  * One decode step: one new token for each of N slots, updating a pooled
  * state in place ("[Feature] Add batch invariance support to GDN_ATTN
  * backend", commit messages: the decode update runs over the state pool

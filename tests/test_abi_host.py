@@ -188,3 +188,28 @@ def test_python_wrapper_rejects_cpu_tensors():
         binding.gdn_prefill_varlen(x, x, x, torch.zeros(4, 1), torch.zeros(4, 1), [0, 4])
     with pytest.raises(ValueError):
         binding.gdn_decode_step(x, x, x, torch.zeros(4, 1), torch.zeros(4, 1), torch.zeros(4, 1, 64, 64))
+
+
+def _pooled(lib, prob, q=1, k=2, v=3, g=4, b=5, cu=6, cw=None, cb=None, cpool=None, pool=9, idx=None, hi=None,
+            o=7, ws=8, ws_bytes=1 << 20):
+    f = lambda x: None if x is None else (_fake(x) if isinstance(x, int) else x)
+    return lib.gdn_prefill_varlen_pooled(ctypes.byref(prob), f(q), f(k), f(v), f(g), f(b), f(cu), f(cw), f(cb),
+                                         f(cpool), f(pool), f(idx), f(hi), f(o), f(ws), ctypes.c_size_t(ws_bytes),
+                                         None)
+
+
+def test_pooled_prefill_rejects_bad_arguments(lib):
+    assert _pooled(lib, _prob(h_v=3), cw=10, cpool=11) == -2
+    assert _pooled(lib, _prob(conv_width=0), pool=None) == -1              # the state pool is required
+    assert _pooled(lib, _prob(), cw=10, cpool=None) == -1                   # conv needs its pool
+    assert _pooled(lib, _prob(), cw=None, cpool=11) == -1                   # conv needs its weights
+    assert _pooled(lib, _prob(conv_width=0), cu=None) == -1
+    assert _pooled(lib, _prob(conv_width=0, d_k=96, d_v=96)) == -4
+    assert _pooled(lib, _prob(conv_width=0), ws=None) == -5
+    assert _pooled(lib, _prob(conv_width=0), o=1) == -7                     # o == q
+    assert _pooled(lib, _prob(conv_width=0), o=9) == -7                     # o == state pool
+    assert _pooled(lib, _prob(conv_width=0), ws=9) == -7                    # workspace == state pool
+    assert _pooled(lib, _prob(), cw=10, cpool=9) == -7                      # conv pool == state pool
+    assert _pooled(lib, _prob(conv_width=0), idx=ctypes.c_void_p(0x10000000 + 12 * 0x1000000 + 2)) == -4
+    assert _pooled(lib, _prob(num_seqs=0, total_tokens=0, conv_width=0), q=None, k=None, v=None, g=None, b=None,
+                   cu=None, pool=None, o=None, ws=None, ws_bytes=0) == 0
