@@ -29,7 +29,8 @@ class GdnProblem(ctypes.Structure):
                 ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
                 ("qkv_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("qk_l2norm", ctypes.c_int32),
-                ("l2_eps", ctypes.c_float), ("conv_width", ctypes.c_int32)]
+                ("l2_eps", ctypes.c_float), ("conv_width", ctypes.c_int32),
+                ("beta_logits", ctypes.c_int32)]
 
 
 class GdnError(RuntimeError):
@@ -98,10 +99,10 @@ def _check(t, name, shape, dtype, device):
 
 
 def make_problem(num_seqs, total_tokens, h_k, h_v, d_k, d_v, qkv_dtype, out_dtype, scale=None,
-                 qk_l2norm=True, l2_eps=1e-6, conv_width=4) -> GdnProblem:
+                 qk_l2norm=True, l2_eps=1e-6, conv_width=4, beta_logits=False) -> GdnProblem:
     return GdnProblem(int(num_seqs), int(total_tokens), int(h_k), int(h_v), int(d_k), int(d_v),
                       int(qkv_dtype), int(out_dtype), float(0.0 if scale is None else scale),
-                      int(bool(qk_l2norm)), float(l2_eps), int(conv_width))
+                      int(bool(qk_l2norm)), float(l2_eps), int(conv_width), int(bool(beta_logits)))
 
 
 def gdn_prefill_workspace_bytes(problem: GdnProblem) -> int:
@@ -121,7 +122,7 @@ def gdn_prefill_varlen(q, k, v, g, beta, cu_seqlens=None, *, conv_weight=None, c
                        conv_state=None, initial_state=None, output_final_state=True,
                        output_conv_state=True, use_qk_l2norm=True, scale=None, l2_eps=1e-6,
                        out_dtype=torch.float32, validate=True, out=None, final_state_out=None,
-                       conv_state_out=None, workspace=None, stream=None, events=None):
+                       conv_state_out=None, workspace=None, stream=None, events=None, beta_logits=False):
     """Chunked varlen prefill (C ABI ``gdn_prefill_varlen``).
 
     q, k: ``[T, h_k, d_k]`` (or ``[B, T, h_k, d_k]`` with equal lengths and no
@@ -187,7 +188,8 @@ def gdn_prefill_varlen(q, k, v, g, beta, cu_seqlens=None, *, conv_weight=None, c
     if output_conv_state and conv_width:
         cso = conv_state_out if conv_state_out is not None else torch.empty((N, C, 3), dtype=qdt, device=dev)
         _check(cso, "conv_state_out", (N, C, 3), qdt, dev)
-    prob = make_problem(N, T, h_k, h_v, d_k, d_v, qcode, ocode, scale, use_qk_l2norm, l2_eps, conv_width)
+    prob = make_problem(N, T, h_k, h_v, d_k, d_v, qcode, ocode, scale, use_qk_l2norm, l2_eps, conv_width,
+                        beta_logits)
     ws_bytes = gdn_prefill_workspace_bytes(prob)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
@@ -235,7 +237,7 @@ def _check_indices(state_indices, N, P, Pc, dev, validate):
 def gdn_prefill_varlen_pooled(q, k, v, g, beta, cu_seqlens, state_pool, *, state_indices=None,
                               has_initial_state=None, conv_weight=None, conv_bias=None, conv_state_pool=None,
                               use_qk_l2norm=True, scale=None, l2_eps=1e-6, out_dtype=torch.float32,
-                              validate=True, out=None, workspace=None, stream=None):
+                              validate=True, out=None, workspace=None, stream=None, beta_logits=False):
     """Chunked varlen prefill over pooled states, in place (C ABI
     ``gdn_prefill_varlen_pooled``).
 
@@ -291,7 +293,8 @@ def gdn_prefill_varlen_pooled(q, k, v, g, beta, cu_seqlens, state_pool, *, state
         _check(has_initial_state, "has_initial_state", (N,), torch.int32, dev)
     o = out if out is not None else torch.empty((T, h_v, d_v), dtype=out_dtype, device=dev)
     _check(o, "out", (T, h_v, d_v), out_dtype, dev)
-    prob = make_problem(N, T, h_k, h_v, d_k, d_v, qcode, ocode, scale, use_qk_l2norm, l2_eps, conv_width)
+    prob = make_problem(N, T, h_k, h_v, d_k, d_v, qcode, ocode, scale, use_qk_l2norm, l2_eps, conv_width,
+                        beta_logits)
     ws_bytes = gdn_prefill_workspace_bytes(prob)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
@@ -311,7 +314,7 @@ def gdn_prefill_varlen_pooled(q, k, v, g, beta, cu_seqlens, state_pool, *, state
 
 def gdn_decode_step(q, k, v, g, beta, state_pool, *, state_indices=None, conv_weight=None,
                     conv_bias=None, conv_state_pool=None, use_qk_l2norm=True, scale=None, l2_eps=1e-6,
-                    out_dtype=torch.float32, validate=True, out=None, stream=None):
+                    out_dtype=torch.float32, validate=True, out=None, stream=None, beta_logits=False):
     """One decode step over a state pool, in place (C ABI ``gdn_decode_step``).
 
     q, k: ``[N, h_k, d_k]``; v: ``[N, h_v, d_v]``; g, beta: ``[N, h_v]`` fp32;
@@ -350,7 +353,8 @@ def gdn_decode_step(q, k, v, g, beta, state_pool, *, state_indices=None, conv_we
     _check_indices(state_indices, N, P, conv_state_pool.shape[0] if conv_width else None, dev, validate)
     o = out if out is not None else torch.empty((N, h_v, d_v), dtype=out_dtype, device=dev)
     _check(o, "out", (N, h_v, d_v), out_dtype, dev)
-    prob = make_problem(N, N, h_k, h_v, d_k, d_v, qcode, ocode, scale, use_qk_l2norm, l2_eps, conv_width)
+    prob = make_problem(N, N, h_k, h_v, d_k, d_v, qcode, ocode, scale, use_qk_l2norm, l2_eps, conv_width,
+                        beta_logits)
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
     st = load().gdn_decode_step(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),

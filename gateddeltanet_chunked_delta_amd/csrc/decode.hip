@@ -164,7 +164,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(const DecodeParams p) 
                 hn[m] = __builtin_nontemporal_load(reinterpret_cast<const float4_t*>(H + DK * DV + (rg + RG * m) * DV) + cg);
         }
         const float decay = expf(p.g[int64_t(n) * p.h_v + h]);
-        const float b = p.beta[int64_t(n) * p.h_v + h];
+        const float b = beta_of(p.beta[int64_t(n) * p.h_v + h], p.beta_logits != 0);
         float dlt[4];
 #pragma unroll
         for (int e = 0; e < 4; e++) {

@@ -35,6 +35,7 @@ gdn_status check_problem(const gdn_problem* p) {
     if (p->d_k < 1 || p->d_v < 1) return GDN_ERR_SHAPE;
     if (p->conv_width != 0 && p->conv_width != 4) return GDN_ERR_UNSUPPORTED;
     if (p->qk_l2norm != 0 && p->qk_l2norm != 1) return GDN_ERR_SHAPE;
+    if (p->beta_logits != 0 && p->beta_logits != 1) return GDN_ERR_SHAPE;
     if (!isfinite(p->scale) || !isfinite(p->l2_eps) || p->l2_eps < 0.0f) return GDN_ERR_SHAPE;
     // keep every element offset well inside int64 and grid sizes inside 2^31
     if (p->total_tokens > (int64_t(1) << 31) || p->num_seqs > (1 << 24) || p->h_v > 4096 ||
@@ -80,7 +81,7 @@ gdn_status launch(const gdn_problem* p, const gdn::PrefillLayout& lay, const voi
     prm.scal_img = reinterpret_cast<float*>(ws + lay.scal_img);
     prm.slots = lay.slots;
     prm.num_seqs = p->num_seqs; prm.h_k = p->h_k; prm.h_v = p->h_v; prm.d_v = p->d_v;
-    prm.conv_width = p->conv_width;
+    prm.conv_width = p->conv_width; prm.beta_logits = p->beta_logits;
     prm.qk_l2norm = p->qk_l2norm; prm.l2_eps = eff_eps(p); prm.scale = eff_scale(p);
     return from_hip(gdn::launch_prefill(prm, p->d_k, p->d_v, p->qkv_dtype, p->out_dtype,
                                         static_cast<hipStream_t>(stream), events));
@@ -260,6 +261,7 @@ gdn_status gdn_decode_step(const gdn_problem* p, const void* q, const void* k, c
     prm.conv_state_pool = p->conv_width == 4 ? conv_state_pool : nullptr;
     prm.state_pool = state_pool; prm.state_indices = state_indices; prm.o = o;
     prm.num_seqs = p->num_seqs; prm.h_k = p->h_k; prm.h_v = p->h_v; prm.conv_width = p->conv_width;
+    prm.beta_logits = p->beta_logits;
     prm.qk_l2norm = p->qk_l2norm; prm.l2_eps = eff_eps(p); prm.scale = eff_scale(p);
     return from_hip(gdn::launch_decode(prm, p->d_k, p->d_v, p->qkv_dtype, p->out_dtype,
                                        static_cast<hipStream_t>(stream)));

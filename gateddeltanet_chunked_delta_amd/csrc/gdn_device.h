@@ -91,6 +91,10 @@ __device__ __forceinline__ void lds_barrier() {
 // A[l%16][8*(l/16) + e] and B[8*(l/16) + e][l%16], e = 0..7, and owns
 // D[4*(l/16) + i][l%16], i = 0..3.
 
+// Write strength from a beta input: the value itself, or sigmoid(b) for raw
+// gates (expf is the accurate library exponential; large |b| saturates to 0 or 1).
+__device__ __forceinline__ float beta_of(float b, bool logits) { return logits ? 1.0f / (1.0f + expf(-b)) : b; }
+
 // y * sigmoid(y) with the hardware exp2 and reciprocal (a few ulp); large
 // negative y gives exp = inf and a zero reciprocal, so the result is -0.
 __device__ __forceinline__ float silu(float y) { return y * __builtin_amdgcn_rcpf(1.0f + __expf(-y)); }

@@ -41,6 +41,7 @@ struct PrefillParams {
     int32_t h_k, h_v;
     int32_t d_v;
     int32_t conv_width;         // 0 or 4
+    int32_t beta_logits;        // 1: beta holds raw gates b, use sigmoid(b)
     int32_t qk_l2norm;
     float l2_eps;
     float scale;
@@ -70,6 +71,7 @@ struct DecodeParams {
     int32_t num_seqs;
     int32_t h_k, h_v;
     int32_t conv_width;
+    int32_t beta_logits;        // 1: beta holds raw gates b, use sigmoid(b)
     int32_t qk_l2norm;
     float l2_eps;
     float scale;

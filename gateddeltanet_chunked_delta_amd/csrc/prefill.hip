@@ -433,7 +433,7 @@ __global__ void __launch_bounds__(kPrepThreads, 1) prep_kernel(const PrefillPara
         if (gw == 0 && gi < G) {
             const bool in = lane < U.L;
             const int64_t at = (U.c0 + (in ? lane : 0)) * p.h_v + U.hk * G + gi;
-            const float gv = p.g[at], bv = p.beta[at];
+            const float gv = p.g[at], bv = beta_of(p.beta[at], p.beta_logits != 0);
             gpre = in ? gv : 0.0f;
             bpre = in ? bv : 0.0f;
         }

@@ -107,6 +107,11 @@ def conv_bias(workload_id: int, geom: Geometry, dtype: str) -> np.ndarray:
     return bf16_round(b) if dtype == "bf16" else b
 
 
+def gate_logits(workload_id: int, rows: int, h_v: int) -> np.ndarray:
+    """Raw write-strength gates b [rows, h_v] = 2 N(0, 1) (fp32), key (workload_id, 1002)."""
+    return (2.0 * _rng(workload_id, 1002).standard_normal((rows, h_v))).astype(np.float32)
+
+
 def state_draw(workload_id: int, seq_id: int, geom: Geometry, std: float = 0.02) -> np.ndarray:
     r = _rng(workload_id, seq_id, 7)
     return (std * r.standard_normal((geom.h_v, geom.d_k, geom.d_v))).astype(np.float32)

@@ -84,6 +84,13 @@ typedef struct gdn_problem {
     int32_t qk_l2norm;     /* 1 => L2-normalise q and k per head; 0 => no */
     float l2_eps;          /* eps of the L2 norm; 0 => 1e-6 */
     int32_t conv_width;    /* 0 => no conv prologue (no SiLU); 4 => conv + SiLU */
+    int32_t beta_logits;   /* 0 => beta is the write strength as given; 1 => beta
+                            * holds the raw gate b and the kernels use
+                            * sigmoid(b) = 1 / (1 + e^{-b}) in fp32, the fused
+                            * sigmoid gating of the decode update ("[Feature] Add
+                            * batch invariance support to GDN_ATTN backend",
+                            * PR description, section "Solution": decode goes
+                            * through fused_sigmoid_gating_delta_rule_update) */
 } gdn_problem;
 
 /* Bytes of device workspace gdn_prefill_varlen needs for this problem: the

@@ -106,6 +106,9 @@ def test_prefill_rejects_bad_flag(lib):
     prob = _prob()
     prob.l2_eps = -1.0
     assert _prefill(lib, prob, cw=9) == -2
+    prob = _prob()
+    prob.beta_logits = 2
+    assert _prefill(lib, prob, cw=9) == -2
 
 
 def test_prefill_null_problem(lib):

@@ -12,7 +12,8 @@ import torch
 
 from gateddeltanet_chunked_delta_amd import binding
 from gateddeltanet_chunked_delta_amd.inputs import (Geometry, bf16_round, conv_bias, conv_state_pool, conv_weights,
-                                                    decode_inputs, prefill_inputs, state_pool, uniform_lengths)
+                                                    decode_inputs, gate_logits, prefill_inputs, state_pool,
+                                                    uniform_lengths)
 from tests.gpu_util import TOL, TORCH_DT, dev, gpu_prefill, head_slice, oracle_prefill, rel_err
 
 pytestmark = pytest.mark.gpu
@@ -89,6 +90,33 @@ def test_conv_bias(oracle_mod, dtype, d):
     print(f"  rel err o={eo:.3e} final_state={ef:.3e} (tol {TOL[dtype]:.0e})", flush=True)
     assert eo <= TOL[dtype] and ef <= TOL[dtype]
     assert np.array_equal(cso.float().cpu().numpy(), rcso)
+
+
+def _sigmoid64(b):
+    return 1.0 / (1.0 + np.exp(-b.astype(np.float64)))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_beta_logits_prefill(oracle_mod, dtype):
+    """beta_logits = 1: the beta input holds raw gates b (2 N(0, 1), some
+    saturating) and the kernels use sigmoid(b); the oracle gets sigmoid(b)."""
+    geom = Geometry(2, 4, 128, 128)
+    x = prefill_inputs(26, [70, 130, 3], geom, dtype, initial_state_std=0.02, conv_state=True)
+    b = gate_logits(26, x.total_tokens, geom.h_v)
+    b[0, 0], b[1, 1] = 60.0, -60.0
+    x.beta = b
+    dt = TORCH_DT[dtype]
+    o, fs, _ = binding.gdn_prefill_varlen(
+        dev(x.q, dt), dev(x.k, dt), dev(x.v, dt), dev(x.g), dev(b), torch.from_numpy(x.cu_seqlens.astype(np.int32)),
+        conv_weight=dev(x.conv_w, dt), conv_state=dev(x.conv_state_in, dt), initial_state=dev(x.initial_state),
+        beta_logits=True)
+    torch.cuda.synchronize()
+    dims = oracle_mod.Dims(2, 4, 128, 128, conv_width=4)
+    ro, rfs, _ = oracle_mod.prefill(dims, x.cu_seqlens, x.q, x.k, x.v, x.g, _sigmoid64(b), x.conv_w, None,
+                                    x.conv_state_in, x.initial_state)
+    eo, ef = rel_err(o.cpu().numpy(), ro), rel_err(fs.cpu().numpy(), rfs)
+    print(f"  rel err o={eo:.3e} final_state={ef:.3e}", flush=True)
+    assert eo <= TOL[dtype] and ef <= TOL[dtype]
 
 
 def test_custom_scale(oracle_mod):
@@ -326,6 +354,23 @@ def test_decode_conv_bias(oracle_mod, dtype):
         assert rel_err(o.cpu().numpy(), ro) <= TOL[dtype]
     assert rel_err(pool.cpu().numpy(), ref_pool) <= TOL[dtype]
     assert np.array_equal(cpool.float().cpu().numpy(), ref_cpool.astype(np.float32))
+
+
+def test_decode_beta_logits(oracle_mod):
+    """Decode with raw gates b in the beta input (beta_logits = 1)."""
+    geom = Geometry(2, 4, 128, 128)
+    P = 3
+    pool_np = state_pool(52, P, geom)
+    pool = dev(pool_np)
+    ref_pool = pool_np.astype(np.float64)
+    dims = oracle_mod.Dims(2, 4, 128, 128, conv_width=0)
+    x = decode_inputs(52, 0, P, geom, "bf16")
+    b = gate_logits(52, P, geom.h_v)
+    o = binding.gdn_decode_step(dev(x.q, torch.bfloat16), dev(x.k, torch.bfloat16), dev(x.v, torch.bfloat16),
+                                dev(x.g), dev(b), pool, beta_logits=True)
+    ro = oracle_mod.decode(dims, x.q, x.k, x.v, x.g, _sigmoid64(b), ref_pool, np.arange(P, dtype=np.int64))
+    assert rel_err(o.cpu().numpy(), ro) <= TOL["bf16"]
+    assert rel_err(pool.cpu().numpy(), ref_pool) <= TOL["bf16"]
 
 
 @pytest.mark.parametrize("h_k,h_v,d_k,d_v", [(3, 3, 64, 64), (2, 6, 128, 64), (1, 4, 64, 128)])
