@@ -388,8 +388,6 @@ __global__ void __launch_bounds__(kPrepThreads, 1) prep_kernel(const PrefillPara
     float* KK = reinterpret_cast<float*>(smem + S::oKK);
     float* QK = reinterpret_cast<float*>(smem + S::oQK);
     float* red = KK;
-    float* rq = reinterpret_cast<float*>(smem + S::oScal) + 2 * kChunk;
-    float* rk = rq + kChunk;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
@@ -496,28 +494,23 @@ __global__ void __launch_bounds__(kPrepThreads, 1) prep_kernel(const PrefillPara
             load_unit(N);
         }
         lds_barrier();
-        // per-row 1/|q| and 1/|k| (fixed summation order)
-        if (tid < 2 * kChunk) {
-            const int r = tid & (kChunk - 1), which = tid / kChunk;
-            const float* rr = red + r * NG + which * NGQ;
-            float sum = 0.0f;
-#pragma unroll
-            for (int q = 0; q < NGQ; q++) sum += rr[q];
-            (which ? rk : rq)[r] = p.qk_l2norm ? 1.0f / sqrtf(sum + p.l2_eps) : 1.0f;
-        }
-        lds_barrier();
-        // normalised rows as split pairs, into LDS and the K|Q image
+        // normalised rows as split pairs, into LDS and the K|Q image; each
+        // thread sums its row's partial sums of squares itself (a fixed order,
+        // so every thread of a row gets the same 1/|q| or 1/|k|)
         {
             // K image first, then Q
             E* img = static_cast<E*>(p.kq_img) + (int64_t(cs) * p.h_k + hk) * Img<DK>::kKQ +
                             (pwhich ? 0 : 2 * kChunk * DK);
             E* dhi = pwhich ? Khi : Qhi;
             E* dlo = pwhich ? Klo : Qlo;
-            const float* rn = pwhich ? rk : rq;
 #pragma unroll
             for (int i = 0; i < RPB; i++) {
                 const int row = prow0 + i;
-                const float sc = rn[row];
+                const float* rr = red + row * NG + pwhich * NGQ;
+                float sum = 0.0f;
+#pragma unroll
+                for (int q = 0; q < NGQ; q++) sum += rr[q];
+                const float sc = p.qk_l2norm ? 1.0f / sqrtf(sum + p.l2_eps) : 1.0f;
                 typedef E E2 __attribute__((ext_vector_type(2)));
                 E2 h16[VEC / 2], l16[VEC / 2];
 #pragma unroll
@@ -539,8 +532,39 @@ __global__ void __launch_bounds__(kPrepThreads, 1) prep_kernel(const PrefillPara
         }
         lds_barrier();
 
+        // Decays of value head gi (the group's first wave): gam = running sum of
+        // g, and the per-token scalars.  gam reaches about -50 over a chunk; in
+        // fp32 its rounding (~4e-6 absolute) would become a relative error of
+        // every decay factor, which the inter- and intra-chunk terms amplify.
+        // Scan in fp64.
+        double* gam = reinterpret_cast<double*>(smem + S::oGam) + grp * kChunk;
+        float* bet = reinterpret_cast<float*>(smem + S::oScal) + grp * kChunk;
+        auto decays = [&](int gi) {
+            const int64_t ih = int64_t(cs) * p.h_v + hk * G + gi;
+            const float gv = gpre, bv = bpre;
+            load_gb(U, gi + 2);
+            double x = gv;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const double t = __shfl_up(x, o);
+                if (lane >= o) x += t;
+            }
+            const double gl = __shfl(x, 63);
+            gam[lane] = x;
+            bet[lane] = bv;
+            const float ex = exp_of_f64(x);
+            float* sc = p.scal_img + ih * Img<DK>::kScal;
+            sc[lane] = bv;
+            sc[kChunk + lane] = ex;
+            sc[2 * kChunk + lane] = exp_of_f64(gl - x);
+            const float exl = __shfl(ex, 63);
+            sc[3 * kChunk + lane] = lane == 0 ? exl : 0.0f;
+        };
+
         // ---- Gram tiles K K^T (waves 0-3) and Q K^T (waves 4-7), lower tiles
-        //      only, raw fp32; wave w takes tile-row w % 4. ----
+        //      only, raw fp32; wave w takes tile-row w % 4.  The waves of
+        //      tile-row 0 (one tile each) also scan the decays of their group's
+        //      first value head. ----
         {
             const int which = wave >> 2, tr = wave & 3;
             const E* Ahi = which ? Qhi : Khi;
@@ -557,6 +581,7 @@ __global__ void __launch_bounds__(kPrepThreads, 1) prep_kernel(const PrefillPara
                 float4_t acc[1];
                 gram_row<0, KS, PK>(Ahi, Alo, Khi, Klo, lr, lg, acc);
                 store_row(acc, 1);
+                if (grp < G) decays(grp);
             } else if (tr == 1) {
                 float4_t acc[2];
                 gram_row<1, KS, PK>(Ahi, Alo, Khi, Klo, lr, lg, acc);
@@ -579,37 +604,16 @@ __global__ void __launch_bounds__(kPrepThreads, 1) prep_kernel(const PrefillPara
         float* Af = reinterpret_cast<float*>(smem + (grp ? S::oA1 : S::oA0));
         float* Tf = reinterpret_cast<float*>(smem + (grp ? S::oT1 : S::oT0));
         float* Td = reinterpret_cast<float*>(smem + S::oTd) + grp * 4 * 16 * PD;
-        double* gam = reinterpret_cast<double*>(smem + S::oGam) + grp * kChunk;
-        float* bet = reinterpret_cast<float*>(smem + S::oScal) + grp * kChunk;
         for (int g0 = 0; g0 < G; g0 += 2) {
             const int gi = g0 + grp;
             const bool act = gi < G;  // both groups run every barrier
             const int h = hk * G + gi;
             const int64_t ih = int64_t(cs) * p.h_v + h;
-            // gam reaches about -50 over a chunk; in fp32 its rounding (~4e-6
-            // absolute) would become a relative error of every decay factor, which
-            // the inter- and intra-chunk terms amplify.  Scan in fp64.
-            if (act && gw == 0) {
-                const float gv = gpre, bv = bpre;
-                load_gb(U, gi + 2);
-                double x = gv;
-#pragma unroll
-                for (int o = 1; o < 64; o <<= 1) {
-                    const double t = __shfl_up(x, o);
-                    if (lane >= o) x += t;
-                }
-                const double gl = __shfl(x, 63);
-                gam[lane] = x;
-                bet[lane] = bv;
-                const float ex = exp_of_f64(x);
-                float* sc = p.scal_img + ih * Img<DK>::kScal;
-                sc[lane] = bv;
-                sc[kChunk + lane] = ex;
-                sc[2 * kChunk + lane] = exp_of_f64(gl - x);
-                const float exl = __shfl(ex, 63);
-                sc[3 * kChunk + lane] = lane == 0 ? exl : 0.0f;
+            // (the first pair's decays were scanned during the Gram tiles)
+            if (g0 > 0) {
+                if (act && gw == 0) decays(gi);
+                lds_barrier();
             }
-            lds_barrier();
             // A (fp32, LDS) and P (split, image): 8 consecutive columns per item
             if (act) {
                 E* pimg = static_cast<E*>(p.tp_img) + ih * Img<DK>::kTP + 2 * TriPack::kPieces * 8;
@@ -657,13 +661,17 @@ __global__ void __launch_bounds__(kPrepThreads, 1) prep_kernel(const PrefillPara
             // substitution, one column per lane (the group's first wave)
             if (act && gw == 0) {
                 const int b = lane >> 4, c = lane & 15;
-                float x[16];
+                // column-oriented: once x[r] is known it is added into every later
+                // row's sum, so the steps of one column are independent (each row
+                // still sums s = 0, 1, ..., r - 1 in order)
+                float x[16], acc[16];
+#pragma unroll
+                for (int r = 0; r < 16; r++) acc[r] = 0.0f;
 #pragma unroll
                 for (int r = 0; r < 16; r++) {
-                    float acc = 0.0f;
+                    x[r] = (r < c) ? 0.0f : ((r == c) ? 1.0f : -acc[r]);
 #pragma unroll
-                    for (int sidx = 0; sidx < r; sidx++) acc += Af[(16 * b + r) * PF + 16 * b + sidx] * x[sidx];
-                    x[r] = (r < c) ? 0.0f : ((r == c) ? 1.0f : -acc);
+                    for (int s2 = r + 1; s2 < 16; s2++) acc[s2] += Af[(16 * b + s2) * PF + 16 * b + r] * x[r];
                 }
 #pragma unroll
                 for (int r = 0; r < 16; r++) Td[(16 * b + r) * PD + c] = x[r];
