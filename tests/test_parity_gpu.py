@@ -119,6 +119,19 @@ def test_beta_logits_prefill(oracle_mod, dtype):
     assert eo <= TOL[dtype] and ef <= TOL[dtype]
 
 
+def test_bf16_inputs_beyond_fp16_range(oracle_mod):
+    """bf16 inputs use split-bf16 products, which keep fp32's range: v and the
+    initial states scaled by 2^22 (state entries far above fp16's 65504) still
+    meet the bar."""
+    geom = Geometry(2, 4, 128, 128)
+    x = prefill_inputs(27, [150, 40], geom, "bf16", initial_state_std=0.02)
+    x.v *= 2.0 ** 22           # exact in bf16
+    x.initial_state *= 2.0 ** 22
+    o, fs = _check_prefill(oracle_mod, x)
+    print(f"  max|final state| = {np.max(np.abs(fs)):.3e}, max|o| = {np.max(np.abs(o)):.3e}", flush=True)
+    assert np.max(np.abs(fs)) > 65504.0
+
+
 def test_custom_scale(oracle_mod):
     x = prefill_inputs(23, [70], Geometry(2, 2, 128, 128), "bf16")
     _check_prefill(oracle_mod, x, scale=0.5)
