@@ -11,7 +11,8 @@ so the roofline entry is for the dominant kernel, the cross-chunk carry, and
 the chunk-local kernel is reported beside it.  The decode half of the metric
 (256 slots x 32 value heads, d = 128, conv update, 512 MiB fp32 state pool
 updated in place, 100 consecutive steps over 4 pools in rotation) is timed
-separately and reported under "decode".  One JSON line is printed.
+separately and reported under "decode", and the multi-token (speculative)
+decode of 4 tokens per slot under "decode_multi".  One JSON line is printed.
 """
 from __future__ import annotations
 
@@ -73,6 +74,16 @@ def decode_algorithmic(N, h_k, h_v, d, in_bytes=2, out_bytes=4, conv=True):
     return bytes_, flops
 
 
+def decode_multi_algorithmic(N, m, h_k, h_v, d, kept, in_bytes=2, out_bytes=4):
+    """m tokens per slot: the state read once and written `kept` times (once
+    per kept token state), per-token q/k/v/g/beta read and o written, the
+    conv history read once and written `kept` times, conv weights read."""
+    state = N * h_v * d * d * 4
+    C = 2 * h_k * d + h_v * d
+    return (state * (1 + kept) + N * m * (C * in_bytes + h_v * 2 * 4 + h_v * d * out_bytes)
+            + N * C * 3 * in_bytes * (1 + kept) + C * 4 * in_bytes)
+
+
 def measured_traffic(kernel):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
     None when the kernel's sources changed since the counters were taken."""
@@ -131,7 +142,7 @@ def main():
     import torch
     import gateddeltanet_chunked_delta_amd as gdn
     from gateddeltanet_chunked_delta_amd.inputs import (Geometry, conv_state_pool, conv_weights, decode_inputs,
-                                                        prefill_inputs, state_pool)
+                                                        multi_decode_inputs, prefill_inputs, state_pool)
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -263,6 +274,54 @@ def main():
                                          "kernel": DECODE_KERNEL,
                                          "algorithmic_bytes": dbytes}}
         print(f"[bench] decode: {us:.1f} us/step, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
+        del pools, cpools, dins
+
+        # Multi-token (speculative) decode: m = 4 tokens per slot in one call,
+        # (a) keeping the state after every token in its own pool entry (2 GiB
+        # pool of 4 entries per slot, for rollback), (b) only the final state,
+        # in place.  Two pool sets in rotation (4 GiB of state traffic apart).
+        m, NSET = 4, 2
+        mins = []
+        for c in range(8):
+            d = multi_decode_inputs(3, c, N, m, geom, "bf16")
+            mins.append(tuple(torch.from_numpy(a).to(dev, dt) for a, dt in
+                              ((d.q, bf), (d.k, bf), (d.v, bf), (d.g, torch.float32), (d.beta, torch.float32))))
+        om = torch.empty((N, m, 32, 128), dtype=torch.float32, device=dev)
+        start = torch.from_numpy(state_pool(3, N, geom)).to(dev)
+        cstart = torch.from_numpy(conv_state_pool(3, N, geom, "bf16")).to(dev, bf)
+        idx = torch.arange(N * m, dtype=torch.int32, device=dev).reshape(N, m)
+        mres = {"workload": f"{m} tokens per slot, 256 slots x 32 value heads (16 key heads), d=128, bf16 "
+                            "q/k/v, conv4+SiLU+L2, fp32 state", "tokens_per_slot": m}
+        for kept, name in ((m, "all_token_states_kept"), (1, "final_state_in_place")):
+            P = N * m if kept == m else N
+            mpools = [torch.zeros((P, 32, 128, 128), dtype=torch.float32, device=dev) for _ in range(NSET)]
+            mcpools = [torch.zeros((P, geom.channels, 3), dtype=bf, device=dev) for _ in range(NSET)]
+            for mp, mc in zip(mpools, mcpools):
+                mp[idx[:, 0].long() if kept == m else slice(None)] = start
+                mc[idx[:, 0].long() if kept == m else slice(None)] = cstart
+
+            def mstep(c):
+                gdn.gdn_decode_multi(*mins[c % len(mins)], mpools[c % NSET], out=om, conv_weight=cw,
+                                     conv_state_pool=mcpools[c % NSET], state_indices=idx if kept == m else None,
+                                     validate=False)
+
+            for c in range(8):
+                mstep(c)
+            torch.cuda.synchronize()
+            calls = 40
+            e0.record(stream)
+            for c in range(calls):
+                mstep(c)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / calls
+            mb = decode_multi_algorithmic(N, m, 16, 32, 128, kept)
+            mres[name] = {"us_per_call": us, "tokens_per_s": N * m / (us * 1e-6), "algorithmic_bytes": mb,
+                          "GB/s": mb / (us * 1e-6) / 1e9, "frac": mb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+            print(f"[bench] decode x{m} ({name}): {us:.1f} us/call, {mb / (us * 1e-6) / 1e9:.0f} GB/s",
+                  file=sys.stderr, flush=True)
+            del mpools, mcpools
+        result["decode_multi"] = mres
 
     if args.copy_calibration:
         nbytes = 1 << 30

@@ -19,7 +19,7 @@ GDN_F32, GDN_BF16 = 0, 1
 _STATUS = {0: "GDN_OK", -1: "GDN_ERR_NULL", -2: "GDN_ERR_SHAPE", -3: "GDN_ERR_DTYPE",
            -4: "GDN_ERR_UNSUPPORTED", -5: "GDN_ERR_WORKSPACE", -6: "GDN_ERR_HIP", -7: "GDN_ERR_ALIAS"}
 EXPORTED = ("gdn_prefill_workspace_bytes", "gdn_prefill_varlen", "gdn_prefill_varlen_timed",
-            "gdn_prefill_varlen_pooled", "gdn_decode_step", "gdn_status_string")
+            "gdn_prefill_varlen_pooled", "gdn_decode_step", "gdn_decode_multi", "gdn_status_string")
 
 
 class GdnProblem(ctypes.Structure):
@@ -61,6 +61,8 @@ def load() -> ctypes.CDLL:
         lib.gdn_prefill_varlen_pooled.restype = ctypes.c_int
         lib.gdn_decode_step.argtypes = [ctypes.POINTER(GdnProblem)] + [vp] * 11 + [vp]
         lib.gdn_decode_step.restype = ctypes.c_int
+        lib.gdn_decode_multi.argtypes = [ctypes.POINTER(GdnProblem), ctypes.c_int32] + [vp] * 13
+        lib.gdn_decode_multi.restype = ctypes.c_int
         lib.gdn_status_string.argtypes = [ctypes.c_int]
         lib.gdn_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -362,4 +364,86 @@ def gdn_decode_step(q, k, v, g, beta, state_pool, *, state_indices=None, conv_we
                                 _ptr(state_indices), _ptr(o), ctypes.c_void_p(stream))
     if st != 0:
         raise GdnError(st, "gdn_decode_step")
+    return o
+
+
+def gdn_decode_multi(q, k, v, g, beta, state_pool, *, state_indices=None, num_accepted=None,
+                     conv_weight=None, conv_bias=None, conv_state_pool=None, use_qk_l2norm=True, scale=None,
+                     l2_eps=1e-6, out_dtype=torch.float32, validate=True, out=None, stream=None,
+                     beta_logits=False):
+    """m tokens per slot in one call (C ABI ``gdn_decode_multi``).
+
+    q, k: ``[N, m, h_k, d_k]``; v: ``[N, m, h_v, d_v]``; g, beta: ``[N, m, h_v]``
+    fp32; state_pool: fp32 ``[P, h_v, d_k, d_v]``; state_indices: int32
+    ``[N, m]`` or None; num_accepted: int32 ``[N]`` (1..m) or None.  Slot n
+    reads entry ``state_indices[n, num_accepted[n] - 1]`` and writes the state
+    (and conv history) after token j to ``state_indices[n, j]`` (-1: not
+    written); without indices entry n is read and receives the state after the
+    last token.  Returns o ``[N, m, h_v, d_v]``.
+    """
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [N, m, H, D]")
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on the GPU")
+    N, m, h_k, d_k = q.shape
+    h_v, d_v = v.shape[2], v.shape[3]
+    qdt = q.dtype
+    qcode = _dtype_code(qdt, "q")
+    ocode = _dtype_code(out_dtype, "out_dtype")
+    _check(q, "q", (N, m, h_k, d_k), qdt, dev)
+    _check(k, "k", (N, m, h_k, d_k), qdt, dev)
+    _check(v, "v", (N, m, h_v, d_v), qdt, dev)
+    _check(g, "g", (N, m, h_v), torch.float32, dev)
+    _check(beta, "beta", (N, m, h_v), torch.float32, dev)
+    if state_pool.dim() != 4:
+        raise ValueError("state_pool must be [P, h_v, d_k, d_v]")
+    P = state_pool.shape[0]
+    _check(state_pool, "state_pool", (P, h_v, d_k, d_v), torch.float32, dev)
+    C = 2 * h_k * d_k + h_v * d_v
+    conv_width = 4 if conv_weight is not None else 0
+    Pc = None
+    if conv_weight is not None:
+        _check(conv_weight, "conv_weight", (C, 4), qdt, dev)
+        _check(conv_bias, "conv_bias", (C,), qdt, dev)
+        if conv_state_pool is None:
+            raise ValueError("conv_weight needs conv_state_pool")
+        if conv_state_pool.dim() != 3:
+            raise ValueError("conv_state_pool must be [P, C, 3]")
+        Pc = conv_state_pool.shape[0]
+        _check(conv_state_pool, "conv_state_pool", (Pc, C, 3), qdt, dev)
+    if state_indices is None:
+        if validate and (N > P or (Pc is not None and N > Pc)):
+            raise ValueError("without state_indices the pools need at least N entries")
+    else:
+        _check(state_indices, "state_indices", (N, m), torch.int32, dev)
+        if validate and N:
+            idx = state_indices.cpu()
+            used = idx[idx >= 0]
+            if bool((idx < -1).any()) or bool((used >= P).any()) or (Pc is not None and bool((used >= Pc).any())):
+                raise ValueError("state_indices out of range")
+            # entries may repeat inside a slot's row, never across slots
+            for n in range(N):
+                mine = set(idx[n][idx[n] >= 0].tolist())
+                others = idx[torch.arange(N) != n]
+                if mine and bool(torch.isin(others, torch.tensor(sorted(mine), dtype=torch.int32)).any()):
+                    raise ValueError("state_indices of different slots must be distinct")
+    if num_accepted is not None:
+        _check(num_accepted, "num_accepted", (N,), torch.int32, dev)
+        if validate and N:
+            acc = num_accepted.cpu()
+            if bool((acc < 1).any()) or bool((acc > m).any()):
+                raise ValueError("num_accepted must lie in 1..m")
+    o = out if out is not None else torch.empty((N, m, h_v, d_v), dtype=out_dtype, device=dev)
+    _check(o, "out", (N, m, h_v, d_v), out_dtype, dev)
+    prob = make_problem(N, N * m, h_k, h_v, d_k, d_v, qcode, ocode, scale, use_qk_l2norm, l2_eps, conv_width,
+                        beta_logits)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    st = load().gdn_decode_multi(ctypes.byref(prob), ctypes.c_int32(m), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                 _ptr(beta), _ptr(conv_weight), _ptr(conv_bias), _ptr(conv_state_pool),
+                                 _ptr(state_pool), _ptr(state_indices), _ptr(num_accepted), _ptr(o),
+                                 ctypes.c_void_p(stream))
+    if st != 0:
+        raise GdnError(st, "gdn_decode_multi")
     return o

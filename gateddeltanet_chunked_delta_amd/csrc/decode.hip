@@ -1,21 +1,30 @@
-// Single-token decode step of the gated delta rule on gfx950.
+// Decode of the gated delta rule on gfx950: m >= 1 new tokens for each of N
+// slots of a pooled state, in order.
 //
 // One workgroup per (slot, key head) handles the value heads that share that
 // key head.  For each of them it streams the fp32 state tile H = S^T
-// (d_k x d_v, d_v contiguous) from HBM once and writes it back once:
-//   p = H^T k,  s = H^T q            (one pass over H, 16-byte loads)
+// (d_k x d_v, d_v contiguous) from HBM once, applies the m tokens with the
+// tile in registers, and writes it back after every token that has an entry
+// to go to:
+//   p = H^T k,  s = H^T q            (one pass over H)
 //   delta = beta (v - e^g p)
 //   o = scale (e^g s + delta (k . q))   = scale S_t q  without a second pass
 //   H <- e^g H + k delta^T
 // ("[Feature] Add batch invariance support to GDN_ATTN backend", commit
 // messages: the decode update runs in place over the state pool addressed by
-// state indices; the rule itself is "Qwen3.5-27B GPTQ Garbage Inference --
-// Root Cause Analysis", section "Why abliteration failed on Qwen3.5", item 3.)
-// The conv history of every q|k|v channel is read and shifted by the one
-// thread that owns the channel, so the pooled conv state is updated in the
-// same launch without a race.  Reductions over d_k run in a fixed order
-// inside the workgroup, so each slot is computed identically whatever the
-// batch.
+// state indices, with separate spec and non-spec decode paths; the rule
+// itself is "Qwen3.5-27B GPTQ Garbage Inference -- Root Cause Analysis",
+// section "Why abliteration failed on Qwen3.5", item 3.)
+// With m > 1 (speculative tokens) the state after token j goes to pool entry
+// idx[n][j], so a caller that accepts only the first a tokens continues from
+// entry idx[n][a - 1]; the next call reads its state from
+// idx[n][accepted[n] - 1].  The conv history is handled the same way.
+// Every q|k|v channel's conv history is read and shifted by the one thread
+// that owns the channel, so the pooled conv state is updated in the same
+// launch without a race.  Reductions over d_k run in a fixed order inside the
+// workgroup, the same for every token, so each slot is computed identically
+// whatever the batch, and m tokens in one call give bit for bit the results
+// of m single-token calls.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -29,6 +38,10 @@ namespace {
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 
+// Every multiply-add below is an explicit fmaf (or an explicit separate
+// product), so the rounding does not depend on which products the compiler
+// would contract: both kernel variants compute each token identically.
+
 // Fixed-pattern butterfly sum over a full wave.
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
@@ -36,40 +49,75 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
-// conv(4) + SiLU of one channel's newest input x with its 3-input history,
-// then the history shifted in place to hold the newest 3 inputs.
-template <typename TIn>
-__device__ __forceinline__ float conv_step(const TIn* cw, const TIn* cb, TIn* hist, int64_t ch, TIn xraw) {
-    const TIn h0 = hist[0], h1 = hist[1], h2 = hist[2];
-    float y = cb ? Elem<TIn>::get(cb + ch) : 0.0f;
-    y += Elem<TIn>::get(cw + ch * 4 + 0) * Elem<TIn>::get(&h0);
-    y += Elem<TIn>::get(cw + ch * 4 + 1) * Elem<TIn>::get(&h1);
-    y += Elem<TIn>::get(cw + ch * 4 + 2) * Elem<TIn>::get(&h2);
-    y += Elem<TIn>::get(cw + ch * 4 + 3) * Elem<TIn>::get(&xraw);
-    hist[0] = h1;
-    hist[1] = h2;
-    hist[2] = xraw;
-    return silu(y);
+// One channel's conv(4) + SiLU over the m <= KMAX new inputs of a slot, in
+// order.  The 3-input history is read from entry `rslot` of the conv pool;
+// the history after token j (the newest 3 raw inputs) is written to entry
+// wslot(j) when that is >= 0.  The history is held in registers, so any
+// entry may be both read and written.  out[j * stride] receives token j.
+// (Loading all m inputs ahead of the stores measured slower: the register
+// array costs the m-token kernel its second resident workgroup per CU.)
+template <typename TIn, typename WSlot>
+__device__ __forceinline__ void conv_tokens(const TIn* cw, const TIn* cb, TIn* cs, int64_t C, int64_t ch,
+                                            int rslot, WSlot wslot, const TIn* x, int64_t xstride, int m,
+                                            float* out, int stride) {
+    const TIn* hist = cs + (int64_t(rslot) * C + ch) * 3;
+    TIn h0 = hist[0], h1 = hist[1], h2 = hist[2];
+    const float w0 = Elem<TIn>::get(cw + ch * 4 + 0), w1 = Elem<TIn>::get(cw + ch * 4 + 1);
+    const float w2 = Elem<TIn>::get(cw + ch * 4 + 2), w3 = Elem<TIn>::get(cw + ch * 4 + 3);
+    const float b = cb ? Elem<TIn>::get(cb + ch) : 0.0f;
+    for (int j = 0; j < m; j++) {
+        const TIn xj = x[j * xstride];
+        float y = b;
+        y = fmaf(w0, Elem<TIn>::get(&h0), y);
+        y = fmaf(w1, Elem<TIn>::get(&h1), y);
+        y = fmaf(w2, Elem<TIn>::get(&h2), y);
+        y = fmaf(w3, Elem<TIn>::get(&xj), y);
+        h0 = h1;
+        h1 = h2;
+        h2 = xj;
+        out[j * stride] = silu(y);
+        const int ws = wslot(j);
+        if (ws >= 0) {
+            TIn* dst = cs + (int64_t(ws) * C + ch) * 3;
+            dst[0] = h0;
+            dst[1] = h1;
+            dst[2] = h2;
+        }
+    }
 }
 
-template <int DK, int DV, typename TIn, typename TOut>
+// KMAX: most tokens per slot the shared buffers hold (1 for the single-token
+// step, so that its LDS footprint stays minimal).
+template <int DK, int DV, int KMAX, typename TIn, typename TOut>
 __global__ void __launch_bounds__(kThreads) decode_kernel(const DecodeParams p) {
     constexpr int CG = DV / 4;           // float4 column groups per row
     constexpr int RG = kThreads / CG;    // row groups
     constexpr int RPT = DK / RG;         // rows per thread
     static_assert(kThreads % CG == 0 && DK % RG == 0 && 64 % CG == 0, "decode tiling");
-    static_assert(2 * DK <= kThreads && DV <= kThreads, "one channel per thread");
+    static_assert(2 * DK <= kThreads - KMAX && DV <= kThreads - KMAX, "one channel per thread, gate threads apart");
 
-    __shared__ float qs[DK], ks[DK], vs[DV];
-    __shared__ float part[kWaves][2][DV];
-    __shared__ float scal[4];  // |q|^2, |k|^2, raw k.q
+    __shared__ float qs[KMAX][DK], ks[KMAX][DK], vs[KMAX][DV];
+    // per-wave partial sums, double-buffered over tokens so that one barrier
+    // per token suffices
+    __shared__ float part[KMAX == 1 ? 1 : 2][kWaves][2][DV];
+    __shared__ float scal[KMAX][4];  // |q|^2, |k|^2, raw k.q per token
+    __shared__ float gate[KMAX][2];  // e^g and beta of the current head per token
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = blockIdx.x / p.h_k, hk = blockIdx.x % p.h_k;
-    const int slot = p.state_indices ? p.state_indices[n] : n;
+    const int m = KMAX == 1 ? 1 : p.tokens;  // the single-token kernel unrolls fully
+    // Pool entries: read from idx[n][accepted - 1], the state after token j
+    // written to idx[n][j]; without indices entry n is read and receives the
+    // state after the last token.
+    const int32_t* irow = p.state_indices ? p.state_indices + int64_t(n) * m : nullptr;
+    int acc = p.num_accepted ? p.num_accepted[n] : 1;
+    acc = acc < 1 ? 1 : (acc > m ? m : acc);
+    const int slot = irow ? irow[acc - 1] : n;
     if (slot < 0) return;
+    auto wslot = [&](int j) { return irow ? irow[j] : (j == m - 1 ? n : -1); };
     const int G = p.h_v / p.h_k;
     const int64_t nq = int64_t(p.h_k) * DK, nv = int64_t(p.h_v) * DV, C = 2 * nq + nv;
+    const int64_t row0 = int64_t(n) * m;  // first token row of this slot
     const TIn* cw = static_cast<const TIn*>(p.conv_w);
     const TIn* cb = static_cast<const TIn*>(p.conv_b);
     TIn* cs = static_cast<TIn*>(p.conv_state_pool);
@@ -79,126 +127,159 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(const DecodeParams p) 
     float* const H0 = p.state_pool + (int64_t(slot) * p.h_v + int64_t(hk) * G) * DK * DV;
     // The state loads are the bulk of the traffic: the first head's are issued
     // before anything else, each following head's as soon as the current
-    // head's reductions are done, ahead of its stores.  Over 4 rotating
+    // head's first reductions are done, ahead of its stores.  Over 4 rotating
     // 512 MiB pools (no cache keeps a pool between its steps) this measured
     // 185 us per step, against 190 loading each head only after the previous
-    // one, and 204 with ordinary instead of nontemporal accesses.
+    // one, and 204 with ordinary instead of nontemporal accesses.  The
+    // m-token kernel loads each head's tile when it starts the head instead:
+    // a second tile in registers would leave room for one workgroup per CU,
+    // and its phases are long enough for two resident workgroups to overlap
+    // one's loads with the other's arithmetic.
+    constexpr bool kPrefetch = KMAX == 1;
     float4_t hv[RPT], hn[RPT];
+    auto load_tile = [&](float4_t (&t)[RPT], const float* H) {
 #pragma unroll
-    for (int m = 0; m < RPT; m++)
-        hn[m] = __builtin_nontemporal_load(reinterpret_cast<const float4_t*>(H0 + (rg + RG * m) * DV) + cg);
+        for (int mm = 0; mm < RPT; mm++)
+            t[mm] = __builtin_nontemporal_load(reinterpret_cast<const float4_t*>(H + (rg + RG * mm) * DV) + cg);
+    };
+    if (kPrefetch) load_tile(hn, H0);
 
-    float rq = 1.0f, rk = 1.0f, kq = 0.0f;
     for (int gi = 0; gi < G; gi++) {
         const int h = hk * G + gi;
-        float* H = H0 + int64_t(gi) * DK * DV;
+        if (kPrefetch) {
 #pragma unroll
-        for (int m = 0; m < RPT; m++) hv[m] = hn[m];
+            for (int mm = 0; mm < RPT; mm++) hv[mm] = hn[mm];
+        } else {
+            load_tile(hv, H0 + int64_t(gi) * DK * DV);
+        }
 
-        // ---- inputs: optional conv(4) + SiLU, one channel per thread ----
+        // ---- inputs of all m tokens: optional conv(4) + SiLU, one channel per thread ----
         if (gi == 0 && tid < 2 * DK) {
             const bool isk = tid >= DK;
             const int c = isk ? tid - DK : tid;
-            const TIn* src = static_cast<const TIn*>(isk ? p.k : p.q) + int64_t(n) * nq + int64_t(hk) * DK + c;
-            const int64_t ch = (isk ? nq : 0) + int64_t(hk) * DK + c;
-            const float a = conv ? conv_step(cw, cb, cs + (int64_t(slot) * C + ch) * 3, ch, *src) : Elem<TIn>::get(src);
-            (isk ? ks : qs)[c] = a;
+            const TIn* src = static_cast<const TIn*>(isk ? p.k : p.q) + row0 * nq + int64_t(hk) * DK + c;
+            float* dst = isk ? &ks[0][c] : &qs[0][c];
+            if (conv) {
+                const int64_t ch = (isk ? nq : 0) + int64_t(hk) * DK + c;
+                conv_tokens<TIn>(cw, cb, cs, C, ch, slot, wslot, src, nq, m, dst, DK);
+            } else {
+                for (int j = 0; j < m; j++) dst[j * DK] = Elem<TIn>::get(src + j * nq);
+            }
+        }
+        // the gates of this head, off the per-token critical path
+        if (tid >= kThreads - KMAX && tid - (kThreads - KMAX) < m) {
+            const int64_t tok = row0 + (tid - (kThreads - KMAX));
+            gate[tid - (kThreads - KMAX)][0] = expf(p.g[tok * p.h_v + h]);
+            gate[tid - (kThreads - KMAX)][1] = beta_of(p.beta[tok * p.h_v + h], p.beta_logits != 0);
         }
         if (tid < DV) {
-            const TIn* src = static_cast<const TIn*>(p.v) + int64_t(n) * nv + int64_t(h) * DV + tid;
-            const int64_t ch = 2 * nq + int64_t(h) * DV + tid;
-            vs[tid] = conv ? conv_step(cw, cb, cs + (int64_t(slot) * C + ch) * 3, ch, *src) : Elem<TIn>::get(src);
+            const TIn* src = static_cast<const TIn*>(p.v) + row0 * nv + int64_t(h) * DV + tid;
+            if (conv) {
+                const int64_t ch = 2 * nq + int64_t(h) * DV + tid;
+                conv_tokens<TIn>(cw, cb, cs, C, ch, slot, wslot, src, nv, m, &vs[0][tid], DV);
+            } else {
+                for (int j = 0; j < m; j++) vs[j][tid] = Elem<TIn>::get(src + j * nv);
+            }
         }
         __syncthreads();
-        // ---- norms and k.q (waves 0, 1, 2; fixed order), once per key head ----
+        // ---- norms and k.q of every token (one wave per quantity; fixed order), once per key head ----
         if (gi == 0) {
-            if (wave < 3) {
-                float acc = 0.0f;
+            for (int it = wave; it < 3 * m; it += kWaves) {
+                const int j = it / 3, w = it % 3;
+                float a = 0.0f;
 #pragma unroll
-                for (int m = 0; m < DK / 64; m++) {
-                    const int i = lane + 64 * m;
-                    acc += wave == 0 ? qs[i] * qs[i] : (wave == 1 ? ks[i] * ks[i] : ks[i] * qs[i]);
+                for (int mm = 0; mm < DK / 64; mm++) {
+                    const int i = lane + 64 * mm;
+                    const float x = w == 1 ? ks[j][i] : qs[j][i], y = w == 0 ? qs[j][i] : ks[j][i];
+                    a = fmaf(x, y, a);
                 }
-                acc = wave_sum(acc);
-                if (lane == 0) scal[wave] = acc;
+                a = wave_sum(a);
+                if (lane == 0) scal[j][w] = a;
             }
             __syncthreads();
-            rq = p.qk_l2norm ? 1.0f / sqrtf(scal[0] + p.l2_eps) : 1.0f;
-            rk = p.qk_l2norm ? 1.0f / sqrtf(scal[1] + p.l2_eps) : 1.0f;
-            kq = scal[2] * rq * rk;
         }
 
-        // ---- p = H^T k, s = H^T q over this thread's rows ----
-        float pk[4] = {0.0f, 0.0f, 0.0f, 0.0f}, pq[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int j = 0; j < m; j++) {
+            const float rq = p.qk_l2norm ? 1.0f / sqrtf(scal[j][0] + p.l2_eps) : 1.0f;
+            const float rk = p.qk_l2norm ? 1.0f / sqrtf(scal[j][1] + p.l2_eps) : 1.0f;
+            const float kq = scal[j][2] * rq * rk;
+            // ---- p = H^T k, s = H^T q over this thread's rows ----
+            float pk[4] = {0.0f, 0.0f, 0.0f, 0.0f}, pq[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int m = 0; m < RPT; m++) {
-            const int i = rg + RG * m;
-            const float kk = ks[i] * rk, qq = qs[i] * rq;
-            const float h4[4] = {hv[m][0], hv[m][1], hv[m][2], hv[m][3]};
+            for (int mm = 0; mm < RPT; mm++) {
+                const int i = rg + RG * mm;
+                const float kk = ks[j][i] * rk, qq = qs[j][i] * rq;
+                const float h4[4] = {hv[mm][0], hv[mm][1], hv[mm][2], hv[mm][3]};
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    pk[e] = fmaf(h4[e], kk, pk[e]);
+                    pq[e] = fmaf(h4[e], qq, pq[e]);
+                }
+            }
+            // row groups inside a wave: lanes that differ in the bits above CG
+#pragma unroll
+            for (int o = CG; o < 64; o <<= 1) {
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    pk[e] += __shfl_xor(pk[e], o);
+                    pq[e] += __shfl_xor(pq[e], o);
+                }
+            }
+            float(*pt)[2][DV] = part[KMAX == 1 ? 0 : (j & 1)];
+            if (lane < CG) {
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    pt[wave][0][4 * cg + e] = pk[e];
+                    pt[wave][1][4 * cg + e] = pq[e];
+                }
+            }
+            __syncthreads();
+            if (kPrefetch && gi + 1 < G) load_tile(hn, H0 + int64_t(gi + 1) * DK * DV);
+            const int64_t tok = row0 + j;
+            const float decay = gate[j][0], b = gate[j][1];
+            float dlt[4];
 #pragma unroll
             for (int e = 0; e < 4; e++) {
-                pk[e] += h4[e] * kk;
-                pq[e] += h4[e] * qq;
+                const int c = 4 * cg + e;
+                float sk = 0.0f, sq = 0.0f;
+#pragma unroll
+                for (int w = 0; w < kWaves; w++) {
+                    sk += pt[w][0][c];
+                    sq += pt[w][1][c];
+                }
+                dlt[e] = b * fmaf(-decay, sk, vs[j][c]);
+                if (rg == 0) {
+                    TOut* op = static_cast<TOut*>(p.o) + (tok * p.h_v + h) * DV + c;
+                    Elem<TOut>::put(op, p.scale * fmaf(decay, sq, dlt[e] * kq));
+                }
             }
-        }
-        // row groups inside a wave: lanes that differ in the bits above CG
+            // ---- H <- e^g H + k delta^T, written to the token's entry ----
+            const int ws = wslot(j);
+            float* Hw = p.state_pool + (int64_t(ws) * p.h_v + h) * DK * DV;
 #pragma unroll
-        for (int o = CG; o < 64; o <<= 1) {
+            for (int mm = 0; mm < RPT; mm++) {
+                const int i = rg + RG * mm;
+                const float kk = ks[j][i] * rk;
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-                pk[e] += __shfl_xor(pk[e], o);
-                pq[e] += __shfl_xor(pq[e], o);
+                for (int e = 0; e < 4; e++) hv[mm][e] = fmaf(kk, dlt[e], decay * hv[mm][e]);
+                if (ws >= 0) __builtin_nontemporal_store(hv[mm], reinterpret_cast<float4_t*>(Hw + i * DV) + cg);
             }
+            // A wave writes token j + 2's partial sums into this token's
+            // buffer only after every wave has passed token j + 1's barrier,
+            // i.e. has finished reading this one; vs, qs and ks are rewritten
+            // by the next head.
+            if (j == m - 1) __syncthreads();
         }
-        if (lane < CG) {
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                part[wave][0][4 * cg + e] = pk[e];
-                part[wave][1][4 * cg + e] = pq[e];
-            }
-        }
-        __syncthreads();
-        if (gi + 1 < G) {
-#pragma unroll
-            for (int m = 0; m < RPT; m++)
-                hn[m] = __builtin_nontemporal_load(reinterpret_cast<const float4_t*>(H + DK * DV + (rg + RG * m) * DV) + cg);
-        }
-        const float decay = expf(p.g[int64_t(n) * p.h_v + h]);
-        const float b = beta_of(p.beta[int64_t(n) * p.h_v + h], p.beta_logits != 0);
-        float dlt[4];
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-            const int j = 4 * cg + e;
-            float sk = 0.0f, sq = 0.0f;
-#pragma unroll
-            for (int w = 0; w < kWaves; w++) {
-                sk += part[w][0][j];
-                sq += part[w][1][j];
-            }
-            dlt[e] = b * (vs[j] - decay * sk);
-            if (rg == 0) {
-                TOut* op = static_cast<TOut*>(p.o) + (int64_t(n) * p.h_v + h) * DV + j;
-                Elem<TOut>::put(op, p.scale * (decay * sq + dlt[e] * kq));
-            }
-        }
-        // ---- H <- e^g H + k delta^T, written back in place ----
-#pragma unroll
-        for (int m = 0; m < RPT; m++) {
-            const int i = rg + RG * m;
-            const float kk = ks[i] * rk;
-            float4_t nh;
-#pragma unroll
-            for (int e = 0; e < 4; e++) nh[e] = decay * hv[m][e] + kk * dlt[e];
-            __builtin_nontemporal_store(nh, reinterpret_cast<float4_t*>(H + i * DV) + cg);
-        }
-        // vs and part are rewritten by the next value head
-        __syncthreads();
     }
 }
 
 template <int DK, int DV, typename TIn, typename TOut>
 hipError_t run(const DecodeParams& p, hipStream_t stream) {
-    decode_kernel<DK, DV, TIn, TOut><<<dim3(unsigned(int64_t(p.num_seqs) * p.h_k)), dim3(kThreads), 0, stream>>>(p);
+    const dim3 grid(unsigned(int64_t(p.num_seqs) * p.h_k)), block(kThreads);
+    if (p.tokens == 1)
+        decode_kernel<DK, DV, 1, TIn, TOut><<<grid, block, 0, stream>>>(p);
+    else
+        decode_kernel<DK, DV, kDecodeMaxTokens, TIn, TOut><<<grid, block, 0, stream>>>(p);
     return hipGetLastError();
 }
 
@@ -221,6 +302,7 @@ int decode_supported(int d_k, int d_v, int qkv_dtype, int out_dtype) {
 hipError_t launch_decode(const DecodeParams& p, int d_k, int d_v, int qkv_dtype, int out_dtype,
                          hipStream_t stream) {
     if (p.num_seqs <= 0) return hipSuccess;
+    if (p.tokens < 1 || p.tokens > kDecodeMaxTokens) return hipErrorInvalidValue;
     if (qkv_dtype == 1)
         return out_dtype == 1 ? run_dims<bf16_t, bf16_t>(p, d_k, d_v, stream) : run_dims<bf16_t, float>(p, d_k, d_v, stream);
     return out_dtype == 1 ? run_dims<float, bf16_t>(p, d_k, d_v, stream) : run_dims<float, float>(p, d_k, d_v, stream);

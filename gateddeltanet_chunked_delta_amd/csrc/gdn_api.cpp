@@ -49,6 +49,52 @@ float eff_eps(const gdn_problem* p) { return p->l2_eps != 0.0f ? p->l2_eps : 1e-
 
 gdn_status from_hip(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_HIP; }
 
+// Decode of m tokens per slot; gdn_decode_step is m = 1.
+gdn_status decode(const gdn_problem* p, int32_t m, const void* q, const void* k, const void* v, const float* g,
+                  const float* beta, const void* conv_w, const void* conv_b, void* conv_state_pool,
+                  float* state_pool, const int32_t* state_indices, const int32_t* num_accepted, void* o,
+                  void* stream) {
+    gdn_status st = check_problem(p);
+    if (st != GDN_OK) return st;
+    const int64_t N = p->num_seqs;
+    if (m < 1 || m > gdn::kDecodeMaxTokens) return m < 1 ? GDN_ERR_SHAPE : GDN_ERR_UNSUPPORTED;
+    if (p->total_tokens != N * m) return GDN_ERR_SHAPE;
+    if (N > 0 && (!q || !k || !v || !g || !beta || !o || !state_pool)) return GDN_ERR_NULL;
+    if (p->conv_width == 4 && (!conv_w || !conv_state_pool)) return GDN_ERR_NULL;
+    if (!gdn::decode_supported(p->d_k, p->d_v, p->qkv_dtype, p->out_dtype)) return GDN_ERR_UNSUPPORTED;
+    if (N == 0) return GDN_OK;
+    const int64_t T = N * m;
+    const int64_t eb = elem_bytes(p->qkv_dtype), ob = elem_bytes(p->out_dtype);
+    const int64_t nq = int64_t(p->h_k) * p->d_k, nv = int64_t(p->h_v) * p->d_v, C = 2 * nq + nv;
+    if (!aligned(state_pool, 16) || !aligned(g, 4) || !aligned(beta, 4) || !aligned(o, size_t(ob)) ||
+        !aligned(q, size_t(eb)) || !aligned(k, size_t(eb)) || !aligned(v, size_t(eb)) ||
+        (state_indices && !aligned(state_indices, 4)) || (num_accepted && !aligned(num_accepted, 4)))
+        return GDN_ERR_UNSUPPORTED;
+    // The pool sizes are not known here; check o against the per-step inputs.
+    const Range ro = range_of(o, T * nv * ob);
+    const Range in[] = {range_of(q, T * nq * eb), range_of(k, T * nq * eb), range_of(v, T * nv * eb),
+                        range_of(g, T * p->h_v * 4), range_of(beta, T * p->h_v * 4),
+                        range_of(conv_w, p->conv_width == 4 ? C * 4 * eb : 0),
+                        range_of(conv_b, p->conv_width == 4 ? C * eb : 0),
+                        range_of(state_indices, T * 4), range_of(num_accepted, N * 4)};
+    for (const Range& r : in)
+        if (overlaps(ro, r)) return GDN_ERR_ALIAS;
+    if (reinterpret_cast<uintptr_t>(o) == reinterpret_cast<uintptr_t>(state_pool) ||
+        (conv_state_pool && reinterpret_cast<uintptr_t>(o) == reinterpret_cast<uintptr_t>(conv_state_pool)))
+        return GDN_ERR_ALIAS;
+
+    gdn::DecodeParams prm;
+    prm.q = q; prm.k = k; prm.v = v; prm.g = g; prm.beta = beta; prm.conv_w = conv_w; prm.conv_b = conv_b;
+    prm.conv_state_pool = p->conv_width == 4 ? conv_state_pool : nullptr;
+    prm.state_pool = state_pool; prm.state_indices = state_indices; prm.num_accepted = num_accepted; prm.o = o;
+    prm.tokens = m;
+    prm.num_seqs = p->num_seqs; prm.h_k = p->h_k; prm.h_v = p->h_v; prm.conv_width = p->conv_width;
+    prm.beta_logits = p->beta_logits;
+    prm.qk_l2norm = p->qk_l2norm; prm.l2_eps = eff_eps(p); prm.scale = eff_scale(p);
+    return from_hip(gdn::launch_decode(prm, p->d_k, p->d_v, p->qkv_dtype, p->out_dtype,
+                                       static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -229,42 +275,16 @@ gdn_status gdn_decode_step(const gdn_problem* p, const void* q, const void* k, c
                            const float* g, const float* beta, const void* conv_w, const void* conv_b,
                            void* conv_state_pool, float* state_pool, const int32_t* state_indices, void* o,
                            void* stream) {
-    gdn_status st = check_problem(p);
-    if (st != GDN_OK) return st;
-    const int64_t N = p->num_seqs;
-    if (p->total_tokens != N) return GDN_ERR_SHAPE;
-    if (N > 0 && (!q || !k || !v || !g || !beta || !o || !state_pool)) return GDN_ERR_NULL;
-    if (p->conv_width == 4 && (!conv_w || !conv_state_pool)) return GDN_ERR_NULL;
-    if (!gdn::decode_supported(p->d_k, p->d_v, p->qkv_dtype, p->out_dtype)) return GDN_ERR_UNSUPPORTED;
-    if (N == 0) return GDN_OK;
-    const int64_t eb = elem_bytes(p->qkv_dtype), ob = elem_bytes(p->out_dtype);
-    const int64_t nq = int64_t(p->h_k) * p->d_k, nv = int64_t(p->h_v) * p->d_v, C = 2 * nq + nv;
-    if (!aligned(state_pool, 16) || !aligned(g, 4) || !aligned(beta, 4) || !aligned(o, size_t(ob)) ||
-        !aligned(q, size_t(eb)) || !aligned(k, size_t(eb)) || !aligned(v, size_t(eb)) ||
-        (state_indices && !aligned(state_indices, 4)))
-        return GDN_ERR_UNSUPPORTED;
-    // The pool sizes are not known here; check o against the per-step inputs.
-    const Range ro = range_of(o, N * nv * ob);
-    const Range in[] = {range_of(q, N * nq * eb), range_of(k, N * nq * eb), range_of(v, N * nv * eb),
-                        range_of(g, N * p->h_v * 4), range_of(beta, N * p->h_v * 4),
-                        range_of(conv_w, p->conv_width == 4 ? C * 4 * eb : 0),
-                        range_of(conv_b, p->conv_width == 4 ? C * eb : 0),
-                        range_of(state_indices, N * 4)};
-    for (const Range& r : in)
-        if (overlaps(ro, r)) return GDN_ERR_ALIAS;
-    if (reinterpret_cast<uintptr_t>(o) == reinterpret_cast<uintptr_t>(state_pool) ||
-        (conv_state_pool && reinterpret_cast<uintptr_t>(o) == reinterpret_cast<uintptr_t>(conv_state_pool)))
-        return GDN_ERR_ALIAS;
+    return decode(p, 1, q, k, v, g, beta, conv_w, conv_b, conv_state_pool, state_pool, state_indices, nullptr, o,
+                  stream);
+}
 
-    gdn::DecodeParams prm;
-    prm.q = q; prm.k = k; prm.v = v; prm.g = g; prm.beta = beta; prm.conv_w = conv_w; prm.conv_b = conv_b;
-    prm.conv_state_pool = p->conv_width == 4 ? conv_state_pool : nullptr;
-    prm.state_pool = state_pool; prm.state_indices = state_indices; prm.o = o;
-    prm.num_seqs = p->num_seqs; prm.h_k = p->h_k; prm.h_v = p->h_v; prm.conv_width = p->conv_width;
-    prm.beta_logits = p->beta_logits;
-    prm.qk_l2norm = p->qk_l2norm; prm.l2_eps = eff_eps(p); prm.scale = eff_scale(p);
-    return from_hip(gdn::launch_decode(prm, p->d_k, p->d_v, p->qkv_dtype, p->out_dtype,
-                                       static_cast<hipStream_t>(stream)));
+gdn_status gdn_decode_multi(const gdn_problem* p, int32_t tokens_per_slot, const void* q, const void* k,
+                            const void* v, const float* g, const float* beta, const void* conv_w,
+                            const void* conv_b, void* conv_state_pool, float* state_pool,
+                            const int32_t* state_indices, const int32_t* num_accepted, void* o, void* stream) {
+    return decode(p, tokens_per_slot, q, k, v, g, beta, conv_w, conv_b, conv_state_pool, state_pool, state_indices,
+                  num_accepted, o, stream);
 }
 
 const char* gdn_status_string(gdn_status s) {

@@ -56,18 +56,23 @@ struct PrefillLayout {
 PrefillLayout prefill_layout(int64_t num_seqs, int64_t total_tokens, int64_t h_k, int64_t h_v, int64_t d_k,
                              int64_t d_v);
 
+// Most tokens per slot one decode call takes.
+constexpr int kDecodeMaxTokens = 8;
+
 struct DecodeParams {
-    const void* q;              // [N][h_k][d_k]
-    const void* k;              // [N][h_k][d_k]
-    const void* v;              // [N][h_v][d_v]
-    const float* g;             // [N][h_v]
-    const float* beta;          // [N][h_v]
+    const void* q;              // [N * m][h_k][d_k], slot-major (row n * m + j = token j of slot n)
+    const void* k;              // [N * m][h_k][d_k]
+    const void* v;              // [N * m][h_v][d_v]
+    const float* g;             // [N * m][h_v]
+    const float* beta;          // [N * m][h_v]
     const void* conv_w;         // [C][4] or null
     const void* conv_b;         // [C] or null
     void* conv_state_pool;      // [P][C][3] or null
     float* state_pool;          // [P][h_v][d_k][d_v]
-    const int32_t* state_indices; // [N] or null
-    void* o;                    // [N][h_v][d_v]
+    const int32_t* state_indices; // [N][m] or null: read idx[n][accepted - 1], token j's state to idx[n][j]
+    const int32_t* num_accepted;  // [N] in 1..m or null (all 1)
+    void* o;                    // [N * m][h_v][d_v]
+    int32_t tokens;             // m, tokens per slot: 1 .. kDecodeMaxTokens
     int32_t num_seqs;
     int32_t h_k, h_v;
     int32_t conv_width;

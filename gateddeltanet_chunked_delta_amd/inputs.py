@@ -223,6 +223,15 @@ def decode_inputs(workload_id: int, step: int, n: int, geom: Geometry, dtype: st
                         _sigmoid(b_raw).astype(np.float32))
 
 
+def multi_decode_inputs(workload_id: int, call: int, n: int, m: int, geom: Geometry, dtype: str) -> DecodeInputs:
+    """m tokens per slot for n slots (arrays [n, m, ...]); token j of call c is
+    drawn like decode step 64 c + j, so a slot's tokens are the same whatever
+    m-token calls they are issued in."""
+    steps = [decode_inputs(workload_id, 64 * call + j, n, geom, dtype) for j in range(m)]
+    stack = lambda f: np.ascontiguousarray(np.stack([getattr(s, f) for s in steps], axis=1))
+    return DecodeInputs(geom, dtype, stack("q"), stack("k"), stack("v"), stack("g"), stack("beta"))
+
+
 def state_pool(workload_id: int, pool: int, geom: Geometry, std: float = 0.02) -> np.ndarray:
     """fp32 state pool [pool, h_v, d_k, d_v] ~ std * N(0, 1)."""
     r = _rng(workload_id, 2_000_000)

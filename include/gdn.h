@@ -238,6 +238,47 @@ gdn_status gdn_decode_step(const gdn_problem* p,
                            float* state_pool, const int32_t* state_indices,
                            void* o, void* stream);
 
+/*
+ * Multi-token (speculative) decode: m = tokens_per_slot new tokens for each of
+ * N slots, applied in order in one call ("[Feature] Add batch invariance
+ * support to GDN_ATTN backend", commit messages: decode runs as separate spec
+ * and non-spec paths over the state pool addressed by state indices).  The
+ * state after every token can be kept, so a caller that accepts only the
+ * first a tokens of a slot resumes from the state after token a - 1.
+ *
+ *  q, k             [N * m][h_k][d_k]  qkv_dtype  slot-major: row n * m + j
+ *                                                 is token j of slot n
+ *  v                [N * m][h_v][d_v]  qkv_dtype
+ *  g, beta          [N * m][h_v]       fp32
+ *  conv_w, conv_b, conv_state_pool     as in gdn_decode_step
+ *  state_pool       [P][h_v][d_k][d_v] fp32      read-modify-write
+ *  state_indices    [N][m] int32, or NULL.  With indices, slot n reads its
+ *                   recurrent state and conv history from entry
+ *                   idx[n][a_n - 1] (a_n = num_accepted[n]) and writes the
+ *                   state and conv history after token j to entry idx[n][j]
+ *                   (not written when idx[n][j] = -1; the read entry may be
+ *                   one of them).  idx[n][a_n - 1] = -1 skips the slot: its o
+ *                   rows and every pool entry stay untouched.  NULL: slot n
+ *                   reads entry n and writes the state after its last token
+ *                   back to entry n.
+ *  num_accepted     [N] int32 in 1..m, or NULL (all 1): the tokens of the
+ *                   previous call the caller accepted; values outside 1..m
+ *                   are clamped into it.
+ *  o                [N * m][h_v][d_v]  out_dtype
+ *
+ * p->num_seqs = N and p->total_tokens = N * m.  tokens_per_slot: 1..8
+ * (GDN_ERR_SHAPE below 1, GDN_ERR_UNSUPPORTED above 8).  Entries must be in
+ * range, and distinct across slots (except -1).  Token j's results are bit
+ * for bit those of j + 1 single-token gdn_decode_step calls; with m = 1 the
+ * call is gdn_decode_step.  Other arguments and errors as in gdn_decode_step.
+ */
+gdn_status gdn_decode_multi(const gdn_problem* p, int32_t tokens_per_slot,
+                            const void* q, const void* k, const void* v,
+                            const float* g, const float* beta,
+                            const void* conv_w, const void* conv_b, void* conv_state_pool,
+                            float* state_pool, const int32_t* state_indices,
+                            const int32_t* num_accepted, void* o, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* gdn_status_string(gdn_status s);
 

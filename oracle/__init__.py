@@ -165,3 +165,51 @@ def decode(dims: Dims, q_raw, k_raw, v_raw, g, beta, state_pool, state_indices=N
                           _p(_f64(conv_w)), _p(_f64(conv_b)), _p(conv_state_pool),
                           _p(state_pool), _p(idx), _p(o), ctypes.c_int(nthreads))
     return o
+
+
+def decode_multi(dims: Dims, q_raw, k_raw, v_raw, g, beta, state_pool, state_indices=None,
+                 num_accepted=None, conv_w=None, conv_b=None, conv_state_pool=None, nthreads=0):
+    """m decode tokens per slot, in order (multi-token / speculative decode).
+
+    The definition is m single-token decode steps per slot ("[Feature] Add
+    batch invariance support to GDN_ATTN backend", commit messages: separate
+    spec and non-spec decode over the state pool), with the pool bookkeeping
+    of the library's m-token call: slot n starts from entry
+    ``state_indices[n, num_accepted[n] - 1]`` (entry n without indices) and
+    the state and conv history after token j are copied to entry
+    ``state_indices[n, j]`` when it is >= 0 (entry n after the last token
+    without indices); a start entry of -1 skips the slot.
+    q_raw, k_raw ``[N, m, h_k, d_k]``; v_raw ``[N, m, h_v, d_v]``; g, beta
+    ``[N, m, h_v]``.  Pools (float64) are updated IN PLACE.  Returns o
+    ``[N, m, h_v, d_v]`` (rows of skipped slots are 0)."""
+    q_raw, k_raw, v_raw, g, beta = map(_f64, (q_raw, k_raw, v_raw, g, beta))
+    N, m = q_raw.shape[0], q_raw.shape[1]
+    conv = dims.conv_width > 0
+    acc = np.ones(N, dtype=np.int64) if num_accepted is None else np.asarray(num_accepted, dtype=np.int64)
+    if state_indices is None:
+        start = np.arange(N)
+        dest = np.full((N, m), -1, dtype=np.int64)
+        dest[:, m - 1] = np.arange(N)
+    else:
+        idx = np.asarray(state_indices, dtype=np.int64).reshape(N, m)
+        start = idx[np.arange(N), acc - 1]
+        dest = idx
+    # the running state of every slot, gathered from its start entry
+    live = start >= 0
+    work = np.zeros((N,) + state_pool.shape[1:])
+    work[live] = state_pool[start[live]]
+    cwork = None
+    if conv:
+        cwork = np.zeros((N,) + conv_state_pool.shape[1:])
+        cwork[live] = conv_state_pool[start[live]]
+    sel = np.where(live, np.arange(N), -1)
+    o = np.zeros((N, m, dims.h_v, dims.d_v))
+    for j in range(m):
+        o[:, j] = decode(dims, q_raw[:, j], k_raw[:, j], v_raw[:, j], g[:, j], beta[:, j], work, sel,
+                         conv_w, conv_b, cwork, nthreads=nthreads)
+        for n in range(N):
+            if live[n] and dest[n, j] >= 0:
+                state_pool[dest[n, j]] = work[n]
+                if conv:
+                    conv_state_pool[dest[n, j]] = cwork[n]
+    return o

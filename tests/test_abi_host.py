@@ -184,6 +184,27 @@ def test_decode_rejects_bad_arguments(lib):
                    b=None, pool=None, o=None) == 0
 
 
+def _multi(lib, prob, m, q=1, k=2, v=3, g=4, b=5, cw=None, cb=None, cs=None, pool=6, idx=None, acc=None, o=7):
+    f = lambda x: None if x is None else (_fake(x) if isinstance(x, int) else x)
+    return lib.gdn_decode_multi(ctypes.byref(prob), ctypes.c_int32(m), f(q), f(k), f(v), f(g), f(b), f(cw), f(cb),
+                                f(cs), f(pool), f(idx), f(acc), f(o), None)
+
+
+def test_decode_multi_rejects_bad_arguments(lib):
+    ok = dict(num_seqs=4, total_tokens=12, conv_width=0)
+    assert _multi(lib, _prob(**ok), 0) == -2                                 # m < 1
+    assert _multi(lib, _prob(num_seqs=4, total_tokens=36, conv_width=0), 9) == -4  # m above 8
+    assert _multi(lib, _prob(num_seqs=4, total_tokens=11, conv_width=0), 3) == -2  # total_tokens != N m
+    assert _multi(lib, _prob(**ok), 3, pool=None) == -1
+    assert _multi(lib, _prob(num_seqs=4, total_tokens=12), 3, cw=9, cs=None) == -1
+    assert _multi(lib, _prob(**ok), 3, o=1) == -7                            # o == q
+    assert _multi(lib, _prob(**ok), 3, o=6) == -7                            # o == state pool
+    assert _multi(lib, _prob(**ok), 3, o=10, acc=10) == -7                   # o over num_accepted
+    assert _multi(lib, _prob(**ok), 3, acc=ctypes.c_void_p(0x10000000 + 12 * 0x1000000 + 2)) == -4
+    assert _multi(lib, _prob(num_seqs=0, total_tokens=0, conv_width=0), 3, q=None, k=None, v=None, g=None,
+                  b=None, pool=None, o=None) == 0
+
+
 def test_python_wrapper_rejects_cpu_tensors():
     import torch
     x = torch.zeros(4, 1, 64)

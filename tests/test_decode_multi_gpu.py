@@ -1,0 +1,129 @@
+"""Multi-token (speculative) decode through the C ABI (gdn_decode_multi):
+parity with the fp64 oracle, the pool bookkeeping for rollback
+(num_accepted), and bit-identity with single-token decode steps."""
+import numpy as np
+import pytest
+import torch
+
+from gateddeltanet_chunked_delta_amd import binding
+from gateddeltanet_chunked_delta_amd.inputs import (Geometry, conv_state_pool, conv_weights, multi_decode_inputs,
+                                                    state_pool)
+from tests.gpu_util import TOL, TORCH_DT, dev, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+def _multi(x, dt, pool, **kw):
+    return binding.gdn_decode_multi(dev(x.q, dt), dev(x.k, dt), dev(x.v, dt), dev(x.g), dev(x.beta), pool, **kw)
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 128), ("bf16", 64), ("f32", 64)])
+def test_decode_multi_vs_oracle_with_rollback(oracle_mod, dtype, d):
+    """Two 4-token calls over a pool with per-token entries: the second call
+    resumes each slot from the entry of its last accepted token.  Covers a
+    skipped slot, -1 (unkept) entries, an entry written twice in one call and
+    a slot whose read entry is also written."""
+    geom = Geometry(2, 4, d, d)
+    N, m, P = 5, 4, 24
+    dt = TORCH_DT[dtype]
+    pool_np = state_pool(60, P, geom)
+    cpool_np = conv_state_pool(60, P, geom, dtype)
+    w_np = conv_weights(60, geom, dtype)
+    idx = np.array([[0, 1, 2, 3], [4, 5, -1, 7], [-1, -1, -1, -1], [12, 13, 14, 12], [16, 17, 18, 19]],
+                   dtype=np.int32)
+    pool, cpool = dev(pool_np), dev(cpool_np, dt)
+    ref_pool, ref_cpool = pool_np.astype(np.float64), cpool_np.astype(np.float64)
+    dims = oracle_mod.Dims(2, 4, d, d, conv_width=4)
+    for call, acc in enumerate(([1, 2, 1, 1, 3], [3, 2, 1, 4, 1])):
+        x = multi_decode_inputs(60, call, N, m, geom, dtype)
+        acc_np = np.array(acc, dtype=np.int32)
+        o = _multi(x, dt, pool, state_indices=dev(idx, torch.int32), num_accepted=dev(acc_np, torch.int32),
+                   conv_weight=dev(w_np, dt), conv_state_pool=cpool)
+        ro = oracle_mod.decode_multi(dims, x.q, x.k, x.v, x.g, x.beta, ref_pool, idx, acc_np, w_np, None,
+                                     ref_cpool)
+        live = np.array([r[a - 1] >= 0 for r, a in zip(idx, acc)])
+        e = rel_err(o.cpu().numpy()[live], ro[live])
+        print(f"  call {call}: rel err o={e:.3e}", flush=True)
+        assert e <= TOL[dtype]
+    used = sorted({int(e) for e in idx.ravel() if e >= 0})
+    got = pool.cpu().numpy()
+    assert rel_err(got[used], ref_pool[used]) <= TOL[dtype]
+    assert np.array_equal(cpool.float().cpu().numpy(), ref_cpool.astype(np.float32))
+    untouched = [e for e in range(P) if e not in used]
+    assert np.array_equal(got[untouched], pool_np[untouched])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("beta_logits", [False, True])
+def test_decode_multi_bitwise_equals_single_steps(dtype, beta_logits):
+    """m tokens in one call == m single-token gdn_decode_step calls, bit for
+    bit (outputs, recurrent states and conv states)."""
+    geom = Geometry(2, 4, 128, 128)
+    N, m = 6, 5
+    dt = TORCH_DT[dtype]
+    pool_a = dev(state_pool(61, N, geom))
+    pool_b = pool_a.clone()
+    cpool_a = dev(conv_state_pool(61, N, geom, dtype), dt)
+    cpool_b = cpool_a.clone()
+    w = dev(conv_weights(61, geom, dtype), dt)
+    x = multi_decode_inputs(61, 0, N, m, geom, dtype)
+    o_multi = _multi(x, dt, pool_a, conv_weight=w, conv_state_pool=cpool_a, beta_logits=beta_logits)
+    for j in range(m):
+        o_j = binding.gdn_decode_step(dev(x.q[:, j], dt), dev(x.k[:, j], dt), dev(x.v[:, j], dt), dev(x.g[:, j]),
+                                      dev(x.beta[:, j]), pool_b, conv_weight=w, conv_state_pool=cpool_b,
+                                      beta_logits=beta_logits)
+        assert torch.equal(o_multi[:, j], o_j), j
+    assert torch.equal(pool_a, pool_b)
+    assert torch.equal(cpool_a, cpool_b)
+
+
+def test_decode_multi_one_token_is_decode_step():
+    geom = Geometry(2, 4, 128, 128)
+    N = 7
+    pool_a = dev(state_pool(62, N, geom))
+    pool_b = pool_a.clone()
+    x = multi_decode_inputs(62, 0, N, 1, geom, "bf16")
+    idx = torch.tensor([[6], [5], [4], [-1], [2], [1], [0]], dtype=torch.int32, device="cuda")
+    o_multi = _multi(x, torch.bfloat16, pool_a, state_indices=idx)
+    o_step = binding.gdn_decode_step(dev(x.q[:, 0], torch.bfloat16), dev(x.k[:, 0], torch.bfloat16),
+                                     dev(x.v[:, 0], torch.bfloat16), dev(x.g[:, 0]), dev(x.beta[:, 0]), pool_b,
+                                     state_indices=idx[:, 0].contiguous())
+    live = idx[:, 0] >= 0
+    assert torch.equal(o_multi[live, 0], o_step[live])
+    assert torch.equal(pool_a, pool_b)
+
+
+def test_decode_multi_256_slots_sampled(oracle_mod):
+    """256 slots x 32 value heads (16 key heads), d = 128, bf16 inputs, 4
+    speculative tokens per slot with every token's state kept (a 2 GiB pool of
+    1024 entries), conv on; sampled slots vs the oracle."""
+    geom = Geometry(16, 32, 128, 128)
+    N, m = 256, 4
+    P = N * m
+    start = state_pool(63, N, geom)
+    pool = torch.zeros((P, 32, 128, 128), dtype=torch.float32, device="cuda")
+    idx = np.arange(P, dtype=np.int32).reshape(N, m)
+    pool[idx[:, 0].astype(np.int64)] = dev(start)
+    cstart = conv_state_pool(63, N, geom, "bf16")
+    cpool = torch.zeros((P, geom.channels, 3), dtype=torch.bfloat16, device="cuda")
+    cpool[idx[:, 0].astype(np.int64)] = dev(cstart, torch.bfloat16)
+    w_np = conv_weights(63, geom, "bf16")
+    x = multi_decode_inputs(63, 0, N, m, geom, "bf16")
+    o = _multi(x, torch.bfloat16, pool, state_indices=dev(idx, torch.int32), conv_weight=dev(w_np, torch.bfloat16),
+               conv_state_pool=cpool)
+    torch.cuda.synchronize()
+    sample = [0, 77, 255]
+    dims = oracle_mod.Dims(16, 32, 128, 128, conv_width=4)
+    ref_pool = np.zeros((len(sample) * m, 32, 128, 128))
+    ref_cpool = np.zeros((len(sample) * m, geom.channels, 3))
+    sidx = np.arange(len(sample) * m).reshape(len(sample), m)
+    ref_pool[sidx[:, 0]] = start[sample]
+    ref_cpool[sidx[:, 0]] = cstart[sample]
+    ro = oracle_mod.decode_multi(dims, x.q[sample], x.k[sample], x.v[sample], x.g[sample], x.beta[sample], ref_pool,
+                                 sidx, None, w_np, None, ref_cpool)
+    e = rel_err(o[sample].cpu().numpy(), ro)
+    es = rel_err(pool[idx[sample].ravel().astype(np.int64)].cpu().numpy(), ref_pool)
+    print(f"  rel err o={e:.3e} states={es:.3e}", flush=True)
+    assert e <= TOL["bf16"] and es <= TOL["bf16"]
+    assert np.array_equal(cpool[idx[sample].ravel().astype(np.int64)].float().cpu().numpy(),
+                          ref_cpool.astype(np.float32))

@@ -314,6 +314,51 @@ def test_decode_skips_negative_index(oracle_mod):
     assert not od[0].any() and od[1].any()
 
 
+def test_decode_multi_equals_prefill_prefixes(oracle_mod):
+    """m tokens per slot in one multi-token decode: token j's output and the
+    state kept after it equal a prefill of the slot's first j + 1 tokens from
+    the start entry (the prefill recurrence is separate code from the decode
+    step); num_accepted picks the start entry; a -1 start skips the slot."""
+    o = oracle_mod
+    rng = np.random.default_rng(21)
+    dims = o.Dims(2, 4, 8, 8, conv_width=4, qk_l2norm=True)
+    N, m, P = 3, 4, 16
+    C = dims.channels
+    pool0 = 0.05 * _rand(rng, P, 4, 8, 8)
+    cpool0 = _rand(rng, P, C, 3)
+    q, k = _rand(rng, N, m, 2, 8), _rand(rng, N, m, 2, 8)
+    v = _rand(rng, N, m, 4, 8)
+    g, b = -rng.uniform(0, 2, (N, m, 4)), rng.uniform(0, 1, (N, m, 4))
+    w, bias = 0.5 * _rand(rng, C, 4), 0.1 * _rand(rng, C)
+    idx = np.array([[3, 4, -1, 6], [-1, -1, -1, -1], [9, 10, 11, 12]])
+    acc = np.array([2, 1, 1])  # slot 0 resumes from entry 4, slot 2 from entry 9
+    pool, cpool = pool0.copy(), cpool0.copy()
+    od = o.decode_multi(dims, q, k, v, g, b, pool, idx, acc, w, bias, cpool)
+    for n, start in ((0, 4), (2, 9)):
+        for j in range(m):
+            ref_o, ref_s, ref_c = o.prefill(dims, _cu([j + 1]), q[n, :j + 1], k[n, :j + 1], v[n, :j + 1],
+                                            g[n, :j + 1], b[n, :j + 1], w, bias, cpool0[start:start + 1],
+                                            pool0[start:start + 1])
+            np.testing.assert_allclose(od[n, j], ref_o[j], rtol=0, atol=1e-13)
+            if idx[n, j] >= 0:
+                np.testing.assert_allclose(pool[idx[n, j]], ref_s[0], rtol=0, atol=1e-13)
+                assert np.array_equal(cpool[idx[n, j]], ref_c[0])
+    assert not od[1].any()
+    untouched = [e for e in range(P) if e not in (3, 4, 6, 9, 10, 11, 12)]
+    assert np.array_equal(pool[untouched], pool0[untouched]) and np.array_equal(cpool[untouched], cpool0[untouched])
+    assert np.array_equal(pool[5], pool0[5])
+    # without indices: entry n is read and receives the state after the last token
+    pool2, cpool2 = pool0.copy(), cpool0.copy()
+    od2 = o.decode_multi(dims, q, k, v, g, b, pool2, None, None, w, bias, cpool2)
+    for n in range(N):
+        ref_o, ref_s, ref_c = o.prefill(dims, _cu([m]), q[n], k[n], v[n], g[n], b[n], w, bias,
+                                        cpool0[n:n + 1], pool0[n:n + 1])
+        np.testing.assert_allclose(od2[n], ref_o, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(pool2[n], ref_s[0], rtol=0, atol=1e-13)
+        assert np.array_equal(cpool2[n], ref_c[0])
+    assert np.array_equal(pool2[N:], pool0[N:])
+
+
 def test_dv_permutation_permutes_rows(oracle_mod):
     """Rows of S (the d_v coordinates) evolve independently."""
     o = oracle_mod
