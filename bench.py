@@ -316,8 +316,10 @@ def main():
             torch.cuda.synchronize()
             us = e0.elapsed_time(e1) * 1e3 / calls
             mb = decode_multi_algorithmic(N, m, 16, 32, 128, kept)
+            tkey = "decode_kernel_m4_all_states" if kept == m else "decode_kernel_m4_final_state"
             mres[name] = {"us_per_call": us, "tokens_per_s": N * m / (us * 1e-6), "algorithmic_bytes": mb,
-                          "GB/s": mb / (us * 1e-6) / 1e9, "frac": mb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+                          "GB/s": mb / (us * 1e-6) / 1e9, "frac": mb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                          "traffic": measured_traffic(tkey)}
             print(f"[bench] decode x{m} ({name}): {us:.1f} us/call, {mb / (us * 1e-6) / 1e9:.0f} GB/s",
                   file=sys.stderr, flush=True)
             del mpools, mcpools
