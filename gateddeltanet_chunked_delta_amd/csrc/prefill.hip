@@ -28,8 +28,10 @@
 //                     and lo planes) of K, Q, T, P and the per-token scalars to the workspace.
 //   carry_kernel      per (sequence, value head, 64 columns of d_v): conv of
 //                     v, then the chain above with the state slice held in
-//                     matrix-core accumulators.  The next chunk's images are
-//                     loaded into registers while the current chunk computes.
+//                     matrix-core accumulators by four waves, while four
+//                     helper waves stage the chunks and compute Q H, P D and
+//                     the output.  The next chunk's images are loaded into
+//                     registers while the current chunk computes.
 //   conv_state_kernel the final conv states.
 //
 // Precision: every product takes split operands (x = hi + lo, three 16-bit
@@ -49,7 +51,6 @@ namespace gdn {
 namespace {
 
 constexpr int kChunk = 64;
-constexpr int kThreads = 256;
 constexpr int kLdsLimit = 163840;  // gfx950: 160 KiB per workgroup
 constexpr int kDvs = 64;           // d_v columns per carry workgroup
 // s_waitcnt immediate that waits for every outstanding vector memory
@@ -742,42 +743,73 @@ template <> __device__ __forceinline__ void buf_put<bf16_t>(__amdgpu_buffer_rsrc
     __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(x), r, off, 0, 0);
 }
 
+// ---------------------------------------------------------------- carry: the state chain
+
+// Workgroup = (sequence, value head, 64-column slice of d_v), 8 waves in two
+// roles, so that the work off the state's dependent path runs beside it:
+// waves 0-3 ("main") hold the state columns [16w, 16w + 16) in matrix-core
+// accumulators for the whole sequence and compute K H, R, D = T R and the
+// update;
+// wave 4 + w ("helper") covers the same columns and does the rest of the
+// staging (T|P images, scalars, conv + SiLU of v) and its loads, Q H, P D and
+// the output.  The K|Q image goes through the main waves' registers (a helper
+// holding it too would exceed its 256 registers).  Per chunk, three
+// workgroup barriers:
+//   stage:  all waves write the chunk to LDS; main also splits the state
+//           operand and hands it to the helpers through LDS.
+//   B:      main: K H, R, D = T R; D's split operand goes to LDS (over this
+//           wave's own columns of V, which only it reads).  helpers: Q H.
+//   C:      main: the state update.  helpers: P D and the output rows.
+// Each role issues its part of the next chunk's loads as phase B starts.
+// The two roles run separate loops with the same barriers, so their register
+// live ranges do not overlap.
+constexpr int kCarryThreads = 512;
+
 template <int DK>
 struct CarrySmem {
     static constexpr int kPitchK = DK + 8;      // K, Q image rows (16-bit)
     static constexpr int kPitchT = kChunk + 8;  // T, P image rows (16-bit)
-    static constexpr int kPitchV = kDvs + 4;    // V rows (fp32)
+    static constexpr int kPitchV = kDvs + 4;    // V rows (fp32); D's operand afterwards
+    static constexpr int KS = DK / 32;
     static constexpr size_t szKQ = size_t(kChunk) * kPitchK * sizeof(uint16_t);
     static constexpr size_t szTP = size_t(kChunk) * kPitchT * sizeof(uint16_t);
     static constexpr size_t oKQ = 0;         // K hi, K lo, Q hi, Q lo
     static constexpr size_t oTP = 4 * szKQ;  // T hi, T lo, P hi, P lo
     static constexpr size_t oV = oTP + 4 * szTP;
     static constexpr size_t oScal = oV + size_t(kChunk) * kPitchV * sizeof(float);
-    static constexpr size_t kBytes = oScal + Img<DK>::kScal * sizeof(float);
+    static constexpr size_t oHB = oScal + Img<DK>::kScal * sizeof(float);  // [wave][ks][hi|lo][lane] 16 B
+    static constexpr size_t kBytes = oHB + size_t(4) * KS * 2 * 64 * 16;
     static_assert(kBytes <= size_t(kLdsLimit), "LDS budget");
-    static_assert(oTP % 16 == 0 && oV % 16 == 0 && oScal % 16 == 0, "16-byte aligned regions");
+    static_assert(oTP % 16 == 0 && oV % 16 == 0 && oScal % 16 == 0 && oHB % 16 == 0, "16-byte aligned regions");
+    static_assert(kPitchV * 4 % 16 == 0 && 4 * 16 * (kPitchV * 4) >= 4 * 64 * 16, "D operand fits V's rows");
 };
 
-// Workgroup = (sequence, value head, 64-column slice of d_v); wave w owns the
-// 16 state columns [16w, 16w + 16) of the slice in accumulator layout.  The
-// workgroups of one (sequence, key head) group are mapped to the same XCD, so
-// their shared K and Q images are read through one L2.
+// Byte offset, in the V region, of piece p (0..3: D k-step 0 hi, lo, k-step 1
+// hi, lo) of lane l of column block w: rows 16 p + l/4, bytes [64 w, 64 w + 64)
+// of the row, which hold exactly V's columns [16 w, 16 w + 16).
+template <int PV>
+__device__ __forceinline__ int dop_offset(int w, int piece, int l) {
+    return (16 * piece + (l >> 2)) * (PV * 4) + 64 * w + 16 * (l & 3);
+}
+
 template <int DK, int DV, typename TIn, typename TOut>
-__global__ void __launch_bounds__(kThreads, 1) carry_kernel(const PrefillParams p) {
+__global__ void __launch_bounds__(kCarryThreads, 1) carry_kernel(const PrefillParams p) {
     constexpr int NS = DV / kDvs;
+    constexpr int HT = kCarryThreads / 2;                 // helper threads
     constexpr int VEC = Elem<TIn>::kVec;
     constexpr int NGV = kDvs / VEC;                    // 16-byte groups of a v slice row
-    constexpr int VRPB = kChunk / (kThreads / NGV);    // v rows per thread
+    constexpr int VRPB = kChunk / (HT / NGV);          // v rows per helper thread
     constexpr int KT = DK / 16, KS = DK / 32;
-    constexpr int NKQ = Img<DK>::kKQ / 8 / kThreads;   // 16-byte image pieces per thread
-    constexpr int NTP = Img<DK>::kTP / 8 / kThreads;
-    static_assert(Img<DK>::kKQ % (8 * kThreads) == 0 && Img<DK>::kTP % (8 * kThreads) == 0, "image pieces");
-    static_assert(NTP * kThreads == 4 * TriPack::kPieces, "T|P pieces");
-    static_assert(Img<DK>::kScal == kThreads, "one scalar per thread");
-    static_assert(kThreads % NGV == 0 && kChunk % (kThreads / NGV) == 0, "v prologue tiling");
+    constexpr int NKQ = Img<DK>::kKQ / 8 / HT;         // 16-byte K|Q pieces per main thread
+    constexpr int NTP = Img<DK>::kTP / 8 / HT;         // 16-byte T|P pieces per helper thread
+    static_assert(Img<DK>::kKQ % (8 * HT) == 0 && Img<DK>::kTP % (8 * HT) == 0, "image pieces");
+    static_assert(NTP * HT == 4 * TriPack::kPieces, "T|P pieces");
+    static_assert(Img<DK>::kScal == HT, "one scalar per helper thread");
+    static_assert(HT % NGV == 0 && kChunk % (HT / NGV) == 0, "v prologue tiling");
     static_assert(DV % kDvs == 0, "d_v slices");
     using S = CarrySmem<DK>;
     using E = typename OpFor<TIn>::type;
+    typedef typename OpVec<E>::v8 V8;
     constexpr int PK = S::kPitchK, PT = S::kPitchT, PV = S::kPitchV;
 
     __shared__ __attribute__((aligned(16))) char smem[S::kBytes];
@@ -792,12 +824,15 @@ __global__ void __launch_bounds__(kThreads, 1) carry_kernel(const PrefillParams 
     const E* Phi = tp + 2 * kChunk * PT;
     const E* Plo = tp + 3 * kChunk * PT;
     float* Vf = reinterpret_cast<float*>(smem + S::oV);
+    char* dop = smem + S::oV;
     float* scal = reinterpret_cast<float*>(smem + S::oScal);
+    char* hbs = smem + S::oHB;
     const float* bet = scal;
     const float* eg = scal + kChunk;
     const float* dl = scal + 2 * kChunk;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int cw = wave & 3;  // column block of this wave (main and helper alike)
     const int lr = lane & 15, lg = lane >> 4;
     // XCD-aware unit map: workgroup b runs on XCD b % 8; the M = G * NS
     // members of group g = (order index, key head) share XCD g % 8.
@@ -809,55 +844,165 @@ __global__ void __launch_bounds__(kThreads, 1) carry_kernel(const PrefillParams 
     const int hk = grp % p.h_k, gi = mem / NS, slice = mem % NS;
     const int n = p.order[grp / p.h_k];
     const int h = hk * G + gi;
-    const int wcol = 16 * wave + lr;      // this lane's column within the slice
+    const int wcol = 16 * cw + lr;        // this lane's column within the slice
     const int col = slice * kDvs + wcol;  // ... and within d_v
     const int64_t bos = p.cu_seqlens[n], eos = p.cu_seqlens[n + 1];
     const int nch = int((eos - bos + kChunk - 1) / kChunk);
     const int cb = p.chunk_base[n];
-    const int64_t nq = int64_t(p.h_k) * DK, nv = int64_t(p.h_v) * DV, C = 2 * nq + nv;
-    const bool conv = p.conv_width == 4;
-    TOut* out = static_cast<TOut*>(p.o);
     const int slot = state_slot(p, n);
     const bool has_init = slot_has_initial(p, n, slot);
-    const int64_t state_base = (int64_t(slot) * p.h_v + h) * DK * DV + col;  // used only when slot >= 0
 
-    // State column: hacc[it][e] = H[16 it + 4 lg + e][col].
-    float4_t hacc[KT];
+    if (wave < 4) {
+        // ======== main waves: the state and its dependent chain ========
+        const int64_t state_base = (int64_t(slot) * p.h_v + h) * DK * DV + col;  // used only when slot >= 0
+        // State column: hacc[it][e] = H[16 it + 4 lg + e][col].
+        float4_t hacc[KT];
 #pragma unroll
-    for (int it = 0; it < KT; it++)
+        for (int it = 0; it < KT; it++)
 #pragma unroll
-        for (int e = 0; e < 4; e++)
-            hacc[it][e] = (p.initial_state && has_init)
-                              ? p.initial_state[state_base + int64_t(16 * it + 4 * lg + e) * DV] : 0.0f;
+            for (int e = 0; e < 4; e++)
+                hacc[it][e] = (p.initial_state && has_init)
+                                  ? p.initial_state[state_base + int64_t(16 * it + 4 * lg + e) * DV] : 0.0f;
+        u32x4_t pkq[NKQ];
+        auto fetch_kq = [&](int j) {
+            const u32x4_t* skq = reinterpret_cast<const u32x4_t*>(static_cast<const E*>(p.kq_img) +
+                                                                  ((int64_t(cb) + j) * p.h_k + hk) * Img<DK>::kKQ);
+#pragma unroll
+            for (int i = 0; i < NKQ; i++) pkq[i] = skq[tid + HT * i];
+        };
+        if (nch > 0) fetch_kq(0);
 
-    // v prologue: one 16-byte channel group of the slice for VRPB rows
-    const int vg = tid % NGV, vrow0 = (tid / NGV) * VRPB;
-    const int64_t vch = 2 * nq + int64_t(h) * DV + slice * kDvs + vg * VEC;
-    const TIn* vbase = static_cast<const TIn*>(p.v) + int64_t(h) * DV + slice * kDvs + vg * VEC;
-    const TIn* vhist = (p.conv_state_in && has_init)
-                           ? static_cast<const TIn*>(p.conv_state_in) + (int64_t(slot) * C + vch) * 3 : nullptr;
-    u32x4_t vwp[4];
-    float vbias[VEC];
-    conv_params<TIn>(p, vch, vwp, vbias);
+        for (int j = 0; j < nch; j++) {
+            // ---- stage: the K|Q image, and the state as the B operand (also handed to the helpers) ----
+#pragma unroll
+            for (int i = 0; i < NKQ; i++) {
+                const int pc = tid + HT * i;  // piece: plane, row, 8 columns
+                const int plane = pc / (kChunk * DK / 8), rem = pc % (kChunk * DK / 8);
+                *reinterpret_cast<u32x4_t*>(kq + plane * kChunk * PK + (rem / (DK / 8)) * PK + 8 * (rem % (DK / 8))) =
+                    pkq[i];
+            }
+            SFrag<E> hb[KS];
+#pragma unroll
+            for (int ks = 0; ks < KS; ks++) {
+                float x[8];
+                acc_to_operand(hacc[2 * ks], hacc[2 * ks + 1], x);
+                hb[ks] = split8<E>(x);
+                *reinterpret_cast<V8*>(hbs + (((cw * KS + ks) * 2 + 0) * 64 + lane) * 16) = hb[ks].hi;
+                *reinterpret_cast<V8*>(hbs + (((cw * KS + ks) * 2 + 1) * 64 + lane) * 16) = hb[ks].lo;
+            }
+            lds_barrier();
+            // the next chunk's K|Q image: two phases to arrive before it is staged
+            if (j + 1 < nch) fetch_kq(j + 1);
 
-    // The next chunk's images and raw v rows, in registers.
-    u32x4_t pkq[NKQ], ptp[NTP], xv[VRPB + 3];
-    float psc;
-    // The next chunk's loads are spread over the phases of the current one
-    // (part 0..4), so that their issue overlaps the matrix-core work instead
-    // of stalling the waves in one block.
-    auto fetch = [&](int j, int part) {
-        const int64_t slot = int64_t(cb) + j;
-        const u32x4_t* skq = reinterpret_cast<const u32x4_t*>(static_cast<const E*>(p.kq_img) +
-                                                              (slot * p.h_k + hk) * Img<DK>::kKQ);
-        const u32x4_t* stp = reinterpret_cast<const u32x4_t*>(static_cast<const E*>(p.tp_img) +
-                                                              (slot * p.h_v + h) * Img<DK>::kTP);
-        // part 0: raw v rows and scalars; parts 1-4: a quarter of the K|Q
-        // pieces each, parts 1-3 also a third of the T|P pieces
-        constexpr int Q4 = NKQ / 4, T3 = (NTP + 2) / 3;
-        static_assert(NKQ % 4 == 0, "K|Q pieces in four parts");
-        if (part == 0) {
-            psc = p.scal_img[(slot * p.h_v + h) * Img<DK>::kScal + tid];
+            // ---- B: R = beta (V - e^gam K H), D = T R; D's operand to LDS ----
+            float4_t rr[4];
+#pragma unroll
+            for (int tb = 0; tb < 4; tb++) {
+                float4_t khh = kZero4, khx = kZero4;
+#pragma unroll
+                for (int ks = 0; ks < KS; ks++)
+                    mma3(khh, khx, lds_sfrag(Khi, Klo, PK, 16 * tb + lr, 32 * ks + 8 * lg), hb[ks]);
+                const float4_t kh = combine<E>(khh, khx);
+                const float4 egv = *reinterpret_cast<const float4*>(eg + 16 * tb + 4 * lg);
+                const float4 btv = *reinterpret_cast<const float4*>(bet + 16 * tb + 4 * lg);
+                const float egr[4] = {egv.x, egv.y, egv.z, egv.w}, btr[4] = {btv.x, btv.y, btv.z, btv.w};
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const int r = 16 * tb + 4 * lg + e;
+                    rr[tb][e] = btr[e] * (Vf[r * PV + wcol] - egr[e] * kh[e]);
+                }
+            }
+            float4_t dd[4];
+            {
+                SFrag<E> rb[2];
+#pragma unroll
+                for (int s = 0; s < 2; s++) {
+                    float x[8];
+                    acc_to_operand(rr[2 * s], rr[2 * s + 1], x);
+                    rb[s] = split8<E>(x);
+                }
+#pragma unroll
+                for (int tb = 0; tb < 4; tb++) {
+                    float4_t hh = kZero4, xx = kZero4;
+#pragma unroll
+                    for (int ks = 0; ks <= tb / 2; ks++)
+                        mma3(hh, xx, lds_sfrag(Thi, Tlo, PT, 16 * tb + lr, 32 * ks + 8 * lg), rb[ks]);
+                    dd[tb] = combine<E>(hh, xx);
+                }
+            }
+            // D's operand overwrites this wave's own V columns, which only this
+            // wave has read (R above, on which D depends).
+#pragma unroll
+            for (int s = 0; s < 2; s++) {
+                float x[8];
+                acc_to_operand(dd[2 * s], dd[2 * s + 1], x);
+                const SFrag<E> f = split8<E>(x);
+                *reinterpret_cast<V8*>(dop + dop_offset<PV>(cw, 2 * s, lane)) = f.hi;
+                *reinterpret_cast<V8*>(dop + dop_offset<PV>(cw, 2 * s + 1, lane)) = f.lo;
+            }
+            lds_barrier();
+
+            // ---- C: H <- e^{gam_last} H + K^T diag(e^{gam_last - gam}) D ----
+            {
+                SFrag<E> ab[2];
+#pragma unroll
+                for (int s = 0; s < 2; s++) {
+                    float4_t a0, a1;
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        const int r0 = 32 * s + 4 * lg + e, r1 = r0 + 16;
+                        a0[e] = dl[r0] * dd[2 * s][e];
+                        a1[e] = dl[r1] * dd[2 * s + 1][e];
+                    }
+                    float x[8];
+                    acc_to_operand(a0, a1, x);
+                    ab[s] = split8<E>(x);
+                }
+                const float decay = scal[3 * kChunk];
+#pragma unroll
+                for (int it = 0; it < KT; it++) {
+                    float4_t hh = hacc[it] * decay, xx = kZero4;
+#pragma unroll
+                    for (int s = 0; s < 2; s++)
+                        mma3(hh, xx, lds_sfrag_tr(Khi, Klo, PK, 32 * s + 8 * lg, 16 * it), ab[s]);
+                    hacc[it] = combine<E>(hh, xx);
+                }
+            }
+            lds_barrier();
+        }
+
+        if (p.final_state && slot >= 0) {
+#pragma unroll
+            for (int it = 0; it < KT; it++)
+#pragma unroll
+                for (int e = 0; e < 4; e++)
+                    p.final_state[state_base + int64_t(16 * it + 4 * lg + e) * DV] = hacc[it][e];
+        }
+    } else {
+        // ======== helper waves: staging, loads, Q H, P D and the output ========
+        const int ht = tid - HT;
+        const int64_t nq = int64_t(p.h_k) * DK, nv = int64_t(p.h_v) * DV, C = 2 * nq + nv;
+        const bool conv = p.conv_width == 4;
+        TOut* out = static_cast<TOut*>(p.o);
+        // v prologue: one 16-byte channel group of the slice for VRPB rows
+        const int vg = ht % NGV, vrow0 = (ht / NGV) * VRPB;
+        const int64_t vch = 2 * nq + int64_t(h) * DV + slice * kDvs + vg * VEC;
+        const TIn* vbase = static_cast<const TIn*>(p.v) + int64_t(h) * DV + slice * kDvs + vg * VEC;
+        const TIn* vhist = (p.conv_state_in && has_init)
+                               ? static_cast<const TIn*>(p.conv_state_in) + (int64_t(slot) * C + vch) * 3 : nullptr;
+        u32x4_t vwp[4];
+        float vbias[VEC];
+        conv_params<TIn>(p, vch, vwp, vbias);
+
+        u32x4_t ptp[NTP], xv[VRPB + 3];
+        float psc;
+        // The next chunk's T|P pieces, scalars and raw v rows (issued once the
+        // chunk is staged, consumed at the next staging).
+        auto fetch = [&](int j) {
+            const int64_t cslot = int64_t(cb) + j;
+            const u32x4_t* stp = reinterpret_cast<const u32x4_t*>(static_cast<const E*>(p.tp_img) +
+                                                                  (cslot * p.h_v + h) * Img<DK>::kTP);
+            psc = p.scal_img[(cslot * p.h_v + h) * Img<DK>::kScal + ht];
             const int64_t c0 = bos + int64_t(j) * kChunk;
             if (c0 - 3 >= bos && c0 + kChunk <= eos) {
                 // interior chunk: every row, history included, is in the sequence
@@ -868,178 +1013,97 @@ __global__ void __launch_bounds__(kThreads, 1) carry_kernel(const PrefillParams 
                 const int L = int(eos - c0 < kChunk ? eos - c0 : kChunk);
                 load_rows<TIn, VRPB>(xv, vbase, nv, c0, vrow0, L, bos, conv, vhist);
             }
-        } else {
 #pragma unroll
-            for (int i = 0; i < Q4; i++) pkq[(part - 1) * Q4 + i] = skq[tid + kThreads * ((part - 1) * Q4 + i)];
-#pragma unroll
-            for (int i = 0; i < T3; i++) {
-                const int t = (part - 1) * T3 + i;
-                if (t < NTP) ptp[t] = stp[tid + kThreads * t];
-            }
+            for (int i = 0; i < NTP; i++) ptp[i] = stp[ht + HT * i];
+        };
+        // Blocks (0, 1) and (2, 3) of the T and P planes are read by the
+        // products (k-steps of 32 columns) but never staged: zero them once.
+        for (int i = ht; i < 4 * 2 * 16 * 2; i += HT) {
+            const int plane = i >> 6, blk = (i >> 5) & 1, rr = (i >> 1) & 15, half = i & 1;
+            const int r = 32 * blk + rr, c = 32 * blk + 16 + 8 * half;
+            *reinterpret_cast<u32x4_t*>(tp + plane * kChunk * PT + r * PT + c) = u32x4_t{0u, 0u, 0u, 0u};
         }
-    };
-    auto fetch_all = [&](int j) {
-#pragma unroll
-        for (int part = 0; part < 5; part++) fetch(j, part);
-    };
-    // Blocks (0, 1) and (2, 3) of the T and P planes are read by the products
-    // (k-steps of 32 columns) but never staged: zero them once.
-    for (int i = tid; i < 4 * 2 * 16 * 2; i += kThreads) {
-        const int plane = i >> 6, blk = (i >> 5) & 1, rr = (i >> 1) & 15, half = i & 1;
-        const int r = 32 * blk + rr, c = 32 * blk + 16 + 8 * half;
-        *reinterpret_cast<u32x4_t*>(tp + plane * kChunk * PT + r * PT + c) = u32x4_t{0u, 0u, 0u, 0u};
-    }
-    if (nch > 0) fetch_all(0);
+        if (nch > 0) fetch(0);
 
-    for (int j = 0; j < nch; j++) {
-        const int64_t c0 = bos + int64_t(j) * kChunk;
-        const int L = int(eos - c0 < kChunk ? eos - c0 : kChunk);
+        for (int j = 0; j < nch; j++) {
+            const int64_t c0 = bos + int64_t(j) * kChunk;
+            const int L = int(eos - c0 < kChunk ? eos - c0 : kChunk);
 
-        // ---- stage the chunk (every wave is done with the previous one) ----
+            // ---- stage the chunk (every wave is done with the previous one) ----
 #pragma unroll
-        for (int i = 0; i < NKQ; i++) {
-            const int pc = tid + kThreads * i;  // piece: plane, row, 8 columns
-            const int plane = pc / (kChunk * DK / 8), rem = pc % (kChunk * DK / 8);
-            *reinterpret_cast<u32x4_t*>(kq + plane * kChunk * PK + (rem / (DK / 8)) * PK + 8 * (rem % (DK / 8))) =
-                pkq[i];
-        }
+            for (int i = 0; i < NTP; i++) {
+                const int pc = ht + HT * i;
+                const int plane = pc / TriPack::kPieces;
+                int r, c8;
+                TriPack::locate(pc % TriPack::kPieces, r, c8);
+                *reinterpret_cast<u32x4_t*>(tp + plane * kChunk * PT + r * PT + 8 * c8) = ptp[i];
+            }
+            scal[ht] = psc;
 #pragma unroll
-        for (int i = 0; i < NTP; i++) {
-            const int pc = tid + kThreads * i;
-            const int plane = pc / TriPack::kPieces;
-            int r, c8;
-            TriPack::locate(pc % TriPack::kPieces, r, c8);
-            *reinterpret_cast<u32x4_t*>(tp + plane * kChunk * PT + r * PT + 8 * c8) = ptp[i];
-        }
-        scal[tid] = psc;
+            for (int i = 0; i < VRPB; i++) {
+                const int row = vrow0 + i;
+                float y[VEC];
+                conv_row<TIn>(conv, xv, vwp, vbias, i, y);
 #pragma unroll
-        for (int i = 0; i < VRPB; i++) {
-            const int row = vrow0 + i;
-            float y[VEC];
-            conv_row<TIn>(conv, xv, vwp, vbias, i, y);
-#pragma unroll
-            for (int e = 0; e < VEC; e++) Vf[row * PV + vg * VEC + e] = (row < L) ? y[e] : 0.0f;
-        }
-        lds_barrier();
-        const bool more = j + 1 < nch;
-        if (more) fetch(j + 1, 0);
+                for (int e = 0; e < VEC; e++) Vf[row * PV + vg * VEC + e] = (row < L) ? y[e] : 0.0f;
+            }
+            lds_barrier();
+            if (j + 1 < nch) fetch(j + 1);
 
-        // ---- the state as the B operand of this chunk's products ----
-        SFrag<E> hb[KS];
+            // ---- B: e^gam Q H from the state operand the main wave left in LDS ----
+            float4_t eqh[4];
+            {
+                SFrag<E> hb[KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ks++) {
-            float x[8];
-            acc_to_operand(hacc[2 * ks], hacc[2 * ks + 1], x);
-            hb[ks] = split8<E>(x);
-        }
-        // ---- R = beta (V - e^gam K H) and e^gam Q H, sharing the state operand ----
-        float4_t rr[4], eqh[4];
+                for (int ks = 0; ks < KS; ks++) {
+                    hb[ks].hi = *reinterpret_cast<const V8*>(hbs + (((cw * KS + ks) * 2 + 0) * 64 + lane) * 16);
+                    hb[ks].lo = *reinterpret_cast<const V8*>(hbs + (((cw * KS + ks) * 2 + 1) * 64 + lane) * 16);
+                }
 #pragma unroll
-        for (int tb = 0; tb < 4; tb++) {
-            float4_t khh = kZero4, khx = kZero4, qhh = kZero4, qhx = kZero4;
+                for (int tb = 0; tb < 4; tb++) {
+                    float4_t qhh = kZero4, qhx = kZero4;
 #pragma unroll
-            for (int ks = 0; ks < KS; ks++) {
-                mma3(khh, khx, lds_sfrag(Khi, Klo, PK, 16 * tb + lr, 32 * ks + 8 * lg), hb[ks]);
-                mma3(qhh, qhx, lds_sfrag(Qhi, Qlo, PK, 16 * tb + lr, 32 * ks + 8 * lg), hb[ks]);
-            }
-            const float4_t kh = combine<E>(khh, khx), qh = combine<E>(qhh, qhx);
-            const float4 egv = *reinterpret_cast<const float4*>(eg + 16 * tb + 4 * lg);
-            const float4 btv = *reinterpret_cast<const float4*>(bet + 16 * tb + 4 * lg);
-            const float egr[4] = {egv.x, egv.y, egv.z, egv.w}, btr[4] = {btv.x, btv.y, btv.z, btv.w};
+                    for (int ks = 0; ks < KS; ks++)
+                        mma3(qhh, qhx, lds_sfrag(Qhi, Qlo, PK, 16 * tb + lr, 32 * ks + 8 * lg), hb[ks]);
+                    const float4_t qh = combine<E>(qhh, qhx);
+                    const float4 egv = *reinterpret_cast<const float4*>(eg + 16 * tb + 4 * lg);
+                    const float egr[4] = {egv.x, egv.y, egv.z, egv.w};
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const int r = 16 * tb + 4 * lg + e;
-                rr[tb][e] = btr[e] * (Vf[r * PV + wcol] - egr[e] * kh[e]);
-                eqh[tb][e] = egr[e] * qh[e];
-            }
-        }
-        if (more) fetch(j + 1, 1);
-        // ---- D = T R (T lower triangular: row block tb needs k-steps <= tb/2) ----
-        float4_t dd[4];
-        {
-            SFrag<E> rb[2];
-#pragma unroll
-            for (int s = 0; s < 2; s++) {
-                float x[8];
-                acc_to_operand(rr[2 * s], rr[2 * s + 1], x);
-                rb[s] = split8<E>(x);
-            }
-#pragma unroll
-            for (int tb = 0; tb < 4; tb++) {
-                float4_t hh = kZero4, xx = kZero4;
-#pragma unroll
-                for (int ks = 0; ks <= tb / 2; ks++)
-                    mma3(hh, xx, lds_sfrag(Thi, Tlo, PT, 16 * tb + lr, 32 * ks + 8 * lg), rb[ks]);
-                dd[tb] = combine<E>(hh, xx);
-            }
-        }
-        if (more) fetch(j + 1, 2);
-        // ---- o = scale (e^gam Q H + P D) ----
-        {
-            // The chunk's rows of o through a buffer resource whose extent ends
-            // after row L - 1: the hardware drops the stores of rows past the
-            // sequence's end, so no store needs a branch of its own.
-            const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
-                out + c0 * p.h_v * DV, short(0), L * p.h_v * DV * int(sizeof(TOut)), kBufferFlags);
-            SFrag<E> db[2];
-#pragma unroll
-            for (int s = 0; s < 2; s++) {
-                float x[8];
-                acc_to_operand(dd[2 * s], dd[2 * s + 1], x);
-                db[s] = split8<E>(x);
-            }
-#pragma unroll
-            for (int tb = 0; tb < 4; tb++) {
-                float4_t phh = kZero4, phx = kZero4;
-#pragma unroll
-                for (int ks = 0; ks <= tb / 2; ks++)
-                    mma3(phh, phx, lds_sfrag(Phi, Plo, PT, 16 * tb + lr, 32 * ks + 8 * lg), db[ks]);
-                const float4_t pd = combine<E>(phh, phx);
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    const int r = 16 * tb + 4 * lg + e;
-                    buf_put<TOut>(orsrc, ((r * p.h_v + h) * DV + col) * int(sizeof(TOut)),
-                                  p.scale * (eqh[tb][e] + pd[e]));
+                    for (int e = 0; e < 4; e++) eqh[tb][e] = egr[e] * qh[e];
                 }
             }
-        }
-        if (more) fetch(j + 1, 3);
-        // ---- H <- e^{gam_last} H + K^T diag(e^{gam_last - gam}) D ----
-        {
-            SFrag<E> ab[2];
-#pragma unroll
-            for (int s = 0; s < 2; s++) {
-                float4_t a0, a1;
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    const int r0 = 32 * s + 4 * lg + e, r1 = r0 + 16;
-                    a0[e] = dl[r0] * dd[2 * s][e];
-                    a1[e] = dl[r1] * dd[2 * s + 1][e];
-                }
-                float x[8];
-                acc_to_operand(a0, a1, x);
-                ab[s] = split8<E>(x);
-            }
-            const float decay = scal[3 * kChunk];
-#pragma unroll
-            for (int it = 0; it < KT; it++) {
-                float4_t hh = hacc[it] * decay, xx = kZero4;
-#pragma unroll
-                for (int s = 0; s < 2; s++)
-                    mma3(hh, xx, lds_sfrag_tr(Khi, Klo, PK, 32 * s + 8 * lg, 16 * it), ab[s]);
-                hacc[it] = combine<E>(hh, xx);
-            }
-        }
-        if (more) fetch(j + 1, 4);
-        lds_barrier();
-    }
+            lds_barrier();
 
-    if (p.final_state && slot >= 0) {
+            // ---- C: o = scale (e^gam Q H + P D) ----
+            {
+                // The chunk's rows of o through a buffer resource whose extent ends
+                // after row L - 1: the hardware drops the stores of rows past the
+                // sequence's end, so no store needs a branch of its own.
+                const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+                    out + c0 * p.h_v * DV, short(0), L * p.h_v * DV * int(sizeof(TOut)), kBufferFlags);
+                SFrag<E> db[2];
 #pragma unroll
-        for (int it = 0; it < KT; it++)
+                for (int s = 0; s < 2; s++) {
+                    db[s].hi = *reinterpret_cast<const V8*>(dop + dop_offset<PV>(cw, 2 * s, lane));
+                    db[s].lo = *reinterpret_cast<const V8*>(dop + dop_offset<PV>(cw, 2 * s + 1, lane));
+                }
 #pragma unroll
-            for (int e = 0; e < 4; e++)
-                p.final_state[state_base + int64_t(16 * it + 4 * lg + e) * DV] = hacc[it][e];
+                for (int tb = 0; tb < 4; tb++) {
+                    float4_t phh = kZero4, phx = kZero4;
+#pragma unroll
+                    for (int ks = 0; ks <= tb / 2; ks++)
+                        mma3(phh, phx, lds_sfrag(Phi, Plo, PT, 16 * tb + lr, 32 * ks + 8 * lg), db[ks]);
+                    const float4_t pd = combine<E>(phh, phx);
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        const int r = 16 * tb + 4 * lg + e;
+                        buf_put<TOut>(orsrc, ((r * p.h_v + h) * DV + col) * int(sizeof(TOut)),
+                                      p.scale * (eqh[tb][e] + pd[e]));
+                    }
+                }
+            }
+            lds_barrier();
+        }
     }
 }
 
@@ -1116,7 +1180,7 @@ hipError_t run(const PrefillParams& p, hipStream_t stream, void* const* events) 
     err = record(events, 1, stream);
     if (err != hipSuccess) return err;
     carry_kernel<DK, DV, TIn, TOut>
-        <<<dim3(unsigned(carry_blocks(p.num_seqs, p.h_k, p.h_v, DV))), dim3(kThreads), 0, stream>>>(p);
+        <<<dim3(unsigned(carry_blocks(p.num_seqs, p.h_k, p.h_v, DV))), dim3(kCarryThreads), 0, stream>>>(p);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     return record(events, 2, stream);
