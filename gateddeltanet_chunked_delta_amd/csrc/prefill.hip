@@ -759,7 +759,8 @@ template <> __device__ __forceinline__ void buf_put<bf16_t>(__amdgpu_buffer_rsrc
 //           operand and hands it to the helpers through LDS.
 //   B:      main: K H, R, D = T R; D's split operand goes to LDS (over this
 //           wave's own columns of V, which only it reads).  helpers: Q H.
-//   C:      main: the state update.  helpers: P D and the output rows.
+//   C:      main: the state update.  helpers: P D and the output rows, then
+//           conv + SiLU of the next chunk's v rows (kept in registers).
 // Each role issues its part of the next chunk's loads as phase B starts.
 // The two roles run separate loops with the same barriers, so their register
 // live ranges do not overlap.
@@ -1023,7 +1024,33 @@ __global__ void __launch_bounds__(kCarryThreads, 1) carry_kernel(const PrefillPa
             const int r = 32 * blk + rr, c = 32 * blk + 16 + 8 * half;
             *reinterpret_cast<u32x4_t*>(tp + plane * kChunk * PT + r * PT + c) = u32x4_t{0u, 0u, 0u, 0u};
         }
-        if (nch > 0) fetch(0);
+        // LDS offsets of this thread's T|P pieces (the same every chunk)
+        int tpo[NTP];
+#pragma unroll
+        for (int i = 0; i < NTP; i++) {
+            const int pc = ht + HT * i;
+            int r, c8;
+            TriPack::locate(pc % TriPack::kPieces, r, c8);
+            tpo[i] = (pc / TriPack::kPieces) * kChunk * PT + r * PT + 8 * c8;
+        }
+        // conv(4) + SiLU of this thread's v rows of chunk j (zero past its end),
+        // computed from the raw rows during the previous chunk's phase C
+        float vy[VRPB][VEC];
+        auto conv_v = [&](int j) {
+            const int64_t c0 = bos + int64_t(j) * kChunk;
+            const int L = int(eos - c0 < kChunk ? eos - c0 : kChunk);
+#pragma unroll
+            for (int i = 0; i < VRPB; i++) {
+                float y[VEC];
+                conv_row<TIn>(conv, xv, vwp, vbias, i, y);
+#pragma unroll
+                for (int e = 0; e < VEC; e++) vy[i][e] = (vrow0 + i < L) ? y[e] : 0.0f;
+            }
+        };
+        if (nch > 0) {
+            fetch(0);
+            conv_v(0);
+        }
 
         for (int j = 0; j < nch; j++) {
             const int64_t c0 = bos + int64_t(j) * kChunk;
@@ -1031,22 +1058,12 @@ __global__ void __launch_bounds__(kCarryThreads, 1) carry_kernel(const PrefillPa
 
             // ---- stage the chunk (every wave is done with the previous one) ----
 #pragma unroll
-            for (int i = 0; i < NTP; i++) {
-                const int pc = ht + HT * i;
-                const int plane = pc / TriPack::kPieces;
-                int r, c8;
-                TriPack::locate(pc % TriPack::kPieces, r, c8);
-                *reinterpret_cast<u32x4_t*>(tp + plane * kChunk * PT + r * PT + 8 * c8) = ptp[i];
-            }
+            for (int i = 0; i < NTP; i++) *reinterpret_cast<u32x4_t*>(tp + tpo[i]) = ptp[i];
             scal[ht] = psc;
 #pragma unroll
-            for (int i = 0; i < VRPB; i++) {
-                const int row = vrow0 + i;
-                float y[VEC];
-                conv_row<TIn>(conv, xv, vwp, vbias, i, y);
+            for (int i = 0; i < VRPB; i++)
 #pragma unroll
-                for (int e = 0; e < VEC; e++) Vf[row * PV + vg * VEC + e] = (row < L) ? y[e] : 0.0f;
-            }
+                for (int e = 0; e < VEC; e++) Vf[(vrow0 + i) * PV + vg * VEC + e] = vy[i][e];
             lds_barrier();
             if (j + 1 < nch) fetch(j + 1);
 
@@ -1102,6 +1119,7 @@ __global__ void __launch_bounds__(kCarryThreads, 1) carry_kernel(const PrefillPa
                     }
                 }
             }
+            if (j + 1 < nch) conv_v(j + 1);
             lds_barrier();
         }
     }
