@@ -88,28 +88,32 @@ struct Img {
 
 // ---------------------------------------------------------------- prologue
 
-// conv(4) + SiLU of row i of one 16-byte channel group: xr[i .. i+3] hold the
-// raw rows from 3 before it; wp the taps as raw packs (w[4 e + tap]).
-template <typename TIn>
-__device__ __forceinline__ void conv_row(bool conv, const u32x4_t* xr, const u32x4_t (&wp)[4],
-                                         const float (&bias)[Elem<TIn>::kVec], int i,
-                                         float (&y)[Elem<TIn>::kVec]) {
+// conv(4) + SiLU of rows 0..R-1 of one 16-byte channel group (xr[0 .. R+2]
+// hold the raw rows from 3 before the first), with the taps and each raw row
+// unpacked once: y[i][e] = SiLU(bias[e] + sum_jj w[e][jj] x[i + jj][e]), the taps
+// summed in order jj = 0..3 (w[c][3] hits the newest row).
+template <typename TIn, int R>
+__device__ __forceinline__ void conv_rows(bool conv, const u32x4_t (&xr)[R + 3], const u32x4_t (&wp)[4],
+                                          const float (&bias)[Elem<TIn>::kVec], float (&y)[R][Elem<TIn>::kVec]) {
     constexpr int VEC = Elem<TIn>::kVec;
     if (conv) {
-        float wv[4 * VEC], xs[4][VEC];
+        float wv[4 * VEC], xs[R + 3][VEC];
 #pragma unroll
         for (int m = 0; m < 4; m++) Elem<TIn>::unpack16(to_uint4(wp[m]), wv + m * VEC);
 #pragma unroll
-        for (int jj = 0; jj < 4; jj++) Elem<TIn>::unpack16(to_uint4(xr[i + jj]), xs[jj]);
+        for (int jj = 0; jj < R + 3; jj++) Elem<TIn>::unpack16(to_uint4(xr[jj]), xs[jj]);
 #pragma unroll
-        for (int e = 0; e < VEC; e++) {
-            float acc = bias[e];
+        for (int i = 0; i < R; i++)
 #pragma unroll
-            for (int jj = 0; jj < 4; jj++) acc += wv[4 * e + jj] * xs[jj][e];
-            y[e] = silu(acc);
-        }
+            for (int e = 0; e < VEC; e++) {
+                float acc = bias[e];
+#pragma unroll
+                for (int jj = 0; jj < 4; jj++) acc += wv[4 * e + jj] * xs[i + jj][e];
+                y[i][e] = silu(acc);
+            }
     } else {
-        Elem<TIn>::unpack16(to_uint4(xr[i + 3]), y);
+#pragma unroll
+        for (int i = 0; i < R; i++) Elem<TIn>::unpack16(to_uint4(xr[i + 3]), y[i]);
     }
 }
 
@@ -476,9 +480,9 @@ __global__ void __launch_bounds__(kPrepThreads, 1) prep_kernel(const PrefillPara
 #pragma unroll
         for (int e = 0; e < VEC; e++) pbias[e] = __uint_as_float(pbraw[e]);
         float y[RPB][VEC];
+        conv_rows<TIn, RPB>(conv, xr, pw, pbias, y);
 #pragma unroll
         for (int i = 0; i < RPB; i++) {
-            conv_row<TIn>(conv, xr, pw, pbias, i, y[i]);
             float ss = 0.0f;
 #pragma unroll
             for (int e = 0; e < VEC; e++) {
@@ -508,9 +512,16 @@ __global__ void __launch_bounds__(kPrepThreads, 1) prep_kernel(const PrefillPara
             for (int i = 0; i < RPB; i++) {
                 const int row = prow0 + i;
                 const float* rr = red + row * NG + pwhich * NGQ;
+                static_assert(NGQ % 4 == 0, "partial sums in 16-byte loads");
                 float sum = 0.0f;
 #pragma unroll
-                for (int q = 0; q < NGQ; q++) sum += rr[q];
+                for (int q = 0; q < NGQ; q += 4) {
+                    const float4 r4 = *reinterpret_cast<const float4*>(rr + q);
+                    sum += r4.x;
+                    sum += r4.y;
+                    sum += r4.z;
+                    sum += r4.w;
+                }
                 const float sc = p.qk_l2norm ? 1.0f / sqrtf(sum + p.l2_eps) : 1.0f;
                 typedef E E2 __attribute__((ext_vector_type(2)));
                 E2 h16[VEC / 2], l16[VEC / 2];
@@ -1039,13 +1050,12 @@ __global__ void __launch_bounds__(kCarryThreads, 1) carry_kernel(const PrefillPa
         auto conv_v = [&](int j) {
             const int64_t c0 = bos + int64_t(j) * kChunk;
             const int L = int(eos - c0 < kChunk ? eos - c0 : kChunk);
+            float y[VRPB][VEC];
+            conv_rows<TIn, VRPB>(conv, xv, vwp, vbias, y);
 #pragma unroll
-            for (int i = 0; i < VRPB; i++) {
-                float y[VEC];
-                conv_row<TIn>(conv, xv, vwp, vbias, i, y);
+            for (int i = 0; i < VRPB; i++)
 #pragma unroll
-                for (int e = 0; e < VEC; e++) vy[i][e] = (vrow0 + i < L) ? y[e] : 0.0f;
-            }
+                for (int e = 0; e < VEC; e++) vy[i][e] = (vrow0 + i < L) ? y[i][e] : 0.0f;
         };
         if (nch > 0) {
             fetch(0);
