@@ -127,3 +127,60 @@ def test_decode_multi_256_slots_sampled(oracle_mod):
     assert e <= TOL["bf16"] and es <= TOL["bf16"]
     assert np.array_equal(cpool[idx[sample].ravel().astype(np.int64)].float().cpu().numpy(),
                           ref_cpool.astype(np.float32))
+
+
+@pytest.mark.parametrize("dtype,d,out", [("f32", 64, "f32"), ("bf16", 128, "bf16")])
+def test_decode_multi_eight_tokens_without_conv(oracle_mod, dtype, d, out):
+    """The largest m (8), no conv prologue, raw gates (sigmoid in the kernel),
+    fp32 or bf16 outputs; every token's state kept."""
+    geom = Geometry(2, 4, d, d)
+    N, m = 3, 8
+    dt = TORCH_DT[dtype]
+    P = N * m
+    pool_np = np.zeros((P, 4, d, d), dtype=np.float32)
+    idx = np.arange(P, dtype=np.int32).reshape(N, m)
+    pool_np[idx[:, 0]] = state_pool(64, N, geom)
+    pool = dev(pool_np)
+    ref_pool = pool_np.astype(np.float64)
+    x = multi_decode_inputs(64, 0, N, m, geom, dtype)
+    b_raw = np.log(x.beta / (1.0 - x.beta)).astype(np.float32)  # raw gates with sigmoid(b) ~ beta
+    beta_used = 1.0 / (1.0 + np.exp(-b_raw.astype(np.float64)))
+    o = binding.gdn_decode_multi(dev(x.q, dt), dev(x.k, dt), dev(x.v, dt), dev(x.g), dev(b_raw), pool,
+                                 state_indices=dev(idx, torch.int32), beta_logits=True,
+                                 out_dtype=TORCH_DT[out])
+    dims = oracle_mod.Dims(2, 4, d, d, conv_width=0)
+    ro = oracle_mod.decode_multi(dims, x.q, x.k, x.v, x.g, beta_used, ref_pool, idx)
+    got = o.float().cpu().numpy()
+    if out == "bf16":
+        # bf16 o is the fp32 result rounded once: within one bf16 ulp of the oracle
+        assert np.all(np.abs(got - ro) <= np.abs(ro) * 2.0 ** -8 + 1e-2 * np.sqrt(np.mean(ro ** 2)))
+    else:
+        assert rel_err(got, ro) <= TOL[dtype]
+    assert rel_err(pool.cpu().numpy(), ref_pool) <= TOL[dtype]
+
+
+def test_decode_multi_binding_validation():
+    """Host-side checks of the Python binding: num_accepted outside 1..m and an
+    entry shared by two slots are refused before any launch; a slot may reuse
+    its own entry."""
+    geom = Geometry(1, 2, 64, 64)
+    N, m = 2, 3
+    x = multi_decode_inputs(65, 0, N, m, geom, "bf16")
+    bf = torch.bfloat16
+    args = (dev(x.q, bf), dev(x.k, bf), dev(x.v, bf), dev(x.g), dev(x.beta))
+    pool = torch.zeros((8, 2, 64, 64), dtype=torch.float32, device="cuda")
+    ok = torch.tensor([[0, 1, 0], [2, 3, -1]], dtype=torch.int32, device="cuda")
+    binding.gdn_decode_multi(*args, pool, state_indices=ok)
+    torch.cuda.synchronize()
+    with pytest.raises(ValueError):
+        binding.gdn_decode_multi(*args, pool, state_indices=ok,
+                                 num_accepted=torch.tensor([1, 4], dtype=torch.int32, device="cuda"))
+    with pytest.raises(ValueError):
+        binding.gdn_decode_multi(*args, pool, state_indices=ok,
+                                 num_accepted=torch.tensor([0, 1], dtype=torch.int32, device="cuda"))
+    shared = torch.tensor([[0, 1, 2], [2, 3, 4]], dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError):
+        binding.gdn_decode_multi(*args, pool, state_indices=shared)
+    with pytest.raises(ValueError):
+        binding.gdn_decode_multi(*args, pool, state_indices=torch.tensor([[0, 1, 8], [2, 3, 4]], dtype=torch.int32,
+                                                                         device="cuda"))
