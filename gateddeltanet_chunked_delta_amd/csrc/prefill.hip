@@ -730,7 +730,12 @@ __global__ void __launch_bounds__(kPrepThreads, 1) prep_kernel(const PrefillPara
                     }
                 }
             }
-            lds_barrier();
+            // No barrier here: Tf is next written three barriers later (the
+            // next pair's inverse columns) or, after the last pair, by the next
+            // unit's split planes, which come after the prologue's barrier; the
+            // next pair's decays and the next prologue touch only gam, bet and
+            // the partial sums.  A wave may start them while others still read
+            // Tf for this image.
         }
         if (more) {
             load_gb(N, grp);
