@@ -12,7 +12,9 @@ the chunk-local kernel is reported beside it.  The decode half of the metric
 (256 slots x 32 value heads, d = 128, conv update, 512 MiB fp32 state pool
 updated in place, 100 consecutive steps over 4 pools in rotation) is timed
 separately and reported under "decode", and the multi-token (speculative)
-decode of 4 tokens per slot under "decode_multi".  One JSON line is printed.
+decode of 4 tokens per slot under "decode_multi"; the packed varlen batch (60
+sequences, h_v = 48) and a 32768-token sequence are timed under
+"other_prefill_configs".  One JSON line is printed.
 """
 from __future__ import annotations
 
@@ -84,6 +86,46 @@ def decode_multi_algorithmic(N, m, h_k, h_v, d, kept, in_bytes=2, out_bytes=4):
             + N * C * 3 * in_bytes * (1 + kept) + C * 4 * in_bytes)
 
 
+def extra_prefill(gdn, torch, dev, lengths, h_k, h_v, d, init_std, steps, seed):
+    """Prefill throughput at another geometry, inputs drawn on the GPU with the
+    distributions of the seeded workloads (q, k, v ~ N(0, 1) in bf16, conv taps
+    0.5 N(0, 1), beta = sigmoid(N(0, 1)), g = -softplus(N(0, 1)), initial
+    states init_std N(0, 1)); returns (us per call, tokens/s, prep us, carry us)."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    T, N = int(sum(lengths)), len(lengths)
+    bf = torch.bfloat16
+    rn = lambda *shape: torch.randn(*shape, generator=gen, device=dev, dtype=torch.float32)
+    q, k = rn(T, h_k, d).to(bf), rn(T, h_k, d).to(bf)
+    v = rn(T, h_v, d).to(bf)
+    beta = torch.sigmoid(rn(T, h_v))
+    g = -torch.nn.functional.softplus(rn(T, h_v))
+    C = 2 * h_k * d + h_v * d
+    w = (0.5 * rn(C, 4)).to(bf)
+    h0 = init_std * rn(N, h_v, d, d) if init_std else None
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32), device=dev)
+    o = torch.empty((T, h_v, d), dtype=torch.float32, device=dev)
+    fs = torch.empty((N, h_v, d, d), dtype=torch.float32, device=dev)
+    prob = gdn.binding.make_problem(N, T, h_k, h_v, d, d, gdn.GDN_BF16, gdn.GDN_F32)
+    ws = torch.empty(gdn.binding.gdn_prefill_workspace_bytes(prob), dtype=torch.uint8, device=dev)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+
+    def call(e=None):
+        gdn.gdn_prefill_varlen(q, k, v, g, beta, cu, conv_weight=w, initial_state=h0, out=o, final_state_out=fs,
+                               output_conv_state=False, workspace=ws, validate=False, events=e)
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    for e in evs:
+        call(e)
+    torch.cuda.synchronize()
+    us = float(np.mean([e[0].elapsed_time(e[3]) for e in evs])) * 1e3
+    prep = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e3
+    carry = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e3
+    return us, T / (us * 1e-6), prep, carry
+
+
 def measured_traffic(kernel):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
     None when the kernel's sources changed since the counters were taken."""
@@ -129,6 +171,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-extra-configs", action="store_true",
+                    help="skip the other prefill geometries (packed varlen batch, long single sequence)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also time a plain 1 GiB device-to-device copy (the reference for measured "
                          "HBM bandwidth and for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -142,7 +186,8 @@ def main():
     import torch
     import gateddeltanet_chunked_delta_amd as gdn
     from gateddeltanet_chunked_delta_amd.inputs import (Geometry, conv_state_pool, conv_weights, decode_inputs,
-                                                        multi_decode_inputs, prefill_inputs, state_pool)
+                                                        multi_decode_inputs, prefill_inputs, state_pool,
+                                                        uniform_lengths)
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -324,6 +369,26 @@ def main():
                   file=sys.stderr, flush=True)
             del mpools, mcpools
         result["decode_multi"] = mres
+
+    if not args.no_extra_configs:
+        extra = {}
+        lens = uniform_lengths(2, 60, 1, 8192)
+        print(f"[bench] packed varlen: 60 sequences, {int(lens.sum())} tokens, h_k=16 h_v=48", file=sys.stderr,
+              flush=True)
+        us, tps, pr, ca = extra_prefill(gdn, torch, dev, lens, 16, 48, 128, 0.02, 5, 2)
+        extra["packed_varlen_60seq_hk16_hv48"] = {
+            "workload": f"60 sequences, lengths uniform 1..8192 (seeded, {int(lens.sum())} tokens), h_k=16, "
+                        "h_v=48, d=128, bf16 q/k/v, fp32 initial states 0.02 N(0,1), conv4+SiLU+L2",
+            "us_per_call": us, "tokens_per_s": tps, "prep_kernel_us": pr, "carry_kernel_us": ca}
+        print(f"[bench] packed varlen: {us:.0f} us/call, {tps / 1e6:.1f} M tokens/s", file=sys.stderr, flush=True)
+        us, tps, pr, ca = extra_prefill(gdn, torch, dev, [32768], 16, 32, 128, 0.0, 5, 4)
+        extra["single_sequence_32768_hk16_hv32"] = {
+            "workload": "one sequence of 32768 tokens, h_k=16, h_v=32, d=128, bf16 q/k/v, zero initial state, "
+                        "conv4+SiLU+L2 (a chain of 512 chunks)",
+            "us_per_call": us, "tokens_per_s": tps, "prep_kernel_us": pr, "carry_kernel_us": ca}
+        print(f"[bench] 32768-token sequence: {us:.0f} us/call, {tps / 1e6:.1f} M tokens/s", file=sys.stderr,
+              flush=True)
+        result["other_prefill_configs"] = extra
 
     if args.copy_calibration:
         nbytes = 1 << 30
