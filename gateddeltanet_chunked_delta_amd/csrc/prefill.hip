@@ -802,11 +802,13 @@ struct CarrySmem {
 };
 
 // Byte offset, in the V region, of piece p (0..3: D k-step 0 hi, lo, k-step 1
-// hi, lo) of lane l of column block w: rows 16 p + l/4, bytes [64 w, 64 w + 64)
-// of the row, which hold exactly V's columns [16 w, 16 w + 16).
+// hi, lo) of lane l of column block w: row 16 p + l % 16, 16 bytes at 16 (l/16)
+// within bytes [64 w, 64 w + 64) of the row, which hold exactly V's columns
+// [16 w, 16 w + 16).  Lanes 0-15 of one access take 16 rows (row pitch 68
+// words), so their 16-byte pieces fall on distinct banks.
 template <int PV>
 __device__ __forceinline__ int dop_offset(int w, int piece, int l) {
-    return (16 * piece + (l >> 2)) * (PV * 4) + 64 * w + 16 * (l & 3);
+    return (16 * piece + (l & 15)) * (PV * 4) + 64 * w + 16 * (l >> 4);
 }
 
 template <int DK, int DV, typename TIn, typename TOut>
@@ -1075,10 +1077,13 @@ __global__ void __launch_bounds__(kCarryThreads, 1) carry_kernel(const PrefillPa
 #pragma unroll
             for (int i = 0; i < NTP; i++) *reinterpret_cast<u32x4_t*>(tp + tpo[i]) = ptp[i];
             scal[ht] = psc;
+            // 16-byte stores (scalar ones collided 8-way on the banks)
 #pragma unroll
             for (int i = 0; i < VRPB; i++)
 #pragma unroll
-                for (int e = 0; e < VEC; e++) Vf[(vrow0 + i) * PV + vg * VEC + e] = vy[i][e];
+                for (int e = 0; e < VEC; e += 4)
+                    *reinterpret_cast<float4*>(Vf + (vrow0 + i) * PV + vg * VEC + e) =
+                        make_float4(vy[i][e], vy[i][e + 1], vy[i][e + 2], vy[i][e + 3]);
             lds_barrier();
             if (j + 1 < nch) fetch(j + 1);
 
