@@ -54,12 +54,14 @@ __device__ __forceinline__ float wave_sum(float x) {
 // the history after token j (the newest 3 raw inputs) is written to entry
 // wslot(j) when that is >= 0.  The history is held in registers, so any
 // entry may be both read and written.  out[j * stride] receives token j.
-// (Loading all m inputs ahead of the stores measured slower: the register
-// array costs the m-token kernel its second resident workgroup per CU.)
+// The inputs, the taps and the pool do not overlap (the caller checks that o
+// and the inputs are apart; the pool is neither), so the compiler may issue
+// the next token's input load ahead of this token's history stores.
 template <typename TIn, typename WSlot>
-__device__ __forceinline__ void conv_tokens(const TIn* cw, const TIn* cb, TIn* cs, int64_t C, int64_t ch,
-                                            int rslot, WSlot wslot, const TIn* x, int64_t xstride, int m,
-                                            float* out, int stride) {
+__device__ __forceinline__ void conv_tokens(const TIn* __restrict__ cw, const TIn* __restrict__ cb,
+                                            TIn* __restrict__ cs, int64_t C, int64_t ch, int rslot, WSlot wslot,
+                                            const TIn* __restrict__ x, int64_t xstride, int m, float* out,
+                                            int stride) {
     const TIn* hist = cs + (int64_t(rslot) * C + ch) * 3;
     TIn h0 = hist[0], h1 = hist[1], h2 = hist[2];
     const float w0 = Elem<TIn>::get(cw + ch * 4 + 0), w1 = Elem<TIn>::get(cw + ch * 4 + 1);

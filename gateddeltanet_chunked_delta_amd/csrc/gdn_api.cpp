@@ -77,8 +77,14 @@ gdn_status decode(const gdn_problem* p, int32_t m, const void* q, const void* k,
                         range_of(conv_w, p->conv_width == 4 ? C * 4 * eb : 0),
                         range_of(conv_b, p->conv_width == 4 ? C * eb : 0),
                         range_of(state_indices, T * 4), range_of(num_accepted, N * 4)};
-    for (const Range& r : in)
+    // The pools are read and written while the inputs are read: no input may
+    // reach a pool's first byte (the pool sizes are not known here).
+    const Range pools[] = {range_of(state_pool, 1), range_of(conv_state_pool, 1)};
+    for (const Range& r : in) {
         if (overlaps(ro, r)) return GDN_ERR_ALIAS;
+        for (const Range& pr : pools)
+            if (overlaps(pr, r)) return GDN_ERR_ALIAS;
+    }
     if (reinterpret_cast<uintptr_t>(o) == reinterpret_cast<uintptr_t>(state_pool) ||
         (conv_state_pool && reinterpret_cast<uintptr_t>(o) == reinterpret_cast<uintptr_t>(conv_state_pool)))
         return GDN_ERR_ALIAS;

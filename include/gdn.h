@@ -229,7 +229,9 @@ gdn_status gdn_prefill_varlen_pooled(const gdn_problem* p,
  *
  * p->total_tokens must equal p->num_seqs.  Each slot is computed alone, so
  * results do not depend on N or on the other slots.  Supported: d_k, d_v in
- * {64, 128}, any qkv dtype.
+ * {64, 128}, any qkv dtype.  The pools must not overlap q, k, v, g, beta,
+ * conv_w, conv_b, state_indices or o (GDN_ERR_ALIAS when an input or o
+ * covers a pool's first byte; other overlaps are not detected).
  */
 gdn_status gdn_decode_step(const gdn_problem* p,
                            const void* q, const void* k, const void* v,
