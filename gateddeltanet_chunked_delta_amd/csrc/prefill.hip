@@ -22,6 +22,8 @@
 //   chunk_map_kernel  chunk_base[n] = chunks before sequence n
 //   slot_map_kernel   per chunk slot: its sequence, first token and length
 //   order_kernel      sequences by descending chunk count (longest first)
+//   (small_map_kernel: the three maps in one workgroup for up to 512
+//   sequences and 65536 chunk slots)
 //   prep_kernel       per (chunk, key head): conv(4) + SiLU + L2 norm of q
 //                     and k; K K^T and Q K^T; then per value head of the
 //                     group: the decays, T and P.  Writes split images (hi
@@ -318,6 +320,66 @@ __global__ void __launch_bounds__(256) order_kernel(const int32_t* __restrict__ 
         rank += (cj > ci) || (cj == ci && j < i);
     }
     order[rank] = i;
+}
+
+// The three maps above in one workgroup, for problems small enough that one
+// workgroup's loops are short (kSmallMapSeqs sequences, kSmallMapSlots chunk
+// slots): saves two launches.  Same integer results as the three kernels.
+constexpr int kSmallMapSeqs = 512;
+constexpr int64_t kSmallMapSlots = 65536;
+__global__ void __launch_bounds__(256) small_map_kernel(const int32_t* __restrict__ cu, int32_t n,
+                                                         int32_t* __restrict__ base, int32_t* __restrict__ order,
+                                                         int4* __restrict__ desc) {
+    __shared__ int32_t s[256];
+    __shared__ int32_t sb[kSmallMapSeqs + 1];
+    const int t = threadIdx.x;
+    // chunk_base: the same tile scan as chunk_map_kernel, kept in LDS too
+    int32_t carry = 0;
+    for (int t0 = 0; t0 < n; t0 += 256) {
+        const int i = t0 + t;
+        const int32_t c = i < n ? int32_t((int64_t(cu[i + 1]) - cu[i] + kChunk - 1) / kChunk) : 0;
+        s[t] = c;
+        __syncthreads();
+        for (int o = 1; o < 256; o <<= 1) {
+            const int32_t x = t >= o ? s[t - o] : 0;
+            __syncthreads();
+            s[t] += x;
+            __syncthreads();
+        }
+        if (i < n) {
+            base[i] = carry + s[t] - c;
+            sb[i] = carry + s[t] - c;
+        }
+        carry += s[255];
+        __syncthreads();
+    }
+    if (t == 0) {
+        base[n] = carry;
+        sb[n] = carry;
+    }
+    __syncthreads();
+    // order: rank by descending chunk count, ties by index
+    for (int i = t; i < n; i += 256) {
+        const int32_t ci = sb[i + 1] - sb[i];
+        int rank = 0;
+        for (int j = 0; j < n; j++) {
+            const int32_t cj = sb[j + 1] - sb[j];
+            rank += (cj > ci) || (cj == ci && j < i);
+        }
+        order[rank] = i;
+    }
+    // slot descriptors
+    for (int64_t sl = t; sl < carry; sl += 256) {
+        int lo = 0, hi = n - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (sb[mid] <= sl) lo = mid;
+            else hi = mid - 1;
+        }
+        const int32_t bos = cu[lo], c0 = bos + int32_t(sl - sb[lo]) * kChunk;
+        const int32_t left = cu[lo + 1] - c0;
+        desc[sl] = int4{lo, c0, left < kChunk ? left : kChunk, bos};
+    }
 }
 
 // ---------------------------------------------------------------- prep: q|k prologue and chunk-local terms
@@ -1275,17 +1337,25 @@ hipError_t launch_prefill(const PrefillParams& p, int d_k, int d_v, int qkv_dtyp
         }
         return hipSuccess;
     }
-    chunk_map_kernel<<<dim3(1), dim3(256), 0, stream>>>(p.cu_seqlens, p.num_seqs, p.chunk_base);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    order_kernel<<<dim3((p.num_seqs + 255) / 256), dim3(256), 0, stream>>>(p.cu_seqlens, p.num_seqs, p.order);
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    if (p.slots > 0) {
-        slot_map_kernel<<<dim3(unsigned((p.slots + 255) / 256)), dim3(256), 0, stream>>>(
-            p.cu_seqlens, p.num_seqs, p.chunk_base, reinterpret_cast<int4*>(p.slot_desc));
+    hipError_t err;
+    if (p.num_seqs <= kSmallMapSeqs && p.slots <= kSmallMapSlots) {
+        small_map_kernel<<<dim3(1), dim3(256), 0, stream>>>(p.cu_seqlens, p.num_seqs, p.chunk_base, p.order,
+                                                            reinterpret_cast<int4*>(p.slot_desc));
         err = hipGetLastError();
         if (err != hipSuccess) return err;
+    } else {
+        chunk_map_kernel<<<dim3(1), dim3(256), 0, stream>>>(p.cu_seqlens, p.num_seqs, p.chunk_base);
+        err = hipGetLastError();
+        if (err != hipSuccess) return err;
+        order_kernel<<<dim3((p.num_seqs + 255) / 256), dim3(256), 0, stream>>>(p.cu_seqlens, p.num_seqs, p.order);
+        err = hipGetLastError();
+        if (err != hipSuccess) return err;
+        if (p.slots > 0) {
+            slot_map_kernel<<<dim3(unsigned((p.slots + 255) / 256)), dim3(256), 0, stream>>>(
+                p.cu_seqlens, p.num_seqs, p.chunk_base, reinterpret_cast<int4*>(p.slot_desc));
+            err = hipGetLastError();
+            if (err != hipSuccess) return err;
+        }
     }
     if (qkv_dtype == 1)
         err = out_dtype == 1 ? run_dtype<bf16_t, bf16_t>(p, d_k, d_v, stream, events)
