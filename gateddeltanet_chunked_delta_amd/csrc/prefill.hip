@@ -838,7 +838,8 @@ template <> __device__ __forceinline__ void buf_put<bf16_t>(__amdgpu_buffer_rsrc
 //   B:      main: K H, R, D = T R; D's split operand goes to LDS (over this
 //           wave's own columns of V, which only it reads).  helpers: Q H.
 //   C:      main: the state update.  helpers: P D and the output rows, then
-//           conv + SiLU of the next chunk's v rows (kept in registers).
+//           conv + SiLU of half of the next chunk's v rows (the other half
+//           while staging).
 // Each role issues its part of the next chunk's loads as phase B starts.
 // The two roles run separate loops with the same barriers, so their register
 // live ranges do not overlap.
@@ -1115,20 +1116,25 @@ __global__ void __launch_bounds__(kCarryThreads, 1) carry_kernel(const PrefillPa
         }
         // conv(4) + SiLU of this thread's v rows of chunk j (zero past its end),
         // computed from the raw rows during the previous chunk's phase C
+        // Half of the rows (h = 1) are convolved during the previous chunk's
+        // phase C, the other half (h = 0) while staging, which balances both
+        // roles at both barriers.
+        constexpr int VH = VRPB / 2;
+        static_assert(VRPB % 2 == 0, "v rows in two halves");
         float vy[VRPB][VEC];
-        auto conv_v = [&](int j) {
+        auto conv_v = [&](int j, int h) {
             const int64_t c0 = bos + int64_t(j) * kChunk;
             const int L = int(eos - c0 < kChunk ? eos - c0 : kChunk);
-            float y[VRPB][VEC];
-            conv_rows<TIn, VRPB>(conv, xv, vwp, vbias, y);
+            float y[VH][VEC];
+            conv_rows<TIn, VH>(conv, *reinterpret_cast<const u32x4_t(*)[VH + 3]>(xv + h * VH), vwp, vbias, y);
 #pragma unroll
-            for (int i = 0; i < VRPB; i++)
+            for (int i = 0; i < VH; i++)
 #pragma unroll
-                for (int e = 0; e < VEC; e++) vy[i][e] = (vrow0 + i < L) ? y[i][e] : 0.0f;
+                for (int e = 0; e < VEC; e++) vy[h * VH + i][e] = (vrow0 + h * VH + i < L) ? y[i][e] : 0.0f;
         };
         if (nch > 0) {
             fetch(0);
-            conv_v(0);
+            conv_v(0, 1);
         }
 
         for (int j = 0; j < nch; j++) {
@@ -1139,6 +1145,7 @@ __global__ void __launch_bounds__(kCarryThreads, 1) carry_kernel(const PrefillPa
 #pragma unroll
             for (int i = 0; i < NTP; i++) *reinterpret_cast<u32x4_t*>(tp + tpo[i]) = ptp[i];
             scal[ht] = psc;
+            conv_v(j, 0);
             // 16-byte stores (scalar ones collided 8-way on the banks)
 #pragma unroll
             for (int i = 0; i < VRPB; i++)
@@ -1201,7 +1208,7 @@ __global__ void __launch_bounds__(kCarryThreads, 1) carry_kernel(const PrefillPa
                     }
                 }
             }
-            if (j + 1 < nch) conv_v(j + 1);
+            if (j + 1 < nch) conv_v(j + 1, 1);
             lds_barrier();
         }
     }
