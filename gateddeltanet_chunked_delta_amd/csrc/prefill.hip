@@ -388,7 +388,9 @@ constexpr int kPrepThreads = 512;  // 8 waves: two groups of 4 take two value he
 
 template <int DK, int VEC>
 struct PrepSmem {
-    static constexpr int kPitchK = DK + 8;      // K, Q rows: [token][d_k] (16-bit)
+    // K, Q rows: [token][d_k] (16-bit); 72-word rows for d_k = 128 keep the
+    // Gram fragment reads free of bank conflicts (68-word rows halved their rate)
+    static constexpr int kPitchK = DK == 128 ? DK + 16 : DK + 8;
     static constexpr int kPitchF = kChunk + 4;  // [token][token] (fp32)
     static constexpr int kPitchD = 20;          // diagonal inverse blocks: [4][16][kPitchD]
     static constexpr int kNG = 2 * (DK / VEC);  // q|k 16-byte groups per row
@@ -847,8 +849,13 @@ constexpr int kCarryThreads = 512;
 
 template <int DK>
 struct CarrySmem {
-    static constexpr int kPitchK = DK + 8;      // K, Q image rows (16-bit)
-    static constexpr int kPitchT = kChunk + 8;  // T, P image rows (16-bit)
+    // K, Q image rows (16-bit).  Fragment reads (16 rows, one 16-byte piece
+    // each) measured bank-conflict-free on gfx950 with 72-word rows (d_k = 128)
+    // and at half speed with the 68-word rows of d_k + 8.
+    static constexpr int kPitchK = DK == 128 ? DK + 16 : DK + 8;
+    // T, P image rows (16-bit): 64 columns unpadded, 16-byte pieces swizzled
+    // by row (tp_off), which measured conflict-free where 72-column rows did not
+    static constexpr int kPitchT = kChunk;
     static constexpr int kPitchV = kDvs + 4;    // V rows (fp32); D's operand afterwards
     static constexpr int KS = DK / 32;
     static constexpr size_t szKQ = size_t(kChunk) * kPitchK * sizeof(uint16_t);
@@ -863,6 +870,21 @@ struct CarrySmem {
     static_assert(oTP % 16 == 0 && oV % 16 == 0 && oScal % 16 == 0 && oHB % 16 == 0, "16-byte aligned regions");
     static_assert(kPitchV * 4 % 16 == 0 && 4 * 16 * (kPitchV * 4) >= 4 * 64 * 16, "D operand fits V's rows");
 };
+
+// Element offset of (row, col) in a T|P plane of the carry kernel: 64-column
+// rows whose 16-byte pieces are XOR-swizzled by row % 8.
+__device__ __forceinline__ int tp_off(int row, int col) {
+    return row * kChunk + ((((col >> 3) ^ row) & 7) << 3) + (col & 7);
+}
+template <typename E>
+__device__ __forceinline__ SFrag<E> tp_frag(const E* hi, const E* lo, int row, int k) {
+    typedef typename OpVec<E>::v8 V8;
+    const int o = tp_off(row, k);
+    SFrag<E> f;
+    f.hi = *reinterpret_cast<const V8*>(hi + o);
+    f.lo = *reinterpret_cast<const V8*>(lo + o);
+    return f;
+}
 
 // Byte offset, in the V region, of piece p (0..3: D k-step 0 hi, lo, k-step 1
 // hi, lo) of lane l of column block w: row 16 p + l % 16, 16 bytes at 16 (l/16)
@@ -1008,7 +1030,7 @@ __global__ void __launch_bounds__(kCarryThreads, 1) carry_kernel(const PrefillPa
                     float4_t hh = kZero4, xx = kZero4;
 #pragma unroll
                     for (int ks = 0; ks <= tb / 2; ks++)
-                        mma3(hh, xx, lds_sfrag(Thi, Tlo, PT, 16 * tb + lr, 32 * ks + 8 * lg), rb[ks]);
+                        mma3(hh, xx, tp_frag(Thi, Tlo, 16 * tb + lr, 32 * ks + 8 * lg), rb[ks]);
                     dd[tb] = combine<E>(hh, xx);
                 }
             }
@@ -1103,7 +1125,7 @@ __global__ void __launch_bounds__(kCarryThreads, 1) carry_kernel(const PrefillPa
         for (int i = ht; i < 4 * 2 * 16 * 2; i += HT) {
             const int plane = i >> 6, blk = (i >> 5) & 1, rr = (i >> 1) & 15, half = i & 1;
             const int r = 32 * blk + rr, c = 32 * blk + 16 + 8 * half;
-            *reinterpret_cast<u32x4_t*>(tp + plane * kChunk * PT + r * PT + c) = u32x4_t{0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4_t*>(tp + plane * kChunk * PT + tp_off(r, c)) = u32x4_t{0u, 0u, 0u, 0u};
         }
         // LDS offsets of this thread's T|P pieces (the same every chunk)
         int tpo[NTP];
@@ -1112,7 +1134,7 @@ __global__ void __launch_bounds__(kCarryThreads, 1) carry_kernel(const PrefillPa
             const int pc = ht + HT * i;
             int r, c8;
             TriPack::locate(pc % TriPack::kPieces, r, c8);
-            tpo[i] = (pc / TriPack::kPieces) * kChunk * PT + r * PT + 8 * c8;
+            tpo[i] = (pc / TriPack::kPieces) * kChunk * PT + tp_off(r, 8 * c8);
         }
         // conv(4) + SiLU of this thread's v rows of chunk j (zero past its end),
         // computed from the raw rows during the previous chunk's phase C
@@ -1198,7 +1220,7 @@ __global__ void __launch_bounds__(kCarryThreads, 1) carry_kernel(const PrefillPa
                     float4_t phh = kZero4, phx = kZero4;
 #pragma unroll
                     for (int ks = 0; ks <= tb / 2; ks++)
-                        mma3(phh, phx, lds_sfrag(Phi, Plo, PT, 16 * tb + lr, 32 * ks + 8 * lg), db[ks]);
+                        mma3(phh, phx, tp_frag(Phi, Plo, 16 * tb + lr, 32 * ks + 8 * lg), db[ks]);
                     const float4_t pd = combine<E>(phh, phx);
 #pragma unroll
                     for (int e = 0; e < 4; e++) {
