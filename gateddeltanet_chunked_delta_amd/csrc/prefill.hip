@@ -889,8 +889,10 @@ __device__ __forceinline__ SFrag<E> tp_frag(const E* hi, const E* lo, int row, i
 // Byte offset, in the V region, of piece p (0..3: D k-step 0 hi, lo, k-step 1
 // hi, lo) of lane l of column block w: row 16 p + l % 16, 16 bytes at 16 (l/16)
 // within bytes [64 w, 64 w + 64) of the row, which hold exactly V's columns
-// [16 w, 16 w + 16).  Lanes 0-15 of one access take 16 rows (row pitch 68
-// words), so their 16-byte pieces fall on distinct banks.
+// [16 w, 16 w + 16).  Lanes 0-15 of one access take 16 rows (measured fewer
+// bank conflicts in the kernel than 4 lanes per row; 16 rows of 68 words
+// still run at half the conflict-free rate, but V's row pitch serves its own
+// reads without conflicts).
 template <int PV>
 __device__ __forceinline__ int dop_offset(int w, int piece, int l) {
     return (16 * piece + (l & 15)) * (PV * 4) + 64 * w + 16 * (l >> 4);
