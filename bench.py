@@ -12,7 +12,8 @@ the chunk-local kernel is reported beside it.  The decode half of the metric
 (256 slots x 32 value heads, d = 128, conv update, 512 MiB fp32 state pool
 updated in place, 100 consecutive steps over 4 pools in rotation) is timed
 separately and reported under "decode", and the multi-token (speculative)
-decode of 4 tokens per slot under "decode_multi"; the packed varlen batch (60
+decode of 4 tokens per slot under "decode_multi"; the same prefill with bf16
+outputs under "prefill_bf16_out"; the packed varlen batch (60
 sequences, h_v = 48) and a 32768-token sequence are timed under
 "other_prefill_configs".  One JSON line is printed.
 """
@@ -273,6 +274,28 @@ def main():
                  "TFLOP/s": pflops / avg_call_s / 1e12},
         "mfma_util": pflops / avg_call_s / (MFMA_F16_PEAK_TFLOPS * 1e12),
     }
+
+    # The same workload with bf16 outputs (o rounded once, to nearest even)
+    o16 = torch.empty((T, 32, 128), dtype=bf, device=dev)
+
+    def step16(events=None):
+        gdn.gdn_prefill_varlen(q, k, v, g, beta, cu, conv_weight=w, out=o16, final_state_out=fs,
+                               conv_state_out=cso, workspace=ws, validate=False, events=events,
+                               out_dtype=torch.bfloat16)
+
+    for i in range(20):
+        step16()
+    torch.cuda.synchronize()
+    for e in evs:
+        step16(e)
+    torch.cuda.synchronize()
+    c16 = float(np.mean([e[0].elapsed_time(e[3]) for e in evs])) * 1e3
+    b16, _ = prefill_algorithmic(T, B, 16, 32, 128, out_bytes=2)
+    result["prefill_bf16_out"] = {"us_per_call": c16, "tokens_per_s": T / (c16 * 1e-6),
+                                  "carry_kernel_us": float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e3,
+                                  "algorithmic_bytes": b16, "GB/s": b16 / (c16 * 1e-6) / 1e9}
+    print(f"[bench] prefill, bf16 o: {c16:.1f} us/call (events)", file=sys.stderr, flush=True)
+    del o16
 
     if not args.no_decode:
         N = 256

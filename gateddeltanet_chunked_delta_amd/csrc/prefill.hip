@@ -819,9 +819,6 @@ template <typename T> __device__ __forceinline__ void buf_put(__amdgpu_buffer_rs
 template <> __device__ __forceinline__ void buf_put<float>(__amdgpu_buffer_rsrc_t r, int off, float x) {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, off, 0, 0);
 }
-template <> __device__ __forceinline__ void buf_put<bf16_t>(__amdgpu_buffer_rsrc_t r, int off, float x) {
-    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(x), r, off, 0, 0);
-}
 
 // ---------------------------------------------------------------- carry: the state chain
 
@@ -1224,11 +1221,32 @@ __global__ void __launch_bounds__(kCarryThreads, 1) carry_kernel(const PrefillPa
                     for (int ks = 0; ks <= tb / 2; ks++)
                         mma3(phh, phx, tp_frag(Phi, Plo, 16 * tb + lr, 32 * ks + 8 * lg), db[ks]);
                     const float4_t pd = combine<E>(phh, phx);
+                    float val[4];
 #pragma unroll
-                    for (int e = 0; e < 4; e++) {
-                        const int r = 16 * tb + 4 * lg + e;
-                        buf_put<TOut>(orsrc, ((r * p.h_v + h) * DV + col) * int(sizeof(TOut)),
-                                      p.scale * (eqh[tb][e] + pd[e]));
+                    for (int e = 0; e < 4; e++) val[e] = p.scale * (eqh[tb][e] + pd[e]);
+                    if constexpr (sizeof(TOut) == 2) {
+                        // Lanes lr and lr ^ 1 hold columns 2c and 2c + 1 of the same
+                        // rows: the even lane takes rows 4 lg + 0, 1 and the odd lane
+                        // rows 4 lg + 2, 3 of both columns, converted two at a time
+                        // (round to nearest even) and stored as 4-byte pairs.
+                        const bool odd = (lr & 1) != 0;
+                        const float q0 = __shfl_xor(odd ? val[0] : val[2], 1);
+                        const float q1 = __shfl_xor(odd ? val[1] : val[3], 1);
+                        const float2_t a = odd ? float2_t{q0, val[2]} : float2_t{val[0], q0};
+                        const float2_t b = odd ? float2_t{q1, val[3]} : float2_t{val[1], q1};
+                        const int r = 16 * tb + 4 * lg + (odd ? 2 : 0), c2 = col & ~1;
+                        const bf16x2_t pa = __builtin_convertvector(a, bf16x2_t);
+                        const bf16x2_t pb = __builtin_convertvector(b, bf16x2_t);
+                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, pa), orsrc,
+                                                              ((r * p.h_v + h) * DV + c2) * 2, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, pb), orsrc,
+                                                              (((r + 1) * p.h_v + h) * DV + c2) * 2, 0, 0);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; e++) {
+                            const int r = 16 * tb + 4 * lg + e;
+                            buf_put<TOut>(orsrc, ((r * p.h_v + h) * DV + col) * int(sizeof(TOut)), val[e]);
+                        }
                     }
                 }
             }
