@@ -175,8 +175,10 @@ def main():
     ap.add_argument("--no-extra-configs", action="store_true",
                     help="skip the other prefill geometries (packed varlen batch, long single sequence)")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="also time a plain 1 GiB device-to-device copy (the reference for measured "
-                         "HBM bandwidth and for scaling FETCH_SIZE / WRITE_SIZE counters)")
+                    help="time the plain 1 GiB device-to-device copy (the measured HBM reference) even "
+                         "with --no-decode")
+    ap.add_argument("--no-copy-calibration", action="store_true",
+                    help="skip the 1 GiB copy that the decode legs are compared with")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -413,7 +415,7 @@ def main():
               flush=True)
         result["other_prefill_configs"] = extra
 
-    if args.copy_calibration:
+    if (args.copy_calibration or not args.no_decode) and not args.no_copy_calibration:
         nbytes = 1 << 30
         src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
@@ -428,8 +430,15 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / reps
+        copy_gbs = 2 * nbytes / (us * 1e-6) / 1e9
         result["copy_calibration"] = {"bytes_read": nbytes, "bytes_written": nbytes, "us_per_copy": us,
-                                      "GB/s": 2 * nbytes / (us * 1e-6) / 1e9}
+                                      "GB/s": copy_gbs}
+        # the decode legs against the measured copy as well as the datasheet peak
+        if "decode" in result:
+            result["decode"]["roofline"]["frac_of_measured_copy"] = result["decode"]["GB/s"] / copy_gbs
+        for leg in result.get("decode_multi", {}).values():
+            if isinstance(leg, dict):
+                leg["frac_of_measured_copy"] = leg["GB/s"] / copy_gbs
         print(f"[bench] copy 1 GiB: {us:.1f} us, {2 * nbytes / (us * 1e-6) / 1e9:.0f} GB/s", file=sys.stderr, flush=True)
         del src, dst
 
