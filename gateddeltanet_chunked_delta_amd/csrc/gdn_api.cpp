@@ -59,6 +59,7 @@ gdn_status decode(const gdn_problem* p, int32_t m, const void* q, const void* k,
     const int64_t N = p->num_seqs;
     if (m < 1 || m > gdn::kDecodeMaxTokens) return m < 1 ? GDN_ERR_SHAPE : GDN_ERR_UNSUPPORTED;
     if (p->total_tokens != N * m) return GDN_ERR_SHAPE;
+    if (N * p->h_k >= (int64_t(1) << 31)) return GDN_ERR_SHAPE;  // one workgroup per (slot, key head)
     if (N > 0 && (!q || !k || !v || !g || !beta || !o || !state_pool)) return GDN_ERR_NULL;
     if (p->conv_width == 4 && (!conv_w || !conv_state_pool)) return GDN_ERR_NULL;
     if (!gdn::decode_supported(p->d_k, p->d_v, p->qkv_dtype, p->out_dtype)) return GDN_ERR_UNSUPPORTED;

@@ -181,6 +181,8 @@ def test_decode_rejects_bad_arguments(lib):
     assert _decode(lib, _prob(num_seqs=4, total_tokens=4, conv_width=0), o=1) == -7
     assert _decode(lib, _prob(num_seqs=4, total_tokens=4, conv_width=0), o=6) == -7  # o == state pool
     assert _decode(lib, _prob(num_seqs=4, total_tokens=4, conv_width=0), v=6) == -7  # v over the state pool
+    big = _prob(num_seqs=1 << 24, total_tokens=1 << 24, conv_width=0, h_k=256, h_v=256)
+    assert _decode(lib, big) == -2                                                   # grid of 2^32 workgroups
     assert _decode(lib, _prob(num_seqs=4, total_tokens=4), cw=9, cs=2) == -7         # k over the conv pool
     assert _decode(lib, _prob(num_seqs=0, total_tokens=0, conv_width=0), q=None, k=None, v=None, g=None,
                    b=None, pool=None, o=None) == 0
