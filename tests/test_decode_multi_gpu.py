@@ -7,7 +7,7 @@ import torch
 
 from gateddeltanet_chunked_delta_amd import binding
 from gateddeltanet_chunked_delta_amd.inputs import (Geometry, conv_state_pool, conv_weights, multi_decode_inputs,
-                                                    state_pool)
+                                                    prefill_inputs, state_pool)
 from tests.gpu_util import TOL, TORCH_DT, dev, rel_err
 
 pytestmark = pytest.mark.gpu
@@ -184,3 +184,56 @@ def test_decode_multi_binding_validation():
     with pytest.raises(ValueError):
         binding.gdn_decode_multi(*args, pool, state_indices=torch.tensor([[0, 1, 8], [2, 3, 4]], dtype=torch.int32,
                                                                          device="cuda"))
+
+
+def test_pooled_prefill_then_speculative_decode(oracle_mod):
+    """A serving flow over one pool: a pooled prefill of a prompt per slot, then
+    two 3-token decode calls keeping every token's state; after the first call
+    slot 0 accepts 2 tokens and slot 1 all 3, and the second call resumes from
+    those entries.  The outputs and final states equal the oracle's prefill of
+    each slot's accepted token stream (the prompt, then the accepted tokens)."""
+    geom = Geometry(2, 4, 128, 128)
+    dt = torch.bfloat16
+    lengths = [70, 129]
+    N, m = 2, 3
+    P = 1 + N * m  # entry 0 unused, slot n uses entries 1 + n m .. n m + m
+    x = prefill_inputs(66, lengths, geom, "bf16", initial_state_std=0.02, conv_state=True)
+    w_np = x.conv_w
+    pool = torch.zeros((P, 4, 128, 128), dtype=torch.float32, device="cuda")
+    cpool = torch.zeros((P, geom.channels, 3), dtype=dt, device="cuda")
+    idx = np.array([[1, 2, 3], [4, 5, 6]], dtype=np.int32)
+    start = idx[:, 0].astype(np.int64)
+    pool[start] = dev(x.initial_state)
+    cpool[start] = dev(x.conv_state_in, dt)
+    binding.gdn_prefill_varlen_pooled(dev(x.q, dt), dev(x.k, dt), dev(x.v, dt), dev(x.g), dev(x.beta),
+                                      torch.from_numpy(x.cu_seqlens.astype(np.int32)).cuda(), pool,
+                                      state_indices=dev(idx[:, 0].copy(), torch.int32), conv_weight=dev(w_np, dt),
+                                      conv_state_pool=cpool)
+    calls = [multi_decode_inputs(66, c, N, m, geom, "bf16") for c in range(2)]
+    accepted = [np.array([1, 1], dtype=np.int32), np.array([2, 3], dtype=np.int32)]  # read entry per call
+    outs = []
+    for c in range(2):
+        y = calls[c]
+        outs.append(binding.gdn_decode_multi(dev(y.q, dt), dev(y.k, dt), dev(y.v, dt), dev(y.g), dev(y.beta), pool,
+                                             state_indices=dev(idx, torch.int32),
+                                             num_accepted=dev(accepted[c], torch.int32),
+                                             conv_weight=dev(w_np, dt), conv_state_pool=cpool).cpu().numpy())
+    # each slot's stream: prompt, the accepted tokens of call 0, then all of call 1
+    keep0 = accepted[1]  # tokens of call 0 the second call builds on
+    cu = x.cu_seqlens
+    dims = oracle_mod.Dims(2, 4, 128, 128, conv_width=4)
+    for n in range(N):
+        s0 = slice(int(cu[n]), int(cu[n + 1]))
+        a = int(keep0[n])
+        cat = lambda f, pre: np.concatenate([pre[s0], getattr(calls[0], f)[n, :a], getattr(calls[1], f)[n]])
+        q = cat("q", x.q); k = cat("k", x.k); v = cat("v", x.v); g = cat("g", x.g); b = cat("beta", x.beta)
+        L = q.shape[0]
+        ro, rfs, rcs = oracle_mod.prefill(dims, np.array([0, L]), q, k, v, g, b, w_np, None,
+                                          x.conv_state_in[n:n + 1], x.initial_state[n:n + 1])
+        lp = lengths[n]
+        e1 = rel_err(outs[1][n], ro[lp + a:])
+        e0 = rel_err(outs[0][n, :a], ro[lp:lp + a])
+        es = rel_err(pool[int(idx[n, m - 1])].cpu().numpy(), rfs[0])
+        print(f"  slot {n}: rel err call0 o={e0:.3e} call1 o={e1:.3e} state={es:.3e}", flush=True)
+        assert e0 <= TOL["bf16"] and e1 <= TOL["bf16"] and es <= TOL["bf16"]
+        assert np.array_equal(cpool[int(idx[n, m - 1])].float().cpu().numpy(), rcs[0])

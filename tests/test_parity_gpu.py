@@ -173,6 +173,15 @@ def test_many_short_ragged_sequences(oracle_mod):
     _check_prefill(oracle_mod, x)
 
 
+@pytest.mark.parametrize("n_seqs", [512, 513])
+def test_map_paths_at_the_boundary(oracle_mod, n_seqs):
+    """512 sequences take the one-workgroup map kernel, 513 the three map
+    kernels (chunk map, order, slot descriptors); both against the oracle."""
+    lengths = uniform_lengths(45 + n_seqs, n_seqs, 0, 70)
+    x = prefill_inputs(45, lengths, Geometry(1, 1, 64, 64), "bf16", initial_state_std=0.02, conv_state=True)
+    _check_prefill(oracle_mod, x)
+
+
 def test_full_prefill_4x4096_sampled(oracle_mod):
     """4 x 4096 tokens, h_k = 16, h_v = 32, d = 128, bf16: whole-run sanity plus
     oracle parity on sampled (sequence, key head) units."""
