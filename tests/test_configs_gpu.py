@@ -12,6 +12,9 @@ gdn_prefill_varlen over the whole packed batch).
   outputs and final states must be bit-identical across all batchings.
 * Long context: one sequence of 32768 tokens at the same geometry, sampled
   against the oracle.
+* Offsets past 32 bits: a short sequence packed after 540,032 tokens, whose
+  output rows start beyond element 2^31 of o, against the oracle and against
+  a call that holds it alone (bitwise).
 """
 import numpy as np
 import pytest
@@ -105,3 +108,62 @@ def test_long_sequence_32768(oracle_mod):
     o, fs = _run(x)
     assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(fs).all())
     _check_units(oracle_mod, x, o, fs, [(0, 5)], "32768 tokens")
+
+
+def test_offsets_beyond_32_bits(oracle_mod):
+    """A 100-token sequence packed after one of 540,032 tokens (h_k = 16, h_v =
+    32, d = 128, bf16): its output rows start at element 2.2e9 (> 2^31) of o and
+    its K|Q image at byte 8.8e9, so every offset past 32 bits is exercised.  The
+    short sequence (with initial recurrent and conv states) must match the
+    oracle and be bit-identical to a call that holds it alone; the long one's
+    outputs and final state must be finite.  The long sequence's inputs are
+    drawn on the device (q, k, v ~ N(0, 1) in bf16, beta = sigmoid(N(0, 1)),
+    g = -softplus(N(0, 1))); ~36 GB of device memory."""
+    geom = Geometry(16, 32, 128, 128)
+    long_len = 540_032
+    xs = prefill_inputs(61, [100], geom, "bf16", initial_state_std=0.02, conv_state=True)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(61)
+    rn = lambda *shape: torch.randn(*shape, generator=gen, device="cuda", dtype=torch.float32)
+    T = long_len + 100
+    q = torch.empty((T, 16, 128), dtype=BF, device="cuda")
+    k = torch.empty_like(q)
+    v = torch.empty((T, 32, 128), dtype=BF, device="cuda")
+    g = torch.empty((T, 32), dtype=torch.float32, device="cuda")
+    beta = torch.empty_like(g)
+    for lo in range(0, long_len, 1 << 16):
+        hi = min(lo + (1 << 16), long_len)
+        q[lo:hi], k[lo:hi], v[lo:hi] = rn(hi - lo, 16, 128), rn(hi - lo, 16, 128), rn(hi - lo, 32, 128)
+        g[lo:hi] = -torch.nn.functional.softplus(rn(hi - lo, 32))
+        beta[lo:hi] = torch.sigmoid(rn(hi - lo, 32))
+    q[long_len:], k[long_len:], v[long_len:] = dev(xs.q, BF), dev(xs.k, BF), dev(xs.v, BF)
+    g[long_len:], beta[long_len:] = dev(xs.g), dev(xs.beta)
+    C = geom.channels
+    h0 = torch.zeros((2, 32, 128, 128), dtype=torch.float32, device="cuda")
+    h0[1] = dev(xs.initial_state[0])
+    cs0 = torch.zeros((2, C, 3), dtype=BF, device="cuda")
+    cs0[1] = dev(xs.conv_state_in[0], BF)
+    w = dev(xs.conv_w, BF)
+    cu = torch.tensor([0, long_len, T], dtype=torch.int32)
+
+    o, fs, cso = binding.gdn_prefill_varlen(q, k, v, g, beta, cu, conv_weight=w, conv_state=cs0, initial_state=h0)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o[:long_len]).all()) and bool(torch.isfinite(fs[0]).all())
+    o_tail, fs_tail, cso_tail = o[long_len:].cpu().numpy(), fs[1].cpu().numpy(), cso[1].float().cpu().numpy()
+    del o, fs, q, k, v, g, beta
+    torch.cuda.empty_cache()
+
+    o1, fs1, cso1 = binding.gdn_prefill_varlen(
+        dev(xs.q, BF), dev(xs.k, BF), dev(xs.v, BF), dev(xs.g), dev(xs.beta),
+        torch.from_numpy(xs.cu_seqlens.astype(np.int32)), conv_weight=w,
+        conv_state=dev(xs.conv_state_in, BF), initial_state=dev(xs.initial_state))
+    torch.cuda.synchronize()
+    assert np.array_equal(o_tail, o1.cpu().numpy())
+    assert np.array_equal(fs_tail, fs1[0].cpu().numpy())
+    assert np.array_equal(cso_tail, cso1[0].float().cpu().numpy())
+
+    ro, rfs, rcso = oracle_prefill(oracle_mod, xs)
+    eo, ef = rel_err(o_tail, ro), rel_err(fs_tail, rfs[0])
+    print(f"  tail sequence at token {long_len}: rel err o={eo:.3e} final={ef:.3e}", flush=True)
+    assert eo <= TOL["bf16"] and ef <= TOL["bf16"]
+    assert np.array_equal(cso_tail, rcso[0])
