@@ -6,8 +6,8 @@ import pytest
 import torch
 
 from gateddeltanet_chunked_delta_amd import binding
-from gateddeltanet_chunked_delta_amd.inputs import (Geometry, conv_state_pool, conv_weights, multi_decode_inputs,
-                                                    prefill_inputs, state_pool)
+from gateddeltanet_chunked_delta_amd.inputs import (Geometry, conv_state_pool, conv_weights, decode_inputs,
+                                                    multi_decode_inputs, prefill_inputs, state_pool)
 from tests.gpu_util import TOL, TORCH_DT, dev, rel_err
 
 pytestmark = pytest.mark.gpu
@@ -237,3 +237,72 @@ def test_pooled_prefill_then_speculative_decode(oracle_mod):
         print(f"  slot {n}: rel err call0 o={e0:.3e} call1 o={e1:.3e} state={es:.3e}", flush=True)
         assert e0 <= TOL["bf16"] and e1 <= TOL["bf16"] and es <= TOL["bf16"]
         assert np.array_equal(cpool[int(idx[n, m - 1])].float().cpu().numpy(), rcs[0])
+
+
+def test_decode_pool_entries_beyond_32_bits(oracle_mod):
+    """Decode over a 4200-entry state pool (h_v = 32, d = 128: 8.8 GB, entry
+    4096 starts at element 2^31): slots whose entries lie past that point, a
+    skipped slot and a low entry.  Two single-token steps with the conv update
+    are checked against the oracle; those steps and then a 3-token call (each
+    token's state to its own high entry, resume from the accepted one) must
+    give bit for bit what the same calls give on a compact 6-entry pool."""
+    geom = Geometry(16, 32, 128, 128)
+    P, N, m = 4200, 6, 3
+    dt = torch.bfloat16
+    big = np.array([4199, 4097, -1, 4098, 100, 4150], dtype=np.int32)
+    small = np.array([0, 1, -1, 3, 4, 5], dtype=np.int32)
+    pool_np = state_pool(70, N, geom)
+    cpool_np = conv_state_pool(70, N, geom, "bf16")
+    w = dev(conv_weights(70, geom, "bf16"), dt)
+    pool_big = torch.zeros((P, 32, 128, 128), dtype=torch.float32, device="cuda")
+    cpool_big = torch.zeros((P, geom.channels, 3), dtype=dt, device="cuda")
+    for i in range(N):
+        if big[i] >= 0:
+            pool_big[int(big[i])] = dev(pool_np[i])
+            cpool_big[int(big[i])] = dev(cpool_np[i], dt)
+    pool_small, cpool_small = dev(pool_np), dev(cpool_np, dt)
+    ref_pool, ref_cpool = pool_np.astype(np.float64), cpool_np.astype(np.float64)
+    dims = oracle_mod.Dims(16, 32, 128, 128, conv_width=4)
+    used = big >= 0
+
+    for s in range(2):
+        x = decode_inputs(70, s, N, geom, "bf16")
+        args = (dev(x.q, dt), dev(x.k, dt), dev(x.v, dt), dev(x.g), dev(x.beta))
+        o_big = binding.gdn_decode_step(*args, pool_big, state_indices=dev(big, torch.int32), conv_weight=w,
+                                        conv_state_pool=cpool_big)
+        o_small = binding.gdn_decode_step(*args, pool_small, state_indices=dev(small, torch.int32), conv_weight=w,
+                                          conv_state_pool=cpool_small)
+        ro = oracle_mod.decode(dims, x.q, x.k, x.v, x.g, x.beta, ref_pool, small.astype(np.int64),
+                               conv_weights(70, geom, "bf16"), None, ref_cpool)
+        torch.cuda.synchronize()
+        ob, osm = o_big.cpu().numpy(), o_small.cpu().numpy()
+        assert np.array_equal(ob[used], osm[used])
+        e = rel_err(ob[used], ro[used])
+        print(f"  step {s}: rel err o={e:.3e}", flush=True)
+        assert e <= TOL["bf16"]
+    for i in range(N):
+        if big[i] >= 0:
+            assert np.array_equal(pool_big[int(big[i])].cpu().numpy(), pool_small[i].cpu().numpy())
+            assert np.array_equal(cpool_big[int(big[i])].float().cpu().numpy(), cpool_small[i].float().cpu().numpy())
+    assert rel_err(pool_small.cpu().numpy()[used], ref_pool[used]) <= TOL["bf16"]
+
+    # 3 tokens per slot: token j's state to entry 4100 + 3 i + j (compact: 6 + 3 i + j),
+    # read from the entry the single steps left
+    pool_small = torch.cat([pool_small, torch.zeros((3 * N, 32, 128, 128), device="cuda")])
+    cpool_small = torch.cat([cpool_small, torch.zeros((3 * N, geom.channels, 3), dtype=dt, device="cuda")])
+    rows_big = np.stack([[big[i]] + [4100 + 3 * i + j for j in range(m - 1)] for i in range(N)]).astype(np.int32)
+    rows_small = np.stack([[small[i]] + [6 + 3 * i + j for j in range(m - 1)] for i in range(N)]).astype(np.int32)
+    rows_big[2, :], rows_small[2, :] = -1, -1
+    acc = np.ones(N, dtype=np.int32)
+    x = multi_decode_inputs(70, 0, N, m, geom, "bf16")
+    o_big = _multi(x, dt, pool_big, state_indices=dev(rows_big, torch.int32), num_accepted=dev(acc, torch.int32),
+                   conv_weight=w, conv_state_pool=cpool_big)
+    o_small = _multi(x, dt, pool_small, state_indices=dev(rows_small, torch.int32),
+                     num_accepted=dev(acc, torch.int32), conv_weight=w, conv_state_pool=cpool_small)
+    torch.cuda.synchronize()
+    assert np.array_equal(o_big.cpu().numpy()[used], o_small.cpu().numpy()[used])
+    for i in range(N):
+        for j in range(m):
+            if rows_big[i, j] >= 0:
+                assert np.array_equal(pool_big[int(rows_big[i, j])].cpu().numpy(),
+                                      pool_small[int(rows_small[i, j])].cpu().numpy())
