@@ -9,6 +9,7 @@ states live in pools addressed by state_indices (with has_initial_state).
   of 64 tokens equals one call, bit for bit.
 * Mixed batch: length-1 sequences continuing from their entries (decode
   tokens) next to new prefills, against the oracle.
+* Pool entries past element 2^31 give the bits of a compact pool.
 """
 import numpy as np
 import pytest
@@ -126,3 +127,39 @@ def test_pooled_mixed_prefill_and_decode(oracle_mod, dtype):
     assert eo <= TOL[dtype] and ef <= TOL[dtype]
     assert np.array_equal(ca[idx], rcso.astype(np.float32))
     assert np.array_equal(pa[2], pool_np[2])
+
+
+def test_pooled_entries_beyond_32_bits():
+    """Pooled prefill over a 4200-entry pool (h_v = 32, d = 128: entry 4096
+    starts at element 2^31): sequences reading and writing entries past that
+    point give bit for bit the outputs, final states and conv states of the same
+    call on a compact pool holding those entries."""
+    geom = Geometry(16, 32, 128, 128)
+    P = 4200
+    lengths = [70, 1, 130, 3]
+    big = np.array([4199, 4097, -1, 100], dtype=np.int32)
+    small = np.array([0, 1, -1, 3], dtype=np.int32)
+    dt = torch.bfloat16
+    x = prefill_inputs(62, lengths, geom, "bf16")
+    pool_np = state_pool(62, len(lengths), geom)
+    cpool_np = conv_state_pool(62, len(lengths), geom, "bf16")
+    pool_big = torch.zeros((P, 32, 128, 128), dtype=torch.float32, device="cuda")
+    cpool_big = torch.zeros((P, geom.channels, 3), dtype=dt, device="cuda")
+    for n in range(len(lengths)):
+        if big[n] >= 0:
+            pool_big[int(big[n])] = dev(pool_np[n])
+            cpool_big[int(big[n])] = dev(cpool_np[n], dt)
+    pool_small, cpool_small = dev(pool_np), dev(cpool_np, dt)
+    args = (dev(x.q, dt), dev(x.k, dt), dev(x.v, dt), dev(x.g), dev(x.beta))
+    cu = torch.from_numpy(x.cu_seqlens.astype(np.int32))
+    w = dev(x.conv_w, dt)
+    o_big = binding.gdn_prefill_varlen_pooled(*args, cu, pool_big, state_indices=dev(big, torch.int32),
+                                              conv_weight=w, conv_state_pool=cpool_big)
+    o_small = binding.gdn_prefill_varlen_pooled(*args, cu, pool_small, state_indices=dev(small, torch.int32),
+                                                conv_weight=w, conv_state_pool=cpool_small)
+    torch.cuda.synchronize()
+    assert torch.equal(o_big, o_small)
+    for n in range(len(lengths)):
+        if big[n] >= 0:
+            assert torch.equal(pool_big[int(big[n])], pool_small[int(small[n])])
+            assert torch.equal(cpool_big[int(big[n])], cpool_small[int(small[n])])
