@@ -33,8 +33,8 @@
 //                     matrix-core accumulators by four waves, while four
 //                     helper waves stage the chunks and compute Q H, P D and
 //                     the output.  The next chunk's images are loaded into
-//                     registers while the current chunk computes.
-//   conv_state_kernel the final conv states.
+//                     registers while the current chunk computes.  At the
+//                     end its helper waves write the final conv states.
 //
 // Precision: every product takes split operands (x = hi + lo, three 16-bit
 // matrix-core steps, fp32 accumulation): bf16 pairs (about 16 significant
@@ -1253,43 +1253,48 @@ __global__ void __launch_bounds__(kCarryThreads, 1) carry_kernel(const PrefillPa
             if (j + 1 < nch) conv_v(j + 1, 1);
             lds_barrier();
         }
-    }
-}
 
-// Final conv state of every sequence: its last 3 raw inputs per channel,
-// reaching into its conv history for sequences shorter than 3; both are
-// entry state_slot(n) of their arrays (no write without an entry).  One
-// thread per (sequence, channel) reads all three values before writing, so
-// the output may be the input buffer itself.
-template <typename TIn>
-__global__ void __launch_bounds__(256) conv_state_kernel(const PrefillParams p, int dk, int dv) {
-    const int64_t nq = int64_t(p.h_k) * dk, nv = int64_t(p.h_v) * dv, C = 2 * nq + nv;
-    const int64_t e = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (e >= int64_t(p.num_seqs) * C) return;
-    const int64_t n = e / C, c = e % C;
-    const int sl = state_slot(p, int(n));
-    if (sl < 0) return;  // no pool entry: nothing to write
-    const bool hist = slot_has_initial(p, int(n), sl);
-    const int64_t at = (int64_t(sl) * C + c) * 3;
-    const int64_t bos = p.cu_seqlens[n], len = p.cu_seqlens[n + 1] - bos;
-    const TIn* qin = static_cast<const TIn*>(p.q);
-    const TIn* kin = static_cast<const TIn*>(p.k);
-    const TIn* vin = static_cast<const TIn*>(p.v);
-    const TIn* csi = static_cast<const TIn*>(p.conv_state_in);
-    TIn* cso = static_cast<TIn*>(p.conv_state_out);
-    TIn vals[3];
+        // Final conv state: the sequence's last 3 raw inputs for this
+        // workgroup's v channels and, in its group's first member, the key
+        // head's q and k channels; a sequence shorter than 3 reaches into its
+        // conv history.  Both are entry `slot` of their arrays (nothing is
+        // written without one).  Every history read of these channels came
+        // before (q and k: the chunk-local kernel; v: this workgroup's first
+        // chunk), and one thread reads a channel's three values before writing
+        // them, so the output may be the history buffer itself.
+        if (p.conv_state_out && conv && slot >= 0) {
+            const int64_t len = eos - bos;
+            const TIn* csi = (p.conv_state_in && has_init) ? static_cast<const TIn*>(p.conv_state_in) : nullptr;
+            TIn* cso = static_cast<TIn*>(p.conv_state_out);
+            const int nch_out = kDvs + (mem == 0 ? 2 * DK : 0);
+            for (int i = ht; i < nch_out; i += HT) {
+                int64_t c, stride;
+                const TIn* src;
+                if (i < kDvs) {
+                    c = 2 * nq + int64_t(h) * DV + slice * kDvs + i;
+                    src = static_cast<const TIn*>(p.v) + (c - 2 * nq);
+                    stride = nv;
+                } else if (i < kDvs + DK) {
+                    c = int64_t(hk) * DK + (i - kDvs);
+                    src = static_cast<const TIn*>(p.q) + c;
+                    stride = nq;
+                } else {
+                    c = nq + int64_t(hk) * DK + (i - kDvs - DK);
+                    src = static_cast<const TIn*>(p.k) + (c - nq);
+                    stride = nq;
+                }
+                const int64_t at = (int64_t(slot) * C + c) * 3;
+                TIn vals[3];
 #pragma unroll
-    for (int j = 0; j < 3; j++) {
-        const int64_t pos = len - 3 + j;
-        if (pos >= 0) {
-            const int64_t t = bos + pos;
-            vals[j] = c < nq ? qin[t * nq + c] : (c < 2 * nq ? kin[t * nq + c - nq] : vin[t * nv + c - 2 * nq]);
-        } else {
-            vals[j] = (csi && hist) ? csi[at + 3 + pos] : TIn(0);
+                for (int jj = 0; jj < 3; jj++) {
+                    const int64_t pos = len - 3 + jj;
+                    vals[jj] = pos >= 0 ? src[(bos + pos) * stride] : (csi ? csi[at + 3 + pos] : TIn(0));
+                }
+#pragma unroll
+                for (int jj = 0; jj < 3; jj++) cso[at + jj] = vals[jj];
+            }
         }
     }
-#pragma unroll
-    for (int j = 0; j < 3; j++) cso[at + j] = vals[j];
 }
 
 int64_t carry_blocks(int64_t num_seqs, int64_t h_k, int64_t h_v, int64_t d_v) {
@@ -1413,14 +1418,6 @@ hipError_t launch_prefill(const PrefillParams& p, int d_k, int d_v, int qkv_dtyp
         err = out_dtype == 1 ? run_dtype<float, bf16_t>(p, d_k, d_v, stream, events)
                              : run_dtype<float, float>(p, d_k, d_v, stream, events);
     if (err != hipSuccess) return err;
-    if (p.conv_state_out && p.conv_width == 4) {
-        const int64_t total = int64_t(p.num_seqs) * (2 * int64_t(p.h_k) * d_k + int64_t(p.h_v) * d_v);
-        const unsigned grid = unsigned((total + 255) / 256);
-        if (qkv_dtype == 1) conv_state_kernel<bf16_t><<<dim3(grid), dim3(256), 0, stream>>>(p, d_k, d_v);
-        else conv_state_kernel<float><<<dim3(grid), dim3(256), 0, stream>>>(p, d_k, d_v);
-        err = hipGetLastError();
-        if (err != hipSuccess) return err;
-    }
     return record(events, 3, stream);
 }
 
