@@ -132,6 +132,16 @@ def test_bf16_inputs_beyond_fp16_range(oracle_mod):
     assert np.max(np.abs(fs)) > 65504.0
 
 
+@pytest.mark.parametrize("h_k,h_v,d,dtype", [(1, 8, 128, "bf16"), (2, 10, 64, "f32"), (2, 16, 128, "bf16")])
+def test_large_gqa_groups(oracle_mod, h_k, h_v, d, dtype):
+    """8, 5 (odd) and 8 value heads per key head: the chunk-local kernel takes
+    the group's value heads two at a time, the carry one workgroup per
+    (value head, slice)."""
+    x = prefill_inputs(27 + h_v, [100, 64, 1, 150], Geometry(h_k, h_v, d, d), dtype, initial_state_std=0.02,
+                       conv_state=True)
+    _check_prefill(oracle_mod, x)
+
+
 def test_custom_scale(oracle_mod):
     x = prefill_inputs(23, [70], Geometry(2, 2, 128, 128), "bf16")
     _check_prefill(oracle_mod, x, scale=0.5)
