@@ -405,7 +405,8 @@ def test_decode_beta_logits(oracle_mod):
     assert rel_err(pool.cpu().numpy(), ref_pool) <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("h_k,h_v,d_k,d_v", [(3, 3, 64, 64), (2, 6, 128, 64), (1, 4, 64, 128)])
+@pytest.mark.parametrize("h_k,h_v,d_k,d_v", [(3, 3, 64, 64), (2, 6, 128, 64), (1, 4, 64, 128), (1, 8, 128, 128),
+                                             (2, 10, 64, 64)])
 def test_decode_gqa_groups(oracle_mod, h_k, h_v, d_k, d_v):
     """Value heads per key head 1, 3 and 4 (one workgroup serves the group and
     shifts its conv history), with d_k != d_v, conv and an index map."""
