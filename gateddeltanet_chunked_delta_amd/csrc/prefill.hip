@@ -967,13 +967,14 @@ __global__ void __launch_bounds__(kCarryThreads, 1) carry_kernel(const PrefillPa
                 hacc[it][e] = (p.initial_state && has_init)
                                   ? p.initial_state[state_base + int64_t(16 * it + 4 * lg + e) * DV] : 0.0f;
         u32x4_t pkq[NKQ];
-        auto fetch_kq = [&](int j) {
+        auto fetch_kq = [&](int j, int i0, int i1) {
             const u32x4_t* skq = reinterpret_cast<const u32x4_t*>(static_cast<const E*>(p.kq_img) +
                                                                   ((int64_t(cb) + j) * p.h_k + hk) * Img<DK>::kKQ);
 #pragma unroll
-            for (int i = 0; i < NKQ; i++) pkq[i] = skq[tid + HT * i];
+            for (int i = 0; i < NKQ; i++)
+                if (i >= i0 && i < i1) pkq[i] = skq[tid + HT * i];
         };
-        if (nch > 0) fetch_kq(0);
+        if (nch > 0) fetch_kq(0, 0, NKQ);
 
         for (int j = 0; j < nch; j++) {
             // ---- stage: the K|Q image, and the state as the B operand (also handed to the helpers) ----
@@ -994,8 +995,6 @@ __global__ void __launch_bounds__(kCarryThreads, 1) carry_kernel(const PrefillPa
                 *reinterpret_cast<V8*>(hbs + (((cw * KS + ks) * 2 + 1) * 64 + lane) * 16) = hb[ks].lo;
             }
             lds_barrier();
-            // the next chunk's K|Q image: two phases to arrive before it is staged
-            if (j + 1 < nch) fetch_kq(j + 1);
 
             // ---- B: R = beta (V - e^gam K H), D = T R; D's operand to LDS ----
             float4_t rr[4];
@@ -1015,6 +1014,13 @@ __global__ void __launch_bounds__(kCarryThreads, 1) carry_kernel(const PrefillPa
                     rr[tb][e] = btr[e] * (Vf[r * PV + wcol] - egr[e] * kh[e]);
                 }
             }
+            // The next chunk's K|Q image, half of it here, once K H has read this
+            // chunk's planes, half at the start of phase C.  Issued right after
+            // the staging barrier, with the helpers' T|P, scalar and v loads, the
+            // two queued in the CU's vector memory pipeline and delayed the
+            // helpers' Q H; all of it here or all in phase C measured slower
+            // (the issue on the chain, or the data late for the next staging).
+            if (j + 1 < nch) fetch_kq(j + 1, 0, NKQ / 2);
             float4_t dd[4];
             {
                 SFrag<E> rb[2];
@@ -1046,6 +1052,7 @@ __global__ void __launch_bounds__(kCarryThreads, 1) carry_kernel(const PrefillPa
             lds_barrier();
 
             // ---- C: H <- e^{gam_last} H + K^T diag(e^{gam_last - gam}) D ----
+            if (j + 1 < nch) fetch_kq(j + 1, NKQ / 2, NKQ);
             {
                 SFrag<E> ab[2];
 #pragma unroll
