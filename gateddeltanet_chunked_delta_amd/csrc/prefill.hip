@@ -1206,6 +1206,10 @@ __global__ void __launch_bounds__(kCarryThreads, 1) carry_kernel(const PrefillPa
                     for (int e = 0; e < 4; e++) eqh[tb][e] = egr[e] * qh[e];
                 }
             }
+            // half of the next chunk's v conv (its raw rows were requested at
+            // the start of this phase), in the time the main waves' phase B
+            // takes beyond Q H
+            if (j + 1 < nch) conv_v(j + 1, 1);
             lds_barrier();
 
             // ---- C: o = scale (e^gam Q H + P D) ----
@@ -1257,7 +1261,6 @@ __global__ void __launch_bounds__(kCarryThreads, 1) carry_kernel(const PrefillPa
                     }
                 }
             }
-            if (j + 1 < nch) conv_v(j + 1, 1);
             lds_barrier();
         }
 
