@@ -1015,11 +1015,12 @@ __global__ void __launch_bounds__(kCarryThreads, 1) carry_kernel(const PrefillPa
                 }
             }
             // The next chunk's K|Q image, half of it here, once K H has read this
-            // chunk's planes, half at the start of phase C.  Issued right after
-            // the staging barrier, with the helpers' T|P, scalar and v loads, the
-            // two queued in the CU's vector memory pipeline and delayed the
-            // helpers' Q H; all of it here or all in phase C measured slower
-            // (the issue on the chain, or the data late for the next staging).
+            // chunk's planes, half after D's operand is written.  Issued right
+            // after the staging barrier, with the helpers' T|P, scalar and v
+            // loads, the two queued in the CU's vector memory pipeline and
+            // delayed the helpers' Q H; all of it here, or half or all in phase C,
+            // measured slower (the issue on the chain, or the data late for the
+            // next staging).
             if (j + 1 < nch) fetch_kq(j + 1, 0, NKQ / 2);
             float4_t dd[4];
             {
@@ -1049,10 +1050,10 @@ __global__ void __launch_bounds__(kCarryThreads, 1) carry_kernel(const PrefillPa
                 *reinterpret_cast<V8*>(dop + dop_offset<PV>(cw, 2 * s, lane)) = f.hi;
                 *reinterpret_cast<V8*>(dop + dop_offset<PV>(cw, 2 * s + 1, lane)) = f.lo;
             }
+            if (j + 1 < nch) fetch_kq(j + 1, NKQ / 2, NKQ);
             lds_barrier();
 
             // ---- C: H <- e^{gam_last} H + K^T diag(e^{gam_last - gam}) D ----
-            if (j + 1 < nch) fetch_kq(j + 1, NKQ / 2, NKQ);
             {
                 SFrag<E> ab[2];
 #pragma unroll
