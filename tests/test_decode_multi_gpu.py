@@ -306,3 +306,59 @@ def test_decode_pool_entries_beyond_32_bits(oracle_mod):
             if rows_big[i, j] >= 0:
                 assert np.array_equal(pool_big[int(rows_big[i, j])].cpu().numpy(),
                                       pool_small[int(rows_small[i, j])].cpu().numpy())
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_decode_multi_sweep(oracle_mod, case):
+    """Seeded sweep: key heads 1-3, group 1-4, d_k and d_v in {64, 128}
+    independently, bf16 or fp32, 1-8 tokens per slot, conv on or off, slots
+    that keep every token's state, only some or none, and a skipped slot; two
+    calls, the second resuming from each slot's accepted token, against the
+    oracle."""
+    r = np.random.default_rng([4242, case])
+    h_k, G = int(r.integers(1, 4)), int(r.integers(1, 5))
+    d_k, d_v = int(r.choice([64, 128])), int(r.choice([64, 128]))
+    dtype = str(r.choice(["bf16", "f32"]))
+    m, N = int(r.integers(1, 9)), int(r.integers(1, 7))
+    conv = bool(r.random() < 0.7)
+    geom = Geometry(h_k, h_k * G, d_k, d_v)
+    print(f"  case {case}: {geom} {dtype} m={m} N={N} conv={conv}", flush=True)
+    P = N * m + 2
+    dt = TORCH_DT[dtype]
+    pool_np = state_pool(90 + case, P, geom)
+    cpool_np = conv_state_pool(90 + case, P, geom, dtype) if conv else None
+    w_np = conv_weights(90 + case, geom, dtype) if conv else None
+    # slot n owns entries n*m .. n*m + m - 1; some tokens are not kept (-1), the
+    # last slot is skipped when there are several
+    idx = np.arange(N * m, dtype=np.int32).reshape(N, m)
+    drop = r.random((N, m)) < 0.3
+    drop[:, 0] = False
+    idx[drop] = -1
+    if N > 1:
+        idx[N - 1, :] = -1
+    pool = dev(pool_np)
+    cpool = dev(cpool_np, dt) if conv else None
+    ref_pool = pool_np.astype(np.float64)
+    ref_cpool = cpool_np.astype(np.float64) if conv else None
+    dims = oracle_mod.Dims(h_k, h_k * G, d_k, d_v, conv_width=4 if conv else 0)
+    for call in range(2):
+        # accepted counts point at kept entries (the read entry must exist)
+        acc_np = np.array([max([j + 1 for j in range(m) if idx[n, j] >= 0] or [1]) if call else
+                           int(r.integers(1, m + 1)) for n in range(N)], dtype=np.int32)
+        for n in range(N):
+            while acc_np[n] > 1 and idx[n, acc_np[n] - 1] < 0:
+                acc_np[n] -= 1
+        x = multi_decode_inputs(90 + case, call, N, m, geom, dtype)
+        o = _multi(x, dt, pool, state_indices=dev(idx, torch.int32), num_accepted=dev(acc_np, torch.int32),
+                   conv_weight=dev(w_np, dt) if conv else None, conv_state_pool=cpool)
+        ro = oracle_mod.decode_multi(dims, x.q, x.k, x.v, x.g, x.beta, ref_pool, idx, acc_np, w_np, None,
+                                     ref_cpool)
+        live = np.array([row[a - 1] >= 0 for row, a in zip(idx, acc_np)])
+        if live.any():
+            e = rel_err(o.cpu().numpy()[live], ro[live])
+            print(f"  call {call}: rel err o={e:.3e}", flush=True)
+            assert e <= TOL[dtype]
+    used = sorted({int(e) for e in idx.ravel() if e >= 0})
+    assert rel_err(pool.cpu().numpy()[used], ref_pool[used]) <= TOL[dtype]
+    if conv:
+        assert np.array_equal(cpool.float().cpu().numpy(), ref_cpool.astype(np.float32))
