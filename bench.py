@@ -5,76 +5,103 @@
 A timed step is one chunked varlen prefill of the 4 x 4096-token workload
 (h_k = 16, h_v = 32, d = 128, bf16 q/k/v, fp32 g/beta/state/output, width-4
 conv + SiLU + q/k L2 norm, final recurrent and conv states written), inputs
-resident in HBM.  `value` is prefill tokens/s.  The library records HIP
-events on its stream around its two main kernels (gdn_prefill_varlen_timed),
-so the roofline entry is for the dominant kernel, the cross-chunk carry, and
-the chunk-local kernel is reported beside it.  The decode half of the metric
-(256 slots x 32 value heads, d = 128, conv update, 512 MiB fp32 state pool
-updated in place, 100 consecutive steps over 4 pools in rotation) is timed
-separately and reported under "decode", and the multi-token (speculative)
-decode of 4 tokens per slot under "decode_multi"; the same prefill with bf16
-outputs under "prefill_bf16_out"; the packed varlen batch (60
-sequences, h_v = 48) and a 32768-token sequence are timed under
-"other_prefill_configs".  One JSON line is printed.
+resident in HBM.  `value` is prefill tokens/s over the K timed steps.
+
+Before the W warm-up steps the GPU is brought to its steady clocks by a fixed
+stretch of untimed prefill calls (reported as "device_warmup"): without it the
+first ~100 back-to-back calls run measurably slower.
+
+Rooflines follow one rule: a kernel's (or a call's) floor is
+max(algorithmic flops / matrix-core peak, algorithmic bytes / HBM peak), and
+`frac` = floor / measured time against the roof that binds.  Algorithmic bytes
+count each input read once and each output and final state written once, no
+workspace; they are split between the two prefill kernels by who reads or
+writes them (chunk-local kernel: q, k, g, beta; carry kernel: v, o, final
+recurrent and conv states, initial states).  The library records HIP events on
+its launch stream around each kernel (gdn_prefill_varlen_timed), so kernel
+times are measured live.  `roofline` is the dominant kernel, the cross-chunk
+carry; `call` is the whole prefill.  A plain streaming device copy (the
+library's gdn_stream_copy) gives a measured HBM peak beside the datasheet's.
+
+Other legs: the same prefill with bf16 outputs; the decode step (256 slots x 32
+value heads, d = 128, conv update, 512 MiB fp32 state pool in place, 100
+consecutive steps over 4 pools in rotation) and the 4-token decode; the packed
+varlen batch (60 sequences, h_v = 48) and a 32768-token sequence; the fp64
+oracle on the host cores (all threads and one, plus the decode step).  One
+JSON line is printed.
 """
 from __future__ import annotations
 
 import argparse
 import json
 import os
+import subprocess
 import sys
 import time
 
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
-MFMA_F16_PEAK_TFLOPS = 2500.0  # dense fp16/bf16 matrix cores
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix cores
 PREP_KERNEL = "prep_kernel"
 CARRY_KERNEL = "carry_kernel"
 DECODE_KERNEL = "decode_kernel"
+CHUNK = 64
 
 
-def prefill_algorithmic(T, N, h_k, h_v, d, in_bytes=2, out_bytes=4, chunk=64):
-    """Bytes: each input read once, outputs and final states written once.
-    Flops per (token, value head): (4/G + 6) * chunk * d + 6 * d^2."""
+def roofline(nbytes, flops, seconds, kernel=None):
+    """The binding roof of work (bytes, flops) done in `seconds`."""
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    r = {"bound": "hbm" if t_hbm >= t_mfma else "mfma"}
+    if r["bound"] == "hbm":
+        r.update(achieved=nbytes / seconds / 1e9, peak=HBM_PEAK_GBS, unit="GB/s")
+    else:
+        r.update(achieved=flops / seconds / 1e12, peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s")
+    r["frac"] = r["achieved"] / r["peak"]
+    r.update(algorithmic_bytes=nbytes, algorithmic_flops=flops, floor_us=max(t_hbm, t_mfma) * 1e6,
+             avg_us=seconds * 1e6, mfma_frac=flops / seconds / 1e12 / MFMA_BF16_PEAK_TFLOPS)
+    if kernel:
+        r["kernel"] = kernel
+    return r
+
+
+def prefill_work(lengths, h_k, h_v, d, in_bytes=2, out_bytes=4, initial_states=False, conv_state_out=True):
+    """Algorithmic (bytes, flops) of one prefill call, split into the
+    chunk-local kernel's and the carry kernel's shares.
+
+    Flops per (token, value head): the Gram products K K^T and Q K^T shared by
+    the G value heads of a key head (2 chunk d each), A, P (chunk d each per
+    value head, folded into the (4/G + 6) chunk d of the textbook count), and
+    the state-side work of the carry: three d x d products (K H, Q H and the
+    update, 2 d^2 each) and T R, P D (2 (chunk + 1) d: lower-triangular 64 x 64
+    products).  Total (4/G + 6) chunk d + 6 d^2."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    T, N = int(lengths.sum()), len(lengths)
     G = h_v // h_k
     C = 2 * h_k * d + h_v * d
-    per_token = (2 * h_k * d + h_v * d) * in_bytes + 2 * h_v * 4 + h_v * d * out_bytes
-    bytes_ = T * per_token + N * h_v * d * d * 4 + C * 4 * in_bytes + (N + 1) * 4 + N * C * 3 * in_bytes
-    flops = T * h_v * ((4.0 / G + 6.0) * chunk * d + 6.0 * d * d)
-    return bytes_, flops
-
-
-def carry_algorithmic(T, h_v, d, chunk=64):
-    """Flops of the cross-chunk kernel per call: per (token, value head) the
-    three d x d state products K H, Q H and the update (2 d^2 each) and the
-    two lower-triangular 64 x 64 products T R and P D (chunk + 1 MACs per
-    column on average: (chunk + 1) d flops each)."""
-    return T * h_v * (6.0 * d * d + 2.0 * (chunk + 1) * d)
-
-
-def prep_bytes(T, N, h_k, h_v, d, in_bytes=2, chunk=64):
-    """Bytes the chunk-local kernel must move: raw q and k (with the 3-row
-    conv history per chunk), g and beta, and the chunk images it writes
-    (split-fp16 K and Q; the 10 lower 16x16 blocks of T and P; 4 scalars per
-    token), for the chunks of N equal sequences."""
-    chunks = N * ((T // N + chunk - 1) // chunk)
-    raw = (T + 3 * chunks) * 2 * h_k * d * in_bytes + T * h_v * 2 * 4
-    images = chunks * (h_k * 2 * 2 * chunk * d * 2 + h_v * (2 * 2 * 320 * 8 * 2 + 4 * chunk * 4))
-    return raw + images
+    state = N * h_v * d * d * 4
+    prep_b = T * (2 * h_k * d * in_bytes + 2 * h_v * 4)
+    carry_b = T * (h_v * d * in_bytes + h_v * d * out_bytes) + state + C * 4 * in_bytes + (N + 1) * 4
+    if initial_states:
+        carry_b += state
+    if conv_state_out:
+        carry_b += N * C * 3 * in_bytes
+    total_f = T * h_v * ((4.0 / G + 6.0) * CHUNK * d + 6.0 * d * d)
+    carry_f = T * h_v * (6.0 * d * d + 2.0 * (CHUNK + 1) * d)
+    return {"prep": (prep_b, total_f - carry_f), "carry": (carry_b, carry_f), "call": (prep_b + carry_b, total_f)}
 
 
 def decode_algorithmic(N, h_k, h_v, d, in_bytes=2, out_bytes=4, conv=True):
     """State read + write, q/k/v/g/beta read, o written, and with the conv
     prologue the conv history read + written and the conv weights read;
-    ~ (6 d^2 + O(d)) flops per (slot, head)."""
+    ~ 7 d^2 flops per (slot, head)."""
     state = N * h_v * d * d * 4
     C = 2 * h_k * d + h_v * d
     bytes_ = 2 * state + N * C * in_bytes + N * h_v * 2 * 4 + N * h_v * d * out_bytes
     if conv:
         bytes_ += 2 * N * C * 3 * in_bytes + C * 4 * in_bytes
-    flops = N * h_v * 7.0 * d * d
-    return bytes_, flops
+    return bytes_, N * h_v * 7.0 * d * d
 
 
 def decode_multi_algorithmic(N, m, h_k, h_v, d, kept, in_bytes=2, out_bytes=4):
@@ -87,11 +114,31 @@ def decode_multi_algorithmic(N, m, h_k, h_v, d, kept, in_bytes=2, out_bytes=4):
             + N * C * 3 * in_bytes * (1 + kept) + C * 4 * in_bytes)
 
 
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when the kernel's sources changed since the counters were taken."""
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    try:
+        with open(os.path.join(root, "profiles", "traffic.json")) as f:
+            t = json.load(f)
+        k = t[kernel]
+        h = hashlib.sha256()
+        for src in k["sources"]:
+            with open(os.path.join(root, src), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest()[:16] != k["src_sha256_16"]:
+            return None
+        return (k["fetch_kib"] * t["fetch_scale"] + k["write_kib"] * t["write_scale"]) * 1024.0
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def extra_prefill(gdn, torch, dev, lengths, h_k, h_v, d, init_std, steps, seed):
-    """Prefill throughput at another geometry, inputs drawn on the GPU with the
+    """Prefill at another geometry, inputs drawn on the GPU with the
     distributions of the seeded workloads (q, k, v ~ N(0, 1) in bf16, conv taps
     0.5 N(0, 1), beta = sigmoid(N(0, 1)), g = -softplus(N(0, 1)), initial
-    states init_std N(0, 1)); returns (us per call, tokens/s, prep us, carry us)."""
+    states init_std N(0, 1)); mean event times over `steps` calls."""
     gen = torch.Generator(device=dev)
     gen.manual_seed(seed)
     T, N = int(sum(lengths)), len(lengths)
@@ -124,61 +171,107 @@ def extra_prefill(gdn, torch, dev, lengths, h_k, h_v, d, init_std, steps, seed):
     us = float(np.mean([e[0].elapsed_time(e[3]) for e in evs])) * 1e3
     prep = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e3
     carry = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e3
-    return us, T / (us * 1e-6), prep, carry
+    work = prefill_work(lengths, h_k, h_v, d, initial_states=init_std is not None and init_std > 0,
+                        conv_state_out=False)
+    return {"us_per_call": us, "tokens_per_s": T / (us * 1e-6), "prep_kernel_us": prep, "carry_kernel_us": carry,
+            "roofline": roofline(*work["call"], us * 1e-6),
+            "carry_roofline": roofline(*work["carry"], carry * 1e-6, CARRY_KERNEL)}
 
 
-def measured_traffic(kernel):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None when the kernel's sources changed since the counters were taken."""
-    import hashlib
-    root = os.path.dirname(os.path.abspath(__file__))
+def stream_copy_peak(gdn, torch, dev, stream):
+    """Best read + write bandwidth of the library's streaming copy of 1 GiB
+    over a few grid sizes (the measured HBM peak)."""
+    nbytes = 1 << 30
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = None
+    for per_cu in (2, 4, 8, 16):
+        blocks = per_cu * cus
+        for _ in range(3):
+            gdn.binding.gdn_stream_copy(dst, src, blocks)
+        torch.cuda.synchronize()
+        reps = 10
+        e0.record(stream)
+        for _ in range(reps):
+            gdn.binding.gdn_stream_copy(dst, src, blocks)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        gbs = 2 * nbytes / (us * 1e-6) / 1e9
+        if best is None or gbs > best["GB/s"]:
+            best = {"bytes_read": nbytes, "bytes_written": nbytes, "us_per_copy": us, "GB/s": gbs,
+                    "workgroups": blocks, "kernel": "stream_copy_kernel (16-byte nontemporal loads and stores)"}
+    assert bool((dst == 1.0).all()), "stream copy produced wrong data"
+    del src, dst
+    return best
+
+
+def cpu_model():
     try:
-        with open(os.path.join(root, "profiles", "traffic.json")) as f:
-            t = json.load(f)
-        k = t[kernel]
-        h = hashlib.sha256()
-        for src in k["sources"]:
-            with open(os.path.join(root, src), "rb") as f:
-                h.update(f.read())
-        if h.hexdigest()[:16] != k["src_sha256_16"]:
-            return None
-        return (k["fetch_kib"] * t["fetch_scale"] + k["write_kib"] * t["write_scale"]) * 1024.0
-    except (OSError, KeyError, ValueError):
-        return None
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for ln in out.splitlines():
+            if ln.lower().startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    return "unknown"
 
 
-def cpu_baseline(x, nthreads):
-    """The fp64 oracle on the same seeded inputs (all sequences, all heads), wall clock."""
+def cpu_baselines(x, geom, nthreads):
+    """The fp64 oracle on the host cores: the whole prefill workload on every
+    thread, one of its sequences on one thread, and two decode steps of the
+    256-slot workload on every thread (wall clock; bounded samples)."""
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
     import oracle
+    from gateddeltanet_chunked_delta_amd.inputs import conv_state_pool, conv_weights, decode_inputs, state_pool
     oracle.build(force=False)
-    g = x.geom
-    dims = oracle.Dims(g.h_k, g.h_v, g.d_k, g.d_v, conv_width=4)
+    dims = oracle.Dims(geom.h_k, geom.h_v, geom.d_k, geom.d_v, conv_width=4)
     t0 = time.perf_counter()
     oracle.prefill(dims, x.cu_seqlens, x.q, x.k, x.v, x.g, x.beta, x.conv_w, nthreads=nthreads)
     dt = time.perf_counter() - t0
+    L = int(x.cu_seqlens[1])
+    t0 = time.perf_counter()
+    oracle.prefill(dims, x.cu_seqlens[:2], x.q[:L], x.k[:L], x.v[:L], x.g[:L], x.beta[:L], x.conv_w, nthreads=1)
+    dt1 = time.perf_counter() - t0
+    N, steps = 256, 2
+    pool = state_pool(3, N, geom).astype(np.float64)
+    cpool = conv_state_pool(3, N, geom, "bf16").astype(np.float64)
+    cw = conv_weights(3, geom, "bf16")
+    ins = [decode_inputs(3, s, N, geom, "bf16") for s in range(steps)]
+    idx = np.arange(N)
+    t0 = time.perf_counter()
+    for d in ins:
+        oracle.decode(dims, d.q, d.k, d.v, d.g, d.beta, pool, idx, cw, None, cpool, nthreads=nthreads)
+    ddt = (time.perf_counter() - t0) / steps
+    dbytes, _ = decode_algorithmic(N, geom.h_k, geom.h_v, geom.d_k)
     return {"value": x.total_tokens / dt, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
-            "sample": f"whole workload ({x.num_seqs} x {x.total_tokens // x.num_seqs} tokens, all heads), "
-                      f"fp64, one run of {dt:.2f} s"}
+            "sample": f"whole prefill workload ({x.num_seqs} x {L} tokens, all heads, conv + SiLU + L2), fp64, "
+                      f"one run of {dt:.2f} s on {nthreads} threads",
+            "cpu_model": cpu_model(),
+            "one_core": {"value": L / dt1, "unit": "tokens/s", "cores": 1,
+                         "sample": f"one sequence of {L} tokens, all heads, one run of {dt1:.2f} s"},
+            "decode": {"value": dbytes / ddt / 1e9, "unit": "GB/s", "cores": nthreads,
+                       "sample": f"{steps} decode steps of 256 slots x 32 value heads with the conv update, fp64 "
+                                 f"state, {ddt * 1e3:.1f} ms per step; GB/s of the GPU step's algorithmic bytes "
+                                 "(fp32 state) so the two rates compare"}}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    # The GPU reaches steady clocks only after ~100 prefill calls (~0.1 s) of
-    # work; fewer warmup steps under-report the carry kernel by ~8%.
-    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--device-warmup-ms", type=float, default=400.0,
+                    help="untimed prefill calls before the warm-up steps, until this much wall time has passed "
+                         "(brings the GPU to its steady clocks)")
     ap.add_argument("--decode-steps", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-extra-configs", action="store_true",
                     help="skip the other prefill geometries (packed varlen batch, long single sequence)")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="time the plain 1 GiB device-to-device copy (the measured HBM reference) even "
-                         "with --no-decode")
-    ap.add_argument("--no-copy-calibration", action="store_true",
-                    help="skip the 1 GiB copy that the decode legs are compared with")
+    ap.add_argument("--no-copy-peak", action="store_true", help="skip the streaming-copy HBM reference")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -218,10 +311,18 @@ def main():
         gdn.gdn_prefill_varlen(q, k, v, g, beta, cu, conv_weight=w, out=o, final_state_out=fs,
                                conv_state_out=cso, workspace=ws, validate=False, events=events)
 
-    print("[bench] warmup", file=sys.stderr, flush=True)
     # HIP events recorded by the library on its stream around each stage:
     # [before prep_kernel, before carry_kernel, after it, after the last launch]
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    print("[bench] device warm-up", file=sys.stderr, flush=True)
+    dw_calls, t0 = 0, time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < args.device_warmup_ms:
+        for _ in range(10):
+            step()
+        dw_calls += 10
+        torch.cuda.synchronize()
+    dw_ms = (time.perf_counter() - t0) * 1e3
+    print(f"[bench] warmup ({args.warmup} steps)", file=sys.stderr, flush=True)
     for i in range(args.warmup):
         step(evs[i % args.steps])
     torch.cuda.synchronize()
@@ -230,19 +331,20 @@ def main():
         step(e)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    call_ms = [e[0].elapsed_time(e[3]) for e in evs]
-    prep_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    carry_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    call_s = float(np.mean([e[0].elapsed_time(e[3]) for e in evs])) / 1e3
+    prep_s = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) / 1e3
+    carry_s = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) / 1e3
     ms_step = wall * 1e3 / args.steps
-    avg_call_s = float(np.mean(call_ms)) / 1e3
-    prep_s, carry_s = float(np.mean(prep_ms)) / 1e3, float(np.mean(carry_ms)) / 1e3
-    pbytes, pflops = prefill_algorithmic(T, B, 16, 32, 128)
-    cflops = carry_algorithmic(T, 32, 128)
-    prbytes = prep_bytes(T, B, 16, 32, 128)
-    print(f"[bench] prefill: {ms_step:.3f} ms/step wall, {avg_call_s * 1e3:.3f} ms/call, "
+    work = prefill_work([Tseq] * B, 16, 32, 128)
+    print(f"[bench] prefill: {ms_step:.3f} ms/step wall, {call_s * 1e3:.3f} ms/call, "
           f"prep_kernel {prep_s * 1e6:.1f} us, carry_kernel {carry_s * 1e6:.1f} us (events)",
           file=sys.stderr, flush=True)
 
+    carry_roof = roofline(*work["carry"], carry_s, CARRY_KERNEL)
+    carry_roof["traffic"] = measured_traffic(CARRY_KERNEL)
+    prep_roof = roofline(*work["prep"], prep_s, PREP_KERNEL)
+    prep_roof["traffic"] = measured_traffic(PREP_KERNEL)
+    call_roof = roofline(*work["call"], call_s)
     result = {
         "metric": "GDN prefill tokens/s (MFMA util); decode state-update HBM GB/s vs peak",
         "value": T / (wall / args.steps),
@@ -259,22 +361,12 @@ def main():
         "config": {"workload": "chunked varlen prefill, 4 sequences x 4096 tokens, h_k=16, h_v=32, "
                                "d_k=d_v=128, bf16 q/k/v, fp32 g/beta/state/o, conv4+SiLU+L2, chunk 64",
                    "num_seqs": B, "seq_len": Tseq, "h_k": 16, "h_v": 32, "d": 128},
-        # dominant kernel: the cross-chunk carry (dependent chain of matrix-core products)
-        "roofline": {"bound": "mfma", "achieved": cflops / carry_s / 1e12, "peak": MFMA_F16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": cflops / carry_s / 1e12 / MFMA_F16_PEAK_TFLOPS,
-                     "traffic": measured_traffic(CARRY_KERNEL), "kernel": CARRY_KERNEL,
-                     "algorithmic_flops": cflops, "avg_launch_us": carry_s * 1e6},
-        "kernels": {
-            PREP_KERNEL: {"avg_launch_us": prep_s * 1e6, "bound": "hbm", "moved_bytes": prbytes,
-                          "GB/s": prbytes / prep_s / 1e9, "frac": prbytes / prep_s / 1e9 / HBM_PEAK_GBS,
-                          "traffic": measured_traffic(PREP_KERNEL)},
-            CARRY_KERNEL: {"avg_launch_us": carry_s * 1e6, "bound": "mfma", "algorithmic_flops": cflops,
-                           "TFLOP/s": cflops / carry_s / 1e12},
-        },
-        "call": {"avg_us": avg_call_s * 1e6, "algorithmic_bytes": pbytes, "GB/s": pbytes / avg_call_s / 1e9,
-                 "hbm_frac": pbytes / avg_call_s / 1e9 / HBM_PEAK_GBS, "algorithmic_flops": pflops,
-                 "TFLOP/s": pflops / avg_call_s / 1e12},
-        "mfma_util": pflops / avg_call_s / (MFMA_F16_PEAK_TFLOPS * 1e12),
+        "device_warmup": {"calls": dw_calls, "ms": dw_ms,
+                          "note": "untimed prefill calls before the warm-up steps, to reach steady GPU clocks"},
+        "roofline": carry_roof,
+        "kernels": {PREP_KERNEL: prep_roof, CARRY_KERNEL: carry_roof},
+        "call": call_roof,
+        "mfma_util": call_roof["mfma_frac"],
     }
 
     # The same workload with bf16 outputs (o rounded once, to nearest even)
@@ -291,12 +383,12 @@ def main():
     for e in evs:
         step16(e)
     torch.cuda.synchronize()
-    c16 = float(np.mean([e[0].elapsed_time(e[3]) for e in evs])) * 1e3
-    b16, _ = prefill_algorithmic(T, B, 16, 32, 128, out_bytes=2)
-    result["prefill_bf16_out"] = {"us_per_call": c16, "tokens_per_s": T / (c16 * 1e-6),
+    c16 = float(np.mean([e[0].elapsed_time(e[3]) for e in evs])) / 1e3
+    w16 = prefill_work([Tseq] * B, 16, 32, 128, out_bytes=2)
+    result["prefill_bf16_out"] = {"us_per_call": c16 * 1e6, "tokens_per_s": T / c16,
                                   "carry_kernel_us": float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e3,
-                                  "algorithmic_bytes": b16, "GB/s": b16 / (c16 * 1e-6) / 1e9}
-    print(f"[bench] prefill, bf16 o: {c16:.1f} us/call (events)", file=sys.stderr, flush=True)
+                                  "roofline": roofline(*w16["call"], c16)}
+    print(f"[bench] prefill, bf16 o: {c16 * 1e6:.1f} us/call (events)", file=sys.stderr, flush=True)
     del o16
 
     if not args.no_decode:
@@ -334,16 +426,15 @@ def main():
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / nsteps
         dbytes, dflops = decode_algorithmic(N, 16, 32, 128)
-        gbs = dbytes / (us * 1e-6) / 1e9
+        droof = roofline(dbytes, dflops, us * 1e-6, DECODE_KERNEL)
+        droof["traffic"] = measured_traffic(DECODE_KERNEL)
         result["decode"] = {"workload": "decode step, 256 slots x 32 value heads (16 key heads), d=128, "
                                         "bf16 q/k/v, conv4+SiLU+L2, fp32 512 MiB state pool in place, "
                                         f"{NPOOL} pools in rotation",
-                            "steps": nsteps, "us_per_step": us, "GB/s": gbs,
-                            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                         "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic(DECODE_KERNEL),
-                                         "kernel": DECODE_KERNEL,
-                                         "algorithmic_bytes": dbytes}}
-        print(f"[bench] decode: {us:.1f} us/step, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
+                            "steps": nsteps, "us_per_step": us, "GB/s": dbytes / (us * 1e-6) / 1e9,
+                            "roofline": droof}
+        print(f"[bench] decode: {us:.1f} us/step, {dbytes / (us * 1e-6) / 1e9:.0f} GB/s", file=sys.stderr,
+              flush=True)
         del pools, cpools, dins
 
         # Multi-token (speculative) decode: m = 4 tokens per slot in one call,
@@ -386,10 +477,8 @@ def main():
             torch.cuda.synchronize()
             us = e0.elapsed_time(e1) * 1e3 / calls
             mb = decode_multi_algorithmic(N, m, 16, 32, 128, kept)
-            tkey = "decode_kernel_m4_all_states" if kept == m else "decode_kernel_m4_final_state"
-            mres[name] = {"us_per_call": us, "tokens_per_s": N * m / (us * 1e-6), "algorithmic_bytes": mb,
-                          "GB/s": mb / (us * 1e-6) / 1e9, "frac": mb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
-                          "traffic": measured_traffic(tkey)}
+            mres[name] = {"us_per_call": us, "tokens_per_s": N * m / (us * 1e-6),
+                          "roofline": roofline(mb, N * m * 32 * 7.0 * 128 * 128, us * 1e-6)}
             print(f"[bench] decode x{m} ({name}): {us:.1f} us/call, {mb / (us * 1e-6) / 1e9:.0f} GB/s",
                   file=sys.stderr, flush=True)
             del mpools, mcpools
@@ -400,53 +489,41 @@ def main():
         lens = uniform_lengths(2, 60, 1, 8192)
         print(f"[bench] packed varlen: 60 sequences, {int(lens.sum())} tokens, h_k=16 h_v=48", file=sys.stderr,
               flush=True)
-        us, tps, pr, ca = extra_prefill(gdn, torch, dev, lens, 16, 48, 128, 0.02, 5, 2)
-        extra["packed_varlen_60seq_hk16_hv48"] = {
-            "workload": f"60 sequences, lengths uniform 1..8192 (seeded, {int(lens.sum())} tokens), h_k=16, "
-                        "h_v=48, d=128, bf16 q/k/v, fp32 initial states 0.02 N(0,1), conv4+SiLU+L2",
-            "us_per_call": us, "tokens_per_s": tps, "prep_kernel_us": pr, "carry_kernel_us": ca}
-        print(f"[bench] packed varlen: {us:.0f} us/call, {tps / 1e6:.1f} M tokens/s", file=sys.stderr, flush=True)
-        us, tps, pr, ca = extra_prefill(gdn, torch, dev, [32768], 16, 32, 128, 0.0, 5, 4)
-        extra["single_sequence_32768_hk16_hv32"] = {
-            "workload": "one sequence of 32768 tokens, h_k=16, h_v=32, d=128, bf16 q/k/v, zero initial state, "
-                        "conv4+SiLU+L2 (a chain of 512 chunks)",
-            "us_per_call": us, "tokens_per_s": tps, "prep_kernel_us": pr, "carry_kernel_us": ca}
-        print(f"[bench] 32768-token sequence: {us:.0f} us/call, {tps / 1e6:.1f} M tokens/s", file=sys.stderr,
-              flush=True)
+        r = extra_prefill(gdn, torch, dev, lens, 16, 48, 128, 0.02, 5, 2)
+        r["workload"] = (f"60 sequences, lengths uniform 1..8192 (seeded, {int(lens.sum())} tokens), h_k=16, "
+                         "h_v=48, d=128, bf16 q/k/v, fp32 initial states 0.02 N(0,1), conv4+SiLU+L2")
+        extra["packed_varlen_60seq_hk16_hv48"] = r
+        print(f"[bench] packed varlen: {r['us_per_call']:.0f} us/call, {r['tokens_per_s'] / 1e6:.1f} M tokens/s",
+              file=sys.stderr, flush=True)
+        r = extra_prefill(gdn, torch, dev, [32768], 16, 32, 128, 0.0, 5, 4)
+        r["workload"] = ("one sequence of 32768 tokens, h_k=16, h_v=32, d=128, bf16 q/k/v, zero initial state, "
+                         "conv4+SiLU+L2 (a chain of 512 chunks)")
+        extra["single_sequence_32768_hk16_hv32"] = r
+        print(f"[bench] 32768-token sequence: {r['us_per_call']:.0f} us/call, "
+              f"{r['tokens_per_s'] / 1e6:.1f} M tokens/s", file=sys.stderr, flush=True)
         result["other_prefill_configs"] = extra
 
-    if (args.copy_calibration or not args.no_decode) and not args.no_copy_calibration:
-        nbytes = 1 << 30
-        src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        reps = 10
-        e0.record(stream)
-        for _ in range(reps):
-            dst.copy_(src)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / reps
-        copy_gbs = 2 * nbytes / (us * 1e-6) / 1e9
-        result["copy_calibration"] = {"bytes_read": nbytes, "bytes_written": nbytes, "us_per_copy": us,
-                                      "GB/s": copy_gbs}
-        # the decode legs against the measured copy as well as the datasheet peak
-        if "decode" in result:
-            result["decode"]["roofline"]["frac_of_measured_copy"] = result["decode"]["GB/s"] / copy_gbs
-        for leg in result.get("decode_multi", {}).values():
-            if isinstance(leg, dict):
-                leg["frac_of_measured_copy"] = leg["GB/s"] / copy_gbs
-        print(f"[bench] copy 1 GiB: {us:.1f} us, {2 * nbytes / (us * 1e-6) / 1e9:.0f} GB/s", file=sys.stderr, flush=True)
-        del src, dst
+    if not args.no_copy_peak:
+        peak = stream_copy_peak(gdn, torch, dev, stream)
+        result["measured_hbm_peak"] = peak
+        mp = peak["GB/s"]
+        # fractions of every HBM-bound figure against the measured peak too
+        for r in [result["roofline"], result["kernels"][PREP_KERNEL], result["call"],
+                  result["prefill_bf16_out"]["roofline"]] + \
+                ([result["decode"]["roofline"]] if "decode" in result else []) + \
+                [leg["roofline"] for leg in result.get("decode_multi", {}).values() if isinstance(leg, dict)] + \
+                [leg[key] for leg in result.get("other_prefill_configs", {}).values()
+                 for key in ("roofline", "carry_roofline")]:
+            if r["bound"] == "hbm":
+                r["frac_of_measured_peak"] = r["achieved"] / mp
+        print(f"[bench] stream copy 1 GiB: {peak['us_per_copy']:.1f} us, {mp:.0f} GB/s "
+              f"({peak['workgroups']} workgroups)", file=sys.stderr, flush=True)
 
     if not args.no_cpu_baseline:
         n = len(os.sched_getaffinity(0))
         n = min(n, int(os.environ.get("OMP_NUM_THREADS", n)))
-        print(f"[bench] cpu baseline: fp64 oracle on {n} threads", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(x, n)
+        print(f"[bench] cpu baseline: fp64 oracle on {n} threads and on 1", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baselines(x, geom, n)
     print(json.dumps(result), flush=True)
 
 

@@ -1,7 +1,9 @@
 """ctypes binding of libgdn.so: argument checks and marshalling only.
 
 Every step of the computation runs in the HIP kernels behind the C ABI
-(include/gdn.h).  PyTorch supplies device memory and the current stream.
+(include/gdn.h).  PyTorch supplies device memory and streams: the kernels go to
+torch's current stream or a given torch.cuda.Stream, on which the call's
+temporaries and default outputs are allocated too.
 There is no fallback: if libgdn.so is missing or a call fails, this module
 raises.
 """
@@ -19,7 +21,8 @@ GDN_F32, GDN_BF16 = 0, 1
 _STATUS = {0: "GDN_OK", -1: "GDN_ERR_NULL", -2: "GDN_ERR_SHAPE", -3: "GDN_ERR_DTYPE",
            -4: "GDN_ERR_UNSUPPORTED", -5: "GDN_ERR_WORKSPACE", -6: "GDN_ERR_HIP", -7: "GDN_ERR_ALIAS"}
 EXPORTED = ("gdn_prefill_workspace_bytes", "gdn_prefill_varlen", "gdn_prefill_varlen_timed",
-            "gdn_prefill_varlen_pooled", "gdn_decode_step", "gdn_decode_multi", "gdn_status_string")
+            "gdn_prefill_varlen_pooled", "gdn_decode_step", "gdn_decode_multi",
+            "gdn_stream_copy", "gdn_status_string")
 
 
 class GdnProblem(ctypes.Structure):
@@ -63,6 +66,8 @@ def load() -> ctypes.CDLL:
         lib.gdn_decode_step.restype = ctypes.c_int
         lib.gdn_decode_multi.argtypes = [ctypes.POINTER(GdnProblem), ctypes.c_int32] + [vp] * 13
         lib.gdn_decode_multi.restype = ctypes.c_int
+        lib.gdn_stream_copy.argtypes = [vp, vp, c64, ctypes.c_int32, vp]
+        lib.gdn_stream_copy.restype = ctypes.c_int
         lib.gdn_status_string.argtypes = [ctypes.c_int]
         lib.gdn_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -83,6 +88,29 @@ def _dtype_code(dt: torch.dtype, what: str) -> int:
 
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _resolve_stream(stream, dev):
+    """The stream the kernels go to: torch's current stream of `dev`, or the
+    given torch.cuda.Stream (a raw handle is refused: the temporaries of a
+    call must be allocated on the stream that uses them)."""
+    if stream is None:
+        return torch.cuda.current_stream(dev)
+    if not isinstance(stream, torch.cuda.Stream):
+        raise ValueError("stream must be a torch.cuda.Stream (or None for the current stream)")
+    if stream.device != dev:
+        raise ValueError(f"stream is on {stream.device}, the inputs on {dev}")
+    return stream
+
+
+def _hold_for(s, dev, tensors):
+    """On a stream other than the current one, mark every tensor the kernels
+    use as in use by that stream, so that the caching allocator does not hand
+    its memory to other work before the kernels are done with it."""
+    if s != torch.cuda.current_stream(dev):
+        for t in tensors:
+            if isinstance(t, torch.Tensor) and t.is_cuda:
+                t.record_stream(s)
 
 
 def _check(t, name, shape, dtype, device):
@@ -133,6 +161,9 @@ def gdn_prefill_varlen(q, k, v, g, beta, cu_seqlens=None, *, conv_weight=None, c
     ``(o, final_state or None, conv_state_out or None)``.  With ``events`` (four
     ``torch.cuda.Event(enable_timing=True)``) the call goes through
     ``gdn_prefill_varlen_timed``, which records them around its stages.
+    ``stream``: a
+    ``torch.cuda.Stream`` or None (the current stream); temporaries and
+    default outputs are allocated on it.
     """
     if q.dim() == 4:
         if cu_seqlens is not None:
@@ -146,6 +177,7 @@ def gdn_prefill_varlen(q, k, v, g, beta, cu_seqlens=None, *, conv_weight=None, c
     dev = q.device
     if dev.type != "cuda":
         raise ValueError("inputs must be on the GPU")
+    s = _resolve_stream(stream, dev)
     T, h_k, d_k = q.shape
     if v.dim() != 3 or v.shape[0] != T:
         raise ValueError("v must be [T, h_v, d_v]")
@@ -166,9 +198,10 @@ def gdn_prefill_varlen(q, k, v, g, beta, cu_seqlens=None, *, conv_weight=None, c
         raise ValueError("cu_seqlens must be a 1-D int32 tensor")
     if validate:
         _validate_cu(cu_seqlens.cpu(), T)
-    if cu_seqlens.device != dev:
-        cu_seqlens = cu_seqlens.to(dev)
-    cu_seqlens = cu_seqlens.contiguous()
+    with torch.cuda.stream(s):
+        if cu_seqlens.device != dev:
+            cu_seqlens = cu_seqlens.to(dev)
+        cu_seqlens = cu_seqlens.contiguous()
     N = cu_seqlens.numel() - 1
     C = 2 * h_k * d_k + h_v * d_v
     conv_width = 4 if conv_weight is not None else 0
@@ -180,29 +213,31 @@ def gdn_prefill_varlen(q, k, v, g, beta, cu_seqlens=None, *, conv_weight=None, c
         raise ValueError("conv_bias/conv_state given without conv_weight")
     _check(initial_state, "initial_state", (N, h_v, d_k, d_v), torch.float32, dev)
 
-    o = out if out is not None else torch.empty((T, h_v, d_v), dtype=out_dtype, device=dev)
+    with torch.cuda.stream(s):
+        o = out if out is not None else torch.empty((T, h_v, d_v), dtype=out_dtype, device=dev)
+        fs = None
+        if output_final_state:
+            fs = final_state_out if final_state_out is not None else torch.empty((N, h_v, d_k, d_v), dtype=torch.float32, device=dev)
+        cso = None
+        if output_conv_state and conv_width:
+            cso = conv_state_out if conv_state_out is not None else torch.empty((N, C, 3), dtype=qdt, device=dev)
     _check(o, "out", (T, h_v, d_v), out_dtype, dev)
-    fs = None
-    if output_final_state:
-        fs = final_state_out if final_state_out is not None else torch.empty((N, h_v, d_k, d_v), dtype=torch.float32, device=dev)
-        _check(fs, "final_state_out", (N, h_v, d_k, d_v), torch.float32, dev)
-    cso = None
-    if output_conv_state and conv_width:
-        cso = conv_state_out if conv_state_out is not None else torch.empty((N, C, 3), dtype=qdt, device=dev)
-        _check(cso, "conv_state_out", (N, C, 3), qdt, dev)
+    _check(fs, "final_state_out", (N, h_v, d_k, d_v), torch.float32, dev)
+    _check(cso, "conv_state_out", (N, C, 3), qdt, dev)
     prob = make_problem(N, T, h_k, h_v, d_k, d_v, qcode, ocode, scale, use_qk_l2norm, l2_eps, conv_width,
                         beta_logits)
     ws_bytes = gdn_prefill_workspace_bytes(prob)
     if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+        with torch.cuda.stream(s):
+            workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     elif workspace.numel() < ws_bytes:
         raise ValueError("workspace too small")
-    if stream is None:
-        stream = torch.cuda.current_stream(dev).cuda_stream
+    _hold_for(s, dev, (q, k, v, g, beta, cu_seqlens, conv_weight, conv_bias, conv_state, cso, initial_state, o, fs,
+                       workspace))
     args = (ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
             _ptr(cu_seqlens), _ptr(conv_weight), _ptr(conv_bias), _ptr(conv_state),
             _ptr(cso), _ptr(initial_state), _ptr(o), _ptr(fs), _ptr(workspace),
-            ctypes.c_size_t(workspace.numel()), ctypes.c_void_p(stream))
+            ctypes.c_size_t(workspace.numel()), ctypes.c_void_p(s.cuda_stream))
     if events is None:
         st = load().gdn_prefill_varlen(*args)
     else:
@@ -218,6 +253,23 @@ def gdn_prefill_varlen(q, k, v, g, beta, cu_seqlens=None, *, conv_weight=None, c
     if st != 0:
         raise GdnError(st, "gdn_prefill_varlen")
     return o, fs, cso
+
+
+
+def gdn_stream_copy(dst, src, blocks, stream=None):
+    """Device copy of src into dst (same byte size) by the library's streaming
+    copy kernel (C ABI ``gdn_stream_copy``), a bandwidth reference."""
+    if dst.device != src.device or dst.device.type != "cuda":
+        raise ValueError("dst and src must be on the same GPU")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes or not (src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("dst and src must be contiguous buffers of the same size")
+    s = _resolve_stream(stream, src.device)
+    _hold_for(s, src.device, (dst, src))
+    st = load().gdn_stream_copy(_ptr(dst), _ptr(src), ctypes.c_size_t(nbytes), ctypes.c_int32(blocks),
+                                ctypes.c_void_p(s.cuda_stream))
+    if st != 0:
+        raise GdnError(st, "gdn_stream_copy")
 
 
 def _check_indices(state_indices, N, P, Pc, dev, validate):
@@ -272,7 +324,9 @@ def gdn_prefill_varlen_pooled(q, k, v, g, beta, cu_seqlens, state_pool, *, state
         raise ValueError("cu_seqlens must be a 1-D int32 tensor")
     if validate:
         _validate_cu(cu_seqlens.cpu(), T)
-    cu_seqlens = cu_seqlens.to(dev).contiguous()
+    s = _resolve_stream(stream, dev)
+    with torch.cuda.stream(s):
+        cu_seqlens = cu_seqlens.to(dev).contiguous()
     N = cu_seqlens.numel() - 1
     if state_pool.dim() != 4:
         raise ValueError("state_pool must be [P, h_v, d_k, d_v]")
@@ -293,22 +347,24 @@ def gdn_prefill_varlen_pooled(q, k, v, g, beta, cu_seqlens, state_pool, *, state
     _check_indices(state_indices, N, P, Pc, dev, validate)
     if has_initial_state is not None:
         _check(has_initial_state, "has_initial_state", (N,), torch.int32, dev)
-    o = out if out is not None else torch.empty((T, h_v, d_v), dtype=out_dtype, device=dev)
+    with torch.cuda.stream(s):
+        o = out if out is not None else torch.empty((T, h_v, d_v), dtype=out_dtype, device=dev)
     _check(o, "out", (T, h_v, d_v), out_dtype, dev)
     prob = make_problem(N, T, h_k, h_v, d_k, d_v, qcode, ocode, scale, use_qk_l2norm, l2_eps, conv_width,
                         beta_logits)
     ws_bytes = gdn_prefill_workspace_bytes(prob)
     if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+        with torch.cuda.stream(s):
+            workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     elif workspace.numel() < ws_bytes:
         raise ValueError("workspace too small")
-    if stream is None:
-        stream = torch.cuda.current_stream(dev).cuda_stream
+    _hold_for(s, dev, (q, k, v, g, beta, cu_seqlens, conv_weight, conv_bias, conv_state_pool, state_pool,
+                       state_indices, has_initial_state, o, workspace))
     st = load().gdn_prefill_varlen_pooled(
         ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
         _ptr(conv_weight), _ptr(conv_bias), _ptr(conv_state_pool), _ptr(state_pool), _ptr(state_indices),
         _ptr(has_initial_state), _ptr(o), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
-        ctypes.c_void_p(stream))
+        ctypes.c_void_p(s.cuda_stream))
     if st != 0:
         raise GdnError(st, "gdn_prefill_varlen_pooled")
     return o
@@ -353,15 +409,16 @@ def gdn_decode_step(q, k, v, g, beta, state_pool, *, state_indices=None, conv_we
             raise ValueError("conv_state_pool must be [P, C, 3]")
         _check(conv_state_pool, "conv_state_pool", (conv_state_pool.shape[0], C, 3), qdt, dev)
     _check_indices(state_indices, N, P, conv_state_pool.shape[0] if conv_width else None, dev, validate)
-    o = out if out is not None else torch.empty((N, h_v, d_v), dtype=out_dtype, device=dev)
+    s = _resolve_stream(stream, dev)
+    with torch.cuda.stream(s):
+        o = out if out is not None else torch.empty((N, h_v, d_v), dtype=out_dtype, device=dev)
     _check(o, "out", (N, h_v, d_v), out_dtype, dev)
     prob = make_problem(N, N, h_k, h_v, d_k, d_v, qcode, ocode, scale, use_qk_l2norm, l2_eps, conv_width,
                         beta_logits)
-    if stream is None:
-        stream = torch.cuda.current_stream(dev).cuda_stream
+    _hold_for(s, dev, (q, k, v, g, beta, conv_weight, conv_bias, conv_state_pool, state_pool, state_indices, o))
     st = load().gdn_decode_step(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                 _ptr(conv_weight), _ptr(conv_bias), _ptr(conv_state_pool), _ptr(state_pool),
-                                _ptr(state_indices), _ptr(o), ctypes.c_void_p(stream))
+                                _ptr(state_indices), _ptr(o), ctypes.c_void_p(s.cuda_stream))
     if st != 0:
         raise GdnError(st, "gdn_decode_step")
     return o
@@ -434,16 +491,18 @@ def gdn_decode_multi(q, k, v, g, beta, state_pool, *, state_indices=None, num_ac
             acc = num_accepted.cpu()
             if bool((acc < 1).any()) or bool((acc > m).any()):
                 raise ValueError("num_accepted must lie in 1..m")
-    o = out if out is not None else torch.empty((N, m, h_v, d_v), dtype=out_dtype, device=dev)
+    s = _resolve_stream(stream, dev)
+    with torch.cuda.stream(s):
+        o = out if out is not None else torch.empty((N, m, h_v, d_v), dtype=out_dtype, device=dev)
     _check(o, "out", (N, m, h_v, d_v), out_dtype, dev)
     prob = make_problem(N, N * m, h_k, h_v, d_k, d_v, qcode, ocode, scale, use_qk_l2norm, l2_eps, conv_width,
                         beta_logits)
-    if stream is None:
-        stream = torch.cuda.current_stream(dev).cuda_stream
+    _hold_for(s, dev, (q, k, v, g, beta, conv_weight, conv_bias, conv_state_pool, state_pool, state_indices,
+                       num_accepted, o))
     st = load().gdn_decode_multi(ctypes.byref(prob), ctypes.c_int32(m), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                  _ptr(beta), _ptr(conv_weight), _ptr(conv_bias), _ptr(conv_state_pool),
                                  _ptr(state_pool), _ptr(state_indices), _ptr(num_accepted), _ptr(o),
-                                 ctypes.c_void_p(stream))
+                                 ctypes.c_void_p(s.cuda_stream))
     if st != 0:
         raise GdnError(st, "gdn_decode_multi")
     return o

@@ -1,5 +1,5 @@
 // Device-side helpers for the gfx950 GDN kernels: element conversion,
-// 16-byte vector loads and the 16x16x32 matrix-core step.
+// 16-byte vector loads and the matrix-core operand fragments and steps.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -7,7 +7,6 @@
 
 namespace gdn {
 
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 // 16 raw bytes as a native vector (kept in registers across loop iterations,
 // where a struct-typed uint4 array can end up in scratch memory).
@@ -99,32 +98,40 @@ __device__ __forceinline__ float beta_of(float b, bool logits) { return logits ?
 // negative y gives exp = inf and a zero reciprocal, so the result is -0.
 __device__ __forceinline__ float silu(float y) { return y * __builtin_amdgcn_rcpf(1.0f + __expf(-y)); }
 
-// ---- split operands: x ~= hi + lo, both halves 16-bit matrix-core inputs ----
-// A product of two split operands takes three 16-bit matrix-core steps,
-// lo*hi + hi*lo + hi*hi (lo*lo is dropped), accumulated in fp32.  Two element
-// types are used:
-//  * bf16 (operands of bf16-input calls): hi = bf16(x), lo = bf16(x - hi),
-//    both rounded to nearest even.  The pair keeps about 16 significant bits
-//    (|x - hi - lo| <= 2^-16 |x|) over the whole fp32 range, and costs three
-//    vector instructions per value (two values per packed conversion).
-//  * fp16 (operands of fp32-input calls): hi = fp16(x), lo = fp16((x - hi) 2^11).
-//    Scaling the residual by 2^11 keeps lo out of fp16's subnormal range, so
-//    the pair keeps about 22 significant bits for 2^-14 <= |x| < 65504; the
-//    cross terms go into a second accumulator that is scaled by 2^-11 at the end.
-typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+// ---- matrix-core operands ----
+// Every product A B runs on the matrix cores from "fragments": lane l holds 8
+// consecutive K-index values of one row of A (or one column of B), k = 8 (l/16)
+// + e, e = 0..7, in two 16-byte halves `hi` and `lo`.  Two kinds:
+//  * split bf16 (bf16-input calls): x ~= hi + lo with hi = bf16(x) and
+//    lo = bf16(x - hi), both rounded to nearest even; a product takes three
+//    16x16x32 bf16 steps, lo*hi + hi*lo + hi*hi (lo*lo is dropped), fp32
+//    accumulation.  The pair keeps about 16 significant bits
+//    (|x - hi - lo| <= 2^-16 |x|) over the whole fp32 range.
+//  * fp32 (fp32-input calls): the 8 values themselves, `hi` = elements 0..3
+//    and `lo` = elements 4..7; a product takes eight 16x16x4 fp32 steps, step e
+//    multiplying element e of each lane's A and B values (its four k indices,
+//    e, 8 + e, 16 + e, 24 + e, one per 16-lane group), fp32 accumulation.
+//    Full fp32 range and precision, at a sixteenth of the bf16 rate.
+// Both kinds take 32 bytes per lane and fragment, so LDS and workspace images
+// have one layout: planes of 16-bit units, 16-byte pieces of 8 columns, the
+// hi plane holding the first and the lo plane the second 16 bytes of each.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float float2_t __attribute__((ext_vector_type(2)));
 
-template <typename E> struct OpVec;
-template <> struct OpVec<_Float16> { typedef half8_t v8; typedef half4_t v4; };
-template <> struct OpVec<__bf16> { typedef bf16x8_t v8; typedef bf16x4_t v4; };
+// 16-bit storage unit of fp32 operand planes (an fp32 value takes two).
+struct alignas(2) F32Op {
+    uint16_t bits;
+};
 
-// Operand element type for each input element type.
+template <typename E> struct OpVec;
+template <> struct OpVec<__bf16> { typedef bf16x8_t v8; };
+template <> struct OpVec<F32Op> { typedef float4_t v8; };
+
+// Operand kind for each input element type.
 template <typename TIn> struct OpFor;
-template <> struct OpFor<float> { typedef _Float16 type; };
+template <> struct OpFor<float> { typedef F32Op type; };
 template <> struct OpFor<bf16_t> { typedef __bf16 type; };
 
 template <typename E>
@@ -132,25 +139,8 @@ struct SFrag {
     typename OpVec<E>::v8 hi, lo;
 };
 
-constexpr float kLoScale = 2048.0f;
-constexpr float kLoUnscale = 1.0f / 2048.0f;
-
-// fp16: hi is x converted by the hardware converter; the residual x - hi is
-// then exact in fp32 (hi is converted back, so the pair always refers to the
-// stored hi whatever rounding the converter applied) and is scaled by 2^11
-// before its own conversion.  Values below fp16's normal range (2^-14) go
-// entirely into lo: the matrix cores treat fp16 subnormal inputs as zero.
-__device__ __forceinline__ _Float16 split_hi(float x) {
-    return fabsf(x) < 6.103515625e-05f ? static_cast<_Float16>(0.0f) : static_cast<_Float16>(x);
-}
-
-// Splits of the value pair (x0, x1); element 0 of each result belongs to x0.
-__device__ __forceinline__ void split2(float x0, float x1, half2_t& hi, half2_t& lo) {
-    hi = half2_t{split_hi(x0), split_hi(x1)};
-    lo = half2_t{static_cast<_Float16>((x0 - static_cast<float>(hi[0])) * kLoScale),
-                 static_cast<_Float16>((x1 - static_cast<float>(hi[1])) * kLoScale)};
-}
-// bf16: the residual x - hi is exact in fp32 (hi keeps the leading 8 bits of x).
+// bf16 split of the value pair (x0, x1); element 0 of each result belongs to
+// x0.  The residual x - hi is exact in fp32 (hi keeps the leading 8 bits of x).
 __device__ __forceinline__ void split2(float x0, float x1, bf16x2_t& hi, bf16x2_t& lo) {
     const float2_t v = {x0, x1};
     hi = __builtin_convertvector(v, bf16x2_t);
@@ -160,41 +150,31 @@ __device__ __forceinline__ void split2(float x0, float x1, bf16x2_t& hi, bf16x2_
 
 template <typename E>
 __device__ __forceinline__ SFrag<E> split8(const float (&x)[8]) {
-    typedef typename OpVec<E>::v8 V8;
-    typedef E V2 __attribute__((ext_vector_type(2)));
-    V2 h[4], l[4];
-#pragma unroll
-    for (int i = 0; i < 4; i++) split2(x[2 * i], x[2 * i + 1], h[i], l[i]);
     SFrag<E> f;
-    f.hi = V8{h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
-    f.lo = V8{l[0][0], l[0][1], l[1][0], l[1][1], l[2][0], l[2][1], l[3][0], l[3][1]};
+    if constexpr (__is_same(E, F32Op)) {
+        f.hi = float4_t{x[0], x[1], x[2], x[3]};
+        f.lo = float4_t{x[4], x[5], x[6], x[7]};
+    } else {
+        bf16x2_t h[4], l[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) split2(x[2 * i], x[2 * i + 1], h[i], l[i]);
+        f.hi = bf16x8_t{h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
+        f.lo = bf16x8_t{l[0][0], l[0][1], l[1][0], l[1][1], l[2][0], l[2][1], l[3][0], l[3][1]};
+    }
     return f;
 }
 
-// hh += A.hi B.hi; xx += A.lo B.hi + A.hi B.lo (the fp16 cross terms carry the
-// 2^11 scale; the bf16 ones do not and go straight into hh).
-__device__ __forceinline__ void mma3(float4_t& hh, float4_t& xx, const SFrag<_Float16>& a, const SFrag<_Float16>& b) {
-    xx = __builtin_amdgcn_mfma_f32_16x16x32_f16(a.lo, b.hi, xx, 0, 0, 0);
-    xx = __builtin_amdgcn_mfma_f32_16x16x32_f16(a.hi, b.lo, xx, 0, 0, 0);
-    hh = __builtin_amdgcn_mfma_f32_16x16x32_f16(a.hi, b.hi, hh, 0, 0, 0);
+// acc += A B over one 32-deep K step.
+__device__ __forceinline__ void mma3(float4_t& acc, const SFrag<__bf16>& a, const SFrag<__bf16>& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b.hi, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.lo, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, acc, 0, 0, 0);
 }
-__device__ __forceinline__ void mma3(float4_t& hh, float4_t&, const SFrag<__bf16>& a, const SFrag<__bf16>& b) {
-    hh = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b.hi, hh, 0, 0, 0);
-    hh = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.lo, hh, 0, 0, 0);
-    hh = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, hh, 0, 0, 0);
-}
-
-// The finished product.
-template <typename E>
-__device__ __forceinline__ float4_t combine(const float4_t& hh, const float4_t& xx) {
-    if constexpr (__is_same(E, __bf16)) {
-        return hh;
-    } else {
-        float4_t r;
+__device__ __forceinline__ void mma3(float4_t& acc, const SFrag<F32Op>& a, const SFrag<F32Op>& b) {
 #pragma unroll
-        for (int i = 0; i < 4; i++) r[i] = hh[i] + xx[i] * kLoUnscale;
-        return r;
-    }
+    for (int e = 0; e < 4; e++) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[e], b.hi[e], acc, 0, 0, 0);
+#pragma unroll
+    for (int e = 0; e < 4; e++) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[e], b.lo[e], acc, 0, 0, 0);
 }
 
 constexpr float4_t kZero4 = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -210,30 +190,39 @@ __device__ __forceinline__ SFrag<E> lds_sfrag(const E* hi, const E* lo, int pitc
 }
 
 // Fragment whose K index runs down the rows of row-major hi/lo LDS matrices:
-// element e is M[k + e][col0 + l%16], read with the gfx950 LDS transpose load
-// (ds_read_b64_tr_b16), 4 instructions.  Within each 16-lane group the load treats
-// the 8-byte chunks addressed by lanes 0..15 as a 16x4 matrix M and returns
-// M[j/4 + 4m][j%4], m = 0..3, to lane j.  So lane j addresses 4 consecutive
-// columns col0 + 4 (j%4) .. of row k + j/4 and receives column col0 + j of
-// rows k .. k+3; a second load covers rows k+4 .. k+7.  col0 is a multiple of
-// 16 and the rows must be 8-byte aligned.
+// element e is M[k + e][col0 + l%16].  bf16 planes are read with the gfx950
+// LDS transpose load (ds_read_b64_tr_b16), 4 instructions.  Within each
+// 16-lane group the load treats the 8-byte chunks addressed by lanes 0..15 as
+// a 16x4 matrix M and returns M[j/4 + 4m][j%4], m = 0..3, to lane j.  So lane
+// j addresses 4 consecutive columns col0 + 4 (j%4) .. of row k + j/4 and
+// receives column col0 + j of rows k .. k+3; a second load covers rows
+// k+4 .. k+7.  col0 is a multiple of 16 and the rows must be 8-byte aligned.
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4_t lds_short4_t;
 // The loaded vectors are reinterpreted whole and joined with a shuffle: with
 // ROCm 7.2's clang, extracting their 16-bit elements one by one produced code
 // that kept only the first two elements of each load (checked on the GPU).
-template <typename E>
-__device__ __forceinline__ typename OpVec<E>::v4 lds_tr16(const E* p) {
-    return __builtin_bit_cast(typename OpVec<E>::v4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(p)));
+__device__ __forceinline__ bf16x4_t lds_tr16(const __bf16* p) {
+    return __builtin_bit_cast(bf16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(p)));
 }
-template <typename E>
-__device__ __forceinline__ SFrag<E> lds_sfrag_tr(const E* hi, const E* lo, int pitch, int k, int col0) {
+__device__ __forceinline__ SFrag<__bf16> lds_sfrag_tr(const __bf16* hi, const __bf16* lo, int pitch, int k,
+                                                      int col0) {
     const int j = threadIdx.x & 15;
     const int off = (k + (j >> 2)) * pitch + col0 + 4 * (j & 3);
-    SFrag<E> f;
+    SFrag<__bf16> f;
     f.hi = __builtin_shufflevector(lds_tr16(hi + off), lds_tr16(hi + off + 4 * pitch), 0, 1, 2, 3, 4, 5, 6, 7);
     f.lo = __builtin_shufflevector(lds_tr16(lo + off), lds_tr16(lo + off + 4 * pitch), 0, 1, 2, 3, 4, 5, 6, 7);
     return f;
+}
+// fp32 planes: column c of a row sits in plane (c & 4 ? lo : hi) at 16-bit
+// offset (c & ~7) + 2 (c & 3); eight scalar reads.
+__device__ __forceinline__ SFrag<F32Op> lds_sfrag_tr(const F32Op* hi, const F32Op* lo, int pitch, int k, int col0) {
+    const int c = col0 + (threadIdx.x & 15);
+    const F32Op* base = ((c & 4) ? lo : hi) + (c & ~7) + 2 * (c & 3);
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) x[e] = *reinterpret_cast<const float*>(base + (k + e) * pitch);
+    return split8<F32Op>(x);
 }
 
 // Operand fragment from two accumulator tiles that hold rows [32s, 32s+16) and

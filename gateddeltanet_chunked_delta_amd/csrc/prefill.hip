@@ -36,10 +36,10 @@
 //                     registers while the current chunk computes.  At the
 //                     end its helper waves write the final conv states.
 //
-// Precision: every product takes split operands (x = hi + lo, three 16-bit
-// matrix-core steps, fp32 accumulation): bf16 pairs (about 16 significant
-// bits, full fp32 range) for bf16 inputs, fp16 pairs (about 22 significant
-// bits, magnitudes below 65504) for fp32 inputs.  The diagonal blocks of T
+// Precision: every product runs on the matrix cores with fp32 accumulation:
+// split bf16 operands (x = hi + lo, three bf16 steps, about 16 significant
+// bits) for bf16 inputs, fp32 operands (fp32 steps) for fp32 inputs; both
+// keep the whole fp32 range.  The diagonal blocks of T
 // come from an fp32 forward substitution and the off-diagonal blocks from
 // fp32 matrix-core steps; the decays are scanned and exponentiated in fp64.
 //
@@ -421,18 +421,15 @@ struct PrepSmem {
 template <int R, int KS, int PK, typename E>
 __device__ __forceinline__ void gram_row(const E* Ahi, const E* Alo, const E* Khi, const E* Klo, int lr, int lg,
                                          float4_t (&acc)[R + 1]) {
-    float4_t hh[R + 1], xx[R + 1];
 #pragma unroll
-    for (int j = 0; j <= R; j++) hh[j] = xx[j] = kZero4;
+    for (int j = 0; j <= R; j++) acc[j] = kZero4;
 #pragma unroll
     for (int ks = 0; ks < KS; ks++) {
         const int k = 32 * ks + 8 * lg;
         const SFrag<E> a = lds_sfrag(Ahi, Alo, PK, 16 * R + lr, k);
 #pragma unroll
-        for (int t = 0; t <= R; t++) mma3(hh[t], xx[t], a, lds_sfrag(Khi, Klo, PK, 16 * t + lr, k));
+        for (int t = 0; t <= R; t++) mma3(acc[t], a, lds_sfrag(Khi, Klo, PK, 16 * t + lr, k));
     }
-#pragma unroll
-    for (int j = 0; j <= R; j++) acc[j] = combine<E>(hh[j], xx[j]);
 }
 
 // Workgroup = (chunk slot, key head).  Slots past the last chunk exit.
@@ -587,22 +584,24 @@ __global__ void __launch_bounds__(kPrepThreads, 1) prep_kernel(const PrefillPara
                     sum += r4.w;
                 }
                 const float sc = p.qk_l2norm ? 1.0f / sqrtf(sum + p.l2_eps) : 1.0f;
-                typedef E E2 __attribute__((ext_vector_type(2)));
-                E2 h16[VEC / 2], l16[VEC / 2];
-#pragma unroll
-                for (int e = 0; e < VEC / 2; e++) split2(y[i][2 * e] * sc, y[i][2 * e + 1] * sc, h16[e], l16[e]);
                 if constexpr (VEC == 8) {
+                    // bf16 pairs: 8 columns per plane piece
+                    bf16x2_t h16[VEC / 2], l16[VEC / 2];
+#pragma unroll
+                    for (int e = 0; e < VEC / 2; e++) split2(y[i][2 * e] * sc, y[i][2 * e + 1] * sc, h16[e], l16[e]);
                     const uint4 hv = *reinterpret_cast<const uint4*>(h16), lv = *reinterpret_cast<const uint4*>(l16);
                     *reinterpret_cast<uint4*>(dhi + row * PK + poff) = hv;
                     *reinterpret_cast<uint4*>(dlo + row * PK + poff) = lv;
                     *reinterpret_cast<uint4*>(img + row * DK + poff) = hv;
                     *reinterpret_cast<uint4*>(img + kChunk * DK + row * DK + poff) = lv;
                 } else {
-                    const uint2 hv = *reinterpret_cast<const uint2*>(h16), lv = *reinterpret_cast<const uint2*>(l16);
-                    *reinterpret_cast<uint2*>(dhi + row * PK + poff) = hv;
-                    *reinterpret_cast<uint2*>(dlo + row * PK + poff) = lv;
-                    *reinterpret_cast<uint2*>(img + row * DK + poff) = hv;
-                    *reinterpret_cast<uint2*>(img + kChunk * DK + row * DK + poff) = lv;
+                    // fp32 values: columns 8c .. 8c+3 go to the hi plane and
+                    // 8c+4 .. 8c+7 to the lo plane, at the piece of columns 8c
+                    const float4 v = make_float4(y[i][0] * sc, y[i][1] * sc, y[i][2] * sc, y[i][3] * sc);
+                    const int c8 = poff & ~7;
+                    const bool second = (poff & 4) != 0;
+                    *reinterpret_cast<float4*>((second ? dlo : dhi) + row * PK + c8) = v;
+                    *reinterpret_cast<float4*>(img + (second ? kChunk * DK : 0) + row * DK + c8) = v;
                 }
             }
         }
@@ -1000,11 +999,9 @@ __global__ void __launch_bounds__(kCarryThreads, 1) carry_kernel(const PrefillPa
             float4_t rr[4];
 #pragma unroll
             for (int tb = 0; tb < 4; tb++) {
-                float4_t khh = kZero4, khx = kZero4;
+                float4_t kh = kZero4;
 #pragma unroll
-                for (int ks = 0; ks < KS; ks++)
-                    mma3(khh, khx, lds_sfrag(Khi, Klo, PK, 16 * tb + lr, 32 * ks + 8 * lg), hb[ks]);
-                const float4_t kh = combine<E>(khh, khx);
+                for (int ks = 0; ks < KS; ks++) mma3(kh, lds_sfrag(Khi, Klo, PK, 16 * tb + lr, 32 * ks + 8 * lg), hb[ks]);
                 const float4 egv = *reinterpret_cast<const float4*>(eg + 16 * tb + 4 * lg);
                 const float4 btv = *reinterpret_cast<const float4*>(bet + 16 * tb + 4 * lg);
                 const float egr[4] = {egv.x, egv.y, egv.z, egv.w}, btr[4] = {btv.x, btv.y, btv.z, btv.w};
@@ -1033,11 +1030,9 @@ __global__ void __launch_bounds__(kCarryThreads, 1) carry_kernel(const PrefillPa
                 }
 #pragma unroll
                 for (int tb = 0; tb < 4; tb++) {
-                    float4_t hh = kZero4, xx = kZero4;
+                    dd[tb] = kZero4;
 #pragma unroll
-                    for (int ks = 0; ks <= tb / 2; ks++)
-                        mma3(hh, xx, tp_frag(Thi, Tlo, 16 * tb + lr, 32 * ks + 8 * lg), rb[ks]);
-                    dd[tb] = combine<E>(hh, xx);
+                    for (int ks = 0; ks <= tb / 2; ks++) mma3(dd[tb], tp_frag(Thi, Tlo, 16 * tb + lr, 32 * ks + 8 * lg), rb[ks]);
                 }
             }
             // D's operand overwrites this wave's own V columns, which only this
@@ -1072,11 +1067,9 @@ __global__ void __launch_bounds__(kCarryThreads, 1) carry_kernel(const PrefillPa
                 const float decay = scal[3 * kChunk];
 #pragma unroll
                 for (int it = 0; it < KT; it++) {
-                    float4_t hh = hacc[it] * decay, xx = kZero4;
+                    hacc[it] *= decay;
 #pragma unroll
-                    for (int s = 0; s < 2; s++)
-                        mma3(hh, xx, lds_sfrag_tr(Khi, Klo, PK, 32 * s + 8 * lg, 16 * it), ab[s]);
-                    hacc[it] = combine<E>(hh, xx);
+                    for (int s = 0; s < 2; s++) mma3(hacc[it], lds_sfrag_tr(Khi, Klo, PK, 32 * s + 8 * lg, 16 * it), ab[s]);
                 }
             }
             lds_barrier();
@@ -1196,11 +1189,9 @@ __global__ void __launch_bounds__(kCarryThreads, 1) carry_kernel(const PrefillPa
                 }
 #pragma unroll
                 for (int tb = 0; tb < 4; tb++) {
-                    float4_t qhh = kZero4, qhx = kZero4;
+                    float4_t qh = kZero4;
 #pragma unroll
-                    for (int ks = 0; ks < KS; ks++)
-                        mma3(qhh, qhx, lds_sfrag(Qhi, Qlo, PK, 16 * tb + lr, 32 * ks + 8 * lg), hb[ks]);
-                    const float4_t qh = combine<E>(qhh, qhx);
+                    for (int ks = 0; ks < KS; ks++) mma3(qh, lds_sfrag(Qhi, Qlo, PK, 16 * tb + lr, 32 * ks + 8 * lg), hb[ks]);
                     const float4 egv = *reinterpret_cast<const float4*>(eg + 16 * tb + 4 * lg);
                     const float egr[4] = {egv.x, egv.y, egv.z, egv.w};
 #pragma unroll
@@ -1228,11 +1219,9 @@ __global__ void __launch_bounds__(kCarryThreads, 1) carry_kernel(const PrefillPa
                 }
 #pragma unroll
                 for (int tb = 0; tb < 4; tb++) {
-                    float4_t phh = kZero4, phx = kZero4;
+                    float4_t pd = kZero4;
 #pragma unroll
-                    for (int ks = 0; ks <= tb / 2; ks++)
-                        mma3(phh, phx, tp_frag(Phi, Plo, 16 * tb + lr, 32 * ks + 8 * lg), db[ks]);
-                    const float4_t pd = combine<E>(phh, phx);
+                    for (int ks = 0; ks <= tb / 2; ks++) mma3(pd, tp_frag(Phi, Plo, 16 * tb + lr, 32 * ks + 8 * lg), db[ks]);
                     float val[4];
 #pragma unroll
                     for (int e = 0; e < 4; e++) val[e] = p.scale * (eqh[tb][e] + pd[e]);
@@ -1354,6 +1343,8 @@ hipError_t run(const PrefillParams& p, hipStream_t stream, void* const* events) 
 template <typename TIn, typename TOut>
 hipError_t run_dtype(const PrefillParams& p, int d_k, int d_v, hipStream_t stream, void* const* events) {
     if (d_k == 128 && d_v == 128) return run<128, 128, TIn, TOut>(p, stream, events);
+    if (d_k == 128 && d_v == 64) return run<128, 64, TIn, TOut>(p, stream, events);
+    if (d_k == 64 && d_v == 128) return run<64, 128, TIn, TOut>(p, stream, events);
     if (d_k == 64 && d_v == 64) return run<64, 64, TIn, TOut>(p, stream, events);
     return hipErrorInvalidValue;
 }
@@ -1365,7 +1356,7 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 int prefill_supported(int d_k, int d_v, int qkv_dtype, int out_dtype) {
     if (out_dtype != 0 && out_dtype != 1) return 0;
     if (qkv_dtype != 0 && qkv_dtype != 1) return 0;
-    return (d_k == 128 && d_v == 128) || (d_k == 64 && d_v == 64);
+    return (d_k == 64 || d_k == 128) && (d_v == 64 || d_v == 128);
 }
 
 PrefillLayout prefill_layout(int64_t num_seqs, int64_t total_tokens, int64_t h_k, int64_t h_v, int64_t d_k,

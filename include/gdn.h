@@ -133,11 +133,11 @@ size_t gdn_prefill_workspace_bytes(const gdn_problem* p);
  *  workspace       >= gdn_prefill_workspace_bytes(p) bytes, 256-byte aligned
  *
  * Length-0 sequences are allowed (final state = initial state).  o must not
- * overlap any input.  Supported: d_k = d_v in {64, 128}, bf16 or fp32 inputs.
- * Matrix products use split 16-bit operands with fp32 accumulation: bf16
- * pairs (about 16 significant bits each) for bf16 inputs, fp16 pairs (about
- * 21 significant bits) for fp32 inputs, whose intermediate magnitudes must
- * then stay below 65504.
+ * overlap any input.  Supported: d_k, d_v in {64, 128} (any mix), bf16 or
+ * fp32 inputs.  Matrix products run on the matrix cores with fp32
+ * accumulation: split bf16 operands (x = hi + lo, about 16 significant bits)
+ * for bf16 inputs, fp32 operands for fp32 inputs; both over the whole fp32
+ * range.
  */
 gdn_status gdn_prefill_varlen(const gdn_problem* p,
                               const void* q, const void* k, const void* v,
@@ -280,6 +280,17 @@ gdn_status gdn_decode_multi(const gdn_problem* p, int32_t tokens_per_slot,
                             const void* conv_w, const void* conv_b, void* conv_state_pool,
                             float* state_pool, const int32_t* state_indices,
                             const int32_t* num_accepted, void* o, void* stream);
+
+/*
+ * Measurement helper (not part of the recurrence): copies `bytes` bytes from
+ * src to dst on the device with a plain streaming kernel (16-byte
+ * nontemporal loads and stores, `blocks` workgroups of 256 threads striding
+ * over the buffers).  Timed by the benchmark as the measured HBM peak beside
+ * the datasheet figure.  bytes a multiple of 16, pointers 16-byte aligned
+ * (GDN_ERR_UNSUPPORTED), buffers disjoint (GDN_ERR_ALIAS), 1 <= blocks <= 2^20
+ * (GDN_ERR_SHAPE).
+ */
+gdn_status gdn_stream_copy(void* dst, const void* src, size_t bytes, int32_t blocks, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* gdn_status_string(gdn_status s);

@@ -27,20 +27,47 @@ def rel_err(got, ref) -> float:
     return float(np.max(np.abs(got - ref)) / max(rms, 1e-300))
 
 
+def canary(shape, dtype):
+    """A device tensor whose bytes are all 0xFF (NaN in fp32 and bf16): an
+    output element the kernels fail to write stays NaN."""
+    t = torch.empty(shape, dtype=dtype, device="cuda")
+    t.view(torch.uint8).fill_(0xFF)
+    return t
+
+
+def canary_outputs(x: PrefillInputs, out_dtype=torch.float32, conv=True):
+    """NaN-canary o, final states, conv states and workspace for a prefill of x."""
+    g = x.geom
+    N, T = x.num_seqs, x.total_tokens
+    o = canary((T, g.h_v, g.d_v), out_dtype)
+    fs = canary((N, g.h_v, g.d_k, g.d_v), torch.float32)
+    cso = canary((N, g.channels, 3), TORCH_DT[x.dtype]) if conv else None
+    prob = binding.make_problem(N, T, g.h_k, g.h_v, g.d_k, g.d_v, 1, 0)
+    ws = canary((max(binding.gdn_prefill_workspace_bytes(prob), 1),), torch.uint8)
+    return o, fs, cso, ws
+
+
 def gpu_prefill(x: PrefillInputs, *, use_initial=True, use_conv_state=True, out_dtype=torch.float32,
                 conv=True, scale=None, qk_l2norm=True):
+    """The HIP prefill of x with every output and the workspace pre-filled
+    with NaN bytes; asserts that every o row and final state was written."""
     dt = TORCH_DT[x.dtype]
+    conv = conv and x.conv_w is not None
+    o, fs, cso, ws = canary_outputs(x, out_dtype, conv)
     res = binding.gdn_prefill_varlen(
         dev(x.q, dt), dev(x.k, dt), dev(x.v, dt), dev(x.g), dev(x.beta),
         torch.from_numpy(x.cu_seqlens.astype(np.int32)),
-        conv_weight=dev(x.conv_w, dt) if (conv and x.conv_w is not None) else None,
+        conv_weight=dev(x.conv_w, dt) if conv else None,
         conv_state=dev(x.conv_state_in, dt) if (conv and use_conv_state and x.conv_state_in is not None) else None,
         initial_state=dev(x.initial_state) if (use_initial and x.initial_state is not None) else None,
-        out_dtype=out_dtype, scale=scale, use_qk_l2norm=qk_l2norm)
+        out_dtype=out_dtype, scale=scale, use_qk_l2norm=qk_l2norm, out=o, final_state_out=fs,
+        conv_state_out=cso, workspace=ws)
     torch.cuda.synchronize()
     o, fs, cso = res
-    return (o.float().cpu().numpy(), None if fs is None else fs.cpu().numpy(),
-            None if cso is None else cso.float().cpu().numpy())
+    o, fs = o.float().cpu().numpy(), fs.cpu().numpy()
+    assert np.all(np.isfinite(o)), "o has unwritten (NaN canary) or non-finite elements"
+    assert np.all(np.isfinite(fs)), "final states have unwritten (NaN canary) or non-finite elements"
+    return o, fs, None if cso is None else cso.float().cpu().numpy()
 
 
 def oracle_prefill(oracle, x: PrefillInputs, *, use_initial=True, use_conv_state=True, conv=True, scale=None,

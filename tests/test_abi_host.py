@@ -91,7 +91,8 @@ def _prob(**kw):
     (dict(qkv_dtype=7), -3),
     (dict(out_dtype=2), -3),
     (dict(d_k=96, d_v=96), -4),       # no kernel for d = 96
-    (dict(d_k=128, d_v=64), -4),      # prefill needs d_k == d_v
+    (dict(d_k=128, d_v=96), -4),      # no kernel for d_v = 96
+    (dict(d_k=32, d_v=64), -4),       # nor for d_k = 32
     (dict(conv_width=3), -4),
     (dict(num_seqs=0, total_tokens=5), -2),
 ])

@@ -4,14 +4,15 @@ gdn_prefill_varlen over the whole packed batch).
 
 * Packed varlen prefill: 60 sequences with lengths drawn uniformly from
   1..8192, h_k = 16, h_v = 48 (3 value heads per key head), d = 128, bf16
-  q/k/v, fp32 g/beta, per-sequence initial states ~ 0.02 N(0, 1).  Sampled
-  (sequence, key head) units are recomputed by the oracle alone.
+  q/k/v, fp32 g/beta, per-sequence initial states ~ 0.02 N(0, 1).  Every
+  sequence is checked against the oracle on one key head (and its 3 value
+  heads), the key head rotating with the sequence index.
 * Batch invariance: 8 fixed target sequences of 2048 tokens (h_k = 16,
   h_v = 32, d = 128, bf16) alone, packed together, and at random positions
   inside a packed batch of 60 with filler sequences of length 1..8192: their
   outputs and final states must be bit-identical across all batchings.
-* Long context: one sequence of 32768 tokens at the same geometry, sampled
-  against the oracle.
+* Long context: one sequence of 32768 tokens at the same geometry, the whole
+  output and final state against the oracle.
 * Offsets past 32 bits: a short sequence packed after 540,032 tokens, whose
   output rows start beyond element 2^31 of o, against the oracle and against
   a call that holds it alone (bitwise).
@@ -22,7 +23,7 @@ import torch
 
 from gateddeltanet_chunked_delta_amd import binding
 from gateddeltanet_chunked_delta_amd.inputs import Geometry, prefill_inputs, uniform_lengths
-from tests.gpu_util import TOL, dev, head_slice, oracle_prefill, rel_err
+from tests.gpu_util import TOL, canary_outputs, dev, head_slice, oracle_prefill, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -30,11 +31,14 @@ BF = torch.bfloat16
 
 
 def _run(x):
-    """One prefill call over the whole packed batch; device tensors back."""
+    """One prefill call over the whole packed batch, outputs and workspace
+    pre-filled with NaN bytes; device tensors back."""
+    o0, fs0, _, ws = canary_outputs(x, conv=False)
     o, fs, _ = binding.gdn_prefill_varlen(
         dev(x.q, BF), dev(x.k, BF), dev(x.v, BF), dev(x.g), dev(x.beta),
         torch.from_numpy(x.cu_seqlens.astype(np.int32)), conv_weight=dev(x.conv_w, BF),
-        initial_state=None if x.initial_state is None else dev(x.initial_state), output_conv_state=False)
+        initial_state=None if x.initial_state is None else dev(x.initial_state), output_conv_state=False,
+        out=o0, final_state_out=fs0, workspace=ws)
     torch.cuda.synchronize()
     return o, fs
 
@@ -60,8 +64,7 @@ def test_packed_varlen_60_sequences_hv48(oracle_mod):
     print(f"  {x.total_tokens} tokens, lengths {int(lengths.min())}..{int(lengths.max())}", flush=True)
     o, fs = _run(x)
     assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(fs).all())
-    longest, shortest = int(np.argmax(lengths)), int(np.argmin(lengths))
-    _check_units(oracle_mod, x, o, fs, [(longest, 0), (shortest, 15), (30, 7)], "60 packed")
+    _check_units(oracle_mod, x, o, fs, [(n, n % 16) for n in range(60)], "60 packed")
 
 
 def test_batch_invariance_targets_across_batchings(oracle_mod):
@@ -107,7 +110,10 @@ def test_long_sequence_32768(oracle_mod):
     x = prefill_inputs(42, [32768], geom, "bf16", initial_state_std=0.02)
     o, fs = _run(x)
     assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(fs).all())
-    _check_units(oracle_mod, x, o, fs, [(0, 5)], "32768 tokens")
+    ro, rfs, _ = oracle_prefill(oracle_mod, x)
+    eo, ef = rel_err(o.cpu().numpy(), ro), rel_err(fs.cpu().numpy(), rfs)
+    print(f"  32768 tokens, whole: rel err o={eo:.3e} final={ef:.3e}", flush=True)
+    assert eo <= TOL["bf16"] and ef <= TOL["bf16"]
 
 
 def test_offsets_beyond_32_bits(oracle_mod):

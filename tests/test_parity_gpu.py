@@ -4,7 +4,10 @@ Bar: max|gpu - oracle| / rms(oracle) <= 1e-4 for fp32 inputs and <= 1e-2 for
 bf16 inputs, on outputs and on final states; conv states (raw values moved)
 bit-exact.  Sizes span several 64-token chunks with ragged tails; the full
 prefill workload (4 x 4096 tokens, 16 key / 32 value heads, d = 128, bf16) is
-checked on sampled (sequence, key head) units the oracle recomputes alone.
+compared with the oracle on the whole output and every final state, and the
+256-slot decode over 100 consecutive steps on sampled slots.  Prefill outputs
+and workspace start as NaN bytes (tests.gpu_util.gpu_prefill), so an element
+the kernels do not write fails.
 """
 import numpy as np
 import pytest
@@ -132,6 +135,62 @@ def test_bf16_inputs_beyond_fp16_range(oracle_mod):
     assert np.max(np.abs(fs)) > 65504.0
 
 
+def test_fp32_inputs_beyond_fp16_range(oracle_mod):
+    """fp32 inputs take fp32 matrix-core products, which keep fp32's range and
+    precision: v and the initial states scaled by 2^20 (state entries far above
+    fp16's 65504) still meet the fp32 bar."""
+    geom = Geometry(2, 4, 128, 128)
+    x = prefill_inputs(28, [150, 40], geom, "f32", initial_state_std=0.02, conv_state=True)
+    x.v *= 2.0 ** 20
+    x.initial_state *= 2.0 ** 20
+    x.conv_state_in[:, 2 * geom.h_k * geom.d_k:] *= 2.0 ** 20  # the v channels' history
+    o, fs = _check_prefill(oracle_mod, x)
+    print(f"  max|final state| = {np.max(np.abs(fs)):.3e}, max|o| = {np.max(np.abs(o)):.3e}", flush=True)
+    assert np.max(np.abs(fs)) > 65504.0
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d_k,d_v", [(128, 64), (64, 128)])
+def test_mixed_head_dims(oracle_mod, dtype, d_k, d_v):
+    """d_k != d_v (the state is (v_heads, k_head_dim, v_head_dim)): ragged
+    sequences, GQA 2, conv with carried conv states and initial states."""
+    x = prefill_inputs(29 + d_k // 64, [1, 63, 200, 64, 130, 0], Geometry(2, 4, d_k, d_v), dtype,
+                       initial_state_std=0.02, conv_state=True)
+    _check_prefill(oracle_mod, x)
+
+
+def test_side_stream_prefill_is_safe():
+    """A call on a side stream allocates its temporaries there; memory
+    allocated and written on the current stream right after the call cannot
+    reuse them while the kernels still run, so the result is bit-identical to
+    the same call on the current stream."""
+    x = prefill_inputs(46, [700, 300], Geometry(4, 8, 128, 128), "bf16", initial_state_std=0.02, conv_state=True)
+    ref_o, ref_fs, ref_cso = gpu_prefill(x)
+    dt = TORCH_DT["bf16"]
+    args = (dev(x.q, dt), dev(x.k, dt), dev(x.v, dt), dev(x.g), dev(x.beta))
+    w, cs, h0 = dev(x.conv_w, dt), dev(x.conv_state_in, dt), dev(x.initial_state)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    o, fs, cso = binding.gdn_prefill_varlen(*args, x.cu_seqlens.astype(np.int32).tolist(), conv_weight=w,
+                                            conv_state=cs, initial_state=h0, stream=side)
+    # churn the current stream's allocations while the side stream runs
+    junk = [torch.full((1 << 22,), float(i), device="cuda") for i in range(16)]
+    del junk
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert np.array_equal(o.cpu().numpy(), ref_o)
+    assert np.array_equal(fs.cpu().numpy(), ref_fs)
+    assert np.array_equal(cso.float().cpu().numpy(), ref_cso)
+
+
+def test_stream_must_be_a_torch_stream():
+    x = prefill_inputs(47, [10], Geometry(1, 1, 64, 64), "bf16")
+    with pytest.raises(ValueError):
+        binding.gdn_prefill_varlen(dev(x.q, torch.bfloat16), dev(x.k, torch.bfloat16), dev(x.v, torch.bfloat16),
+                                   dev(x.g), dev(x.beta), [0, 10], stream=torch.cuda.current_stream().cuda_stream)
+
+
 @pytest.mark.parametrize("h_k,h_v,d,dtype", [(1, 8, 128, "bf16"), (2, 10, 64, "f32"), (2, 16, 128, "bf16")])
 def test_large_gqa_groups(oracle_mod, h_k, h_v, d, dtype):
     """8, 5 (odd) and 8 value heads per key head: the chunk-local kernel takes
@@ -192,21 +251,19 @@ def test_map_paths_at_the_boundary(oracle_mod, n_seqs):
     _check_prefill(oracle_mod, x)
 
 
-def test_full_prefill_4x4096_sampled(oracle_mod):
-    """4 x 4096 tokens, h_k = 16, h_v = 32, d = 128, bf16: whole-run sanity plus
-    oracle parity on sampled (sequence, key head) units."""
+def test_full_prefill_4x4096_whole(oracle_mod):
+    """4 x 4096 tokens, h_k = 16, h_v = 32, d = 128, bf16, conv + SiLU + L2 (the
+    benchmark's workload and launch): the whole output, every final state and
+    every conv state against the oracle; worst sequence reported."""
     geom = Geometry(16, 32, 128, 128)
     x = prefill_inputs(1, [4096] * 4, geom, "bf16")
-    o, fs, _ = gpu_prefill(x)
-    assert np.all(np.isfinite(o)) and np.all(np.isfinite(fs))
-    for n, hk in [(0, 0), (1, 9), (3, 15)]:
-        xs = head_slice(x, n, hk)
-        ro, rfs, _ = oracle_prefill(oracle_mod, xs)
-        s = slice(int(x.cu_seqlens[n]), int(x.cu_seqlens[n + 1]))
-        eo = rel_err(o[s, 2 * hk:2 * hk + 2], ro)
-        ef = rel_err(fs[n, 2 * hk:2 * hk + 2], rfs[0])
-        print(f"  seq {n} key head {hk}: rel err o={eo:.3e} final={ef:.3e}", flush=True)
-        assert eo <= TOL["bf16"] and ef <= TOL["bf16"]
+    o, fs, cso = gpu_prefill(x)
+    ro, rfs, rcso = oracle_prefill(oracle_mod, x)
+    eo, ef = rel_err(o, ro), rel_err(fs, rfs)
+    per_seq = [rel_err(o[4096 * n:4096 * (n + 1)], ro[4096 * n:4096 * (n + 1)]) for n in range(4)]
+    print(f"  whole: rel err o={eo:.3e} final={ef:.3e}; worst sequence o={max(per_seq):.3e}", flush=True)
+    assert eo <= TOL["bf16"] and ef <= TOL["bf16"]
+    assert np.array_equal(cso, rcso)
 
 
 # ---------------------------------------------------------------- invariants
@@ -304,38 +361,39 @@ def test_empty_and_zero_length():
 
 # -------------------------------------------------------------------- decode
 
-def _oracle_decode_steps(oracle, geom, pool64, steps, n_slots, slots, conv=None, cpool64=None, indices=None):
-    dims = oracle.Dims(geom.h_k, geom.h_v, geom.d_k, geom.d_v, conv_width=4 if conv is not None else 0)
-    outs = []
-    for d in steps:
-        sel = slots
-        q, k, v = d.q[sel], d.k[sel], d.v[sel]
-        idx = np.arange(len(sel)) if indices is None else indices
-        outs.append(oracle.decode(dims, q, k, v, d.g[sel], d.beta[sel], pool64, idx, conv, None, cpool64))
-    return outs
-
-
-def test_decode_256_slots_sampled(oracle_mod):
-    """256 slots x 32 value heads (16 key heads), d = 128, bf16 inputs, fp32
-    pool of 512 MiB updated in place for 3 steps; sampled slots vs the oracle."""
+@pytest.mark.parametrize("conv", [False, True])
+def test_decode_256_slots_100_steps(oracle_mod, conv):
+    """256 slots x 32 value heads (16 key heads), d = 128, bf16 inputs, the fp32
+    pool of 512 MiB updated in place for 100 consecutive steps with fresh
+    seeded inputs (with and without the conv update of a conv pool); sampled
+    slots' outputs at every step and their states after steps 50 and 100
+    against the fp64 oracle run through the same 100 steps."""
     geom = Geometry(16, 32, 128, 128)
-    N = 256
+    N, steps = 256, 100
     pool = dev(state_pool(3, N, geom))
     sample = [0, 77, 255]
     ref_pool = pool[sample].double().cpu().numpy().copy()
-    steps = [decode_inputs(3, s, N, geom, "bf16") for s in range(3)]
-    gpu_out = []
-    for d in steps:
+    cw_np = conv_weights(3, geom, "bf16") if conv else None
+    cpool = dev(conv_state_pool(3, N, geom, "bf16"), torch.bfloat16) if conv else None
+    ref_cpool = cpool[sample].double().cpu().numpy().copy() if conv else None
+    cw = dev(cw_np, torch.bfloat16) if conv else None
+    dims = oracle_mod.Dims(16, 32, 128, 128, conv_width=4 if conv else 0)
+    worst = 0.0
+    for s in range(steps):
+        d = decode_inputs(3, s, N, geom, "bf16")
         o = binding.gdn_decode_step(dev(d.q, torch.bfloat16), dev(d.k, torch.bfloat16), dev(d.v, torch.bfloat16),
-                                    dev(d.g), dev(d.beta), pool)
-        gpu_out.append(o.cpu().numpy())
-    ref = _oracle_decode_steps(oracle_mod, geom, ref_pool, steps, N, sample)
-    for s in range(3):
-        e = rel_err(gpu_out[s][sample], ref[s])
-        print(f"  step {s}: rel err o={e:.3e}", flush=True)
-        assert e <= TOL["bf16"]
-    ef = rel_err(pool[sample].cpu().numpy(), ref_pool)
-    assert ef <= TOL["bf16"]
+                                    dev(d.g), dev(d.beta), pool, conv_weight=cw, conv_state_pool=cpool)
+        ro = oracle_mod.decode(dims, d.q[sample], d.k[sample], d.v[sample], d.g[sample], d.beta[sample], ref_pool,
+                               np.arange(len(sample)), cw_np, None, ref_cpool)
+        e = rel_err(o[sample].cpu().numpy(), ro)
+        worst = max(worst, e)
+        assert e <= TOL["bf16"], (s, e)
+        if s + 1 in (50, steps):
+            ef = rel_err(pool[sample].cpu().numpy(), ref_pool)
+            print(f"  after step {s + 1}: worst o rel err so far {worst:.3e}, states {ef:.3e}", flush=True)
+            assert ef <= TOL["bf16"]
+            if conv:
+                assert np.array_equal(cpool[sample].float().cpu().numpy(), ref_cpool.astype(np.float32))
 
 
 @pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128), ("bf16", 64)])

@@ -30,9 +30,10 @@ def _gather(pool, idx, has, n_seq):
     return out
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_pooled_matches_gathered_states(oracle_mod, dtype):
-    geom = Geometry(2, 4, 128, 128)
+@pytest.mark.parametrize("dtype,d_k,d_v", [("bf16", 128, 128), ("f32", 128, 128), ("bf16", 128, 64),
+                                           ("f32", 64, 128)])
+def test_pooled_matches_gathered_states(oracle_mod, dtype, d_k, d_v):
+    geom = Geometry(2, 4, d_k, d_v)
     lengths = [70, 1, 130, 64, 5]
     idx = np.array([5, -1, 0, 3, 6], dtype=np.int32)
     has = np.array([1, 1, 0, 1, 1], dtype=np.int32)
@@ -62,7 +63,7 @@ def test_pooled_matches_gathered_states(oracle_mod, dtype):
     for i in sorted(set(range(P)) - set(int(j) for j in idx if j >= 0)):
         assert np.array_equal(pool_after[i], pool_np[i])
         assert np.array_equal(cpool_after[i], cpool_np[i])
-    dims = oracle_mod.Dims(2, 4, 128, 128, conv_width=4)
+    dims = oracle_mod.Dims(2, 4, d_k, d_v, conv_width=4)
     ro, rfs, _ = oracle_mod.prefill(dims, x.cu_seqlens, x.q, x.k, x.v, x.g, x.beta, x.conv_w, None, cs0, h0)
     eo = rel_err(o.float().cpu().numpy(), ro)
     used = [n for n in range(len(lengths)) if idx[n] >= 0]
@@ -71,9 +72,10 @@ def test_pooled_matches_gathered_states(oracle_mod, dtype):
     assert eo <= TOL[dtype] and ef <= TOL[dtype]
 
 
-def test_pooled_continuation_bitwise():
+@pytest.mark.parametrize("d_k,d_v", [(128, 128), (64, 128), (128, 64)])
+def test_pooled_continuation_bitwise(d_k, d_v):
     """200 tokens in one pooled call == 128 + 72 tokens in two (entry 2 carries the state)."""
-    geom = Geometry(2, 4, 128, 128)
+    geom = Geometry(2, 4, d_k, d_v)
     dt = TORCH_DT["bf16"]
     x = prefill_inputs(61, [200], geom, "bf16")
     q, k, v, g, b = dev(x.q, dt), dev(x.k, dt), dev(x.v, dt), dev(x.g), dev(x.beta)
