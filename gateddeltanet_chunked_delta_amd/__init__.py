@@ -8,6 +8,6 @@ missing; there is no CPU fallback.
 """
 from .binding import (GDN_BF16, GDN_F32, GdnError, GdnProblem, gdn_decode_multi,  # noqa: F401
                       gdn_decode_step,
-                      gdn_prefill_varlen, gdn_prefill_varlen_pooled,
+                      gdn_prefill_varlen, gdn_prefill_varlen_noalloc, gdn_prefill_varlen_pooled,
                       gdn_prefill_workspace_bytes, load,
                       make_problem, status_string)

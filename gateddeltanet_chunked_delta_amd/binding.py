@@ -19,10 +19,13 @@ LIB_PATH = os.path.join(_PKG, "libgdn.so")
 
 GDN_F32, GDN_BF16 = 0, 1
 _STATUS = {0: "GDN_OK", -1: "GDN_ERR_NULL", -2: "GDN_ERR_SHAPE", -3: "GDN_ERR_DTYPE",
-           -4: "GDN_ERR_UNSUPPORTED", -5: "GDN_ERR_WORKSPACE", -6: "GDN_ERR_HIP", -7: "GDN_ERR_ALIAS"}
+           -4: "GDN_ERR_UNSUPPORTED", -5: "GDN_ERR_WORKSPACE", -6: "GDN_ERR_HIP", -7: "GDN_ERR_ALIAS",
+           -8: "GDN_ERR_SCRATCH"}
 EXPORTED = ("gdn_prefill_workspace_bytes", "gdn_prefill_varlen", "gdn_prefill_varlen_timed",
-            "gdn_prefill_varlen_pooled", "gdn_decode_step", "gdn_decode_multi",
+            "gdn_prefill_varlen_noalloc", "gdn_prefill_varlen_pooled", "gdn_decode_step", "gdn_decode_multi",
             "gdn_stream_copy", "gdn_status_string")
+# Size of the static workspace behind gdn_prefill_varlen_noalloc (GDN_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 128 << 20
 
 
 class GdnProblem(ctypes.Structure):
@@ -60,6 +63,8 @@ def load() -> ctypes.CDLL:
         lib.gdn_prefill_varlen_timed.argtypes = [ctypes.POINTER(GdnProblem)] + [vp] * 14 + [c64, vp,
                                                                                            ctypes.POINTER(vp)]
         lib.gdn_prefill_varlen_timed.restype = ctypes.c_int
+        lib.gdn_prefill_varlen_noalloc.argtypes = [ctypes.POINTER(GdnProblem)] + [vp] * 14
+        lib.gdn_prefill_varlen_noalloc.restype = ctypes.c_int
         lib.gdn_prefill_varlen_pooled.argtypes = [ctypes.POINTER(GdnProblem)] + [vp] * 14 + [c64, vp]
         lib.gdn_prefill_varlen_pooled.restype = ctypes.c_int
         lib.gdn_decode_step.argtypes = [ctypes.POINTER(GdnProblem)] + [vp] * 11 + [vp]
@@ -152,7 +157,8 @@ def gdn_prefill_varlen(q, k, v, g, beta, cu_seqlens=None, *, conv_weight=None, c
                        conv_state=None, initial_state=None, output_final_state=True,
                        output_conv_state=True, use_qk_l2norm=True, scale=None, l2_eps=1e-6,
                        out_dtype=torch.float32, validate=True, out=None, final_state_out=None,
-                       conv_state_out=None, workspace=None, stream=None, events=None, beta_logits=False):
+                       conv_state_out=None, workspace=None, stream=None, events=None, beta_logits=False,
+                       noalloc=False):
     """Chunked varlen prefill (C ABI ``gdn_prefill_varlen``).
 
     q, k: ``[T, h_k, d_k]`` (or ``[B, T, h_k, d_k]`` with equal lengths and no
@@ -161,7 +167,8 @@ def gdn_prefill_varlen(q, k, v, g, beta, cu_seqlens=None, *, conv_weight=None, c
     ``(o, final_state or None, conv_state_out or None)``.  With ``events`` (four
     ``torch.cuda.Event(enable_timing=True)``) the call goes through
     ``gdn_prefill_varlen_timed``, which records them around its stages.
-    ``stream``: a
+    With ``noalloc=True`` the call goes through ``gdn_prefill_varlen_noalloc``
+    (no workspace; the library's static scratch).  ``stream``: a
     ``torch.cuda.Stream`` or None (the current stream); temporaries and
     default outputs are allocated on it.
     """
@@ -226,6 +233,18 @@ def gdn_prefill_varlen(q, k, v, g, beta, cu_seqlens=None, *, conv_weight=None, c
     _check(cso, "conv_state_out", (N, C, 3), qdt, dev)
     prob = make_problem(N, T, h_k, h_v, d_k, d_v, qcode, ocode, scale, use_qk_l2norm, l2_eps, conv_width,
                         beta_logits)
+    if noalloc:
+        if workspace is not None or events is not None:
+            raise ValueError("noalloc takes neither a workspace nor events")
+        _hold_for(s, dev, (q, k, v, g, beta, cu_seqlens, conv_weight, conv_bias, conv_state, cso, initial_state,
+                           o, fs))
+        st = load().gdn_prefill_varlen_noalloc(
+            ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
+            _ptr(conv_weight), _ptr(conv_bias), _ptr(conv_state), _ptr(cso), _ptr(initial_state), _ptr(o),
+            _ptr(fs), ctypes.c_void_p(s.cuda_stream))
+        if st != 0:
+            raise GdnError(st, "gdn_prefill_varlen_noalloc")
+        return o, fs, cso
     ws_bytes = gdn_prefill_workspace_bytes(prob)
     if workspace is None:
         with torch.cuda.stream(s):
@@ -255,6 +274,14 @@ def gdn_prefill_varlen(q, k, v, g, beta, cu_seqlens=None, *, conv_weight=None, c
     return o, fs, cso
 
 
+
+def gdn_prefill_varlen_noalloc(q, k, v, g, beta, cu_seqlens=None, **kw):
+    """Chunked varlen prefill through the C ABI ``gdn_prefill_varlen_noalloc``:
+    the same arguments and results as :func:`gdn_prefill_varlen` (no
+    ``workspace`` or ``events``); the library uses its static scratch, so the
+    C call allocates nothing (pass ``out``, ``final_state_out`` and
+    ``conv_state_out`` to keep this wrapper from allocating outputs)."""
+    return gdn_prefill_varlen(q, k, v, g, beta, cu_seqlens, noalloc=True, **kw)
 
 def gdn_stream_copy(dst, src, blocks, stream=None):
     """Device copy of src into dst (same byte size) by the library's streaming

@@ -140,11 +140,13 @@ gdn_status launch(const gdn_problem* p, const gdn::PrefillLayout& lay, const voi
                                         static_cast<hipStream_t>(stream), events));
 }
 
+// With noalloc the workspace arguments are ignored and the static scratch of
+// the current device is used instead.
 gdn_status prefill(const gdn_problem* p, const void* q, const void* k, const void* v, const float* g,
                    const float* beta, const int32_t* cu_seqlens, const void* conv_w, const void* conv_b,
                    const void* conv_state_in, void* conv_state_out, const float* initial_state, void* o,
                    float* final_state, void* workspace, size_t workspace_bytes, void* stream,
-                   void* const* events) {
+                   void* const* events, bool noalloc = false) {
     gdn_status st = check_problem(p);
     if (st != GDN_OK) return st;
     const int64_t T = p->total_tokens, N = p->num_seqs;
@@ -156,7 +158,13 @@ gdn_status prefill(const gdn_problem* p, const void* q, const void* k, const voi
     const gdn::PrefillLayout lay = gdn::prefill_layout(N, T, p->h_k, p->h_v, p->d_k, p->d_v);
     if (N > 0 && (lay.prep_blocks >= (int64_t(1) << 31) || lay.carry_blocks >= (int64_t(1) << 31)))
         return GDN_ERR_SHAPE;
-    if (N > 0 && (!workspace || workspace_bytes < lay.bytes)) return GDN_ERR_WORKSPACE;
+    if (noalloc) {
+        workspace = nullptr;  // the static scratch: no caller buffer can overlap it
+        workspace_bytes = 0;
+        if (N > 0 && lay.bytes > GDN_NOALLOC_SCRATCH_BYTES) return GDN_ERR_SCRATCH;
+    } else if (N > 0 && (!workspace || workspace_bytes < lay.bytes)) {
+        return GDN_ERR_WORKSPACE;
+    }
     if (N == 0) return GDN_OK;
 
     const int64_t eb = elem_bytes(p->qkv_dtype), ob = elem_bytes(p->out_dtype);
@@ -190,6 +198,19 @@ gdn_status prefill(const gdn_problem* p, const void* q, const void* k, const voi
         overlaps(rc, rw))
         return GDN_ERR_ALIAS;
 
+    if (noalloc) {
+        // the scratch copy that is used is the current device's: the stream
+        // must run on it
+        int cur = -1;
+        hipDevice_t sdev = -1;
+        if (hipGetDevice(&cur) != hipSuccess ||
+            hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev) != hipSuccess)
+            return GDN_ERR_HIP;
+        if (sdev != cur) return GDN_ERR_UNSUPPORTED;
+        size_t bytes = 0;
+        if (gdn::noalloc_scratch(&workspace, &bytes) != hipSuccess) return GDN_ERR_HIP;
+        if (bytes < lay.bytes) return GDN_ERR_SCRATCH;
+    }
     return launch(p, lay, q, k, v, g, beta, cu_seqlens, conv_w, conv_b, conv_state_in, conv_state_out,
                   initial_state, o, final_state, nullptr, nullptr, workspace, stream, events);
 }
@@ -268,6 +289,15 @@ gdn_status gdn_prefill_varlen_timed(const gdn_problem* p, const void* q, const v
                    initial_state, o, final_state, workspace, workspace_bytes, stream, events);
 }
 
+gdn_status gdn_prefill_varlen_noalloc(const gdn_problem* p, const void* q, const void* k, const void* v,
+                                      const float* g, const float* beta, const int32_t* cu_seqlens,
+                                      const void* conv_w, const void* conv_b, const void* conv_state_in,
+                                      void* conv_state_out, const float* initial_state, void* o,
+                                      float* final_state, void* stream) {
+    return prefill(p, q, k, v, g, beta, cu_seqlens, conv_w, conv_b, conv_state_in, conv_state_out,
+                   initial_state, o, final_state, nullptr, 0, stream, nullptr, true);
+}
+
 gdn_status gdn_prefill_varlen_pooled(const gdn_problem* p, const void* q, const void* k, const void* v,
                                      const float* g, const float* beta, const int32_t* cu_seqlens,
                                      const void* conv_w, const void* conv_b, void* conv_state_pool,
@@ -304,6 +334,7 @@ const char* gdn_status_string(gdn_status s) {
         case GDN_ERR_WORKSPACE: return "workspace missing or too small";
         case GDN_ERR_HIP: return "HIP kernel launch failed";
         case GDN_ERR_ALIAS: return "an output overlaps a buffer it must not";
+        case GDN_ERR_SCRATCH: return "problem needs more workspace than the static scratch of the no-alloc entry point";
     }
     return "unknown status";
 }

@@ -89,6 +89,10 @@ hipError_t launch_prefill(const PrefillParams& p, int d_k, int d_v, int qkv_dtyp
                           hipStream_t stream, void* const* events);
 int prefill_supported(int d_k, int d_v, int qkv_dtype, int out_dtype);
 
+// The static workspace of gdn_prefill_varlen_noalloc on the current device:
+// its device address (looked up at the first call on each device) and size.
+hipError_t noalloc_scratch(void** ptr, size_t* bytes);
+
 hipError_t launch_decode(const DecodeParams& p, int d_k, int d_v, int qkv_dtype, int out_dtype,
                          hipStream_t stream);
 int decode_supported(int d_k, int d_v, int qkv_dtype, int out_dtype);

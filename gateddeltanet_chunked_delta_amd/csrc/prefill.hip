@@ -46,6 +46,9 @@
 // All reductions run in a fixed order inside one workgroup, with no atomics
 // and no batch-dependent split: a sequence's results are bit-identical
 // whatever else shares the call.
+#include <mutex>
+
+#include "../../include/gdn.h"
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -1352,6 +1355,34 @@ hipError_t run_dtype(const PrefillParams& p, int d_k, int d_v, hipStream_t strea
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 }  // namespace
+
+// Workspace of gdn_prefill_varlen_noalloc: a static device array, one copy on
+// every GPU the library runs on.  In host code its name stands for a host-side
+// symbol, not a device address: the address of the current device's copy is
+// looked up once per device with hipGetSymbolAddress, and only that address is
+// passed to the kernels.
+static __device__ __align__(256) unsigned char scratch[GDN_NOALLOC_SCRATCH_BYTES];
+
+hipError_t noalloc_scratch(void** ptr, size_t* bytes) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* a = nullptr;
+        err = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+        if (err != hipSuccess) return err;
+        if (!a) return hipErrorInvalidSymbol;
+        addr[dev] = a;
+    }
+    *ptr = addr[dev];
+    *bytes = sizeof(scratch);
+    return hipSuccess;
+}
 
 int prefill_supported(int d_k, int d_v, int qkv_dtype, int out_dtype) {
     if (out_dtype != 0 && out_dtype != 1) return 0;

@@ -70,7 +70,9 @@ typedef enum gdn_status {
     GDN_ERR_UNSUPPORTED = -4, /* valid request this build has no kernel for */
     GDN_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than required */
     GDN_ERR_HIP = -6,         /* a kernel launch failed */
-    GDN_ERR_ALIAS = -7        /* an output overlaps a buffer it must not */
+    GDN_ERR_ALIAS = -7,       /* an output overlaps a buffer it must not */
+    GDN_ERR_SCRATCH = -8      /* the problem needs more than the static scratch
+                               * of gdn_prefill_varlen_noalloc */
 } gdn_status;
 
 typedef struct gdn_problem {
@@ -208,6 +210,35 @@ gdn_status gdn_prefill_varlen_pooled(const gdn_problem* p,
                                      const int32_t* has_initial_state,
                                      void* o, void* workspace, size_t workspace_bytes,
                                      void* stream);
+
+/*
+ * gdn_prefill_varlen for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation and results, bit for bit, with no
+ * workspace argument.  The workspace lives in a static device array of
+ * GDN_NOALLOC_SCRATCH_BYTES bytes that the library holds on every GPU it runs
+ * on until the process ends; its address is looked up once per device, at
+ * the first call with that device current.  Problems whose
+ * gdn_prefill_workspace_bytes() exceeds GDN_NOALLOC_SCRATCH_BYTES return
+ * GDN_ERR_SCRATCH (e.g. more than about 4,700 tokens in one call at
+ * h_k = 16, h_v = 32, d = 128).  The call allocates and frees nothing.
+ * Calls on one GPU share its array: calls that overlap in time on one GPU
+ * (different streams, or different host threads) race and must be ordered by
+ * the caller.  Every byte a call reads from the array it has written earlier
+ * in the same call, so no clearing is needed between calls.  `stream` must
+ * belong to the current device (GDN_ERR_UNSUPPORTED otherwise).  Other
+ * arguments, errors and conventions as in gdn_prefill_varlen.
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+gdn_status gdn_prefill_varlen_noalloc(const gdn_problem* p,
+                                      const void* q, const void* k, const void* v,
+                                      const float* g, const float* beta,
+                                      const int32_t* cu_seqlens,
+                                      const void* conv_w, const void* conv_b,
+                                      const void* conv_state_in, void* conv_state_out,
+                                      const float* initial_state,
+                                      void* o, float* final_state,
+                                      void* stream);
 
 /*
  * One decode step: one new token for each of N slots, updating a pooled

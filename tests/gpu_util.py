@@ -48,7 +48,7 @@ def canary_outputs(x: PrefillInputs, out_dtype=torch.float32, conv=True):
 
 
 def gpu_prefill(x: PrefillInputs, *, use_initial=True, use_conv_state=True, out_dtype=torch.float32,
-                conv=True, scale=None, qk_l2norm=True):
+                conv=True, scale=None, qk_l2norm=True, noalloc=False):
     """The HIP prefill of x with every output and the workspace pre-filled
     with NaN bytes; asserts that every o row and final state was written."""
     dt = TORCH_DT[x.dtype]
@@ -61,7 +61,7 @@ def gpu_prefill(x: PrefillInputs, *, use_initial=True, use_conv_state=True, out_
         conv_state=dev(x.conv_state_in, dt) if (conv and use_conv_state and x.conv_state_in is not None) else None,
         initial_state=dev(x.initial_state) if (use_initial and x.initial_state is not None) else None,
         out_dtype=out_dtype, scale=scale, use_qk_l2norm=qk_l2norm, out=o, final_state_out=fs,
-        conv_state_out=cso, workspace=ws)
+        conv_state_out=cso, workspace=None if noalloc else ws, noalloc=noalloc)
     torch.cuda.synchronize()
     o, fs, cso = res
     o, fs = o.float().cpu().numpy(), fs.cpu().numpy()

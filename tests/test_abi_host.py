@@ -57,7 +57,7 @@ def test_problem_struct_layout_matches_c(tmp_path):
 
 
 def test_status_strings(lib):
-    for code in range(-7, 1):
+    for code in range(-8, 1):
         s = binding.status_string(code)
         assert s and s != "unknown status"
     assert binding.status_string(-99) == "unknown status"
@@ -110,6 +110,34 @@ def test_prefill_rejects_bad_flag(lib):
     prob = _prob()
     prob.beta_logits = 2
     assert _prefill(lib, prob, cw=9) == -2
+
+
+def _noalloc(lib, prob, q=1, k=2, v=3, g=4, b=5, cu=6, cw=None, cb=None, csi=None, cso=None, h0=None, o=7,
+             fs=None):
+    f = lambda x: None if x is None else (_fake(x) if isinstance(x, int) else x)
+    return lib.gdn_prefill_varlen_noalloc(ctypes.byref(prob), f(q), f(k), f(v), f(g), f(b), f(cu), f(cw), f(cb),
+                                          f(csi), f(cso), f(h0), f(o), f(fs), None)
+
+
+def test_noalloc_rejects_before_any_hip_call(lib):
+    """The allocation-free prefill validates like gdn_prefill_varlen and
+    refuses problems whose workspace exceeds its static scratch."""
+    assert lib.gdn_prefill_varlen_noalloc(None, *([None] * 14)) == -1
+    assert _noalloc(lib, _prob(h_v=3), cw=9) == -2
+    assert _noalloc(lib, _prob(d_k=96, d_v=96), cw=9) == -4
+    assert _noalloc(lib, _prob(), cw=None) == -1
+    assert _noalloc(lib, _prob(conv_width=0), o=1) == -7                 # o == q
+    # the workspace need grows with the tokens: find a size just past the scratch
+    big = _prob(num_seqs=4, total_tokens=4 * 4096, h_k=16, h_v=32, conv_width=0)
+    assert binding.gdn_prefill_workspace_bytes(big) > binding.NOALLOC_SCRATCH_BYTES
+    assert _noalloc(lib, big) == -8
+    assert binding.status_string(-8) != "unknown status"
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define GDN_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == binding.NOALLOC_SCRATCH_BYTES
 
 
 def test_prefill_null_problem(lib):
