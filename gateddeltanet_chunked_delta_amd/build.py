@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libgdn.so")
-SOURCES = ["gdn_api.cpp", "prefill.hip", "decode.hip", "measure.hip"]
+SOURCES = ["gdn_api.cpp", "host_layout.cpp", "prefill.hip", "decode.hip", "measure.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -296,11 +296,6 @@ hipError_t run_dims(const DecodeParams& p, int d_k, int d_v, hipStream_t stream)
 
 }  // namespace
 
-int decode_supported(int d_k, int d_v, int qkv_dtype, int out_dtype) {
-    return (d_k == 64 || d_k == 128) && (d_v == 64 || d_v == 128) && (qkv_dtype == 0 || qkv_dtype == 1) &&
-           (out_dtype == 0 || out_dtype == 1);
-}
-
 hipError_t launch_decode(const DecodeParams& p, int d_k, int d_v, int qkv_dtype, int out_dtype,
                          hipStream_t stream) {
     if (p.num_seqs <= 0) return hipSuccess;

@@ -107,8 +107,19 @@ gdn_status decode(const gdn_problem* p, int32_t m, const void* q, const void* k,
 extern "C" {
 
 size_t gdn_prefill_workspace_bytes(const gdn_problem* p) {
-    if (!p || p->num_seqs <= 0 || p->total_tokens < 0) return 0;
+    if (check_problem(p) != GDN_OK || p->num_seqs <= 0 ||
+        !gdn::prefill_supported(p->d_k, p->d_v, p->qkv_dtype, p->out_dtype))
+        return 0;
     return gdn::prefill_layout(p->num_seqs, p->total_tokens, p->h_k, p->h_v, p->d_k, p->d_v).bytes;
+}
+
+gdn_status gdn_stream_copy(void* dst, const void* src, size_t bytes, int32_t blocks, void* stream) {
+    if (bytes == 0) return GDN_OK;
+    if (!dst || !src) return GDN_ERR_NULL;
+    if (blocks < 1 || blocks > (1 << 20)) return GDN_ERR_SHAPE;
+    if (bytes % 16 != 0 || !aligned(dst, 16) || !aligned(src, 16)) return GDN_ERR_UNSUPPORTED;
+    if (overlaps(range_of(dst, int64_t(bytes)), range_of(src, int64_t(bytes)))) return GDN_ERR_ALIAS;
+    return from_hip(gdn::launch_stream_copy(dst, src, int64_t(bytes / 16), blocks, static_cast<hipStream_t>(stream)));
 }
 
 namespace {

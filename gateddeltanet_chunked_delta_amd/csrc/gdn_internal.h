@@ -8,6 +8,11 @@
 
 namespace gdn {
 
+// Sizes shared by the prefill kernels and the host-side layout code.
+constexpr int kChunk = 64;       // tokens per chunk, aligned to each sequence start
+constexpr int kDvs = 64;         // d_v columns per carry workgroup
+constexpr int kTriPieces = 320;  // 16-byte pieces of 8 columns in the lower 16x16 blocks of a 64x64 matrix
+
 // Everything the chunked-prefill kernels need, passed by value.
 struct PrefillParams {
     const void* q;              // [T][h_k][d_k]
@@ -55,6 +60,9 @@ struct PrefillLayout {
 };
 PrefillLayout prefill_layout(int64_t num_seqs, int64_t total_tokens, int64_t h_k, int64_t h_v, int64_t d_k,
                              int64_t d_v);
+// Carry workgroups of a prefill: per (sequence, key head) group rounded up to
+// a multiple of 8 groups (one per XCD), G value heads x d_v / kDvs slices each.
+int64_t carry_blocks(int64_t num_seqs, int64_t h_k, int64_t h_v, int64_t d_v);
 
 // Most tokens per slot one decode call takes.
 constexpr int kDecodeMaxTokens = 8;
@@ -96,5 +104,8 @@ hipError_t noalloc_scratch(void** ptr, size_t* bytes);
 hipError_t launch_decode(const DecodeParams& p, int d_k, int d_v, int qkv_dtype, int out_dtype,
                          hipStream_t stream);
 int decode_supported(int d_k, int d_v, int qkv_dtype, int out_dtype);
+
+// The measurement copy: n16 16-byte pieces from src to dst.
+hipError_t launch_stream_copy(void* dst, const void* src, int64_t n16, int blocks, hipStream_t stream);
 
 }  // namespace gdn

@@ -1,8 +1,8 @@
 // Measurement helper: a plain streaming device copy, the reference against
 // which the kernels' achieved HBM bandwidth is compared (a measured peak next
 // to the datasheet's 8 TB/s).
-#include "../../include/gdn.h"
 #include "gdn_device.h"
+#include "gdn_internal.h"
 
 namespace gdn {
 namespace {
@@ -33,17 +33,11 @@ __global__ void __launch_bounds__(kCopyThreads) stream_copy_kernel(u32x4_t* __re
 }
 
 }  // namespace
-}  // namespace gdn
 
-extern "C" gdn_status gdn_stream_copy(void* dst, const void* src, size_t bytes, int32_t blocks, void* stream) {
-    if (bytes == 0) return GDN_OK;
-    if (!dst || !src) return GDN_ERR_NULL;
-    if (blocks < 1 || blocks > (1 << 20)) return GDN_ERR_SHAPE;
-    if (bytes % 16 != 0 || reinterpret_cast<uintptr_t>(dst) % 16 != 0 || reinterpret_cast<uintptr_t>(src) % 16 != 0)
-        return GDN_ERR_UNSUPPORTED;
-    const uintptr_t d = reinterpret_cast<uintptr_t>(dst), s = reinterpret_cast<uintptr_t>(src);
-    if (d < s + bytes && s < d + bytes) return GDN_ERR_ALIAS;
-    gdn::stream_copy_kernel<<<dim3(unsigned(blocks)), dim3(gdn::kCopyThreads), 0, static_cast<hipStream_t>(stream)>>>(
-        static_cast<gdn::u32x4_t*>(dst), static_cast<const gdn::u32x4_t*>(src), int64_t(bytes / 16));
-    return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+hipError_t launch_stream_copy(void* dst, const void* src, int64_t n16, int blocks, hipStream_t stream) {
+    stream_copy_kernel<<<dim3(unsigned(blocks)), dim3(kCopyThreads), 0, stream>>>(
+        static_cast<u32x4_t*>(dst), static_cast<const u32x4_t*>(src), n16);
+    return hipGetLastError();
 }
+
+}  // namespace gdn

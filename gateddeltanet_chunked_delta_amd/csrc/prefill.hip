@@ -55,9 +55,7 @@
 namespace gdn {
 namespace {
 
-constexpr int kChunk = 64;
 constexpr int kLdsLimit = 163840;  // gfx950: 160 KiB per workgroup
-constexpr int kDvs = 64;           // d_v columns per carry workgroup
 // s_waitcnt immediate that waits for every outstanding vector memory
 // operation of the wave (vmcnt = 0; expcnt and lgkmcnt left at their maxima).
 constexpr int kVmcnt0 = 0x0f70;
@@ -69,7 +67,7 @@ constexpr int kVmcnt0 = 0x0f70;
 // A TriPack plane stores row r's columns [0, 16 (r/16 + 1)) as 16-byte
 // pieces, rows in order: 320 pieces.
 struct TriPack {
-    static constexpr int kPieces = 320;
+    static constexpr int kPieces = kTriPieces;
     // first piece of row r
     __device__ __forceinline__ static int row_start(int r) {
         const int b = r >> 4;
@@ -1300,11 +1298,6 @@ __global__ void __launch_bounds__(kCarryThreads, 1) carry_kernel(const PrefillPa
     }
 }
 
-int64_t carry_blocks(int64_t num_seqs, int64_t h_k, int64_t h_v, int64_t d_v) {
-    const int64_t groups = num_seqs * h_k, members = (h_v / h_k) * (d_v / kDvs);
-    return (groups + 7) / 8 * 8 * members;
-}
-
 // Compute units of the current device (cached per device).
 int64_t compute_units() {
     static int cached[64] = {0};
@@ -1352,8 +1345,6 @@ hipError_t run_dtype(const PrefillParams& p, int d_k, int d_v, hipStream_t strea
     return hipErrorInvalidValue;
 }
 
-size_t align256(size_t x) { return (x + 255) / 256 * 256; }
-
 }  // namespace
 
 // Workspace of gdn_prefill_varlen_noalloc: a static device array, one copy on
@@ -1382,37 +1373,6 @@ hipError_t noalloc_scratch(void** ptr, size_t* bytes) {
     *ptr = addr[dev];
     *bytes = sizeof(scratch);
     return hipSuccess;
-}
-
-int prefill_supported(int d_k, int d_v, int qkv_dtype, int out_dtype) {
-    if (out_dtype != 0 && out_dtype != 1) return 0;
-    if (qkv_dtype != 0 && qkv_dtype != 1) return 0;
-    return (d_k == 64 || d_k == 128) && (d_v == 64 || d_v == 128);
-}
-
-PrefillLayout prefill_layout(int64_t num_seqs, int64_t total_tokens, int64_t h_k, int64_t h_v, int64_t d_k,
-                             int64_t d_v) {
-    PrefillLayout l{};
-    if (num_seqs <= 0 || h_k <= 0 || h_v <= 0 || d_k <= 0 || d_v <= 0) return l;
-    // sum_n ceil(len_n / 64) <= (T + 63 N) / 64 for any split of T tokens into N sequences
-    l.slots = (total_tokens + 63 * num_seqs) / kChunk;
-    size_t off = 0;
-    l.order = off;
-    off = align256(off + size_t(num_seqs) * sizeof(int32_t));
-    l.chunk_base = off;
-    off = align256(off + size_t(num_seqs + 1) * sizeof(int32_t));
-    l.slot_desc = off;
-    off = align256(off + size_t(l.slots) * 4 * sizeof(int32_t));
-    l.kq_img = off;
-    off = align256(off + size_t(l.slots) * size_t(h_k) * (4 * kChunk * size_t(d_k)) * sizeof(uint16_t));
-    l.tp_img = off;
-    off = align256(off + size_t(l.slots) * size_t(h_v) * (4 * TriPack::kPieces * 8) * sizeof(uint16_t));
-    l.scal_img = off;
-    off = align256(off + size_t(l.slots) * size_t(h_v) * (4 * kChunk) * sizeof(float));
-    l.bytes = off;
-    l.prep_blocks = l.slots * h_k;
-    l.carry_blocks = carry_blocks(num_seqs, h_k, h_v, d_v);
-    return l;
 }
 
 hipError_t launch_prefill(const PrefillParams& p, int d_k, int d_v, int qkv_dtype, int out_dtype,
