@@ -134,7 +134,7 @@ def measured_traffic(kernel):
         return None
 
 
-def extra_prefill(gdn, torch, dev, lengths, h_k, h_v, d, init_std, steps, seed):
+def extra_prefill(gdn, torch, dev, lengths, h_k, h_v, d, init_std, steps, seed, segment_chunks=0):
     """Prefill at another geometry, inputs drawn on the GPU with the
     distributions of the seeded workloads (q, k, v ~ N(0, 1) in bf16, conv taps
     0.5 N(0, 1), beta = sigmoid(N(0, 1)), g = -softplus(N(0, 1)), initial
@@ -154,13 +154,14 @@ def extra_prefill(gdn, torch, dev, lengths, h_k, h_v, d, init_std, steps, seed):
     cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32), device=dev)
     o = torch.empty((T, h_v, d), dtype=torch.float32, device=dev)
     fs = torch.empty((N, h_v, d, d), dtype=torch.float32, device=dev)
-    prob = gdn.binding.make_problem(N, T, h_k, h_v, d, d, gdn.GDN_BF16, gdn.GDN_F32)
+    prob = gdn.binding.make_problem(N, T, h_k, h_v, d, d, gdn.GDN_BF16, gdn.GDN_F32, segment_chunks=segment_chunks)
     ws = torch.empty(gdn.binding.gdn_prefill_workspace_bytes(prob), dtype=torch.uint8, device=dev)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
 
     def call(e=None):
         gdn.gdn_prefill_varlen(q, k, v, g, beta, cu, conv_weight=w, initial_state=h0, out=o, final_state_out=fs,
-                               output_conv_state=False, workspace=ws, validate=False, events=e)
+                               output_conv_state=False, workspace=ws, validate=False, events=e,
+                               segment_chunks=segment_chunks)
 
     for _ in range(3):
         call()
@@ -173,9 +174,13 @@ def extra_prefill(gdn, torch, dev, lengths, h_k, h_v, d, init_std, steps, seed):
     carry = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e3
     work = prefill_work(lengths, h_k, h_v, d, initial_states=init_std is not None and init_std > 0,
                         conv_state_out=False)
-    return {"us_per_call": us, "tokens_per_s": T / (us * 1e-6), "prep_kernel_us": prep, "carry_kernel_us": carry,
-            "roofline": roofline(*work["call"], us * 1e-6),
-            "carry_roofline": roofline(*work["carry"], carry * 1e-6, CARRY_KERNEL)}
+    r = {"us_per_call": us, "tokens_per_s": T / (us * 1e-6), "prep_kernel_us": prep, "carry_kernel_us": carry,
+         "roofline": roofline(*work["call"], us * 1e-6),
+         "carry_roofline": roofline(*work["carry"], carry * 1e-6, CARRY_KERNEL)}
+    if segment_chunks:
+        r["segment_chunks"] = segment_chunks
+        r["combine_and_correct_us"] = float(np.mean([e[2].elapsed_time(e[3]) for e in evs])) * 1e3
+    return r
 
 
 def stream_copy_peak(gdn, torch, dev, stream):
@@ -501,6 +506,13 @@ def main():
         extra["single_sequence_32768_hk16_hv32"] = r
         print(f"[bench] 32768-token sequence: {r['us_per_call']:.0f} us/call, "
               f"{r['tokens_per_s'] / 1e6:.1f} M tokens/s", file=sys.stderr, flush=True)
+        r = extra_prefill(gdn, torch, dev, [32768], 16, 32, 128, 0.0, 5, 4, segment_chunks=256)
+        r["workload"] = ("the same 32768-token sequence with the segment split (segment_chunks = 256: two "
+                         "segments of 256 chunks run in parallel, then combined and corrected)")
+        extra["single_sequence_32768_hk16_hv32_split256"] = r
+        print(f"[bench] 32768-token sequence, split: {r['us_per_call']:.0f} us/call (carry {r['carry_kernel_us']:.0f},"
+              f" combine+correct {r['combine_and_correct_us']:.0f}), {r['tokens_per_s'] / 1e6:.1f} M tokens/s",
+              file=sys.stderr, flush=True)
         result["other_prefill_configs"] = extra
 
     if not args.no_copy_peak:

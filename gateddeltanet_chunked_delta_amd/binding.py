@@ -36,7 +36,7 @@ class GdnProblem(ctypes.Structure):
                 ("qkv_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("qk_l2norm", ctypes.c_int32),
                 ("l2_eps", ctypes.c_float), ("conv_width", ctypes.c_int32),
-                ("beta_logits", ctypes.c_int32)]
+                ("beta_logits", ctypes.c_int32), ("segment_chunks", ctypes.c_int32)]
 
 
 class GdnError(RuntimeError):
@@ -134,10 +134,11 @@ def _check(t, name, shape, dtype, device):
 
 
 def make_problem(num_seqs, total_tokens, h_k, h_v, d_k, d_v, qkv_dtype, out_dtype, scale=None,
-                 qk_l2norm=True, l2_eps=1e-6, conv_width=4, beta_logits=False) -> GdnProblem:
+                 qk_l2norm=True, l2_eps=1e-6, conv_width=4, beta_logits=False, segment_chunks=0) -> GdnProblem:
     return GdnProblem(int(num_seqs), int(total_tokens), int(h_k), int(h_v), int(d_k), int(d_v),
                       int(qkv_dtype), int(out_dtype), float(0.0 if scale is None else scale),
-                      int(bool(qk_l2norm)), float(l2_eps), int(conv_width), int(bool(beta_logits)))
+                      int(bool(qk_l2norm)), float(l2_eps), int(conv_width), int(bool(beta_logits)),
+                      int(segment_chunks))
 
 
 def gdn_prefill_workspace_bytes(problem: GdnProblem) -> int:
@@ -158,7 +159,7 @@ def gdn_prefill_varlen(q, k, v, g, beta, cu_seqlens=None, *, conv_weight=None, c
                        output_conv_state=True, use_qk_l2norm=True, scale=None, l2_eps=1e-6,
                        out_dtype=torch.float32, validate=True, out=None, final_state_out=None,
                        conv_state_out=None, workspace=None, stream=None, events=None, beta_logits=False,
-                       noalloc=False):
+                       noalloc=False, segment_chunks=0):
     """Chunked varlen prefill (C ABI ``gdn_prefill_varlen``).
 
     q, k: ``[T, h_k, d_k]`` (or ``[B, T, h_k, d_k]`` with equal lengths and no
@@ -167,6 +168,8 @@ def gdn_prefill_varlen(q, k, v, g, beta, cu_seqlens=None, *, conv_weight=None, c
     ``(o, final_state or None, conv_state_out or None)``.  With ``events`` (four
     ``torch.cuda.Event(enable_timing=True)``) the call goes through
     ``gdn_prefill_varlen_timed``, which records them around its stages.
+    ``segment_chunks > 0`` turns on the segment split of sequences longer than
+    that many 64-token chunks (see ``gdn_problem.segment_chunks``).
     With ``noalloc=True`` the call goes through ``gdn_prefill_varlen_noalloc``
     (no workspace; the library's static scratch).  ``stream``: a
     ``torch.cuda.Stream`` or None (the current stream); temporaries and
@@ -232,7 +235,7 @@ def gdn_prefill_varlen(q, k, v, g, beta, cu_seqlens=None, *, conv_weight=None, c
     _check(fs, "final_state_out", (N, h_v, d_k, d_v), torch.float32, dev)
     _check(cso, "conv_state_out", (N, C, 3), qdt, dev)
     prob = make_problem(N, T, h_k, h_v, d_k, d_v, qcode, ocode, scale, use_qk_l2norm, l2_eps, conv_width,
-                        beta_logits)
+                        beta_logits, segment_chunks)
     if noalloc:
         if workspace is not None or events is not None:
             raise ValueError("noalloc takes neither a workspace nor events")
@@ -318,7 +321,8 @@ def _check_indices(state_indices, N, P, Pc, dev, validate):
 def gdn_prefill_varlen_pooled(q, k, v, g, beta, cu_seqlens, state_pool, *, state_indices=None,
                               has_initial_state=None, conv_weight=None, conv_bias=None, conv_state_pool=None,
                               use_qk_l2norm=True, scale=None, l2_eps=1e-6, out_dtype=torch.float32,
-                              validate=True, out=None, workspace=None, stream=None, beta_logits=False):
+                              validate=True, out=None, workspace=None, stream=None, beta_logits=False,
+                              segment_chunks=0):
     """Chunked varlen prefill over pooled states, in place (C ABI
     ``gdn_prefill_varlen_pooled``).
 
@@ -378,7 +382,7 @@ def gdn_prefill_varlen_pooled(q, k, v, g, beta, cu_seqlens, state_pool, *, state
         o = out if out is not None else torch.empty((T, h_v, d_v), dtype=out_dtype, device=dev)
     _check(o, "out", (T, h_v, d_v), out_dtype, dev)
     prob = make_problem(N, T, h_k, h_v, d_k, d_v, qcode, ocode, scale, use_qk_l2norm, l2_eps, conv_width,
-                        beta_logits)
+                        beta_logits, segment_chunks)
     ws_bytes = gdn_prefill_workspace_bytes(prob)
     if workspace is None:
         with torch.cuda.stream(s):

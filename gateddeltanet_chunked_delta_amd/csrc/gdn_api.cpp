@@ -37,6 +37,7 @@ gdn_status check_problem(const gdn_problem* p) {
     if (p->qk_l2norm != 0 && p->qk_l2norm != 1) return GDN_ERR_SHAPE;
     if (p->beta_logits != 0 && p->beta_logits != 1) return GDN_ERR_SHAPE;
     if (!isfinite(p->scale) || !isfinite(p->l2_eps) || p->l2_eps < 0.0f) return GDN_ERR_SHAPE;
+    if (p->segment_chunks < 0) return GDN_ERR_SHAPE;
     // keep every element offset well inside int64 and grid sizes inside 2^31
     if (p->total_tokens > (int64_t(1) << 31) || p->num_seqs > (1 << 24) || p->h_v > 4096 ||
         p->h_k > 4096 || p->d_k > 4096 || p->d_v > 4096)
@@ -110,7 +111,7 @@ size_t gdn_prefill_workspace_bytes(const gdn_problem* p) {
     if (check_problem(p) != GDN_OK || p->num_seqs <= 0 ||
         !gdn::prefill_supported(p->d_k, p->d_v, p->qkv_dtype, p->out_dtype))
         return 0;
-    return gdn::prefill_layout(p->num_seqs, p->total_tokens, p->h_k, p->h_v, p->d_k, p->d_v).bytes;
+    return gdn::prefill_layout(p->num_seqs, p->total_tokens, p->h_k, p->h_v, p->d_k, p->d_v, p->segment_chunks).bytes;
 }
 
 gdn_status gdn_stream_copy(void* dst, const void* src, size_t bytes, int32_t blocks, void* stream) {
@@ -144,6 +145,16 @@ gdn_status launch(const gdn_problem* p, const gdn::PrefillLayout& lay, const voi
     prm.tp_img = ws + lay.tp_img;
     prm.scal_img = reinterpret_cast<float*>(ws + lay.scal_img);
     prm.slots = lay.slots;
+    const bool split = p->segment_chunks > 0;
+    prm.segment_chunks = p->segment_chunks;
+    prm.chain_base = split ? reinterpret_cast<int32_t*>(ws + lay.chain_base) : nullptr;
+    prm.chain_desc = split ? reinterpret_cast<int32_t*>(ws + lay.chain_desc) : nullptr;
+    prm.chain_order = split ? reinterpret_cast<int32_t*>(ws + lay.chain_order) : nullptr;
+    prm.seg_state = split ? reinterpret_cast<float*>(ws + lay.seg_state) : nullptr;
+    prm.seg_trans = split ? reinterpret_cast<float*>(ws + lay.seg_trans) : nullptr;
+    prm.seg_y = split ? reinterpret_cast<float*>(ws + lay.seg_y) : nullptr;
+    prm.seg_oloc = split ? reinterpret_cast<float*>(ws + lay.seg_oloc) : nullptr;
+    prm.max_chains = lay.max_chains;
     prm.num_seqs = p->num_seqs; prm.h_k = p->h_k; prm.h_v = p->h_v; prm.d_v = p->d_v;
     prm.conv_width = p->conv_width; prm.beta_logits = p->beta_logits;
     prm.qk_l2norm = p->qk_l2norm; prm.l2_eps = eff_eps(p); prm.scale = eff_scale(p);
@@ -166,8 +177,10 @@ gdn_status prefill(const gdn_problem* p, const void* q, const void* k, const voi
     if (T > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL;
     if (p->conv_width == 4 && !conv_w) return GDN_ERR_NULL;
     if (!gdn::prefill_supported(p->d_k, p->d_v, p->qkv_dtype, p->out_dtype)) return GDN_ERR_UNSUPPORTED;
-    const gdn::PrefillLayout lay = gdn::prefill_layout(N, T, p->h_k, p->h_v, p->d_k, p->d_v);
-    if (N > 0 && (lay.prep_blocks >= (int64_t(1) << 31) || lay.carry_blocks >= (int64_t(1) << 31)))
+    const gdn::PrefillLayout lay = gdn::prefill_layout(N, T, p->h_k, p->h_v, p->d_k, p->d_v, p->segment_chunks);
+    if (N > 0 && (lay.prep_blocks >= (int64_t(1) << 31) || lay.carry_blocks >= (int64_t(1) << 31) ||
+                  lay.max_chains * p->h_k >= (int64_t(1) << 31) ||
+                  (p->segment_chunks > 0 && lay.slots * p->h_v * (p->d_v / 64) >= (int64_t(1) << 31))))
         return GDN_ERR_SHAPE;
     if (noalloc) {
         workspace = nullptr;  // the static scratch: no caller buffer can overlap it
@@ -239,8 +252,10 @@ gdn_status prefill_pooled(const gdn_problem* p, const void* q, const void* k, co
     if (T > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL;
     if (p->conv_width == 4 && (!conv_w || !conv_state_pool)) return GDN_ERR_NULL;
     if (!gdn::prefill_supported(p->d_k, p->d_v, p->qkv_dtype, p->out_dtype)) return GDN_ERR_UNSUPPORTED;
-    const gdn::PrefillLayout lay = gdn::prefill_layout(N, T, p->h_k, p->h_v, p->d_k, p->d_v);
-    if (N > 0 && (lay.prep_blocks >= (int64_t(1) << 31) || lay.carry_blocks >= (int64_t(1) << 31)))
+    const gdn::PrefillLayout lay = gdn::prefill_layout(N, T, p->h_k, p->h_v, p->d_k, p->d_v, p->segment_chunks);
+    if (N > 0 && (lay.prep_blocks >= (int64_t(1) << 31) || lay.carry_blocks >= (int64_t(1) << 31) ||
+                  lay.max_chains * p->h_k >= (int64_t(1) << 31) ||
+                  (p->segment_chunks > 0 && lay.slots * p->h_v * (p->d_v / 64) >= (int64_t(1) << 31))))
         return GDN_ERR_SHAPE;
     if (N > 0 && (!workspace || workspace_bytes < lay.bytes)) return GDN_ERR_WORKSPACE;
     if (N == 0) return GDN_OK;

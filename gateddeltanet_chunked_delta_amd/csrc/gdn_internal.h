@@ -42,6 +42,20 @@ struct PrefillParams {
     void* tp_img;               // [slots][h_v] T|P split images
     float* scal_img;            // [slots][h_v][4][64] per-token scalars
     int64_t slots;              // chunk slots: >= sum_n ceil(len_n / 64)
+    // Segment split (segment_chunks > 0): a sequence of nch > segment_chunks
+    // chunks runs as S = ceil(nch / segment_chunks) chains of ceil(nch / S)
+    // chunks (the last one shorter); chains after the first start from zero
+    // state, and chains of d_k identity columns give each segment's transition
+    // and output map (see the segment kernels).  Null pointers when off.
+    int32_t segment_chunks;
+    int32_t* chain_base;        // [N+1] chains before each sequence
+    int32_t* chain_desc;        // [max_chains][4] sequence, first chunk, chunks, segment index
+    int32_t* chain_order;       // [max_chains] chains by descending length
+    float* seg_state;           // [max_chains][h_v][d_k][d_v] local final state, then start state
+    float* seg_trans;           // [max_chains][h_v][d_k][d_k] transition of the segment
+    float* seg_y;               // [T][h_v][d_k] outputs of the identity columns (o's dependence on the start state)
+    float* seg_oloc;            // [T][h_v][d_v] outputs of segments >= 1 from a zero start
+    int64_t max_chains;
     int32_t num_seqs;
     int32_t h_k, h_v;
     int32_t d_v;
@@ -55,14 +69,18 @@ struct PrefillParams {
 // Byte offsets of the prefill workspace regions (each 256-byte aligned) and
 // the grid sizes the launches will use.
 struct PrefillLayout {
-    size_t order, chunk_base, slot_desc, kq_img, tp_img, scal_img, bytes;
-    int64_t slots, prep_blocks, carry_blocks;
+    size_t order, chunk_base, slot_desc, kq_img, tp_img, scal_img;
+    size_t chain_base, chain_desc, chain_order, seg_state, seg_trans, seg_y, seg_oloc;  // segment split only
+    size_t bytes;
+    int64_t slots, prep_blocks, carry_blocks, max_chains;
 };
 PrefillLayout prefill_layout(int64_t num_seqs, int64_t total_tokens, int64_t h_k, int64_t h_v, int64_t d_k,
-                             int64_t d_v);
-// Carry workgroups of a prefill: per (sequence, key head) group rounded up to
-// a multiple of 8 groups (one per XCD), G value heads x d_v / kDvs slices each.
-int64_t carry_blocks(int64_t num_seqs, int64_t h_k, int64_t h_v, int64_t d_v);
+                             int64_t d_v, int64_t segment_chunks);
+// Carry workgroups of a prefill: per (chain, key head) group rounded up to a
+// multiple of 8 groups (one per XCD), G value heads x d_v / kDvs slices each,
+// plus G x d_k / kDvs identity slices with the segment split.  Without the
+// split a chain is a sequence.
+int64_t carry_blocks(int64_t chains, int64_t h_k, int64_t h_v, int64_t d_k, int64_t d_v, bool split);
 
 // Most tokens per slot one decode call takes.
 constexpr int kDecodeMaxTokens = 8;

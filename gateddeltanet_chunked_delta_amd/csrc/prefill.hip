@@ -383,6 +383,70 @@ __global__ void __launch_bounds__(256) small_map_kernel(const int32_t* __restric
     }
 }
 
+// ---------------------------------------------------------------- segment split: chain map
+
+// Chains of the segment split.  Sequence n of nch chunks runs as
+// S = max(1, ceil(nch / seg)) chains; chain s covers chunks [s Ls, min((s + 1) Ls, nch))
+// with Ls = ceil(nch / S), so the split depends on the sequence's length
+// alone.  chain_base[n] = chains before sequence n (chain_base[N] = all),
+// desc[c] = {sequence, first chunk, chunks, segment index}.  One workgroup
+// scans the sequences in tiles of 256.
+__global__ void __launch_bounds__(256) chain_map_kernel(const int32_t* __restrict__ cu, int32_t n, int32_t seg,
+                                                         int32_t* __restrict__ chain_base, int4* __restrict__ desc) {
+    __shared__ int32_t s[256];
+    const int t = threadIdx.x;
+    int32_t carry = 0;
+    for (int t0 = 0; t0 < n; t0 += 256) {
+        const int i = t0 + t;
+        int32_t nch = 0, S = 0;
+        if (i < n) {
+            nch = int32_t((int64_t(cu[i + 1]) - cu[i] + kChunk - 1) / kChunk);
+            S = nch > seg ? (nch + seg - 1) / seg : 1;
+        }
+        s[t] = S;
+        __syncthreads();
+        for (int o = 1; o < 256; o <<= 1) {
+            const int32_t x = t >= o ? s[t - o] : 0;
+            __syncthreads();
+            s[t] += x;
+            __syncthreads();
+        }
+        if (i < n) {
+            const int32_t base = carry + s[t] - S, Ls = (nch + S - 1) / S;
+            chain_base[i] = base;
+            for (int32_t k = 0; k < S; k++) {
+                const int32_t j0 = k * Ls, len = nch - j0 < Ls ? nch - j0 : Ls;
+                desc[base + k] = int4{i, j0, len, k};
+            }
+        }
+        carry += s[255];
+        __syncthreads();
+    }
+    if (t == 0) chain_base[n] = carry;
+}
+
+// Chains ordered by descending length (ties by index), the longest dependent
+// chains first; beyond kMaxRanked chains the identity order.  Scheduling
+// only: results do not depend on it.
+__global__ void __launch_bounds__(256) chain_order_kernel(const int32_t* __restrict__ count,
+                                                           const int4* __restrict__ desc,
+                                                           int32_t* __restrict__ order) {
+    const int nc = *count;
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= nc) return;
+    if (nc > kMaxRanked) {
+        order[i] = i;
+        return;
+    }
+    const int li = desc[i].z;
+    int rank = 0;
+    for (int j = 0; j < nc; j++) {
+        const int lj = desc[j].z;
+        rank += (lj > li) || (lj == li && j < i);
+    }
+    order[rank] = i;
+}
+
 // ---------------------------------------------------------------- prep: q|k prologue and chunk-local terms
 
 constexpr int kPrepThreads = 512;  // 8 waves: two groups of 4 take two value heads at a time
@@ -895,9 +959,9 @@ __device__ __forceinline__ int dop_offset(int w, int piece, int l) {
     return (16 * piece + (l & 15)) * (PV * 4) + 64 * w + 16 * (l >> 4);
 }
 
-template <int DK, int DV, typename TIn, typename TOut>
+template <int DK, int DV, typename TIn, typename TOut, bool CH>
 __global__ void __launch_bounds__(kCarryThreads, 1) carry_kernel(const PrefillParams p) {
-    constexpr int NS = DV / kDvs;
+    constexpr int NS = DV / kDvs, NSK = DK / kDvs;
     constexpr int HT = kCarryThreads / 2;                 // helper threads
     constexpr int VEC = Elem<TIn>::kVec;
     constexpr int NGV = kDvs / VEC;                    // 16-byte groups of a v slice row
@@ -937,23 +1001,49 @@ __global__ void __launch_bounds__(kCarryThreads, 1) carry_kernel(const PrefillPa
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int cw = wave & 3;  // column block of this wave (main and helper alike)
     const int lr = lane & 15, lg = lane >> 4;
-    // XCD-aware unit map: workgroup b runs on XCD b % 8; the M = G * NS
-    // members of group g = (order index, key head) share XCD g % 8.
-    const int G = p.h_v / p.h_k, M = G * NS;
-    const int ngroups = p.num_seqs * p.h_k;
+    // XCD-aware unit map: workgroup b runs on XCD b % 8; the M members of
+    // group g = (order index, key head) share XCD g % 8.  Without the segment
+    // split a group is a (sequence, key head) with M = G NS members, the value
+    // heads' d_v slices.  With it (CH) a group is a (chain, key head) and has
+    // G NSK more members: the identity chains of the d_k columns.
+    const int G = p.h_v / p.h_k, M = G * (CH ? NS + NSK : NS);
+    const int ngroups = (CH ? p.chain_base[p.num_seqs] : p.num_seqs) * p.h_k;
     const int xcd = int(blockIdx.x & 7u), kx = int(blockIdx.x >> 3);
     const int grp = (kx / M) * 8 + xcd, mem = kx % M;
     if (grp >= ngroups) return;
-    const int hk = grp % p.h_k, gi = mem / NS, slice = mem % NS;
-    const int n = p.order[grp / p.h_k];
+    const bool ident = CH && mem >= G * NS;  // an identity chain (segment split only)
+    const int mrel = ident ? mem - G * NS : mem, nsl = ident ? NSK : NS;
+    const int hk = grp % p.h_k, gi = mrel / nsl, slice = mrel % nsl;
+    // The chain: sequence n's chunks [j0, j0 + nch), segment segi of nseg.
+    int n, j0 = 0, nch = 0, chain = 0, segi = 0, nseg = 1;
+    if constexpr (CH) {
+        chain = p.chain_order[grp / p.h_k];
+        const int4 d = reinterpret_cast<const int4*>(p.chain_desc)[chain];
+        n = d.x;
+        j0 = d.y;
+        nch = d.z;
+        segi = d.w;
+        nseg = p.chain_base[n + 1] - p.chain_base[n];
+        if (ident && segi == 0) return;  // the first segment starts from the true state
+    } else {
+        n = p.order[grp / p.h_k];
+    }
     const int h = hk * G + gi;
     const int wcol = 16 * cw + lr;        // this lane's column within the slice
-    const int col = slice * kDvs + wcol;  // ... and within d_v
+    const int col = slice * kDvs + wcol;  // ... and within d_v (d_k for an identity chain)
     const int64_t bos = p.cu_seqlens[n], eos = p.cu_seqlens[n + 1];
-    const int nch = int((eos - bos + kChunk - 1) / kChunk);
-    const int cb = p.chunk_base[n];
+    if constexpr (!CH) nch = int((eos - bos + kChunk - 1) / kChunk);
+    const int cb = p.chunk_base[n] + j0;               // chunk slot of the chain's first chunk
+    const int64_t tok0 = bos + int64_t(j0) * kChunk;  // its first token
     const int slot = state_slot(p, n);
     const bool has_init = slot_has_initial(p, n, slot);
+    // A value chain of a split sequence leaves its final state in seg_state
+    // (the combine kernel chains them); segments after the first start from
+    // zero and write their outputs to seg_oloc (the correction kernel adds
+    // their dependence on the start state); an identity chain runs from the
+    // d_k identity columns with zero v, leaving the segment's transition in
+    // seg_trans and its outputs in seg_y.
+    const bool split = CH && nseg > 1;
 
     if (wave < 4) {
         // ======== main waves: the state and its dependent chain ========
@@ -963,9 +1053,14 @@ __global__ void __launch_bounds__(kCarryThreads, 1) carry_kernel(const PrefillPa
 #pragma unroll
         for (int it = 0; it < KT; it++)
 #pragma unroll
-            for (int e = 0; e < 4; e++)
-                hacc[it][e] = (p.initial_state && has_init)
-                                  ? p.initial_state[state_base + int64_t(16 * it + 4 * lg + e) * DV] : 0.0f;
+            for (int e = 0; e < 4; e++) {
+                const int row = 16 * it + 4 * lg + e;
+                if (ident)
+                    hacc[it][e] = row == col ? 1.0f : 0.0f;
+                else
+                    hacc[it][e] = (p.initial_state && has_init && segi == 0)
+                                      ? p.initial_state[state_base + int64_t(row) * DV] : 0.0f;
+            }
         u32x4_t pkq[NKQ];
         auto fetch_kq = [&](int j, int i0, int i1) {
             const u32x4_t* skq = reinterpret_cast<const u32x4_t*>(static_cast<const E*>(p.kq_img) +
@@ -1076,7 +1171,14 @@ __global__ void __launch_bounds__(kCarryThreads, 1) carry_kernel(const PrefillPa
             lds_barrier();
         }
 
-        if (p.final_state && slot >= 0) {
+        if (split || ident) {
+            const int rs = ident ? DK : DV;  // row stride of the segment buffers
+            float* dst = (ident ? p.seg_trans : p.seg_state) + (int64_t(chain) * p.h_v + h) * DK * rs + col;
+#pragma unroll
+            for (int it = 0; it < KT; it++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) dst[int64_t(16 * it + 4 * lg + e) * rs] = hacc[it][e];
+        } else if (p.final_state && slot >= 0) {
 #pragma unroll
             for (int it = 0; it < KT; it++)
 #pragma unroll
@@ -1097,7 +1199,14 @@ __global__ void __launch_bounds__(kCarryThreads, 1) carry_kernel(const PrefillPa
                                ? static_cast<const TIn*>(p.conv_state_in) + (int64_t(slot) * C + vch) * 3 : nullptr;
         u32x4_t vwp[4];
         float vbias[VEC];
-        conv_params<TIn>(p, vch, vwp, vbias);
+        if (ident) {  // no v channels: an identity slice may lie past d_v
+#pragma unroll
+            for (int m = 0; m < 4; m++) vwp[m] = u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int e = 0; e < VEC; e++) vbias[e] = 0.0f;
+        } else {
+            conv_params<TIn>(p, vch, vwp, vbias);
+        }
 
         u32x4_t ptp[NTP], xv[VRPB + 3];
         float psc;
@@ -1108,8 +1217,10 @@ __global__ void __launch_bounds__(kCarryThreads, 1) carry_kernel(const PrefillPa
             const u32x4_t* stp = reinterpret_cast<const u32x4_t*>(static_cast<const E*>(p.tp_img) +
                                                                   (cslot * p.h_v + h) * Img<DK>::kTP);
             psc = p.scal_img[(cslot * p.h_v + h) * Img<DK>::kScal + ht];
-            const int64_t c0 = bos + int64_t(j) * kChunk;
-            if (c0 - 3 >= bos && c0 + kChunk <= eos) {
+            const int64_t c0 = tok0 + int64_t(j) * kChunk;
+            if (ident) {
+                // no v: the identity columns start with zero inputs
+            } else if (c0 - 3 >= bos && c0 + kChunk <= eos) {
                 // interior chunk: every row, history included, is in the sequence
 #pragma unroll
                 for (int jj = 0; jj < VRPB + 3; jj++)
@@ -1146,22 +1257,36 @@ __global__ void __launch_bounds__(kCarryThreads, 1) carry_kernel(const PrefillPa
         static_assert(VRPB % 2 == 0, "v rows in two halves");
         float vy[VRPB][VEC];
         auto conv_v = [&](int j, int h) {
-            const int64_t c0 = bos + int64_t(j) * kChunk;
+            const int64_t c0 = tok0 + int64_t(j) * kChunk;
             const int L = int(eos - c0 < kChunk ? eos - c0 : kChunk);
             float y[VH][VEC];
             conv_rows<TIn, VH>(conv, *reinterpret_cast<const u32x4_t(*)[VH + 3]>(xv + h * VH), vwp, vbias, y);
 #pragma unroll
             for (int i = 0; i < VH; i++)
 #pragma unroll
-                for (int e = 0; e < VEC; e++) vy[h * VH + i][e] = (vrow0 + h * VH + i < L) ? y[i][e] : 0.0f;
+                for (int e = 0; e < VEC; e++)
+                    vy[h * VH + i][e] = (vrow0 + h * VH + i < L && !ident) ? y[i][e] : 0.0f;
         };
         if (nch > 0) {
             fetch(0);
             conv_v(0, 1);
         }
 
+        // fp32 outputs of the segment split: identity chains to seg_y (d_k
+        // columns), value chains after the first segment to seg_oloc
+        float* fo = nullptr;
+        int fcols = DV;
+        if constexpr (CH) {
+            if (ident) {
+                fo = p.seg_y;
+                fcols = DK;
+            } else if (segi > 0) {
+                fo = p.seg_oloc;
+            }
+        }
+
         for (int j = 0; j < nch; j++) {
-            const int64_t c0 = bos + int64_t(j) * kChunk;
+            const int64_t c0 = tok0 + int64_t(j) * kChunk;
             const int L = int(eos - c0 < kChunk ? eos - c0 : kChunk);
 
             // ---- stage the chunk (every wave is done with the previous one) ----
@@ -1210,8 +1335,11 @@ __global__ void __launch_bounds__(kCarryThreads, 1) carry_kernel(const PrefillPa
                 // The chunk's rows of o through a buffer resource whose extent ends
                 // after row L - 1: the hardware drops the stores of rows past the
                 // sequence's end, so no store needs a branch of its own.
-                const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
-                    out + c0 * p.h_v * DV, short(0), L * p.h_v * DV * int(sizeof(TOut)), kBufferFlags);
+                const __amdgpu_buffer_rsrc_t orsrc =
+                    (CH && fo) ? __builtin_amdgcn_make_buffer_rsrc(fo + c0 * p.h_v * fcols, short(0),
+                                                                   L * p.h_v * fcols * int(sizeof(float)), kBufferFlags)
+                               : __builtin_amdgcn_make_buffer_rsrc(out + c0 * p.h_v * DV, short(0),
+                                                                   L * p.h_v * DV * int(sizeof(TOut)), kBufferFlags);
                 SFrag<E> db[2];
 #pragma unroll
                 for (int s = 0; s < 2; s++) {
@@ -1226,7 +1354,13 @@ __global__ void __launch_bounds__(kCarryThreads, 1) carry_kernel(const PrefillPa
                     float val[4];
 #pragma unroll
                     for (int e = 0; e < 4; e++) val[e] = p.scale * (eqh[tb][e] + pd[e]);
-                    if constexpr (sizeof(TOut) == 2) {
+                    if (CH && fo) {
+#pragma unroll
+                        for (int e = 0; e < 4; e++) {
+                            const int r = 16 * tb + 4 * lg + e;
+                            buf_put<float>(orsrc, ((r * p.h_v + h) * fcols + col) * int(sizeof(float)), val[e]);
+                        }
+                    } else if constexpr (sizeof(TOut) == 2) {
                         // Lanes lr and lr ^ 1 hold columns 2c and 2c + 1 of the same
                         // rows: the even lane takes rows 4 lg + 0, 1 and the odd lane
                         // rows 4 lg + 2, 3 of both columns, converted two at a time
@@ -1263,7 +1397,7 @@ __global__ void __launch_bounds__(kCarryThreads, 1) carry_kernel(const PrefillPa
         // before (q and k: the chunk-local kernel; v: this workgroup's first
         // chunk), and one thread reads a channel's three values before writing
         // them, so the output may be the history buffer itself.
-        if (p.conv_state_out && conv && slot >= 0) {
+        if (p.conv_state_out && conv && slot >= 0 && !ident && segi == nseg - 1) {
             const int64_t len = eos - bos;
             const TIn* csi = (p.conv_state_in && has_init) ? static_cast<const TIn*>(p.conv_state_in) : nullptr;
             TIn* cso = static_cast<TIn*>(p.conv_state_out);
@@ -1298,6 +1432,172 @@ __global__ void __launch_bounds__(kCarryThreads, 1) carry_kernel(const PrefillPa
     }
 }
 
+// ---------------------------------------------------------------- segment split: combine and correct
+
+// Step 2 of the segment split, per (split sequence, value head, 64 columns
+// of d_v): the segments' start states in order.  H_1 = the first segment's
+// final state; H_{s+1} = M_s H_s + F_s, with M_s the segment's transition
+// (seg_trans) and F_s its final state from a zero start (seg_state).  H_s
+// replaces F_s in seg_state (the correction reads it) and the last H is the
+// sequence's final state.  fp32; each element's products are summed over d_k
+// in order, all of a thread's rows at once (independent accumulators).
+template <int DK, int DV>
+__global__ void __launch_bounds__(256) segment_combine_kernel(const PrefillParams p) {
+    constexpr int NS = DV / kDvs, RPT = DK / 4;
+    __shared__ __attribute__((aligned(16))) float Ms[DK][DK + 4];
+    __shared__ float Hs[DK][kDvs];
+    const int b = int(blockIdx.x);
+    const int slice = b % NS, h = (b / NS) % p.h_v, n = b / (NS * p.h_v);
+    const int c0 = p.chain_base[n], nseg = p.chain_base[n + 1] - c0;
+    if (nseg <= 1) return;
+    const int t = threadIdx.x, cc = t & 63, rg = t >> 6;  // column; rows rg + 4 r
+    float H[RPT];
+    const int64_t colofs = int64_t(slice) * kDvs + cc;
+    const float* f0 = p.seg_state + (int64_t(c0) * p.h_v + h) * DK * DV + colofs;
+#pragma unroll
+    for (int r = 0; r < RPT; r++) H[r] = f0[int64_t(rg + 4 * r) * DV];
+    for (int sg = 1; sg < nseg; sg++) {
+        const int64_t c = c0 + sg;
+        __syncthreads();  // the previous segment's reads of Ms and Hs are done
+#pragma unroll
+        for (int r = 0; r < RPT; r++) Hs[rg + 4 * r][cc] = H[r];
+        const float4* m = reinterpret_cast<const float4*>(p.seg_trans + (c * p.h_v + h) * DK * DK);
+        for (int i = t; i < DK * DK / 4; i += 256)
+            *reinterpret_cast<float4*>(&Ms[i / (DK / 4)][4 * (i % (DK / 4))]) = m[i];
+        float* fs = p.seg_state + (c * p.h_v + h) * DK * DV + colofs;
+        float acc[RPT];
+#pragma unroll
+        for (int r = 0; r < RPT; r++) acc[r] = 0.0f;
+        __syncthreads();
+        for (int k = 0; k < DK; k += 4) {
+            const float h0 = Hs[k][cc], h1 = Hs[k + 1][cc], h2 = Hs[k + 2][cc], h3 = Hs[k + 3][cc];
+#pragma unroll
+            for (int r = 0; r < RPT; r++) {
+                const float4 mv = *reinterpret_cast<const float4*>(&Ms[rg + 4 * r][k]);
+                acc[r] = fmaf(mv.x, h0, acc[r]);
+                acc[r] = fmaf(mv.y, h1, acc[r]);
+                acc[r] = fmaf(mv.z, h2, acc[r]);
+                acc[r] = fmaf(mv.w, h3, acc[r]);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < RPT; r++) {
+            const float f = fs[int64_t(rg + 4 * r) * DV];
+            fs[int64_t(rg + 4 * r) * DV] = H[r];  // start state of segment sg
+            H[r] = acc[r] + f;
+        }
+    }
+    const int slot = state_slot(p, n);
+    if (p.final_state && slot >= 0) {
+        float* fin = p.final_state + (int64_t(slot) * p.h_v + h) * DK * DV + colofs;
+#pragma unroll
+        for (int r = 0; r < RPT; r++) fin[int64_t(rg + 4 * r) * DV] = H[r];
+    }
+}
+
+// Step 3 of the segment split, per (8 consecutive chunk slots, value head):
+// for each chunk of a segment s >= 1, o = O_loc + Y H_s, where O_loc
+// (seg_oloc) is the segment's output from a zero start, Y (seg_y) the output
+// of its identity columns (o's dependence on the start state) and H_s its
+// start state.  Y H_s runs on the matrix cores with the operands of the
+// chain's own products (split bf16 or fp32): wave w takes rows 16 w .. 16 w
+// + 15 of the chunk across all of d_v, so Y is read once; H_s waits in LDS
+// as ready operand fragments, staged again only when the segment changes.
+// Each chunk's loads are all issued before its stores: the vector memory
+// counter retires loads and stores in order, so a load issued behind stores
+// could only be used once they completed.
+constexpr int kCorrectChunks = 8;
+template <int DK, int DV, typename TIn, typename TOut>
+__global__ void __launch_bounds__(256) segment_correct_kernel(const PrefillParams p) {
+    constexpr int KS = DK / 32, NTT = DV / 16;  // k-steps; 16-column tiles of d_v
+    using E = typename OpFor<TIn>::type;
+    typedef typename OpVec<E>::v8 V8;
+    // H_s fragments: [ks][tile][hi, lo][lane], 16 bytes each
+    __shared__ __attribute__((aligned(16))) char hbs[KS * NTT * 2 * 64 * 16];
+    const int h = int(blockIdx.x % unsigned(p.h_v));
+    const int64_t g0 = int64_t(blockIdx.x / unsigned(p.h_v)) * kCorrectChunks;
+    const int64_t nslots = p.chunk_base[p.num_seqs];
+    const int t = threadIdx.x, w = t >> 6, lane = t & 63, lr = lane & 15, lg = lane >> 4;
+    const int64_t ystride = int64_t(p.h_v) * DK, ostride = int64_t(p.h_v) * DV;
+    int64_t cur = -1;  // the chain whose start state hbs holds
+    for (int i = 0; i < kCorrectChunks; i++) {
+        const int64_t cs = g0 + i;
+        if (cs >= nslots) break;
+        const int4 d = reinterpret_cast<const int4*>(p.slot_desc)[cs];  // sequence, first token, length, start
+        const int n = d.x, L = d.z;
+        const int64_t c0 = d.y, bos = d.w;
+        const int cbn = p.chain_base[n], nseg = p.chain_base[n + 1] - cbn;
+        if (nseg <= 1) continue;
+        const int ls = reinterpret_cast<const int4*>(p.chain_desc)[cbn].z;  // chunks per segment (the first is full)
+        const int sg = int((c0 - bos) / kChunk) / ls;
+        if (sg == 0) continue;
+        const int64_t chain = cbn + sg;
+        if (chain != cur) {  // uniform over the workgroup
+            __syncthreads();
+            const float* src = p.seg_state + (chain * p.h_v + h) * DK * DV;
+            for (int f = t; f < KS * NTT * 64; f += 256) {
+                const int ks = f / (NTT * 64), tile = (f / 64) % NTT, l = f % 64;
+                float x[8];
+#pragma unroll
+                for (int e = 0; e < 8; e++) x[e] = src[(32 * ks + 8 * (l >> 4) + e) * DV + 16 * tile + (l & 15)];
+                const SFrag<E> fr = split8<E>(x);
+                *reinterpret_cast<V8*>(hbs + (((ks * NTT + tile) * 2 + 0) * 64 + l) * 16) = fr.hi;
+                *reinterpret_cast<V8*>(hbs + (((ks * NTT + tile) * 2 + 1) * 64 + l) * 16) = fr.lo;
+            }
+            __syncthreads();
+            cur = chain;
+        }
+        // loads: this wave's 16 rows of Y (row 16 w + lr, 8 consecutive k per
+        // k-step) and of O_loc (rows 16 w + 4 lg + e, column 16 tile + lr)
+        const float* __restrict__ y = p.seg_y + (c0 * p.h_v + h) * DK;
+        const float* __restrict__ ol = p.seg_oloc + (c0 * p.h_v + h) * DV;
+        const int arow = 16 * w + lr;
+        float4 yv[KS][2];
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++)
+#pragma unroll
+            for (int hh = 0; hh < 2; hh++)
+                yv[ks][hh] = arow < L ? *reinterpret_cast<const float4*>(y + arow * ystride + 32 * ks + 8 * lg + 4 * hh)
+                                      : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        float res[NTT][4];
+#pragma unroll
+        for (int tile = 0; tile < NTT; tile++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int r = 16 * w + 4 * lg + e;
+                res[tile][e] = r < L ? ol[r * ostride + 16 * tile + lr] : 0.0f;
+            }
+        SFrag<E> a[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++) {
+            const float x[8] = {yv[ks][0].x, yv[ks][0].y, yv[ks][0].z, yv[ks][0].w,
+                                yv[ks][1].x, yv[ks][1].y, yv[ks][1].z, yv[ks][1].w};
+            a[ks] = split8<E>(x);
+        }
+#pragma unroll
+        for (int tile = 0; tile < NTT; tile++) {
+            float4_t acc = kZero4;
+#pragma unroll
+            for (int ks = 0; ks < KS; ks++) {
+                SFrag<E> hb;
+                hb.hi = *reinterpret_cast<const V8*>(hbs + (((ks * NTT + tile) * 2 + 0) * 64 + lane) * 16);
+                hb.lo = *reinterpret_cast<const V8*>(hbs + (((ks * NTT + tile) * 2 + 1) * 64 + lane) * 16);
+                mma3(acc, a[ks], hb);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; e++) res[tile][e] += acc[e];
+        }
+        TOut* __restrict__ out = static_cast<TOut*>(p.o) + (c0 * p.h_v + h) * DV;
+#pragma unroll
+        for (int tile = 0; tile < NTT; tile++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int r = 16 * w + 4 * lg + e;
+                if (r < L) Elem<TOut>::put(out + r * ostride + 16 * tile + lr, res[tile][e]);
+            }
+    }
+}
+
 // Compute units of the current device (cached per device).
 int64_t compute_units() {
     static int cached[64] = {0};
@@ -1315,7 +1615,7 @@ hipError_t record(void* const* events, int i, hipStream_t stream) {
     return events ? hipEventRecord(static_cast<hipEvent_t>(events[i]), stream) : hipSuccess;
 }
 
-template <int DK, int DV, typename TIn, typename TOut>
+template <int DK, int DV, typename TIn, typename TOut, bool CH>
 hipError_t run(const PrefillParams& p, hipStream_t stream, void* const* events) {
     hipError_t err = record(events, 0, stream);
     if (err != hipSuccess) return err;
@@ -1329,19 +1629,37 @@ hipError_t run(const PrefillParams& p, hipStream_t stream, void* const* events) 
     }
     err = record(events, 1, stream);
     if (err != hipSuccess) return err;
-    carry_kernel<DK, DV, TIn, TOut>
-        <<<dim3(unsigned(carry_blocks(p.num_seqs, p.h_k, p.h_v, DV))), dim3(kCarryThreads), 0, stream>>>(p);
+    carry_kernel<DK, DV, TIn, TOut, CH><<<dim3(unsigned(carry_blocks(p.max_chains, p.h_k, p.h_v, DK, DV, CH))),
+                                         dim3(kCarryThreads), 0, stream>>>(p);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
-    return record(events, 2, stream);
+    err = record(events, 2, stream);
+    if (err != hipSuccess) return err;
+    if constexpr (CH) {
+        segment_combine_kernel<DK, DV>
+            <<<dim3(unsigned(int64_t(p.num_seqs) * p.h_v * (DV / kDvs))), dim3(256), 0, stream>>>(p);
+        err = hipGetLastError();
+        if (err != hipSuccess) return err;
+        if (p.slots > 0) {
+            const int64_t groups = (p.slots + kCorrectChunks - 1) / kCorrectChunks;
+            segment_correct_kernel<DK, DV, TIn, TOut><<<dim3(unsigned(groups * p.h_v)), dim3(256), 0, stream>>>(p);
+            err = hipGetLastError();
+        }
+    }
+    return err;
 }
 
 template <typename TIn, typename TOut>
 hipError_t run_dtype(const PrefillParams& p, int d_k, int d_v, hipStream_t stream, void* const* events) {
-    if (d_k == 128 && d_v == 128) return run<128, 128, TIn, TOut>(p, stream, events);
-    if (d_k == 128 && d_v == 64) return run<128, 64, TIn, TOut>(p, stream, events);
-    if (d_k == 64 && d_v == 128) return run<64, 128, TIn, TOut>(p, stream, events);
-    if (d_k == 64 && d_v == 64) return run<64, 64, TIn, TOut>(p, stream, events);
+    const bool ch = p.segment_chunks > 0;
+    if (d_k == 128 && d_v == 128)
+        return ch ? run<128, 128, TIn, TOut, true>(p, stream, events) : run<128, 128, TIn, TOut, false>(p, stream, events);
+    if (d_k == 128 && d_v == 64)
+        return ch ? run<128, 64, TIn, TOut, true>(p, stream, events) : run<128, 64, TIn, TOut, false>(p, stream, events);
+    if (d_k == 64 && d_v == 128)
+        return ch ? run<64, 128, TIn, TOut, true>(p, stream, events) : run<64, 128, TIn, TOut, false>(p, stream, events);
+    if (d_k == 64 && d_v == 64)
+        return ch ? run<64, 64, TIn, TOut, true>(p, stream, events) : run<64, 64, TIn, TOut, false>(p, stream, events);
     return hipErrorInvalidValue;
 }
 
@@ -1403,6 +1721,16 @@ hipError_t launch_prefill(const PrefillParams& p, int d_k, int d_v, int qkv_dtyp
             err = hipGetLastError();
             if (err != hipSuccess) return err;
         }
+    }
+    if (p.segment_chunks > 0) {
+        chain_map_kernel<<<dim3(1), dim3(256), 0, stream>>>(p.cu_seqlens, p.num_seqs, p.segment_chunks, p.chain_base,
+                                                            reinterpret_cast<int4*>(p.chain_desc));
+        err = hipGetLastError();
+        if (err != hipSuccess) return err;
+        chain_order_kernel<<<dim3(unsigned((p.max_chains + 255) / 256)), dim3(256), 0, stream>>>(
+            p.chain_base + p.num_seqs, reinterpret_cast<const int4*>(p.chain_desc), p.chain_order);
+        err = hipGetLastError();
+        if (err != hipSuccess) return err;
     }
     if (qkv_dtype == 1)
         err = out_dtype == 1 ? run_dtype<bf16_t, bf16_t>(p, d_k, d_v, stream, events)

@@ -93,17 +93,39 @@ typedef struct gdn_problem {
                             * batch invariance support to GDN_ATTN backend",
                             * PR description, section "Solution": decode goes
                             * through fused_sigmoid_gating_delta_rule_update) */
+    int32_t segment_chunks; /* prefill only.  0 => one dependent chain per
+                            * sequence.  > 0 => segment split: a sequence of
+                            * nch > segment_chunks 64-token chunks runs as
+                            * S = ceil(nch / segment_chunks) segments of
+                            * ceil(nch / S) chunks, in parallel; each segment
+                            * after the first starts from zero state, beside
+                            * d_k identity columns that give its d_k x d_k
+                            * transition and its outputs' dependence on the
+                            * start state; the start states are then chained
+                            * through the transitions and the outputs
+                            * corrected by one product with them.  The split
+                            * depends on each sequence's length alone, so
+                            * results stay batch-invariant; they differ from
+                            * the unsplit chain by rounding only.  The
+                            * workspace grows by about T h_v (d_k + d_v) 4
+                            * bytes plus 4 h_v d_k (d_k + d_v) bytes per
+                            * segment (the analogue of the context-parallel
+                            * variant of the chunked scan, "[Feature] Add
+                            * batch invariance support to GDN_ATTN backend",
+                            * commit messages) */
 } gdn_problem;
 
-/* Bytes of device workspace gdn_prefill_varlen needs for this problem: the
+/* Bytes of device workspace gdn_prefill_varlen needs for this problem (0 for
+ * a problem the prefill rejects): the
  * chunk map (chunks before each sequence), a dispatch order of the sequences,
  * and the chunk-local terms computed in parallel over all 64-token chunks
  * (split 16-bit images of the normalised K and Q per key head, of
  * T = (I + A)^{-1} and of the decayed Q K^T per value head, and per-token
  * decay scalars), and a 16-byte descriptor per chunk slot.  That is about
  * (T + 63 N) / 64 chunk slots of 512 d_k h_k + 21504 h_v + 16 bytes each,
- * e.g. 27 KB per token for h_k = 16, h_v = 32, d_k = 128.  Depends on
- * num_seqs, total_tokens, h_k, h_v, d_k and d_v; returns 0 for a NULL
+ * e.g. 27 KB per token for h_k = 16, h_v = 32, d_k = 128, plus the segment
+ * split's buffers when segment_chunks > 0.  Depends on num_seqs,
+ * total_tokens, h_k, h_v, d_k, d_v and segment_chunks; returns 0 for a NULL
  * problem or num_seqs <= 0. */
 size_t gdn_prefill_workspace_bytes(const gdn_problem* p);
 

@@ -35,25 +35,25 @@ def canary(shape, dtype):
     return t
 
 
-def canary_outputs(x: PrefillInputs, out_dtype=torch.float32, conv=True):
+def canary_outputs(x: PrefillInputs, out_dtype=torch.float32, conv=True, segment_chunks=0):
     """NaN-canary o, final states, conv states and workspace for a prefill of x."""
     g = x.geom
     N, T = x.num_seqs, x.total_tokens
     o = canary((T, g.h_v, g.d_v), out_dtype)
     fs = canary((N, g.h_v, g.d_k, g.d_v), torch.float32)
     cso = canary((N, g.channels, 3), TORCH_DT[x.dtype]) if conv else None
-    prob = binding.make_problem(N, T, g.h_k, g.h_v, g.d_k, g.d_v, 1, 0)
+    prob = binding.make_problem(N, T, g.h_k, g.h_v, g.d_k, g.d_v, 1, 0, segment_chunks=segment_chunks)
     ws = canary((max(binding.gdn_prefill_workspace_bytes(prob), 1),), torch.uint8)
     return o, fs, cso, ws
 
 
 def gpu_prefill(x: PrefillInputs, *, use_initial=True, use_conv_state=True, out_dtype=torch.float32,
-                conv=True, scale=None, qk_l2norm=True, noalloc=False):
+                conv=True, scale=None, qk_l2norm=True, noalloc=False, segment_chunks=0):
     """The HIP prefill of x with every output and the workspace pre-filled
     with NaN bytes; asserts that every o row and final state was written."""
     dt = TORCH_DT[x.dtype]
     conv = conv and x.conv_w is not None
-    o, fs, cso, ws = canary_outputs(x, out_dtype, conv)
+    o, fs, cso, ws = canary_outputs(x, out_dtype, conv, segment_chunks)
     res = binding.gdn_prefill_varlen(
         dev(x.q, dt), dev(x.k, dt), dev(x.v, dt), dev(x.g), dev(x.beta),
         torch.from_numpy(x.cu_seqlens.astype(np.int32)),
@@ -61,7 +61,7 @@ def gpu_prefill(x: PrefillInputs, *, use_initial=True, use_conv_state=True, out_
         conv_state=dev(x.conv_state_in, dt) if (conv and use_conv_state and x.conv_state_in is not None) else None,
         initial_state=dev(x.initial_state) if (use_initial and x.initial_state is not None) else None,
         out_dtype=out_dtype, scale=scale, use_qk_l2norm=qk_l2norm, out=o, final_state_out=fs,
-        conv_state_out=cso, workspace=None if noalloc else ws, noalloc=noalloc)
+        conv_state_out=cso, workspace=None if noalloc else ws, noalloc=noalloc, segment_chunks=segment_chunks)
     torch.cuda.synchronize()
     o, fs, cso = res
     o, fs = o.float().cpu().numpy(), fs.cpu().numpy()

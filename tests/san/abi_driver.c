@@ -61,6 +61,14 @@ int main(void) {
     EXPECT(gdn_prefill_varlen_pooled(&p, F(1), F(2), F(3), F(4), F(5), F(6), F(9), NULL, F(11), F(12), NULL, NULL,
                                      F(7), F(8), need, NULL), GDN_OK);
     launches++;
+    gdn_problem b = p;
+    b.segment_chunks = 4;
+    EXPECT(pre(&b, F(7), F(8), gdn_prefill_workspace_bytes(&b)), GDN_OK);
+    launches++;
+    EXPECT(gdn_prefill_workspace_bytes(&b) > need, 1);
+    EXPECT(pre(&b, F(7), F(8), need), GDN_ERR_WORKSPACE);
+    b.segment_chunks = -1;
+    EXPECT(pre(&b, F(7), F(8), need), GDN_ERR_SHAPE);
     gdn_problem dp = prob(4, 4, 2, 4, 128);
     EXPECT(gdn_decode_step(&dp, F(1), F(2), F(3), F(4), F(5), F(9), NULL, F(11), F(12), NULL, F(7), NULL), GDN_OK);
     launches++;
@@ -80,7 +88,7 @@ int main(void) {
     EXPECT(gdn_prefill_workspace_bytes(NULL), 0);
 
     /* problem checks */
-    gdn_problem b = p; b.h_v = 3;               EXPECT(pre(&b, F(7), F(8), need), GDN_ERR_SHAPE);
+    b = p; b.h_v = 3;               EXPECT(pre(&b, F(7), F(8), need), GDN_ERR_SHAPE);
     b = p; b.qkv_dtype = 9;                     EXPECT(pre(&b, F(7), F(8), need), GDN_ERR_DTYPE);
     b = p; b.d_k = 96; b.d_v = 96;              EXPECT(pre(&b, F(7), F(8), need), GDN_ERR_UNSUPPORTED);
     b = p; b.conv_width = 3;                    EXPECT(pre(&b, F(7), F(8), need), GDN_ERR_UNSUPPORTED);

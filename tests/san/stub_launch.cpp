@@ -28,6 +28,10 @@ hipError_t launch_prefill(const PrefillParams& p, int d_k, int d_v, int qkv_dtyp
     expect(p.order && p.chunk_base && p.slot_desc && p.kq_img && p.tp_img && p.scal_img, "workspace regions");
     expect((reinterpret_cast<uintptr_t>(p.kq_img) & 255) == 0 && (reinterpret_cast<uintptr_t>(p.tp_img) & 255) == 0,
            "workspace alignment");
+    expect(p.segment_chunks == 0 ? !p.chain_base && !p.seg_y
+                                 : p.chain_base && p.chain_desc && p.chain_order && p.seg_state && p.seg_trans &&
+                                       p.seg_y && p.seg_oloc && p.max_chains >= p.num_seqs,
+           "segment split buffers");
     g_launches++;
     return hipSuccess;
 }
