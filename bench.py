@@ -35,7 +35,6 @@ from __future__ import annotations
 import argparse
 import json
 import os
-import subprocess
 import sys
 import time
 
@@ -214,12 +213,13 @@ def stream_copy_peak(gdn, torch, dev, stream):
 
 
 def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo, no child process)."""
     try:
-        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
-        for ln in out.splitlines():
-            if ln.lower().startswith("model name"):
-                return ln.split(":", 1)[1].strip()
-    except (OSError, subprocess.SubprocessError):
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.lower().startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
         pass
     return "unknown"
 
@@ -483,7 +483,9 @@ def main():
             us = e0.elapsed_time(e1) * 1e3 / calls
             mb = decode_multi_algorithmic(N, m, 16, 32, 128, kept)
             mres[name] = {"us_per_call": us, "tokens_per_s": N * m / (us * 1e-6),
-                          "roofline": roofline(mb, N * m * 32 * 7.0 * 128 * 128, us * 1e-6)}
+                          "roofline": roofline(mb, N * m * 32 * 7.0 * 128 * 128, us * 1e-6, DECODE_KERNEL)}
+            mres[name]["roofline"]["traffic"] = measured_traffic(
+                "decode_kernel_m4_all_states" if kept == m else "decode_kernel_m4_final_state")
             print(f"[bench] decode x{m} ({name}): {us:.1f} us/call, {mb / (us * 1e-6) / 1e9:.0f} GB/s",
                   file=sys.stderr, flush=True)
             del mpools, mcpools
