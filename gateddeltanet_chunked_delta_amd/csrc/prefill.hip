@@ -449,426 +449,338 @@ __global__ void __launch_bounds__(256) chain_order_kernel(const int32_t* __restr
 
 // ---------------------------------------------------------------- prep: q|k prologue and chunk-local terms
 
-constexpr int kPrepThreads = 512;  // 8 waves: two groups of 4 take two value heads at a time
+// Workgroup = (chunk slot, key head): 4 waves; two workgroups fit a CU (LDS
+// below 80 KB, registers below 256 per lane), so one unit's barrier waits
+// overlap the other's work.
+constexpr int kPrepThreads = 256;
 
 template <int DK, int VEC>
 struct PrepSmem {
-    // K, Q rows: [token][d_k] (16-bit); 72-word rows for d_k = 128 keep the
-    // Gram fragment reads free of bank conflicts (68-word rows halved their rate)
+    // K planes (16-bit units; hi, lo) [token][d_k]: 72-word rows for d_k = 128
+    // keep the Gram fragment reads free of bank conflicts
     static constexpr int kPitchK = DK == 128 ? DK + 16 : DK + 8;
-    static constexpr int kPitchF = kChunk + 4;  // [token][token] (fp32)
+    // Q planes, read once per unit: d_k + 8, whose two planes take exactly the
+    // bytes of A and T that replace them after the Gram tiles
+    static constexpr int kPitchQ = DK + 8;
+    static constexpr int kPitchF = kChunk + 4;  // fp32 [token][token]
     static constexpr int kPitchD = 20;          // diagonal inverse blocks: [4][16][kPitchD]
     static constexpr int kNG = 2 * (DK / VEC);  // q|k 16-byte groups per row
-
-    static constexpr size_t szKQ = size_t(kChunk) * kPitchK * sizeof(uint16_t);
+    static constexpr int kRedCols = kNG < 32 ? kNG : 32;  // partial sums kept per row
+    static constexpr size_t szK = size_t(kChunk) * kPitchK * sizeof(uint16_t);
+    static constexpr size_t szQ = size_t(kChunk) * kPitchQ * sizeof(uint16_t);
     static constexpr size_t szF = size_t(kChunk) * kPitchF * sizeof(float);
-    // K and Q split planes; once the Gram tiles are done the same bytes hold
-    // A and T of the two value heads in flight.
-    static constexpr size_t oKhi = 0, oKlo = szKQ, oQhi = 2 * szKQ, oQlo = 3 * szKQ;
-    static constexpr size_t oA0 = 0, oT0 = szF, oA1 = 2 * szF, oT1 = 3 * szF;
-    static constexpr size_t szShared = 4 * szKQ > 4 * szF ? 4 * szKQ : 4 * szF;
-    static constexpr size_t oKK = szShared;  // also the q|k partial sums of squares during the prologue
-    static constexpr size_t oQK = oKK + szF;
-    static constexpr size_t oTd = oQK + szF;                             // [2][4][16][kPitchD]
-    static constexpr size_t oGam = oTd + size_t(2) * 4 * 16 * kPitchD * sizeof(float);  // [2][64] fp64
-    static constexpr size_t oScal = oGam + 2 * kChunk * sizeof(double);  // bet[2][64], rq, rk [64]
-    static constexpr size_t kBytes = oScal + 4 * kChunk * sizeof(float);
-
-    static_assert(size_t(kChunk) * kNG * sizeof(float) <= szF, "partial sums fit the K K^T region");
-    static_assert(kBytes <= size_t(kLdsLimit), "LDS budget");
-    static_assert(oKK % 16 == 0 && oQK % 16 == 0 && oTd % 16 == 0 && oGam % 16 == 0 && oScal % 16 == 0 &&
-                      oA1 % 16 == 0 && oT0 % 16 == 0 && oT1 % 16 == 0,
+    static constexpr size_t oKhi = 0, oKlo = szK;
+    static constexpr size_t oX = 2 * szK;                       // Q hi, Q lo; then A, T (fp32)
+    static constexpr size_t szX = 2 * szQ > 2 * szF ? 2 * szQ : 2 * szF;
+    static constexpr size_t oQhi = oX, oQlo = oX + szQ, oA = oX, oT = oX + szF;
+    static constexpr size_t oR = oX + szX;                      // partial sums; then Td, gam, bet
+    static constexpr size_t szTd = size_t(4) * 16 * kPitchD * sizeof(float);
+    static constexpr size_t szR0 = size_t(kChunk) * kRedCols * sizeof(float);
+    static constexpr size_t szR1 = szTd + kChunk * (sizeof(double) + sizeof(float));
+    static constexpr size_t oTd = oR, oGam = oR + szTd, oBet = oGam + kChunk * sizeof(double);
+    static constexpr size_t kBytes = oR + (szR0 > szR1 ? szR0 : szR1);
+    static_assert(2 * kBytes <= size_t(kLdsLimit), "two workgroups per CU");
+    static_assert(oX % 16 == 0 && oQlo % 16 == 0 && oT % 16 == 0 && oR % 16 == 0 && oGam % 16 == 0 &&
+                      oBet % 16 == 0,
                   "16-byte aligned regions");
 };
 
-// Gram tiles (R, 0..R) of one tile-row of A B^T (A = K or Q rows, B = K rows),
-// accumulated as independent split pairs.
-template <int R, int KS, int PK, typename E>
-__device__ __forceinline__ void gram_row(const E* Ahi, const E* Alo, const E* Khi, const E* Klo, int lr, int lg,
-                                         float4_t (&acc)[R + 1]) {
-#pragma unroll
-    for (int j = 0; j <= R; j++) acc[j] = kZero4;
-#pragma unroll
-    for (int ks = 0; ks < KS; ks++) {
-        const int k = 32 * ks + 8 * lg;
-        const SFrag<E> a = lds_sfrag(Ahi, Alo, PK, 16 * R + lr, k);
-#pragma unroll
-        for (int t = 0; t <= R; t++) mma3(acc[t], a, lds_sfrag(Khi, Klo, PK, 16 * t + lr, k));
-    }
-}
-
-// Workgroup = (chunk slot, key head).  Slots past the last chunk exit.
 template <int DK, typename TIn>
-__global__ void __launch_bounds__(kPrepThreads, 1) prep_kernel(const PrefillParams p) {
+__global__ void __launch_bounds__(kPrepThreads, 2) prep_kernel(const PrefillParams p) {
     constexpr int VEC = Elem<TIn>::kVec;
     constexpr int NGQ = DK / VEC;          // 16-byte groups per q (or k) head row
     constexpr int NG = 2 * NGQ;
     constexpr int RB = kPrepThreads / NG;  // row blocks per chunk
     constexpr int RPB = kChunk / RB;       // rows per thread
     constexpr int KS = DK / 32;
-    static_assert(kPrepThreads % NG == 0 && kChunk % RB == 0, "q|k prologue tiling");
+    static_assert(kPrepThreads % NG == 0 && kChunk % RB == 0 && NG <= 64, "q|k prologue tiling");
     using S = PrepSmem<DK, VEC>;
     using E = typename OpFor<TIn>::type;
-    constexpr int PK = S::kPitchK, PF = S::kPitchF, PD = S::kPitchD;
+    typedef typename OpVec<E>::v8 V8;
+    constexpr int PK = S::kPitchK, PQ = S::kPitchQ, PF = S::kPitchF, PD = S::kPitchD, RC = S::kRedCols;
+    constexpr int PAIR = NG / RC;  // partial sums combined by lane pairs first (1 or 2)
 
     __shared__ __attribute__((aligned(16))) char smem[S::kBytes];
     E* Khi = reinterpret_cast<E*>(smem + S::oKhi);
     E* Klo = reinterpret_cast<E*>(smem + S::oKlo);
     E* Qhi = reinterpret_cast<E*>(smem + S::oQhi);
     E* Qlo = reinterpret_cast<E*>(smem + S::oQlo);
-    float* KK = reinterpret_cast<float*>(smem + S::oKK);
-    float* QK = reinterpret_cast<float*>(smem + S::oQK);
-    float* red = KK;
+    float* Af = reinterpret_cast<float*>(smem + S::oA);
+    float* Tf = reinterpret_cast<float*>(smem + S::oT);
+    float* red = reinterpret_cast<float*>(smem + S::oR);
+    float* Td = reinterpret_cast<float*>(smem + S::oTd);
+    double* gam = reinterpret_cast<double*>(smem + S::oGam);
+    float* bet = reinterpret_cast<float*>(smem + S::oBet);
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t units = int64_t(p.chunk_base[p.num_seqs]) * p.h_k;
+    const int64_t u = blockIdx.x;
+    if (u >= units) return;
+    const int64_t cs = u / p.h_k;
+    const int hk = int(u % p.h_k);
+    const int4 d = reinterpret_cast<const int4*>(p.slot_desc)[cs];  // sequence, first token, length, start
+    const int n = d.x, L = d.z;
+    const int64_t c0 = d.y, bos = d.w;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
     const int G = p.h_v / p.h_k;
     const int64_t nq = int64_t(p.h_k) * DK, C = 2 * nq + int64_t(p.h_v) * p.d_v;
     const bool conv = p.conv_width == 4;
-    const int nunits = p.chunk_base[p.num_seqs] * p.h_k;  // (chunk, key head) units, chunk-major
 
-    // Unit u = (chunk slot cs, key head hk), described by the slot's
-    // descriptor {sequence, first token, length, sequence start}.
-    struct Unit {
-        int cs, hk, n, L;
-        int64_t bos, c0;
-    };
-    const int4* slot_desc = reinterpret_cast<const int4*>(p.slot_desc);
-    auto desc_of = [&](int u) { return u < nunits ? slot_desc[u / p.h_k] : int4{0, 0, 0, 0}; };
-    auto unit_of = [&](int u, const int4& d, Unit& U) {
-        U.cs = u / p.h_k;
-        U.hk = u % p.h_k;
-        U.n = d.x;
-        U.c0 = d.y;
-        U.L = d.z;
-        U.bos = d.w;
-    };
-
-    // Value heads are taken two at a time by wave groups grp = 0 (waves 0-3)
-    // and 1 (waves 4-7).
-    const int grp = wave >> 2, gw = wave & 3;
-    // prologue assignment: one 16-byte channel group of q|k, RPB consecutive rows
+    // ---- prologue: one 16-byte channel group of q|k over RPB consecutive rows
+    //      per thread (the conv history rows and taps loaded once) ----
     const int pg = tid % NG, prow0 = (tid / NG) * RPB;
     const int pwhich = pg / NGQ, poff = (pg % NGQ) * VEC;
-
-    // The workgroup walks units blockIdx.x, blockIdx.x + gridDim.x, ...; the
-    // raw q|k rows, conv taps and first g/beta of the next unit are loaded
-    // while the current one computes.
-    u32x4_t xr[RPB + 3], pw[4];
-    uint32_t pbraw[VEC];
-    float gpre = 0.0f, bpre = 0.0f;
-    // (rows past the chunk's end take g = beta = 0)
-    auto load_gb = [&](const Unit& U, int gi) {
-        if (gw == 0 && gi < G) {
-            const bool in = lane < U.L;
-            const int64_t at = (U.c0 + (in ? lane : 0)) * p.h_v + U.hk * G + gi;
-            const float gv = p.g[at], bv = beta_of(p.beta[at], p.beta_logits != 0);
-            gpre = in ? gv : 0.0f;
-            bpre = in ? bv : 0.0f;
-        }
-    };
-    auto load_unit = [&](const Unit& U) {
-        const int64_t pch = (pwhich ? nq : 0) + int64_t(U.hk) * DK + poff;
-        float unused[VEC];
-        conv_params<TIn>(p, pch, pw, unused);
-        conv_bias_raw<TIn>(p, pch, pbraw);
-        const TIn* pbase = static_cast<const TIn*>(pwhich ? p.k : p.q) + U.hk * DK + poff;
-        if (U.c0 - 3 >= U.bos && U.L == kChunk) {
+    float y[RPB][VEC];
+    {
+        const int64_t pch = (pwhich ? nq : 0) + int64_t(hk) * DK + poff;
+        u32x4_t pw[4];
+        float pbias[VEC];
+        conv_params<TIn>(p, pch, pw, pbias);
+        const TIn* pbase = static_cast<const TIn*>(pwhich ? p.k : p.q) + int64_t(hk) * DK + poff;
+        u32x4_t xr[RPB + 3];
+        if (c0 - 3 >= bos && L == kChunk) {
             // interior chunk: every row, history included, is in the sequence
 #pragma unroll
             for (int jj = 0; jj < RPB + 3; jj++)
-                xr[jj] = *reinterpret_cast<const u32x4_t*>(pbase + (U.c0 + prow0 - 3 + jj) * nq);
+                xr[jj] = *reinterpret_cast<const u32x4_t*>(pbase + (c0 + prow0 - 3 + jj) * nq);
         } else {
-            const int sl = state_slot(p, U.n);
-            const TIn* hist = (p.conv_state_in && slot_has_initial(p, U.n, sl))
+            const int sl = state_slot(p, n);
+            const TIn* hist = (p.conv_state_in && slot_has_initial(p, n, sl))
                                   ? static_cast<const TIn*>(p.conv_state_in) + (int64_t(sl) * C + pch) * 3
                                   : nullptr;
-            load_rows<TIn, RPB>(xr, pbase, nq, U.c0, prow0, U.L, U.bos, conv, hist);
+            load_rows<TIn, RPB>(xr, pbase, nq, c0, prow0, L, bos, conv, hist);
         }
-    };
-
-    // The descriptor of the unit after next is loaded one unit ahead.
-    Unit U;
-    int u = blockIdx.x;
-    int4 dnext = desc_of(u + int(gridDim.x));
-    if (u < nunits) {
-        unit_of(u, desc_of(u), U);
-        load_unit(U);
-        load_gb(U, grp);
-        __builtin_amdgcn_s_waitcnt(kVmcnt0);  // (see the wait in the loop)
-    }
-    for (; u < nunits; u += gridDim.x) {
-        const int cs = U.cs, hk = U.hk, L = U.L;
-        const int64_t c0 = U.c0;
-
-        // ---- prologue: conv + SiLU of this thread's rows, partial sums of squares ----
-        float pbias[VEC];
-#pragma unroll
-        for (int e = 0; e < VEC; e++) pbias[e] = __uint_as_float(pbraw[e]);
-        float y[RPB][VEC];
         conv_rows<TIn, RPB>(conv, xr, pw, pbias, y);
+    }
+    // partial sums of squares per (row, group), pairs of neighbouring groups
+    // combined first when there are more than 32 groups (commuted pairs: both
+    // lanes hold the same sum)
+#pragma unroll
+    for (int i = 0; i < RPB; i++) {
+        float ss = 0.0f;
+#pragma unroll
+        for (int e = 0; e < VEC; e++) {
+            if (prow0 + i >= L) y[i][e] = 0.0f;
+            ss += y[i][e] * y[i][e];
+        }
+        if constexpr (PAIR == 2) ss += __shfl_xor(ss, 1);
+        if (pg % PAIR == 0) red[(prow0 + i) * RC + pg / PAIR] = ss;
+    }
+    // the first value head's decays, by wave 0 after its share of the prologue
+    auto decays = [&](int gi) {
+        const int h = hk * G + gi;
+        const bool in = lane < L;
+        const int64_t at = (c0 + (in ? lane : 0)) * p.h_v + h;
+        const float gv = in ? p.g[at] : 0.0f;
+        const float bv = in ? beta_of(p.beta[at], p.beta_logits != 0) : 0.0f;
+        double x = gv;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const double t = __shfl_up(x, o);
+            if (lane >= o) x += t;
+        }
+        const double gl = __shfl(x, 63);
+        gam[lane] = x;
+        bet[lane] = bv;
+        const float ex = exp_of_f64(x);
+        float* sc = p.scal_img + (cs * p.h_v + h) * Img<DK>::kScal;
+        sc[lane] = bv;
+        sc[kChunk + lane] = ex;
+        sc[2 * kChunk + lane] = exp_of_f64(gl - x);
+        const float exl = __shfl(ex, 63);
+        sc[3 * kChunk + lane] = lane == 0 ? exl : 0.0f;
+    };
+    lds_barrier();
+    // normalised rows as split pairs into the K and Q planes and the K|Q
+    // image; each thread sums its row's partial sums itself, in a fixed order
+    {
+        E* img = static_cast<E*>(p.kq_img) + (cs * p.h_k + hk) * Img<DK>::kKQ + (pwhich ? 0 : 2 * kChunk * DK);
+        E* dhi = pwhich ? Khi : Qhi;
+        E* dlo = pwhich ? Klo : Qlo;
+        const int dp = pwhich ? PK : PQ;
+        float sc[RPB];
 #pragma unroll
         for (int i = 0; i < RPB; i++) {
-            float ss = 0.0f;
+            const float* rr = red + (prow0 + i) * RC + pwhich * (RC / 2);
+            static_assert((RC / 2) % 4 == 0, "partial sums in 16-byte loads");
+            float sum = 0.0f;
 #pragma unroll
-            for (int e = 0; e < VEC; e++) {
-                if (prow0 + i >= L) y[i][e] = 0.0f;
-                ss += y[i][e] * y[i][e];
+            for (int q = 0; q < RC / 2; q += 4) {
+                const float4 r4 = *reinterpret_cast<const float4*>(rr + q);
+                sum += r4.x;
+                sum += r4.y;
+                sum += r4.z;
+                sum += r4.w;
             }
-            red[(prow0 + i) * NG + pg] = ss;
+            sc[i] = p.qk_l2norm ? 1.0f / sqrtf(sum + p.l2_eps) : 1.0f;
         }
-        Unit N;
-        const bool more = u + int(gridDim.x) < nunits;
-        if (more) {
-            unit_of(u + gridDim.x, dnext, N);
-            dnext = desc_of(u + 2 * int(gridDim.x));
-            load_unit(N);
-        }
-        lds_barrier();
-        // normalised rows as split pairs, into LDS and the K|Q image; each
-        // thread sums its row's partial sums of squares itself (a fixed order,
-        // so every thread of a row gets the same 1/|q| or 1/|k|)
-        {
-            // K image first, then Q
-            E* img = static_cast<E*>(p.kq_img) + (int64_t(cs) * p.h_k + hk) * Img<DK>::kKQ +
-                            (pwhich ? 0 : 2 * kChunk * DK);
-            E* dhi = pwhich ? Khi : Qhi;
-            E* dlo = pwhich ? Klo : Qlo;
 #pragma unroll
-            for (int i = 0; i < RPB; i++) {
-                const int row = prow0 + i;
-                const float* rr = red + row * NG + pwhich * NGQ;
-                static_assert(NGQ % 4 == 0, "partial sums in 16-byte loads");
-                float sum = 0.0f;
+        for (int i = 0; i < RPB; i++) {
+            const int row = prow0 + i;
+            if constexpr (VEC == 8) {
+                // bf16 pairs: 8 columns per plane piece
+                bf16x2_t h16[VEC / 2], l16[VEC / 2];
 #pragma unroll
-                for (int q = 0; q < NGQ; q += 4) {
-                    const float4 r4 = *reinterpret_cast<const float4*>(rr + q);
-                    sum += r4.x;
-                    sum += r4.y;
-                    sum += r4.z;
-                    sum += r4.w;
-                }
-                const float sc = p.qk_l2norm ? 1.0f / sqrtf(sum + p.l2_eps) : 1.0f;
-                if constexpr (VEC == 8) {
-                    // bf16 pairs: 8 columns per plane piece
-                    bf16x2_t h16[VEC / 2], l16[VEC / 2];
-#pragma unroll
-                    for (int e = 0; e < VEC / 2; e++) split2(y[i][2 * e] * sc, y[i][2 * e + 1] * sc, h16[e], l16[e]);
-                    const uint4 hv = *reinterpret_cast<const uint4*>(h16), lv = *reinterpret_cast<const uint4*>(l16);
-                    *reinterpret_cast<uint4*>(dhi + row * PK + poff) = hv;
-                    *reinterpret_cast<uint4*>(dlo + row * PK + poff) = lv;
-                    *reinterpret_cast<uint4*>(img + row * DK + poff) = hv;
-                    *reinterpret_cast<uint4*>(img + kChunk * DK + row * DK + poff) = lv;
-                } else {
-                    // fp32 values: columns 8c .. 8c+3 go to the hi plane and
-                    // 8c+4 .. 8c+7 to the lo plane, at the piece of columns 8c
-                    const float4 v = make_float4(y[i][0] * sc, y[i][1] * sc, y[i][2] * sc, y[i][3] * sc);
-                    const int c8 = poff & ~7;
-                    const bool second = (poff & 4) != 0;
-                    *reinterpret_cast<float4*>((second ? dlo : dhi) + row * PK + c8) = v;
-                    *reinterpret_cast<float4*>(img + (second ? kChunk * DK : 0) + row * DK + c8) = v;
-                }
-            }
-        }
-        lds_barrier();
-
-        // Decays of value head gi (the group's first wave): gam = running sum of
-        // g, and the per-token scalars.  gam reaches about -50 over a chunk; in
-        // fp32 its rounding (~4e-6 absolute) would become a relative error of
-        // every decay factor, which the inter- and intra-chunk terms amplify.
-        // Scan in fp64.
-        double* gam = reinterpret_cast<double*>(smem + S::oGam) + grp * kChunk;
-        float* bet = reinterpret_cast<float*>(smem + S::oScal) + grp * kChunk;
-        auto decays = [&](int gi) {
-            const int64_t ih = int64_t(cs) * p.h_v + hk * G + gi;
-            const float gv = gpre, bv = bpre;
-            load_gb(U, gi + 2);
-            double x = gv;
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const double t = __shfl_up(x, o);
-                if (lane >= o) x += t;
-            }
-            const double gl = __shfl(x, 63);
-            gam[lane] = x;
-            bet[lane] = bv;
-            const float ex = exp_of_f64(x);
-            float* sc = p.scal_img + ih * Img<DK>::kScal;
-            sc[lane] = bv;
-            sc[kChunk + lane] = ex;
-            sc[2 * kChunk + lane] = exp_of_f64(gl - x);
-            const float exl = __shfl(ex, 63);
-            sc[3 * kChunk + lane] = lane == 0 ? exl : 0.0f;
-        };
-
-        // ---- Gram tiles K K^T (waves 0-3) and Q K^T (waves 4-7), lower tiles
-        //      only, raw fp32; wave w takes tile-row w % 4.  The waves of
-        //      tile-row 0 (one tile each) also scan the decays of their group's
-        //      first value head. ----
-        {
-            const int which = wave >> 2, tr = wave & 3;
-            const E* Ahi = which ? Qhi : Khi;
-            const E* Alo = which ? Qlo : Klo;
-            float* dst = which ? QK : KK;
-            auto store_row = [&](const float4_t* acc, int ntiles) {
-#pragma unroll
-                for (int t = 0; t < 4; t++)
-                    if (t < ntiles)
-#pragma unroll
-                        for (int e = 0; e < 4; e++) dst[(16 * tr + 4 * lg + e) * PF + 16 * t + lr] = acc[t][e];
-            };
-            if (tr == 0) {
-                float4_t acc[1];
-                gram_row<0, KS, PK>(Ahi, Alo, Khi, Klo, lr, lg, acc);
-                store_row(acc, 1);
-                if (grp < G) decays(grp);
-            } else if (tr == 1) {
-                float4_t acc[2];
-                gram_row<1, KS, PK>(Ahi, Alo, Khi, Klo, lr, lg, acc);
-                store_row(acc, 2);
-            } else if (tr == 2) {
-                float4_t acc[3];
-                gram_row<2, KS, PK>(Ahi, Alo, Khi, Klo, lr, lg, acc);
-                store_row(acc, 3);
+                for (int e = 0; e < VEC / 2; e++)
+                    split2(y[i][2 * e] * sc[i], y[i][2 * e + 1] * sc[i], h16[e], l16[e]);
+                const uint4 hv = *reinterpret_cast<const uint4*>(h16), lv = *reinterpret_cast<const uint4*>(l16);
+                *reinterpret_cast<uint4*>(dhi + row * dp + poff) = hv;
+                *reinterpret_cast<uint4*>(dlo + row * dp + poff) = lv;
+                *reinterpret_cast<uint4*>(img + row * DK + poff) = hv;
+                *reinterpret_cast<uint4*>(img + kChunk * DK + row * DK + poff) = lv;
             } else {
-                float4_t acc[4];
-                gram_row<3, KS, PK>(Ahi, Alo, Khi, Klo, lr, lg, acc);
-                store_row(acc, 4);
+                // fp32 values: columns 8c .. 8c+3 go to the hi plane and
+                // 8c+4 .. 8c+7 to the lo plane, at the piece of columns 8c
+                const float4 v = make_float4(y[i][0] * sc[i], y[i][1] * sc[i], y[i][2] * sc[i], y[i][3] * sc[i]);
+                const int c8 = poff & ~7;
+                const bool second = (poff & 4) != 0;
+                *reinterpret_cast<float4*>((second ? dlo : dhi) + row * dp + c8) = v;
+                *reinterpret_cast<float4*>(img + (second ? kChunk * DK : 0) + row * DK + c8) = v;
+            }
+        }
+    }
+    lds_barrier();
+
+    // ---- Gram tiles of this wave's tile row: K K^T and Q K^T, tiles (w, t),
+    //      t <= w, raw fp32 in accumulator layout (the A operands read once) ----
+    float4_t kk[4], qk[4];
+    {
+        SFrag<E> kf[KS], qf[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++) {
+            kf[ks] = lds_sfrag(Khi, Klo, PK, 16 * w + lr, 32 * ks + 8 * lg);
+            qf[ks] = lds_sfrag(Qhi, Qlo, PQ, 16 * w + lr, 32 * ks + 8 * lg);
+        }
+#pragma unroll
+        for (int t = 0; t < 4; t++) kk[t] = qk[t] = kZero4;
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++)
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                if (t < w) {
+                    const SFrag<E> b = lds_sfrag(Khi, Klo, PK, 16 * t + lr, 32 * ks + 8 * lg);
+                    mma3(kk[t], kf[ks], b);
+                    mma3(qk[t], qf[ks], b);
+                } else if (t == w) {
+                    mma3(kk[t], kf[ks], kf[ks]);
+                    mma3(qk[t], qf[ks], kf[ks]);
+                }
+            }
+    }
+    if (w == 0) decays(0);  // gam, bet: the partial sums' bytes are free now
+    lds_barrier();          // the Q planes are free for A and T; the first decays are in
+
+    // ---- per value head of the group ----
+    for (int gi = 0; gi < G; gi++) {
+        const int h = hk * G + gi;
+        const int64_t ih = cs * p.h_v + h;
+        if (gi > 0) {
+            if (w == 0) decays(gi);
+            lds_barrier();
+        }
+        // A (fp32, LDS) and P (fp32, LDS) from the Gram tiles in registers:
+        // A[r][s] = beta_r e^{gam_r - gam_s} (k_r . k_s) for s < r,
+        // P[r][s] = e^{gam_r - gam_s} (q_r . k_s) for s <= r
+        {
+            double gr[4];
+            float br[4];
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                gr[e] = gam[16 * w + 4 * lg + e];
+                br[e] = bet[16 * w + 4 * lg + e];
+            }
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                if (t > w) continue;
+                const int sidx = 16 * t + lr;
+                const double gs = gam[sidx];
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const int r = 16 * w + 4 * lg + e;
+                    const float ex = __expf(static_cast<float>(gr[e] - gs));
+                    const float dec = sidx <= r ? ex : 0.0f;
+                    Af[r * PF + sidx] = sidx < r ? br[e] * dec * kk[t][e] : 0.0f;
+                    Tf[r * PF + sidx] = sidx <= r ? dec * qk[t][e] : 0.0f;
+                }
             }
         }
         lds_barrier();
-
-        // ---- per value head: decays, A, P, T; wave group grp (4 waves) takes
-        //      value heads grp, grp + 2, ... of the key head's group ----
-        const int gt = tid & 255;
-        float* Af = reinterpret_cast<float*>(smem + (grp ? S::oA1 : S::oA0));
-        float* Tf = reinterpret_cast<float*>(smem + (grp ? S::oT1 : S::oT0));
-        float* Td = reinterpret_cast<float*>(smem + S::oTd) + grp * 4 * 16 * PD;
-        for (int g0 = 0; g0 < G; g0 += 2) {
-            const int gi = g0 + grp;
-            const bool act = gi < G;  // both groups run every barrier
-            const int h = hk * G + gi;
-            const int64_t ih = int64_t(cs) * p.h_v + h;
-            // (the first pair's decays were scanned during the Gram tiles)
-            if (g0 > 0) {
-                if (act && gw == 0) decays(gi);
-                lds_barrier();
-            }
-            // A (fp32, LDS) and P (split, image): 8 consecutive columns per item
-            if (act) {
-                E* pimg = static_cast<E*>(p.tp_img) + ih * Img<DK>::kTP + 2 * TriPack::kPieces * 8;
+        // P image (lower blocks, 8 columns per item), then the inverses of the
+        // 16x16 diagonal blocks of (I + A) by forward substitution (wave 0, one
+        // column per lane)
+        {
+            E* pimg = static_cast<E*>(p.tp_img) + ih * Img<DK>::kTP + 2 * TriPack::kPieces * 8;
 #pragma unroll
-                for (int it = 0; it < 2; it++) {
-                    const int item = gt + 256 * it;
-                    const int r = item >> 3, s0 = (item & 7) * 8;
-                    const double gr = gam[r];
-                    const float br = bet[r];
-                    // All operands are loaded unconditionally (every index is in
-                    // bounds) and masked by selects: conditional loads compiled
-                    // into one branch and one LDS round trip per element.
-                    float kk[8], qk[8];
-                    double gs[8];
-#pragma unroll
-                    for (int h4 = 0; h4 < 2; h4++) {
-                        *reinterpret_cast<float4*>(kk + 4 * h4) = *reinterpret_cast<const float4*>(KK + r * PF + s0 + 4 * h4);
-                        *reinterpret_cast<float4*>(qk + 4 * h4) = *reinterpret_cast<const float4*>(QK + r * PF + s0 + 4 * h4);
-                    }
-#pragma unroll
-                    for (int h2 = 0; h2 < 4; h2++)
-                        *reinterpret_cast<double2*>(gs + 2 * h2) = *reinterpret_cast<const double2*>(gam + s0 + 2 * h2);
-                    float a[8], pp[8];
-#pragma unroll
-                    for (int e = 0; e < 8; e++) {
-                        const int sidx = s0 + e;
-                        const float ex = __expf(static_cast<float>(gr - gs[e]));
-                        const float dec = (sidx <= r) ? ex : 0.0f;
-                        a[e] = (sidx < r) ? br * dec * kk[e] : 0.0f;
-                        pp[e] = (sidx <= r) ? dec * qk[e] : 0.0f;
-                    }
-                    *reinterpret_cast<float4*>(Af + r * PF + s0) = make_float4(a[0], a[1], a[2], a[3]);
-                    *reinterpret_cast<float4*>(Af + r * PF + s0 + 4) = make_float4(a[4], a[5], a[6], a[7]);
-                    if ((s0 >> 4) <= (r >> 4)) {
-                        uint4 hv, lv;
-                        split_pack<E>(pp, hv, lv);
-                        const int q = TriPack::row_start(r) + (s0 >> 3);
-                        *reinterpret_cast<uint4*>(pimg + 8 * q) = hv;
-                        *reinterpret_cast<uint4*>(pimg + 8 * (TriPack::kPieces + q)) = lv;
-                    }
+            for (int it = 0; it < 2; it++) {
+                const int item = tid + 256 * it;
+                const int r = item >> 3, s0 = (item & 7) * 8;
+                if ((s0 >> 4) <= (r >> 4)) {
+                    float pp[8];
+                    *reinterpret_cast<float4*>(pp) = *reinterpret_cast<const float4*>(Tf + r * PF + s0);
+                    *reinterpret_cast<float4*>(pp + 4) = *reinterpret_cast<const float4*>(Tf + r * PF + s0 + 4);
+                    uint4 hv, lv;
+                    split_pack<E>(pp, hv, lv);
+                    const int q = TriPack::row_start(r) + (s0 >> 3);
+                    *reinterpret_cast<uint4*>(pimg + 8 * q) = hv;
+                    *reinterpret_cast<uint4*>(pimg + 8 * (TriPack::kPieces + q)) = lv;
                 }
             }
-            lds_barrier();
-            // inverses of the 16x16 diagonal blocks of (I + A) by forward
-            // substitution, one column per lane (the group's first wave)
-            if (act && gw == 0) {
-                const int b = lane >> 4, c = lane & 15;
-                // column-oriented: once x[r] is known it is added into every later
-                // row's sum, so the steps of one column are independent (each row
-                // still sums s = 0, 1, ..., r - 1 in order)
-                float x[16], acc[16];
+        }
+        if (w == 0) {
+            const int b = lane >> 4, c = lane & 15;
+            // column-oriented: once x[r] is known it is added into every later
+            // row's sum, so the steps of one column are independent (each row
+            // still sums s = 0, 1, ..., r - 1 in order)
+            float x[16], acc[16];
 #pragma unroll
-                for (int r = 0; r < 16; r++) acc[r] = 0.0f;
+            for (int r = 0; r < 16; r++) acc[r] = 0.0f;
 #pragma unroll
-                for (int r = 0; r < 16; r++) {
-                    x[r] = (r < c) ? 0.0f : ((r == c) ? 1.0f : -acc[r]);
+            for (int r = 0; r < 16; r++) {
+                x[r] = (r < c) ? 0.0f : ((r == c) ? 1.0f : -acc[r]);
 #pragma unroll
-                    for (int s2 = r + 1; s2 < 16; s2++) acc[s2] += Af[(16 * b + s2) * PF + 16 * b + r] * x[r];
-                }
-#pragma unroll
-                for (int r = 0; r < 16; r++) Td[(16 * b + r) * PD + c] = x[r];
+                for (int s2 = r + 1; s2 < 16; s2++) acc[s2] += Af[(16 * b + s2) * PF + 16 * b + r] * x[r];
             }
-            // The next unit's raw rows and taps (loaded after this unit's
-            // prologue) have long arrived; waiting for them here, where only
-            // older stores are outstanding, tells the compiler so.  Otherwise the
-            // in-order vector memory counter makes their first use wait for
-            // this unit's last image stores too.
-            __builtin_amdgcn_s_waitcnt(kVmcnt0);
-            lds_barrier();
-            if (act) {
-                if (gw == 0) {
-                    inverse_column<0, PF, PD>(Af, Td, Tf, lr, lg);
-                } else if (gw == 1) {
-                    inverse_column<1, PF, PD>(Af, Td, Tf, lr, lg);
-                } else if (gw == 2) {
-                    inverse_column<2, PF, PD>(Af, Td, Tf, lr, lg);
-                } else if (lane < 16) {  // block (3, 3) is its diagonal inverse
 #pragma unroll
-                    for (int r = 0; r < 16; r++) Tf[(48 + r) * PF + 48 + lane] = Td[(48 + r) * PD + lane];
-                }
-            }
-            lds_barrier();
-            // T image (lower blocks)
-            if (act) {
-                E* timg = static_cast<E*>(p.tp_img) + ih * Img<DK>::kTP;
+            for (int r = 0; r < 16; r++) Td[(16 * b + r) * PD + c] = x[r];
+        }
+        lds_barrier();
+        // off-diagonal blocks of T on fp32 matrix cores, one column block per wave
+        if (w == 0) {
+            inverse_column<0, PF, PD>(Af, Td, Tf, lr, lg);
+        } else if (w == 1) {
+            inverse_column<1, PF, PD>(Af, Td, Tf, lr, lg);
+        } else if (w == 2) {
+            inverse_column<2, PF, PD>(Af, Td, Tf, lr, lg);
+        } else if (lane < 16) {  // block (3, 3) is its diagonal inverse
 #pragma unroll
-                for (int it = 0; it < 2; it++) {
-                    const int item = gt + 256 * it;
-                    const int r = item >> 3, s0 = (item & 7) * 8;
-                    float tl[8];  // loaded unconditionally, masked below
+            for (int r = 0; r < 16; r++) Tf[(48 + r) * PF + 48 + lane] = Td[(48 + r) * PD + lane];
+        }
+        lds_barrier();
+        // T image (lower blocks)
+        {
+            E* timg = static_cast<E*>(p.tp_img) + ih * Img<DK>::kTP;
+#pragma unroll
+            for (int it = 0; it < 2; it++) {
+                const int item = tid + 256 * it;
+                const int r = item >> 3, s0 = (item & 7) * 8;
+                if ((s0 >> 4) <= (r >> 4)) {
+                    float tl[8];
                     *reinterpret_cast<float4*>(tl) = *reinterpret_cast<const float4*>(Tf + r * PF + s0);
                     *reinterpret_cast<float4*>(tl + 4) = *reinterpret_cast<const float4*>(Tf + r * PF + s0 + 4);
-                    if ((s0 >> 4) <= (r >> 4)) {
-                        float t[8];
+                    float t8[8];
 #pragma unroll
-                        for (int e = 0; e < 8; e++) t[e] = ((s0 + e) >> 4 <= (r >> 4)) ? tl[e] : 0.0f;
-                        uint4 hv, lv;
-                        split_pack<E>(t, hv, lv);
-                        const int q = TriPack::row_start(r) + (s0 >> 3);
-                        *reinterpret_cast<uint4*>(timg + 8 * q) = hv;
-                        *reinterpret_cast<uint4*>(timg + 8 * (TriPack::kPieces + q)) = lv;
-                    }
+                    for (int e = 0; e < 8; e++) t8[e] = ((s0 + e) >> 4 <= (r >> 4)) ? tl[e] : 0.0f;
+                    uint4 hv, lv;
+                    split_pack<E>(t8, hv, lv);
+                    const int q = TriPack::row_start(r) + (s0 >> 3);
+                    *reinterpret_cast<uint4*>(timg + 8 * q) = hv;
+                    *reinterpret_cast<uint4*>(timg + 8 * (TriPack::kPieces + q)) = lv;
                 }
             }
-            // No barrier here: Tf is next written three barriers later (the
-            // next pair's inverse columns) or, after the last pair, by the next
-            // unit's split planes, which come after the prologue's barrier; the
-            // next pair's decays and the next prologue touch only gam, bet and
-            // the partial sums.  A wave may start them while others still read
-            // Tf for this image.
         }
-        if (more) {
-            load_gb(N, grp);
-            U = N;
-        }
+        // the next value head's decays touch only gam, bet and the scalar
+        // image, whose last readers came before the previous barrier; its A and
+        // P writes come after the barrier that follows the decays
     }
 }
 
@@ -1598,19 +1510,6 @@ __global__ void __launch_bounds__(256) segment_correct_kernel(const PrefillParam
     }
 }
 
-// Compute units of the current device (cached per device).
-int64_t compute_units() {
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] <= 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cached[dev] = n;
-    }
-    return cached[dev];
-}
-
 hipError_t record(void* const* events, int i, hipStream_t stream) {
     return events ? hipEventRecord(static_cast<hipEvent_t>(events[i]), stream) : hipSuccess;
 }
@@ -1620,10 +1519,8 @@ hipError_t run(const PrefillParams& p, hipStream_t stream, void* const* events) 
     hipError_t err = record(events, 0, stream);
     if (err != hipSuccess) return err;
     if (p.slots > 0) {
-        // one resident workgroup per CU walks the (chunk, key head) units
-        const int64_t units = p.slots * p.h_k;
-        const int64_t grid = units < compute_units() ? units : compute_units();
-        prep_kernel<DK, TIn><<<dim3(unsigned(grid)), dim3(kPrepThreads), 0, stream>>>(p);
+        // one workgroup per (chunk slot, key head); slots past the last chunk exit
+        prep_kernel<DK, TIn><<<dim3(unsigned(p.slots * p.h_k)), dim3(kPrepThreads), 0, stream>>>(p);
         err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
