@@ -485,6 +485,15 @@ struct PrepSmem {
                   "16-byte aligned regions");
 };
 
+// A 16-byte piece of a chunk image.  Nontemporal: the images of one call far
+// exceed the L2 caches, and the carry kernel reads them only after the whole
+// chunk-parallel kernel has run (measured ~1.5% faster per call than plain
+// stores, mostly in the carry kernel's reads).
+template <typename E>
+__device__ __forceinline__ void img_store(E* dst, uint4 v) {
+    __builtin_nontemporal_store(*reinterpret_cast<const u32x4_t*>(&v), reinterpret_cast<u32x4_t*>(dst));
+}
+
 template <int DK, typename TIn>
 __global__ void __launch_bounds__(kPrepThreads, 2) prep_kernel(const PrefillParams p) {
     constexpr int VEC = Elem<TIn>::kVec;
@@ -626,8 +635,8 @@ __global__ void __launch_bounds__(kPrepThreads, 2) prep_kernel(const PrefillPara
                 const uint4 hv = *reinterpret_cast<const uint4*>(h16), lv = *reinterpret_cast<const uint4*>(l16);
                 *reinterpret_cast<uint4*>(dhi + row * dp + poff) = hv;
                 *reinterpret_cast<uint4*>(dlo + row * dp + poff) = lv;
-                *reinterpret_cast<uint4*>(img + row * DK + poff) = hv;
-                *reinterpret_cast<uint4*>(img + kChunk * DK + row * DK + poff) = lv;
+                img_store(img + row * DK + poff, hv);
+                img_store(img + kChunk * DK + row * DK + poff, lv);
             } else {
                 // fp32 values: columns 8c .. 8c+3 go to the hi plane and
                 // 8c+4 .. 8c+7 to the lo plane, at the piece of columns 8c
@@ -635,7 +644,7 @@ __global__ void __launch_bounds__(kPrepThreads, 2) prep_kernel(const PrefillPara
                 const int c8 = poff & ~7;
                 const bool second = (poff & 4) != 0;
                 *reinterpret_cast<float4*>((second ? dlo : dhi) + row * dp + c8) = v;
-                *reinterpret_cast<float4*>(img + (second ? kChunk * DK : 0) + row * DK + c8) = v;
+                img_store(img + (second ? kChunk * DK : 0) + row * DK + c8, *reinterpret_cast<const uint4*>(&v));
             }
         }
     }
@@ -721,8 +730,8 @@ __global__ void __launch_bounds__(kPrepThreads, 2) prep_kernel(const PrefillPara
                     uint4 hv, lv;
                     split_pack<E>(pp, hv, lv);
                     const int q = TriPack::row_start(r) + (s0 >> 3);
-                    *reinterpret_cast<uint4*>(pimg + 8 * q) = hv;
-                    *reinterpret_cast<uint4*>(pimg + 8 * (TriPack::kPieces + q)) = lv;
+                    img_store(pimg + 8 * q, hv);
+                    img_store(pimg + 8 * (TriPack::kPieces + q), lv);
                 }
             }
         }
@@ -773,8 +782,8 @@ __global__ void __launch_bounds__(kPrepThreads, 2) prep_kernel(const PrefillPara
                     uint4 hv, lv;
                     split_pack<E>(t8, hv, lv);
                     const int q = TriPack::row_start(r) + (s0 >> 3);
-                    *reinterpret_cast<uint4*>(timg + 8 * q) = hv;
-                    *reinterpret_cast<uint4*>(timg + 8 * (TriPack::kPieces + q)) = lv;
+                    img_store(timg + 8 * q, hv);
+                    img_store(timg + 8 * (TriPack::kPieces + q), lv);
                 }
             }
         }
