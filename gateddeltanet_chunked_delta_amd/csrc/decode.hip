@@ -239,16 +239,47 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(const DecodeParams p) 
             if (kPrefetch && gi + 1 < G) load_tile(hn, H0 + int64_t(gi + 1) * DK * DV);
             const int64_t tok = row0 + j;
             const float decay = gate[j][0], b = gate[j][1];
+            // The waves' partials of this lane's 4 columns, summed in wave
+            // order.  With 32 column groups the two half-waves hold the same
+            // columns: the lower half sums p, the upper s, and they swap.
+            float skv[4], sqv[4];
+            if constexpr (CG == 32) {
+                const int qn = lane >> 5;
+                float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int w = 0; w < kWaves; w++) {
+                    const float4 v4 = *reinterpret_cast<const float4*>(&pt[w][qn][4 * cg]);
+                    a[0] += v4.x;
+                    a[1] += v4.y;
+                    a[2] += v4.z;
+                    a[3] += v4.w;
+                }
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(a[e]), __float_as_uint(a[e]), false, false);
+                    const float o = __uint_as_float(qn ? sw[0] : sw[1]);
+                    skv[e] = qn ? o : a[e];
+                    sqv[e] = qn ? a[e] : o;
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const int c = 4 * cg + e;
+                    float sk = 0.0f, sq = 0.0f;
+#pragma unroll
+                    for (int w = 0; w < kWaves; w++) {
+                        sk += pt[w][0][c];
+                        sq += pt[w][1][c];
+                    }
+                    skv[e] = sk;
+                    sqv[e] = sq;
+                }
+            }
             float dlt[4];
 #pragma unroll
             for (int e = 0; e < 4; e++) {
                 const int c = 4 * cg + e;
-                float sk = 0.0f, sq = 0.0f;
-#pragma unroll
-                for (int w = 0; w < kWaves; w++) {
-                    sk += pt[w][0][c];
-                    sq += pt[w][1][c];
-                }
+                const float sk = skv[e], sq = sqv[e];
                 dlt[e] = b * fmaf(-decay, sk, vs[j][c]);
                 if (rg == 0) {
                     TOut* op = static_cast<TOut*>(p.o) + (tok * p.h_v + h) * DV + c;
