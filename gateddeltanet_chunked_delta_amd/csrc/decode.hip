@@ -98,11 +98,16 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(const DecodeParams p) 
     static_assert(kThreads % CG == 0 && DK % RG == 0 && 64 % CG == 0, "decode tiling");
     static_assert(2 * DK <= kThreads - KMAX && DV <= kThreads - KMAX, "one channel per thread, gate threads apart");
 
-    __shared__ float qs[KMAX][DK], ks[KMAX][DK], vs[KMAX][DV];
+    // q and k of each token with channel c at (c % RG) RPT + c / RG: a thread's
+    // rows rg + RG mm are contiguous
+    __shared__ __attribute__((aligned(16))) float qs[KMAX][DK], ks[KMAX][DK];
+    __shared__ __attribute__((aligned(16))) float vs[KMAX][DV];
+    auto qk_at = [](int c) { return (c % RG) * RPT + c / RG; };
     // per-wave partial sums, double-buffered over tokens so that one barrier
     // per token suffices
     __shared__ float part[KMAX == 1 ? 1 : 2][kWaves][2][DV];
     __shared__ float scal[KMAX][4];  // |q|^2, |k|^2, raw k.q per token
+    __shared__ __attribute__((aligned(16))) float fac[KMAX][4];  // 1/|q|, 1/|k|, k.q normalised
     __shared__ float gate[KMAX][2];  // e^g and beta of the current head per token
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -160,7 +165,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(const DecodeParams p) 
             const bool isk = tid >= DK;
             const int c = isk ? tid - DK : tid;
             const TIn* src = static_cast<const TIn*>(isk ? p.k : p.q) + row0 * nq + int64_t(hk) * DK + c;
-            float* dst = isk ? &ks[0][c] : &qs[0][c];
+            float* dst = isk ? &ks[0][qk_at(c)] : &qs[0][qk_at(c)];
             if (conv) {
                 const int64_t ch = (isk ? nq : 0) + int64_t(hk) * DK + c;
                 conv_tokens<TIn>(cw, cb, cs, C, ch, slot, wslot, src, nq, m, dst, DK);
@@ -192,25 +197,48 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(const DecodeParams p) 
 #pragma unroll
                 for (int mm = 0; mm < DK / 64; mm++) {
                     const int i = lane + 64 * mm;
-                    const float x = w == 1 ? ks[j][i] : qs[j][i], y = w == 0 ? qs[j][i] : ks[j][i];
+                    const int at = qk_at(i);
+                    const float x = w == 1 ? ks[j][at] : qs[j][at], y = w == 0 ? qs[j][at] : ks[j][at];
                     a = fmaf(x, y, a);
                 }
                 a = wave_sum(a);
                 if (lane == 0) scal[j][w] = a;
             }
             __syncthreads();
+            if (tid < m) {
+                const float rq = p.qk_l2norm ? 1.0f / sqrtf(scal[tid][0] + p.l2_eps) : 1.0f;
+                const float rk = p.qk_l2norm ? 1.0f / sqrtf(scal[tid][1] + p.l2_eps) : 1.0f;
+                fac[tid][0] = rq;
+                fac[tid][1] = rk;
+                fac[tid][2] = scal[tid][2] * rq * rk;
+            }
+            __syncthreads();
         }
 
         for (int j = 0; j < m; j++) {
-            const float rq = p.qk_l2norm ? 1.0f / sqrtf(scal[j][0] + p.l2_eps) : 1.0f;
-            const float rk = p.qk_l2norm ? 1.0f / sqrtf(scal[j][1] + p.l2_eps) : 1.0f;
-            const float kq = scal[j][2] * rq * rk;
+            const float4 f4 = *reinterpret_cast<const float4*>(fac[j]);
+            const float rq = f4.x, rk = f4.y, kq = f4.z;
             // ---- p = H^T k, s = H^T q over this thread's rows ----
             float pk[4] = {0.0f, 0.0f, 0.0f, 0.0f}, pq[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            float kr[RPT], qr[RPT];
+            if constexpr (RPT % 4 == 0) {
+#pragma unroll
+                for (int mm = 0; mm < RPT; mm += 4) {
+                    const float4 k4 = *reinterpret_cast<const float4*>(&ks[j][rg * RPT + mm]);
+                    const float4 q4 = *reinterpret_cast<const float4*>(&qs[j][rg * RPT + mm]);
+                    kr[mm] = k4.x * rk, kr[mm + 1] = k4.y * rk, kr[mm + 2] = k4.z * rk, kr[mm + 3] = k4.w * rk;
+                    qr[mm] = q4.x * rq, qr[mm + 1] = q4.y * rq, qr[mm + 2] = q4.z * rq, qr[mm + 3] = q4.w * rq;
+                }
+            } else {
+#pragma unroll
+                for (int mm = 0; mm < RPT; mm++) {
+                    kr[mm] = ks[j][rg * RPT + mm] * rk;
+                    qr[mm] = qs[j][rg * RPT + mm] * rq;
+                }
+            }
 #pragma unroll
             for (int mm = 0; mm < RPT; mm++) {
-                const int i = rg + RG * mm;
-                const float kk = ks[j][i] * rk, qq = qs[j][i] * rq;
+                const float kk = kr[mm], qq = qr[mm];
                 const float h4[4] = {hv[mm][0], hv[mm][1], hv[mm][2], hv[mm][3]};
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
@@ -275,12 +303,14 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(const DecodeParams p) 
                     sqv[e] = sq;
                 }
             }
+            const float4 v4 = *reinterpret_cast<const float4*>(&vs[j][4 * cg]);
+            const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
             float dlt[4];
 #pragma unroll
             for (int e = 0; e < 4; e++) {
                 const int c = 4 * cg + e;
                 const float sk = skv[e], sq = sqv[e];
-                dlt[e] = b * fmaf(-decay, sk, vs[j][c]);
+                dlt[e] = b * fmaf(-decay, sk, vv[e]);
                 if (rg == 0) {
                     TOut* op = static_cast<TOut*>(p.o) + (tok * p.h_v + h) * DV + c;
                     Elem<TOut>::put(op, p.scale * fmaf(decay, sq, dlt[e] * kq));
@@ -292,7 +322,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(const DecodeParams p) 
 #pragma unroll
             for (int mm = 0; mm < RPT; mm++) {
                 const int i = rg + RG * mm;
-                const float kk = ks[j][i] * rk;
+                const float kk = kr[mm];
 #pragma unroll
                 for (int e = 0; e < 4; e++) hv[mm][e] = fmaf(kk, dlt[e], decay * hv[mm][e]);
                 if (ws >= 0) __builtin_nontemporal_store(hv[mm], reinterpret_cast<float4_t*>(Hw + i * DV) + cg);
