@@ -336,9 +336,10 @@ def main():
         step(e)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    call_s = float(np.mean([e[0].elapsed_time(e[3]) for e in evs])) / 1e3
-    prep_s = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) / 1e3
-    carry_s = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) / 1e3
+    call_us = [e[0].elapsed_time(e[3]) * 1e3 for e in evs]
+    prep_us = [e[0].elapsed_time(e[1]) * 1e3 for e in evs]
+    carry_us = [e[1].elapsed_time(e[2]) * 1e3 for e in evs]
+    call_s, prep_s, carry_s = (float(np.mean(x)) / 1e6 for x in (call_us, prep_us, carry_us))
     ms_step = wall * 1e3 / args.steps
     work = prefill_work([Tseq] * B, 16, 32, 128)
     print(f"[bench] prefill: {ms_step:.3f} ms/step wall, {call_s * 1e3:.3f} ms/call, "
@@ -372,6 +373,10 @@ def main():
         "kernels": {PREP_KERNEL: prep_roof, CARRY_KERNEL: carry_roof},
         "call": call_roof,
         "mfma_util": call_roof["mfma_frac"],
+        # per-call HIP event times over the timed steps (the rooflines use the means)
+        "event_stats_us": {name: {"mean": float(np.mean(x)), "median": float(np.median(x)),
+                                  "min": float(np.min(x)), "max": float(np.max(x)), "n": len(x)}
+                           for name, x in (("call", call_us), (PREP_KERNEL, prep_us), (CARRY_KERNEL, carry_us))},
     }
 
     # The same workload with bf16 outputs (o rounded once, to nearest even)
