@@ -20,7 +20,11 @@ pytestmark = pytest.mark.gpu
 BF = torch.bfloat16
 
 
-def test_prefill_graph_replays_match_eager():
+@pytest.mark.parametrize("mode", ["workspace", "noalloc", "segment_split"])
+def test_prefill_graph_replays_match_eager(mode):
+    """Captured prefill with a caller workspace, with the library's static
+    scratch (the allocation-free entry point), and with the segment split
+    (its chain map and combine kernels in the graph)."""
     geom = Geometry(2, 4, 128, 128)
     lengths = [70, 130, 3, 64]
     xs = [prefill_inputs(80 + i, lengths, geom, "bf16", initial_state_std=0.02, conv_state=True) for i in range(3)]
@@ -30,15 +34,18 @@ def test_prefill_graph_replays_match_eager():
     g, beta = dev(x.g), dev(x.beta)
     w, cs, h0 = dev(x.conv_w, BF), dev(x.conv_state_in, BF), dev(x.initial_state)
     cu = torch.from_numpy(x.cu_seqlens.astype(np.int32)).cuda()
-    prob = binding.make_problem(N, T, 2, 4, 128, 128, 1, 0)
-    ws = torch.empty(binding.gdn_prefill_workspace_bytes(prob), dtype=torch.uint8, device="cuda")
+    seg = 1 if mode == "segment_split" else 0  # one chunk per segment: every multi-chunk sequence splits
+    prob = binding.make_problem(N, T, 2, 4, 128, 128, 1, 0, segment_chunks=seg)
+    ws = None if mode == "noalloc" else torch.empty(binding.gdn_prefill_workspace_bytes(prob), dtype=torch.uint8,
+                                                     device="cuda")
     o = torch.empty((T, 4, 128), device="cuda")
     fs = torch.empty((N, 4, 128, 128), device="cuda")
     cso = torch.empty((N, geom.channels, 3), dtype=BF, device="cuda")
 
     def call(out, fso, csout):
         binding.gdn_prefill_varlen(q, k, v, g, beta, cu, conv_weight=w, conv_state=cs, initial_state=h0, out=out,
-                                   final_state_out=fso, conv_state_out=csout, workspace=ws, validate=False)
+                                   final_state_out=fso, conv_state_out=csout, workspace=ws, validate=False,
+                                   noalloc=mode == "noalloc", segment_chunks=seg)
 
     def load(xi):
         for dst, src, dt in ((q, xi.q, BF), (k, xi.k, BF), (v, xi.v, BF), (g, xi.g, torch.float32),
