@@ -868,6 +868,60 @@ __device__ __forceinline__ SFrag<E> tp_frag(const E* hi, const E* lo, int row, i
     return f;
 }
 
+// Products whose B operand comes from accumulators, in the carry's chain.
+// Within a 32-deep k-step a product may take its k indices in any order that
+// A and B share.  For bf16 operands T R, P D and the state update take, for
+// lane group g = l / 16, k = k0 + 4 g + i (i < 4) and k0 + 16 + 4 g + i - 4
+// (i >= 4): the rows an accumulator pair (rows k0 .. k0 + 15, k0 + 16 .. k0 +
+// 31) already holds in lane l, so the B operand needs no lane exchange, and
+// the A operand is read in two 8-byte halves (the update's transposed reads
+// are 8-byte reads either way): 265 -> 253 us for the carry at 4 x 4096
+// tokens.  K H and Q H keep the K-major order (acc_to_operand on the state):
+// with their 16 A fragments per k-step read in halves the carry took 411 us.
+// fp32 operands keep the K-major order throughout.
+template <typename E>
+__device__ __forceinline__ SFrag<E> acc_pair_operand(const float4_t& t0, const float4_t& t1) {
+    float x[8];
+    if constexpr (__is_same(E, F32Op)) {
+        acc_to_operand(t0, t1, x);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            x[e] = t0[e];
+            x[e + 4] = t1[e];
+        }
+    }
+    return split8<E>(x);
+}
+template <typename E>
+__device__ __forceinline__ SFrag<E> tp_frag_acc(const E* hi, const E* lo, int row, int k0, int g) {
+    if constexpr (__is_same(E, F32Op)) {
+        return tp_frag(hi, lo, row, k0 + 8 * g);
+    } else {
+        const int o0 = tp_off(row, k0 + 4 * g), o1 = tp_off(row, k0 + 16 + 4 * g);
+        SFrag<E> f;
+        f.hi = __builtin_shufflevector(*reinterpret_cast<const bf16x4_t*>(hi + o0),
+                                       *reinterpret_cast<const bf16x4_t*>(hi + o1), 0, 1, 2, 3, 4, 5, 6, 7);
+        f.lo = __builtin_shufflevector(*reinterpret_cast<const bf16x4_t*>(lo + o0),
+                                       *reinterpret_cast<const bf16x4_t*>(lo + o1), 0, 1, 2, 3, 4, 5, 6, 7);
+        return f;
+    }
+}
+// K^T operand (transposed LDS read) in that k order
+template <typename E>
+__device__ __forceinline__ SFrag<E> lds_sfrag_tr_acc(const E* hi, const E* lo, int pitch, int k0, int g, int col0) {
+    if constexpr (__is_same(E, F32Op)) {
+        return lds_sfrag_tr(hi, lo, pitch, k0 + 8 * g, col0);
+    } else {
+        const int j = threadIdx.x & 15;
+        const int off = (k0 + 4 * g + (j >> 2)) * pitch + col0 + 4 * (j & 3);
+        SFrag<E> f;
+        f.hi = __builtin_shufflevector(lds_tr16(hi + off), lds_tr16(hi + off + 16 * pitch), 0, 1, 2, 3, 4, 5, 6, 7);
+        f.lo = __builtin_shufflevector(lds_tr16(lo + off), lds_tr16(lo + off + 16 * pitch), 0, 1, 2, 3, 4, 5, 6, 7);
+        return f;
+    }
+}
+
 // Byte offset, in the V region, of piece p (0..3: D k-step 0 hi, lo, k-step 1
 // hi, lo) of lane l of column block w: row 16 p + l % 16, 16 bytes at 16 (l/16)
 // within bytes [64 w, 64 w + 64) of the row, which hold exactly V's columns
@@ -1041,24 +1095,20 @@ __global__ void __launch_bounds__(kCarryThreads, 1) carry_kernel(const PrefillPa
                 SFrag<E> rb[2];
 #pragma unroll
                 for (int s = 0; s < 2; s++) {
-                    float x[8];
-                    acc_to_operand(rr[2 * s], rr[2 * s + 1], x);
-                    rb[s] = split8<E>(x);
+                    rb[s] = acc_pair_operand<E>(rr[2 * s], rr[2 * s + 1]);
                 }
 #pragma unroll
                 for (int tb = 0; tb < 4; tb++) {
                     dd[tb] = kZero4;
 #pragma unroll
-                    for (int ks = 0; ks <= tb / 2; ks++) mma3(dd[tb], tp_frag(Thi, Tlo, 16 * tb + lr, 32 * ks + 8 * lg), rb[ks]);
+                    for (int ks = 0; ks <= tb / 2; ks++) mma3(dd[tb], tp_frag_acc(Thi, Tlo, 16 * tb + lr, 32 * ks, lg), rb[ks]);
                 }
             }
             // D's operand overwrites this wave's own V columns, which only this
             // wave has read (R above, on which D depends).
 #pragma unroll
             for (int s = 0; s < 2; s++) {
-                float x[8];
-                acc_to_operand(dd[2 * s], dd[2 * s + 1], x);
-                const SFrag<E> f = split8<E>(x);
+                const SFrag<E> f = acc_pair_operand<E>(dd[2 * s], dd[2 * s + 1]);
                 *reinterpret_cast<V8*>(dop + dop_offset<PV>(cw, 2 * s, lane)) = f.hi;
                 *reinterpret_cast<V8*>(dop + dop_offset<PV>(cw, 2 * s + 1, lane)) = f.lo;
             }
@@ -1077,16 +1127,14 @@ __global__ void __launch_bounds__(kCarryThreads, 1) carry_kernel(const PrefillPa
                         a0[e] = dl[r0] * dd[2 * s][e];
                         a1[e] = dl[r1] * dd[2 * s + 1][e];
                     }
-                    float x[8];
-                    acc_to_operand(a0, a1, x);
-                    ab[s] = split8<E>(x);
+                    ab[s] = acc_pair_operand<E>(a0, a1);
                 }
                 const float decay = scal[3 * kChunk];
 #pragma unroll
                 for (int it = 0; it < KT; it++) {
                     hacc[it] *= decay;
 #pragma unroll
-                    for (int s = 0; s < 2; s++) mma3(hacc[it], lds_sfrag_tr(Khi, Klo, PK, 32 * s + 8 * lg, 16 * it), ab[s]);
+                    for (int s = 0; s < 2; s++) mma3(hacc[it], lds_sfrag_tr_acc(Khi, Klo, PK, 32 * s, lg, 16 * it), ab[s]);
                 }
             }
             lds_barrier();
@@ -1271,7 +1319,7 @@ __global__ void __launch_bounds__(kCarryThreads, 1) carry_kernel(const PrefillPa
                 for (int tb = 0; tb < 4; tb++) {
                     float4_t pd = kZero4;
 #pragma unroll
-                    for (int ks = 0; ks <= tb / 2; ks++) mma3(pd, tp_frag(Phi, Plo, 16 * tb + lr, 32 * ks + 8 * lg), db[ks]);
+                    for (int ks = 0; ks <= tb / 2; ks++) mma3(pd, tp_frag_acc(Phi, Plo, 16 * tb + lr, 32 * ks, lg), db[ks]);
                     float val[4];
 #pragma unroll
                     for (int e = 0; e < 4; e++) val[e] = p.scale * (eqh[tb][e] + pd[e]);
