@@ -35,6 +35,14 @@
 //                     the output.  The next chunk's images are loaded into
 //                     registers while the current chunk computes.  At the
 //                     end its helper waves write the final conv states.
+// With the segment split (gdn_problem.segment_chunks > 0) a sequence longer
+// than that many chunks is cut into segments carried in parallel:
+//   chain_map_kernel, chain_order_kernel  the segments ("chains"), longest first
+//   carry_kernel<..., true>   each segment from zero state, beside its identity
+//                     chains (the d_k identity columns, v = 0), which give its
+//                     transition M and the outputs' dependence Y on its start state
+//   segment_combine_kernel    start states H_{s+1} = M_s H_s + F_s in order
+//   segment_correct_kernel    o += Y H_s, on the matrix cores
 //
 // Precision: every product runs on the matrix cores with fp32 accumulation:
 // split bf16 operands (x = hi + lo, three bf16 steps, about 16 significant
@@ -818,13 +826,15 @@ template <> __device__ __forceinline__ void buf_put<float>(__amdgpu_buffer_rsrc_
 // holding it too would exceed its 256 registers).  Per chunk, three
 // workgroup barriers:
 //   stage:  all waves write the chunk to LDS; main also splits the state
-//           operand and hands it to the helpers through LDS.
+//           operand and hands it to the helpers through LDS; the helpers
+//           convolve half of the chunk's v rows.
 //   B:      main: K H, R, D = T R; D's split operand goes to LDS (over this
-//           wave's own columns of V, which only it reads).  helpers: Q H.
-//   C:      main: the state update.  helpers: P D and the output rows, then
-//           conv + SiLU of half of the next chunk's v rows (the other half
-//           while staging).
-// Each role issues its part of the next chunk's loads as phase B starts.
+//           wave's own columns of V, which only it reads).  helpers: Q H,
+//           then conv + SiLU of the other half of the next chunk's v rows.
+//   C:      main: the state update.  helpers: P D and the output rows.
+// The helpers issue their part of the next chunk's loads as phase B starts;
+// the main waves request the next K|Q image in two halves during phase B
+// (after K H, and after D's operand is written).
 // The two roles run separate loops with the same barriers, so their register
 // live ranges do not overlap.
 constexpr int kCarryThreads = 512;
