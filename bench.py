@@ -461,13 +461,16 @@ def main():
             d = multi_decode_inputs(3, c, N, m, geom, "bf16")
             mins.append(tuple(torch.from_numpy(a).to(dev, dt) for a, dt in
                               ((d.q, bf), (d.k, bf), (d.v, bf), (d.g, torch.float32), (d.beta, torch.float32))))
-        om = torch.empty((N, m, 32, 128), dtype=torch.float32, device=dev)
+        oms = {torch.float32: torch.empty((N, m, 32, 128), dtype=torch.float32, device=dev),
+               torch.bfloat16: torch.empty((N, m, 32, 128), dtype=bf, device=dev)}
         start = torch.from_numpy(state_pool(3, N, geom)).to(dev)
         cstart = torch.from_numpy(conv_state_pool(3, N, geom, "bf16")).to(dev, bf)
         idx = torch.arange(N * m, dtype=torch.int32, device=dev).reshape(N, m)
         mres = {"workload": f"{m} tokens per slot, 256 slots x 32 value heads (16 key heads), d=128, bf16 "
                             "q/k/v, conv4+SiLU+L2, fp32 state", "tokens_per_slot": m}
-        for kept, name in ((m, "all_token_states_kept"), (1, "final_state_in_place")):
+        for kept, name, odt in ((m, "all_token_states_kept", torch.float32),
+                                (1, "final_state_in_place", torch.float32),
+                                (1, "final_state_in_place_bf16_out", bf)):
             P = N * m if kept == m else N
             mpools = [torch.zeros((P, 32, 128, 128), dtype=torch.float32, device=dev) for _ in range(NSET)]
             mcpools = [torch.zeros((P, geom.channels, 3), dtype=bf, device=dev) for _ in range(NSET)]
@@ -476,9 +479,9 @@ def main():
                 mc[idx[:, 0].long() if kept == m else slice(None)] = cstart
 
             def mstep(c):
-                gdn.gdn_decode_multi(*mins[c % len(mins)], mpools[c % NSET], out=om, conv_weight=cw,
+                gdn.gdn_decode_multi(*mins[c % len(mins)], mpools[c % NSET], out=oms[odt], conv_weight=cw,
                                      conv_state_pool=mcpools[c % NSET], state_indices=idx if kept == m else None,
-                                     validate=False)
+                                     validate=False, out_dtype=odt)
 
             for c in range(8):
                 mstep(c)
@@ -490,10 +493,11 @@ def main():
             e1.record(stream)
             torch.cuda.synchronize()
             us = e0.elapsed_time(e1) * 1e3 / calls
-            mb = decode_multi_algorithmic(N, m, 16, 32, 128, kept)
+            mb = decode_multi_algorithmic(N, m, 16, 32, 128, kept, out_bytes=2 if odt == bf else 4)
             mres[name] = {"us_per_call": us, "tokens_per_s": N * m / (us * 1e-6),
                           "roofline": roofline(mb, N * m * 32 * 7.0 * 128 * 128, us * 1e-6, DECODE_KERNEL)}
-            mres[name]["roofline"]["traffic"] = measured_traffic(
+            # counters were taken on the fp32-output instances only
+            mres[name]["roofline"]["traffic"] = None if odt == bf else measured_traffic(
                 "decode_kernel_m4_all_states" if kept == m else "decode_kernel_m4_final_state")
             print(f"[bench] decode x{m} ({name}): {us:.1f} us/call, {mb / (us * 1e-6) / 1e9:.0f} GB/s",
                   file=sys.stderr, flush=True)

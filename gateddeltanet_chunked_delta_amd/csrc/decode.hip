@@ -88,10 +88,21 @@ __device__ __forceinline__ void conv_tokens(const TIn* __restrict__ cw, const TI
     }
 }
 
+// Minimum waves per SIMD asked of the compiler.  Two workgroups per CU (four
+// waves per SIMD) need at most 128 registers; the d = 128 m-token kernel with
+// bf16 inputs and outputs takes 129 unbounded and ran one workgroup per CU
+// (4-token final-state call 370 -> 273 us with the bound, 4 registers
+// spilled).  The others are left free: with fp32 outputs it fits in 127
+// unbounded and ran 257 -> 266 us when bounded.
+template <int DK, int DV, int KMAX, typename TIn, typename TOut>
+constexpr int decode_min_waves() {
+    return (DK == 128 && DV == 128 && KMAX > 1 && sizeof(TIn) == 2 && sizeof(TOut) == 2) ? 4 : 1;
+}
+
 // KMAX: most tokens per slot the shared buffers hold (1 for the single-token
 // step, so that its LDS footprint stays minimal).
 template <int DK, int DV, int KMAX, typename TIn, typename TOut>
-__global__ void __launch_bounds__(kThreads) decode_kernel(const DecodeParams p) {
+__global__ void __launch_bounds__(kThreads, (decode_min_waves<DK, DV, KMAX, TIn, TOut>())) decode_kernel(const DecodeParams p) {
     constexpr int CG = DV / 4;           // float4 column groups per row
     constexpr int RG = kThreads / CG;    // row groups
     constexpr int RPT = DK / RG;         // rows per thread

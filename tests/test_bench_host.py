@@ -65,6 +65,12 @@ def test_multi_decode_bytes_count_kept_states():
     assert four - one == 3 * state + 3 * 256 * C * 3 * 2
 
 
+def test_multi_decode_bf16_output_bytes():
+    f32 = bench.decode_multi_algorithmic(256, 4, 16, 32, 128, kept=1)
+    b16 = bench.decode_multi_algorithmic(256, 4, 16, 32, 128, kept=1, out_bytes=2)
+    assert f32 - b16 == 256 * 4 * 32 * 128 * 2
+
+
 def test_roofline_takes_the_binding_roof():
     # HBM-bound work: 8 GB in 2 ms -> 4 TB/s = half of the 8 TB/s peak
     r = bench.roofline(8e9, 1e12, 2e-3, "k")
