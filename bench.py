@@ -91,25 +91,28 @@ def prefill_work(lengths, h_k, h_v, d, in_bytes=2, out_bytes=4, initial_states=F
     return {"prep": (prep_b, total_f - carry_f), "carry": (carry_b, carry_f), "call": (prep_b + carry_b, total_f)}
 
 
-def decode_algorithmic(N, h_k, h_v, d, in_bytes=2, out_bytes=4, conv=True):
+def decode_algorithmic(N, h_k, h_v, d, in_bytes=2, out_bytes=4, conv=True, d_v=None):
     """State read + write, q/k/v/g/beta read, o written, and with the conv
     prologue the conv history read + written and the conv weights read;
-    ~ 7 d^2 flops per (slot, head)."""
-    state = N * h_v * d * d * 4
-    C = 2 * h_k * d + h_v * d
-    bytes_ = 2 * state + N * C * in_bytes + N * h_v * 2 * 4 + N * h_v * d * out_bytes
+    ~ 7 d_k d_v flops per (slot, head).  d is d_k; d_v defaults to it."""
+    dv = d if d_v is None else d_v
+    state = N * h_v * d * dv * 4
+    C = 2 * h_k * d + h_v * dv
+    bytes_ = 2 * state + N * C * in_bytes + N * h_v * 2 * 4 + N * h_v * dv * out_bytes
     if conv:
         bytes_ += 2 * N * C * 3 * in_bytes + C * 4 * in_bytes
-    return bytes_, N * h_v * 7.0 * d * d
+    return bytes_, N * h_v * 7.0 * d * dv
 
 
-def decode_multi_algorithmic(N, m, h_k, h_v, d, kept, in_bytes=2, out_bytes=4):
+def decode_multi_algorithmic(N, m, h_k, h_v, d, kept, in_bytes=2, out_bytes=4, d_v=None):
     """m tokens per slot: the state read once and written `kept` times (once
     per kept token state), per-token q/k/v/g/beta read and o written, the
-    conv history read once and written `kept` times, conv weights read."""
-    state = N * h_v * d * d * 4
-    C = 2 * h_k * d + h_v * d
-    return (state * (1 + kept) + N * m * (C * in_bytes + h_v * 2 * 4 + h_v * d * out_bytes)
+    conv history read once and written `kept` times, conv weights read.  d is
+    d_k; d_v defaults to it."""
+    dv = d if d_v is None else d_v
+    state = N * h_v * d * dv * 4
+    C = 2 * h_k * d + h_v * dv
+    return (state * (1 + kept) + N * m * (C * in_bytes + h_v * 2 * 4 + h_v * dv * out_bytes)
             + N * C * 3 * in_bytes * (1 + kept) + C * 4 * in_bytes)
 
 
@@ -504,6 +507,54 @@ def main():
             del mpools, mcpools
         result["decode_multi"] = mres
 
+        # The other head dims: one step and a 4-token final-state call each
+        # (256 slots, 16 key / 32 value heads, bf16 q/k/v, conv, fp32 o, two
+        # pools in rotation)
+        hres = {}
+        for dk, dv in ((128, 64), (64, 128), (64, 64)):
+            gm = Geometry(16, 32, dk, dv)
+            hpools = [torch.from_numpy(state_pool(3, N, gm)).to(dev)]
+            hpools.append(hpools[0].clone())
+            hcpools = [torch.from_numpy(conv_state_pool(3, N, gm, "bf16")).to(dev, bf) for _ in range(2)]
+            hcw = torch.from_numpy(conv_weights(3, gm, "bf16")).to(dev, bf)
+            leg = {}
+            for mm in (1, 4):
+                hins = []
+                for c in range(4):
+                    d = decode_inputs(3, c, N, gm, "bf16") if mm == 1 else multi_decode_inputs(3, c, N, mm, gm, "bf16")
+                    hins.append(tuple(torch.from_numpy(a).to(dev, dt) for a, dt in
+                                      ((d.q, bf), (d.k, bf), (d.v, bf), (d.g, torch.float32), (d.beta, torch.float32))))
+                ho = torch.empty(((N, 32, dv) if mm == 1 else (N, mm, 32, dv)), dtype=torch.float32, device=dev)
+                call = gdn.gdn_decode_step if mm == 1 else gdn.gdn_decode_multi
+
+                def hstep(c):
+                    call(*hins[c % 4], hpools[c % 2], out=ho, conv_weight=hcw, conv_state_pool=hcpools[c % 2],
+                         validate=False)
+
+                for c in range(8):
+                    hstep(c)
+                torch.cuda.synchronize()
+                calls = 40
+                e0.record(stream)
+                for c in range(calls):
+                    hstep(c)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) * 1e3 / calls
+                if mm == 1:
+                    hb, hf = decode_algorithmic(N, 16, 32, dk, d_v=dv)
+                else:
+                    hb = decode_multi_algorithmic(N, mm, 16, 32, dk, 1, d_v=dv)
+                    hf = N * mm * 32 * 7.0 * dk * dv
+                leg["step" if mm == 1 else f"x{mm}_final_state"] = {
+                    "us_per_call": us, "roofline": roofline(hb, hf, us * 1e-6, DECODE_KERNEL)}
+                leg["step" if mm == 1 else f"x{mm}_final_state"]["roofline"]["traffic"] = None
+                print(f"[bench] decode d_k={dk} d_v={dv} m={mm}: {us:.1f} us/call, "
+                      f"{hb / (us * 1e-6) / 1e9:.0f} GB/s", file=sys.stderr, flush=True)
+            hres[f"dk{dk}_dv{dv}"] = leg
+            del hpools, hcpools
+        result["decode_head_dims"] = hres
+
     if not args.no_extra_configs:
         extra = {}
         lens = uniform_lengths(2, 60, 1, 8192)
@@ -539,6 +590,7 @@ def main():
                   result["prefill_bf16_out"]["roofline"]] + \
                 ([result["decode"]["roofline"]] if "decode" in result else []) + \
                 [leg["roofline"] for leg in result.get("decode_multi", {}).values() if isinstance(leg, dict)] + \
+                [c["roofline"] for leg in result.get("decode_head_dims", {}).values() for c in leg.values()] + \
                 [leg[key] for leg in result.get("other_prefill_configs", {}).values()
                  for key in ("roofline", "carry_roofline")]:
             if r["bound"] == "hbm":

@@ -107,6 +107,7 @@ __global__ void __launch_bounds__(kThreads, (decode_min_waves<DK, DV, KMAX, TIn,
     constexpr int RG = kThreads / CG;    // row groups
     constexpr int RPT = DK / RG;         // rows per thread
     static_assert(kThreads % CG == 0 && DK % RG == 0 && 64 % CG == 0, "decode tiling");
+    static_assert(CG == 32 || CG == 16, "column sums by half- or quarter-waves (d_v = 128 or 64)");
     static_assert(2 * DK <= kThreads - KMAX && DV <= kThreads - KMAX, "one channel per thread, gate threads apart");
 
     // q and k of each token with channel c at (c % RG) RPT + c / RG: a thread's
@@ -279,8 +280,9 @@ __global__ void __launch_bounds__(kThreads, (decode_min_waves<DK, DV, KMAX, TIn,
             const int64_t tok = row0 + j;
             const float decay = gate[j][0], b = gate[j][1];
             // The waves' partials of this lane's 4 columns, summed in wave
-            // order.  With 32 column groups the two half-waves hold the same
-            // columns: the lower half sums p, the upper s, and they swap.
+            // order (d_v = 64: waves 0-3 and 4-7 summed apart, then added).
+            // With 32 column groups the two half-waves hold the same columns:
+            // the lower half sums p, the upper s, and they swap.
             float skv[4], sqv[4];
             if constexpr (CG == 32) {
                 const int qn = lane >> 5;
@@ -300,18 +302,30 @@ __global__ void __launch_bounds__(kThreads, (decode_min_waves<DK, DV, KMAX, TIn,
                     skv[e] = qn ? o : a[e];
                     sqv[e] = qn ? a[e] : o;
                 }
-            } else {
+            } else if constexpr (CG == 16) {
+                // Four quarter-waves over the same columns: quarter qn sums
+                // quantity qn & 1 (p, s) over waves 4 (qn >> 1) .. 4 (qn >> 1) + 3;
+                // the two wave halves are added across lanes l, l ^ 32 (the
+                // first half's sum first), then p and s swap across l, l ^ 16.
+                const int qn = lane >> 4, which = qn & 1, wlo = 4 * (qn >> 1);
+                float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int w = 0; w < 4; w++) {
+                    const float4 v4 = *reinterpret_cast<const float4*>(&pt[wlo + w][which][4 * cg]);
+                    a[0] += v4.x;
+                    a[1] += v4.y;
+                    a[2] += v4.z;
+                    a[3] += v4.w;
+                }
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
-                    const int c = 4 * cg + e;
-                    float sk = 0.0f, sq = 0.0f;
-#pragma unroll
-                    for (int w = 0; w < kWaves; w++) {
-                        sk += pt[w][0][c];
-                        sq += pt[w][1][c];
-                    }
-                    skv[e] = sk;
-                    sqv[e] = sq;
+                    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(a[e]), __float_as_uint(a[e]), false, false);
+                    const float o = __uint_as_float((qn >> 1) ? sw[0] : sw[1]);
+                    const float t = (qn >> 1) ? o + a[e] : a[e] + o;
+                    const auto sw2 = __builtin_amdgcn_permlane16_swap(__float_as_uint(t), __float_as_uint(t), false, false);
+                    const float o2 = __uint_as_float(which ? sw2[0] : sw2[1]);
+                    skv[e] = which ? o2 : t;
+                    sqv[e] = which ? t : o2;
                 }
             }
             const float4 v4 = *reinterpret_cast<const float4*>(&vs[j][4 * cg]);

@@ -57,6 +57,19 @@ def test_decode_step_bytes():
     assert f == 256 * 32 * 7.0 * 128 * 128
 
 
+def test_decode_bytes_with_unequal_head_dims():
+    b, f = bench.decode_algorithmic(256, 16, 32, 128, d_v=64)
+    state = 256 * 32 * 128 * 64 * 4
+    C = 2 * 16 * 128 + 32 * 64
+    assert b == 2 * state + 256 * C * 2 + 256 * 32 * 8 + 256 * 32 * 64 * 4 + 2 * 256 * C * 3 * 2 + C * 4 * 2
+    assert f == 256 * 32 * 7.0 * 128 * 64
+    # d_v defaults to d_k
+    assert bench.decode_algorithmic(8, 2, 4, 64) == bench.decode_algorithmic(8, 2, 4, 64, d_v=64)
+    one = bench.decode_multi_algorithmic(256, 4, 16, 32, 64, kept=1, d_v=128)
+    assert one == (256 * 32 * 64 * 128 * 4 * 2 + 256 * 4 * ((2 * 16 * 64 + 32 * 128) * 2 + 32 * 8 + 32 * 128 * 4)
+                   + 256 * (2 * 16 * 64 + 32 * 128) * 3 * 2 * 2 + (2 * 16 * 64 + 32 * 128) * 4 * 2)
+
+
 def test_multi_decode_bytes_count_kept_states():
     one = bench.decode_multi_algorithmic(256, 4, 16, 32, 128, kept=1)
     four = bench.decode_multi_algorithmic(256, 4, 16, 32, 128, kept=4)
