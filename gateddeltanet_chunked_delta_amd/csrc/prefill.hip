@@ -1375,8 +1375,11 @@ __global__ void __launch_bounds__(kCarryThreads, 1) carry_kernel(const PrefillPa
         // written without one).  Every history read of these channels came
         // before (q and k: the chunk-local kernel; v: this workgroup's first
         // chunk), and one thread reads a channel's three values before writing
-        // them, so the output may be the history buffer itself.
-        if (p.conv_state_out && conv && slot >= 0 && !ident && segi == nseg - 1) {
+        // them, so the output may be the history buffer itself.  With the
+        // segment split the first segment's chain writes it: it is the one
+        // that reads the v history, and a later segment running beside it
+        // could otherwise overwrite that history before it is read.
+        if (p.conv_state_out && conv && slot >= 0 && !ident && segi == 0) {
             const int64_t len = eos - bos;
             const TIn* csi = (p.conv_state_in && has_init) ? static_cast<const TIn*>(p.conv_state_in) : nullptr;
             TIn* cso = static_cast<TIn*>(p.conv_state_out);
@@ -1413,33 +1416,36 @@ __global__ void __launch_bounds__(kCarryThreads, 1) carry_kernel(const PrefillPa
 
 // ---------------------------------------------------------------- segment split: combine and correct
 
-// Step 2 of the segment split, per (split sequence, value head, 64 columns
+// Step 2 of the segment split, per (split sequence, value head, 16 columns
 // of d_v): the segments' start states in order.  H_1 = the first segment's
 // final state; H_{s+1} = M_s H_s + F_s, with M_s the segment's transition
 // (seg_trans) and F_s its final state from a zero start (seg_state).  H_s
 // replaces F_s in seg_state (the correction reads it) and the last H is the
 // sequence's final state.  fp32; each element's products are summed over d_k
-// in order, all of a thread's rows at once (independent accumulators).
+// in order, all of a thread's rows at once (independent accumulators).  16
+// columns per workgroup (64 measured 22.6 us at one 32768-token sequence:
+// too few workgroups for the chip).
+constexpr int kCombineCols = 16;
 template <int DK, int DV>
 __global__ void __launch_bounds__(256) segment_combine_kernel(const PrefillParams p) {
-    constexpr int NS = DV / kDvs, RPT = DK / 4;
+    constexpr int CC = kCombineCols, NS = DV / CC, RGN = 256 / CC, RPT = DK / RGN;
     __shared__ __attribute__((aligned(16))) float Ms[DK][DK + 4];
-    __shared__ float Hs[DK][kDvs];
+    __shared__ float Hs[DK][CC];
     const int b = int(blockIdx.x);
     const int slice = b % NS, h = (b / NS) % p.h_v, n = b / (NS * p.h_v);
     const int c0 = p.chain_base[n], nseg = p.chain_base[n + 1] - c0;
     if (nseg <= 1) return;
-    const int t = threadIdx.x, cc = t & 63, rg = t >> 6;  // column; rows rg + 4 r
+    const int t = threadIdx.x, cc = t % CC, rg = t / CC;  // column; rows rg + RGN r
     float H[RPT];
-    const int64_t colofs = int64_t(slice) * kDvs + cc;
+    const int64_t colofs = int64_t(slice) * CC + cc;
     const float* f0 = p.seg_state + (int64_t(c0) * p.h_v + h) * DK * DV + colofs;
 #pragma unroll
-    for (int r = 0; r < RPT; r++) H[r] = f0[int64_t(rg + 4 * r) * DV];
+    for (int r = 0; r < RPT; r++) H[r] = f0[int64_t(rg + RGN * r) * DV];
     for (int sg = 1; sg < nseg; sg++) {
         const int64_t c = c0 + sg;
         __syncthreads();  // the previous segment's reads of Ms and Hs are done
 #pragma unroll
-        for (int r = 0; r < RPT; r++) Hs[rg + 4 * r][cc] = H[r];
+        for (int r = 0; r < RPT; r++) Hs[rg + RGN * r][cc] = H[r];
         const float4* m = reinterpret_cast<const float4*>(p.seg_trans + (c * p.h_v + h) * DK * DK);
         for (int i = t; i < DK * DK / 4; i += 256)
             *reinterpret_cast<float4*>(&Ms[i / (DK / 4)][4 * (i % (DK / 4))]) = m[i];
@@ -1452,7 +1458,7 @@ __global__ void __launch_bounds__(256) segment_combine_kernel(const PrefillParam
             const float h0 = Hs[k][cc], h1 = Hs[k + 1][cc], h2 = Hs[k + 2][cc], h3 = Hs[k + 3][cc];
 #pragma unroll
             for (int r = 0; r < RPT; r++) {
-                const float4 mv = *reinterpret_cast<const float4*>(&Ms[rg + 4 * r][k]);
+                const float4 mv = *reinterpret_cast<const float4*>(&Ms[rg + RGN * r][k]);
                 acc[r] = fmaf(mv.x, h0, acc[r]);
                 acc[r] = fmaf(mv.y, h1, acc[r]);
                 acc[r] = fmaf(mv.z, h2, acc[r]);
@@ -1461,8 +1467,8 @@ __global__ void __launch_bounds__(256) segment_combine_kernel(const PrefillParam
         }
 #pragma unroll
         for (int r = 0; r < RPT; r++) {
-            const float f = fs[int64_t(rg + 4 * r) * DV];
-            fs[int64_t(rg + 4 * r) * DV] = H[r];  // start state of segment sg
+            const float f = fs[int64_t(rg + RGN * r) * DV];
+            fs[int64_t(rg + RGN * r) * DV] = H[r];  // start state of segment sg
             H[r] = acc[r] + f;
         }
     }
@@ -1470,7 +1476,7 @@ __global__ void __launch_bounds__(256) segment_combine_kernel(const PrefillParam
     if (p.final_state && slot >= 0) {
         float* fin = p.final_state + (int64_t(slot) * p.h_v + h) * DK * DV + colofs;
 #pragma unroll
-        for (int r = 0; r < RPT; r++) fin[int64_t(rg + 4 * r) * DV] = H[r];
+        for (int r = 0; r < RPT; r++) fin[int64_t(rg + RGN * r) * DV] = H[r];
     }
 }
 
@@ -1482,9 +1488,9 @@ __global__ void __launch_bounds__(256) segment_combine_kernel(const PrefillParam
 // chain's own products (split bf16 or fp32): wave w takes rows 16 w .. 16 w
 // + 15 of the chunk across all of d_v, so Y is read once; H_s waits in LDS
 // as ready operand fragments, staged again only when the segment changes.
-// Each chunk's loads are all issued before its stores: the vector memory
-// counter retires loads and stores in order, so a load issued behind stores
-// could only be used once they completed.
+// Each chunk's loads are issued during the previous chunk's products, before
+// its stores: the vector memory counter retires loads and stores in order, so
+// a load issued behind stores could only be used once they completed.
 constexpr int kCorrectChunks = 8;
 template <int DK, int DV, typename TIn, typename TOut>
 __global__ void __launch_bounds__(256) segment_correct_kernel(const PrefillParams p) {
@@ -1498,22 +1504,66 @@ __global__ void __launch_bounds__(256) segment_correct_kernel(const PrefillParam
     const int64_t nslots = p.chunk_base[p.num_seqs];
     const int t = threadIdx.x, w = t >> 6, lane = t & 63, lr = lane & 15, lg = lane >> 4;
     const int64_t ystride = int64_t(p.h_v) * DK, ostride = int64_t(p.h_v) * DV;
+    // The next chunk of this group that needs the correction (its first
+    // token, chain and rows; c0 < 0 when none is left), found by scalar loads
+    // ahead of time, so that its rows can be requested while the previous
+    // chunk's products run.
+    struct Item { int64_t c0, chain; int L; };
+    auto next_item = [&](int& i) {
+        for (; i < kCorrectChunks; i++) {
+            const int64_t cs = g0 + i;
+            if (cs >= nslots) break;
+            const int4 d = reinterpret_cast<const int4*>(p.slot_desc)[cs];  // sequence, first token, length, start
+            const int cbn = p.chain_base[d.x], nseg = p.chain_base[d.x + 1] - cbn;
+            if (nseg <= 1) continue;
+            const int ls = reinterpret_cast<const int4*>(p.chain_desc)[cbn].z;  // chunks per segment (the first is full)
+            const int sg = int((int64_t(d.y) - d.w) / kChunk) / ls;
+            if (sg == 0) continue;
+            i++;
+            return Item{int64_t(d.y), int64_t(cbn) + sg, d.z};
+        }
+        i = kCorrectChunks;
+        return Item{-1, -1, 0};
+    };
+    // loads of one chunk: this wave's 16 rows of Y (row 16 w + lr, 8
+    // consecutive k per k-step) and of O_loc (rows 16 w + 4 lg + e, column
+    // 16 tile + lr)
+    const int arow = 16 * w + lr;
+    auto load = [&](const Item& it, float4 (&yv)[KS][2], float (&res)[NTT][4]) {
+        const float* __restrict__ y = p.seg_y + (it.c0 * p.h_v + h) * DK;
+        const float* __restrict__ ol = p.seg_oloc + (it.c0 * p.h_v + h) * DV;
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++)
+#pragma unroll
+            for (int hh = 0; hh < 2; hh++)
+                yv[ks][hh] = arow < it.L ? *reinterpret_cast<const float4*>(y + arow * ystride + 32 * ks + 8 * lg + 4 * hh)
+                                         : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+        for (int tile = 0; tile < NTT; tile++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int r = 16 * w + 4 * lg + e;
+                res[tile][e] = r < it.L ? ol[r * ostride + 16 * tile + lr] : 0.0f;
+            }
+    };
+    float4 yv[KS][2], yn[KS][2];
+    float res[NTT][4], rn[NTT][4];
+    int pos = 0;
+    Item nx = next_item(pos);
+    if (nx.c0 >= 0) load(nx, yn, rn);
     int64_t cur = -1;  // the chain whose start state hbs holds
-    for (int i = 0; i < kCorrectChunks; i++) {
-        const int64_t cs = g0 + i;
-        if (cs >= nslots) break;
-        const int4 d = reinterpret_cast<const int4*>(p.slot_desc)[cs];  // sequence, first token, length, start
-        const int n = d.x, L = d.z;
-        const int64_t c0 = d.y, bos = d.w;
-        const int cbn = p.chain_base[n], nseg = p.chain_base[n + 1] - cbn;
-        if (nseg <= 1) continue;
-        const int ls = reinterpret_cast<const int4*>(p.chain_desc)[cbn].z;  // chunks per segment (the first is full)
-        const int sg = int((c0 - bos) / kChunk) / ls;
-        if (sg == 0) continue;
-        const int64_t chain = cbn + sg;
-        if (chain != cur) {  // uniform over the workgroup
+    while (nx.c0 >= 0) {
+        const Item it = nx;
+        nx = next_item(pos);
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++) yv[ks][0] = yn[ks][0], yv[ks][1] = yn[ks][1];
+#pragma unroll
+        for (int tile = 0; tile < NTT; tile++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) res[tile][e] = rn[tile][e];
+        if (it.chain != cur) {  // uniform over the workgroup
             __syncthreads();
-            const float* src = p.seg_state + (chain * p.h_v + h) * DK * DV;
+            const float* src = p.seg_state + (it.chain * p.h_v + h) * DK * DV;
             for (int f = t; f < KS * NTT * 64; f += 256) {
                 const int ks = f / (NTT * 64), tile = (f / 64) % NTT, l = f % 64;
                 float x[8];
@@ -1524,28 +1574,10 @@ __global__ void __launch_bounds__(256) segment_correct_kernel(const PrefillParam
                 *reinterpret_cast<V8*>(hbs + (((ks * NTT + tile) * 2 + 1) * 64 + l) * 16) = fr.lo;
             }
             __syncthreads();
-            cur = chain;
+            cur = it.chain;
         }
-        // loads: this wave's 16 rows of Y (row 16 w + lr, 8 consecutive k per
-        // k-step) and of O_loc (rows 16 w + 4 lg + e, column 16 tile + lr)
-        const float* __restrict__ y = p.seg_y + (c0 * p.h_v + h) * DK;
-        const float* __restrict__ ol = p.seg_oloc + (c0 * p.h_v + h) * DV;
-        const int arow = 16 * w + lr;
-        float4 yv[KS][2];
-#pragma unroll
-        for (int ks = 0; ks < KS; ks++)
-#pragma unroll
-            for (int hh = 0; hh < 2; hh++)
-                yv[ks][hh] = arow < L ? *reinterpret_cast<const float4*>(y + arow * ystride + 32 * ks + 8 * lg + 4 * hh)
-                                      : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        float res[NTT][4];
-#pragma unroll
-        for (int tile = 0; tile < NTT; tile++)
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const int r = 16 * w + 4 * lg + e;
-                res[tile][e] = r < L ? ol[r * ostride + 16 * tile + lr] : 0.0f;
-            }
+        // the next chunk's rows, requested before this chunk's stores
+        if (nx.c0 >= 0) load(nx, yn, rn);
         SFrag<E> a[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ks++) {
@@ -1566,13 +1598,13 @@ __global__ void __launch_bounds__(256) segment_correct_kernel(const PrefillParam
 #pragma unroll
             for (int e = 0; e < 4; e++) res[tile][e] += acc[e];
         }
-        TOut* __restrict__ out = static_cast<TOut*>(p.o) + (c0 * p.h_v + h) * DV;
+        TOut* __restrict__ out = static_cast<TOut*>(p.o) + (it.c0 * p.h_v + h) * DV;
 #pragma unroll
         for (int tile = 0; tile < NTT; tile++)
 #pragma unroll
             for (int e = 0; e < 4; e++) {
                 const int r = 16 * w + 4 * lg + e;
-                if (r < L) Elem<TOut>::put(out + r * ostride + 16 * tile + lr, res[tile][e]);
+                if (r < it.L) Elem<TOut>::put(out + r * ostride + 16 * tile + lr, res[tile][e]);
             }
     }
 }
@@ -1601,7 +1633,7 @@ hipError_t run(const PrefillParams& p, hipStream_t stream, void* const* events) 
     if (err != hipSuccess) return err;
     if constexpr (CH) {
         segment_combine_kernel<DK, DV>
-            <<<dim3(unsigned(int64_t(p.num_seqs) * p.h_v * (DV / kDvs))), dim3(256), 0, stream>>>(p);
+            <<<dim3(unsigned(int64_t(p.num_seqs) * p.h_v * (DV / kCombineCols))), dim3(256), 0, stream>>>(p);
         err = hipGetLastError();
         if (err != hipSuccess) return err;
         if (p.slots > 0) {
