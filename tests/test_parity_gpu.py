@@ -336,17 +336,22 @@ def test_split_and_resume_bitwise_at_64_multiples(split):
     assert torch.equal(c2, cso)
 
 
-def test_in_place_state_and_conv_state():
-    """final_state may alias initial_state and conv_state_out conv_state_in."""
+@pytest.mark.parametrize("segment_chunks", [0, 1])
+def test_in_place_state_and_conv_state(segment_chunks):
+    """final_state may alias initial_state and conv_state_out conv_state_in,
+    also with the segment split (the 700-token sequence as 11 one-chunk
+    segments run side by side: the conv history must be read before the
+    final conv state replaces it)."""
     geom = Geometry(2, 4, 128, 128)
-    x = prefill_inputs(44, [100, 7], geom, "bf16", initial_state_std=0.02, conv_state=True)
+    x = prefill_inputs(44, [700, 7], geom, "bf16", initial_state_std=0.02, conv_state=True)
     dt = TORCH_DT["bf16"]
     args = (dev(x.q, dt), dev(x.k, dt), dev(x.v, dt), dev(x.g), dev(x.beta), x.cu_seqlens.astype(np.int32).tolist())
     w = dev(x.conv_w, dt)
     h0, cs = dev(x.initial_state), dev(x.conv_state_in, dt)
-    o, fs, cso = binding.gdn_prefill_varlen(*args, conv_weight=w, conv_state=cs.clone(), initial_state=h0.clone())
+    o, fs, cso = binding.gdn_prefill_varlen(*args, conv_weight=w, conv_state=cs.clone(), initial_state=h0.clone(),
+                                            segment_chunks=segment_chunks)
     o2, fs2, cso2 = binding.gdn_prefill_varlen(*args, conv_weight=w, conv_state=cs, initial_state=h0,
-                                               final_state_out=h0, conv_state_out=cs)
+                                               final_state_out=h0, conv_state_out=cs, segment_chunks=segment_chunks)
     torch.cuda.synchronize()
     assert torch.equal(o, o2) and torch.equal(fs, h0) and torch.equal(cso, cs)
 
