@@ -19,7 +19,8 @@ workspace; they are split between the two prefill kernels by who reads or
 writes them (chunk-local kernel: q, k, g, beta; carry kernel: v, o, final
 recurrent and conv states, initial states).  The library records HIP events on
 its launch stream around each kernel (gdn_prefill_varlen_timed), so kernel
-times are measured live.  `roofline` is the dominant kernel, the cross-chunk
+times are measured live; the events are created without the system-scope
+fence (timing only), whose cache writeback at every record slowed each step.  `roofline` is the dominant kernel, the cross-chunk
 carry; `call` is the whole prefill.  A plain streaming device copy (the
 library's gdn_stream_copy) gives a measured HBM peak beside the datasheet's.
 
@@ -46,6 +47,60 @@ PREP_KERNEL = "prep_kernel"
 CARRY_KERNEL = "carry_kernel"
 DECODE_KERNEL = "decode_kernel"
 CHUNK = 64
+
+
+class TimingEvent:
+    """A HIP event used only for timing, created with hipEventDisableSystemFence:
+    recording it does no system-scope cache writeback and invalidation, which
+    with default events (torch's) cost ~10 us per step and slowed the kernel
+    after each record.  Results are read only after a full device
+    synchronisation.  The HIP runtime is the instance already mapped in the
+    process (the one torch and the library use).  `cuda_event` is the raw
+    handle the library's timed entry point records."""
+    _hip = None
+
+    @classmethod
+    def _runtime(cls):
+        if cls._hip is None:
+            import ctypes
+            path = None
+            with open("/proc/self/maps") as f:
+                for line in f:
+                    if "libamdhip64" in line:
+                        path = line.split()[-1]
+                        break
+            if path is None:
+                raise RuntimeError("the HIP runtime is not loaded")
+            hip = ctypes.CDLL(path)
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            cls._hip = hip
+        return cls._hip
+
+    def __init__(self):
+        import ctypes
+        h = ctypes.c_void_p()
+        err = self._runtime().hipEventCreateWithFlags(ctypes.byref(h), 0x20000000)  # hipEventDisableSystemFence
+        if err != 0 or not h.value:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({err})")
+        self.cuda_event = h.value
+
+    def record(self, stream):
+        import ctypes
+        err = self._runtime().hipEventRecord(ctypes.c_void_p(self.cuda_event), ctypes.c_void_p(stream.cuda_stream))
+        if err != 0:
+            raise RuntimeError(f"hipEventRecord failed ({err})")
+
+    def elapsed_time(self, end):
+        """Milliseconds from this event to `end` (both recorded and completed)."""
+        import ctypes
+        ms = ctypes.c_float()
+        err = self._runtime().hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(self.cuda_event),
+                                                  ctypes.c_void_p(end.cuda_event))
+        if err != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({err})")
+        return ms.value
 
 
 def roofline(nbytes, flops, seconds, kernel=None):
@@ -158,7 +213,7 @@ def extra_prefill(gdn, torch, dev, lengths, h_k, h_v, d, init_std, steps, seed, 
     fs = torch.empty((N, h_v, d, d), dtype=torch.float32, device=dev)
     prob = gdn.binding.make_problem(N, T, h_k, h_v, d, d, gdn.GDN_BF16, gdn.GDN_F32, segment_chunks=segment_chunks)
     ws = torch.empty(gdn.binding.gdn_prefill_workspace_bytes(prob), dtype=torch.uint8, device=dev)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    evs = [[TimingEvent() for _ in range(4)] for _ in range(steps)]
 
     def call(e=None):
         gdn.gdn_prefill_varlen(q, k, v, g, beta, cu, conv_weight=w, initial_state=h0, out=o, final_state_out=fs,
@@ -192,7 +247,7 @@ def stream_copy_peak(gdn, torch, dev, stream):
     src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
     dst = torch.empty_like(src)
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0, e1 = TimingEvent(), TimingEvent()
     best = None
     for per_cu in (2, 4, 8, 16):
         blocks = per_cu * cus
@@ -321,7 +376,7 @@ def main():
 
     # HIP events recorded by the library on its stream around each stage:
     # [before prep_kernel, before carry_kernel, after it, after the last launch]
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[TimingEvent() for _ in range(4)] for _ in range(args.steps)]
     print("[bench] device warm-up", file=sys.stderr, flush=True)
     dw_calls, t0 = 0, time.perf_counter()
     while (time.perf_counter() - t0) * 1e3 < args.device_warmup_ms:
@@ -435,7 +490,7 @@ def main():
         for s in range(max(4 * NPOOL, 20)):
             dstep(s % nsteps)
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0, e1 = TimingEvent(), TimingEvent()
         e0.record(stream)
         for s in range(nsteps):
             dstep(s)

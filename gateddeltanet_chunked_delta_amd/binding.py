@@ -166,8 +166,9 @@ def gdn_prefill_varlen(q, k, v, g, beta, cu_seqlens=None, *, conv_weight=None, c
     cu_seqlens); v: ``[T, h_v, d_v]``; g, beta: ``[T, h_v]`` fp32; cu_seqlens:
     int32 ``[N+1]`` on the device (or a CPU tensor / list, copied).  Returns
     ``(o, final_state or None, conv_state_out or None)``.  With ``events`` (four
-    ``torch.cuda.Event(enable_timing=True)``) the call goes through
-    ``gdn_prefill_varlen_timed``, which records them around its stages.
+    ``torch.cuda.Event(enable_timing=True)``, or objects holding a HIP event
+    handle in ``cuda_event``) the call goes through ``gdn_prefill_varlen_timed``,
+    which records them around its stages.
     ``segment_chunks > 0`` turns on the segment split of sequences longer than
     that many 64-token chunks (see ``gdn_problem.segment_chunks``).
     With ``noalloc=True`` the call goes through ``gdn_prefill_varlen_noalloc``
