@@ -53,25 +53,31 @@ def test_decode_multi_vs_oracle_with_rollback(oracle_mod, dtype, d):
     assert np.array_equal(got[untouched], pool_np[untouched])
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("beta_logits", [False, True])
-def test_decode_multi_bitwise_equals_single_steps(dtype, beta_logits):
+@pytest.mark.parametrize("dtype,beta_logits,d_k,d_v,out", [
+    ("bf16", False, 128, 128, "f32"), ("bf16", True, 128, 128, "f32"), ("f32", False, 128, 128, "f32"),
+    ("f32", True, 128, 128, "f32"), ("bf16", False, 128, 128, "bf16"), ("bf16", False, 128, 64, "f32"),
+    ("f32", True, 128, 64, "bf16"), ("bf16", False, 64, 128, "bf16"), ("bf16", True, 64, 64, "f32"),
+    ("f32", False, 64, 64, "bf16")])
+def test_decode_multi_bitwise_equals_single_steps(dtype, beta_logits, d_k, d_v, out):
     """m tokens in one call == m single-token gdn_decode_step calls, bit for
-    bit (outputs, recurrent states and conv states)."""
-    geom = Geometry(2, 4, 128, 128)
+    bit (outputs, recurrent states and conv states), at each head size (the
+    64-column instances sum their partials by quarter-waves) and output
+    dtype."""
+    geom = Geometry(2, 4, d_k, d_v)
     N, m = 6, 5
-    dt = TORCH_DT[dtype]
+    dt, odt = TORCH_DT[dtype], TORCH_DT[out]
     pool_a = dev(state_pool(61, N, geom))
     pool_b = pool_a.clone()
     cpool_a = dev(conv_state_pool(61, N, geom, dtype), dt)
     cpool_b = cpool_a.clone()
     w = dev(conv_weights(61, geom, dtype), dt)
     x = multi_decode_inputs(61, 0, N, m, geom, dtype)
-    o_multi = _multi(x, dt, pool_a, conv_weight=w, conv_state_pool=cpool_a, beta_logits=beta_logits)
+    o_multi = _multi(x, dt, pool_a, conv_weight=w, conv_state_pool=cpool_a, beta_logits=beta_logits,
+                     out_dtype=odt)
     for j in range(m):
         o_j = binding.gdn_decode_step(dev(x.q[:, j], dt), dev(x.k[:, j], dt), dev(x.v[:, j], dt), dev(x.g[:, j]),
                                       dev(x.beta[:, j]), pool_b, conv_weight=w, conv_state_pool=cpool_b,
-                                      beta_logits=beta_logits)
+                                      beta_logits=beta_logits, out_dtype=odt)
         assert torch.equal(o_multi[:, j], o_j), j
     assert torch.equal(pool_a, pool_b)
     assert torch.equal(cpool_a, cpool_b)
