@@ -519,9 +519,10 @@ def test_decode_steps_match_prefill(oracle_mod):
     assert np.array_equal(cpool.float().cpu().numpy(), cso_pre)
 
 
-def test_decode_batch_invariance_bitwise():
+@pytest.mark.parametrize("d_k,d_v", [(128, 128), (128, 64), (64, 64)])
+def test_decode_batch_invariance_bitwise(d_k, d_v):
     """A slot's output and state do not depend on which other slots share the call."""
-    geom = Geometry(16, 32, 128, 128)
+    geom = Geometry(16, 32, d_k, d_v)
     N = 64
     pool0 = dev(state_pool(52, N, geom))
     x = decode_inputs(52, 0, N, geom, "bf16")
